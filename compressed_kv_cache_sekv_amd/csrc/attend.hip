@@ -1,0 +1,443 @@
+// Decode attention over the SeKV two-resolution cache, gfx950.
+//
+// SeKV article (aitrends.kr/articles/75020), section 방법론 (Method), Stage 2
+// and Fig. 2: the routed spans are rebuilt to token level from their gated
+// factors and merged into the attention output; section 기술 상세 (Technical
+// details) gives the reconstruction Khat_S = sum_i m_i sigma_i u_i v_i^T.
+//
+// One workgroup (4 waves) per work item, partials per item, then a merge
+// kernel.  Items of kind 0 stream 64-row tiles of resident rows (raw tokens,
+// then one pseudo row per span); items of kind 1 take an equal share of the
+// union over the G query heads of a KV head's routed spans.  Per span the
+// reconstruction is never materialised:
+//     t = V^K^T q                    (R)      MFMA 16x16x32, A = V^K^T tile
+//     scores = U^K (t . sigma m^K)/sqrt(d)    MFMA 16x16x16, A = U^K tile
+//     w = U^V^T p                    (R)      MFMA 16x16x16, A = U^V^T tile
+//     o += V^V (sigma m^V . w)       (d)      MFMA 16x16x16, A = V^V tile
+// Each product's D operand (lane = head + 16*(row/4)) is the next product's
+// B operand, so values never leave registers.  Query heads of the GQA group
+// occupy the 16 MFMA columns (G of them live).  fp32 operands that feed a
+// bf16 MFMA (softmax weights, scaled t, gated w) are split hi + lo into two
+// bf16 terms, which keeps ~16 mantissa bits; every accumulation is fp32.
+#include "common.h"
+
+namespace sekv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mfma32(u32x4 a, u32x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(u32x2 a, u32x2 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                   __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_bits(x);
+  lo = bf16_bits(x - __uint_as_float(hi << 16));
+}
+__device__ __forceinline__ void pack4(const floatx4 v, u32x2& hi, u32x2& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split2(v[e], h[e], l[e]);
+  hi = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  lo = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+}
+__device__ __forceinline__ void pack8(const floatx4 a, const floatx4 b, u32x4& hi, u32x4& lo) {
+  u32x2 ha, la, hb, lb;
+  pack4(a, ha, la);
+  pack4(b, hb, lb);
+  hi = u32x4{ha[0], ha[1], hb[0], hb[1]};
+  lo = u32x4{la[0], la[1], lb[0], lb[1]};
+}
+
+__device__ __forceinline__ float xmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float xsum4(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Running softmax state of one lane: head hl = lane & 15; lanes that share hl
+// hold identical m and l.
+template <int ND16>
+struct Acc {
+  float m, l;
+  floatx4 o[ND16];  // o[dim = 16*db + 4*(lane/16) + r][head hl]
+};
+
+// Fold a block of scores (already scaled, masked to -inf) into the state and
+// return the softmax weights relative to the new running max.  `corr` is the
+// factor by which older accumulations must be scaled.
+template <int NB>
+__device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, float& l) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb)
+    if (tb < nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[tb][r]);
+  mx = xmax4(mx);
+  const float mnew = fmaxf(m, mx);
+  const float corr = (m == -INFINITY) ? 0.f : __expf(m - mnew);
+  float ps = 0.f;
+#pragma unroll
+  for (int tb = 0; tb < NB; ++tb)
+    if (tb < nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = sc[tb][r];
+        const float p = (x == -INFINITY) ? 0.f : __expf(x - mnew);
+        sc[tb][r] = p;
+        ps += p;
+      }
+  ps = xsum4(ps);
+  l = l * corr + ps;
+  m = mnew;
+  return corr;
+}
+
+template <int D, int G, int R>
+__global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+  constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
+  static_assert(G >= 1 && G <= 16, "G");
+  __shared__ float s_ml[4][2][G];
+  __shared__ float s_o[4][G][D];
+  __shared__ uint64_t s_uw[1024];
+  __shared__ int32_t s_pre[1025];
+
+  const WorkItem it = a.items[blockIdx.x];
+  const int lc = blockIdx.y, l = a.layer_begin + lc;
+  const int b = it.b, g = it.g;
+  const BMeta bm = a.meta[b];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hl = lane & 15, grp = lane >> 4;
+  const int Hq = a.Hq, Wd = a.W;
+
+  // query operand: B[k = dim][j = head]
+  u32x4 qB[NS32];
+  {
+    const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * Hq + g * G + hl) * D;
+#pragma unroll
+    for (int s = 0; s < NS32; ++s)
+      qB[s] = (hl < G) ? *(const u32x4*)(qp + 32 * s + 8 * grp) : u32x4{0, 0, 0, 0};
+  }
+  const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + lc) * Hq + g * G) * Wd;
+
+  Acc<ND16> acc;
+  acc.m = -INFINITY;
+  acc.l = 0.f;
+#pragma unroll
+  for (int db = 0; db < ND16; ++db) acc.o[db] = floatx4{0, 0, 0, 0};
+  const float scale = a.scale;
+
+  if (it.kind == 0) {
+    // ------------------------------------------------------ resident rows
+    const int64_t lg = (int64_t)l * a.Hkv + g;
+    const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
+    const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
+    const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
+    const int ntiles = bm.n_res_pad >> 6;
+    const int t_end = min(ntiles, (it.j + 1) * a.tpw);
+    for (int t = it.j * a.tpw + wave; t < t_end; t += 4) {
+      u32x4 kt[4][NS32], vt[2][ND16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s = 0; s < NS32; ++s)
+          kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(4 * t + kb) * 16 * D + s * 512 + lane * 8);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int db = 0; db < ND16; ++db)
+          vt[rb][db] = *(const u32x4*)(Vb + (int64_t)(2 * t + rb) * 32 * D + db * 512 + lane * 8);
+      floatx4 S[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        S[kb] = floatx4{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < NS32; ++s) S[kb] = mfma32(kt[kb][s], qB[s], S[kb]);
+      }
+      const int row0 = 64 * t;
+      const bool has_pseudo = row0 + 64 > bm.n_raw;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = row0 + 16 * kb + 4 * grp + r;
+          float x = S[kb][r] * scale;
+          if (hl >= G || row >= bm.n_res) {
+            x = -INFINITY;
+          } else if (has_pseudo && row >= bm.n_raw) {
+            const int sp = row - bm.n_raw;
+            const uint64_t word = mh[sp >> 6];
+            x = ((word >> (sp & 63)) & 1ull) ? -INFINITY : x + a.logn[bm.span_base + sp];
+          }
+          S[kb][r] = x;
+        }
+      const float corr = online<4>(S, 4, acc.m, acc.l);
+#pragma unroll
+      for (int db = 0; db < ND16; ++db) acc.o[db] *= corr;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        u32x4 phi, plo;
+        pack8(S[2 * rb], S[2 * rb + 1], phi, plo);
+#pragma unroll
+        for (int db = 0; db < ND16; ++db) {
+          acc.o[db] = mfma32(vt[rb][db], phi, acc.o[db]);
+          acc.o[db] = mfma32(vt[rb][db], plo, acc.o[db]);
+        }
+      }
+    }
+  } else {
+    // --------------------------------------------------- routed spans
+    // union over the G heads of this KV head, and its prefix counts
+    // (bits at or past N_S(b) are ignored, whatever the caller's mask holds)
+    for (int w = threadIdx.x; w < Wd; w += 256) {
+      uint64_t u = 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) u |= mrow[(int64_t)h * Wd + w];
+      const int left = bm.n_spans - 64 * w;
+      s_uw[w] = left >= 64 ? u : (left > 0 ? u & ((1ull << left) - 1) : 0ull);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int carry = 0;
+      for (int base = 0; base < Wd; base += 64) {
+        const int w = base + lane;
+        int v = (w < Wd) ? __popcll(s_uw[w]) : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(v, d);
+          if (lane >= d) v += y;
+        }
+        if (w < Wd) s_pre[w + 1] = carry + v;
+        carry += __shfl(v, 63);
+      }
+      if (lane == 0) s_pre[0] = 0;
+    }
+    __syncthreads();
+    const int U = s_pre[Wd];
+    const int beg = (int)((int64_t)it.j * U / it.nj), end = (int)((int64_t)(it.j + 1) * U / it.nj);
+    const int k0 = beg + (int)((int64_t)(end - beg) * wave / 4);
+    const int k1 = beg + (int)((int64_t)(end - beg) * (wave + 1) / 4);
+    if (k0 < k1) {
+      // locate rank k0: largest word w with s_pre[w] <= k0 and a set bit
+      int lo = 0, hi = Wd - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= k0) lo = mid; else hi = mid - 1;
+      }
+      int w = uni(lo);
+      uint64_t bits = s_uw[w];
+      for (int skip = k0 - s_pre[w]; skip > 0; --skip) bits &= bits - 1;
+      const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
+      const int64_t* roff = a.ring_off
+          ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans : nullptr;
+      for (int k = k0; k < k1; ++k) {
+        while (bits == 0 && w + 1 < Wd) bits = s_uw[++w];
+        if (bits == 0) break;  // unreachable when the ranks are consistent
+        const int bit = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        const int S = uni(64 * w + bit);
+        int hm = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) hm |= (int)((mrow[(int64_t)h * Wd + w] >> bit) & 1ull) << h;
+        const int n = uni(a.span_len[bm.span_base + S]);
+        const int npad = (n + 15) & ~15;
+        const uint8_t* blob = roff ? a.pool + roff[k] : region + a.span_off[bm.span_base + S];
+        const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt(R, D));
+        const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(R, D));
+        const float* smk = (const float*)(blob + Blob::off_smk(R, D));
+        const float* smv = (const float*)(blob + Blob::off_smv(R, D));
+        const bf16_t* uk = (const bf16_t*)(blob + Blob::off_uk(R, D));
+        const bf16_t* uvt = (const bf16_t*)(blob + Blob::off_uvt(R, D, n));
+
+        // t = V^K^T q, then c = t * sigma m^K / sqrt(d) split into bf16 hi + lo
+        u32x2 chi[NR16], clo[NR16];
+#pragma unroll
+        for (int ib = 0; ib < NR16; ++ib) {
+          floatx4 t = floatx4{0, 0, 0, 0};
+#pragma unroll
+          for (int s = 0; s < NS32; ++s)
+            t = mfma32(*(const u32x4*)(vkt + ib * 16 * D + s * 512 + lane * 8), qB[s], t);
+          const floatx4 sm = *(const floatx4*)(smk + 16 * ib + 4 * grp);
+          pack4(t * sm * scale, chi[ib], clo[ib]);
+        }
+        const bool act = (hl < G) && ((hm >> hl) & 1);
+        floatx4 wacc[NR16];
+#pragma unroll
+        for (int ib = 0; ib < NR16; ++ib) wacc[ib] = floatx4{0, 0, 0, 0};
+        const int ntb = npad >> 4;
+        for (int tb0 = 0; tb0 < ntb; tb0 += 4) {
+          const int nb = min(4, ntb - tb0);
+          floatx4 sc[4];
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            sc[tb] = floatx4{0, 0, 0, 0};
+            if (tb < nb) {
+#pragma unroll
+              for (int kb = 0; kb < NR16; ++kb) {
+                const u32x2 ukv = *(const u32x2*)(uk + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4);
+                sc[tb] = mfma16(ukv, chi[kb], sc[tb]);
+                sc[tb] = mfma16(ukv, clo[kb], sc[tb]);
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int tok = 16 * (tb0 + tb) + 4 * grp + r;
+                if (!act || tok >= n) sc[tb][r] = -INFINITY;
+              }
+            }
+          }
+          const float corr = online<4>(sc, nb, acc.m, acc.l);
+#pragma unroll
+          for (int db = 0; db < ND16; ++db) acc.o[db] *= corr;
+#pragma unroll
+          for (int ib = 0; ib < NR16; ++ib) wacc[ib] *= corr;
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            if (tb < nb) {
+              u32x2 phi, plo;
+              pack4(sc[tb], phi, plo);
+#pragma unroll
+              for (int ib = 0; ib < NR16; ++ib) {
+                const u32x2 uvv = *(const u32x2*)(uvt + ((int64_t)ib * ntb + tb0 + tb) * 256 + lane * 4);
+                wacc[ib] = mfma16(uvv, phi, wacc[ib]);
+                wacc[ib] = mfma16(uvv, plo, wacc[ib]);
+              }
+            }
+          }
+        }
+        // o += V^V (sigma m^V . w)
+        u32x2 whi[NR16], wlo[NR16];
+#pragma unroll
+        for (int ib = 0; ib < NR16; ++ib) {
+          const floatx4 sm = *(const floatx4*)(smv + 16 * ib + 4 * grp);
+          pack4(wacc[ib] * sm, whi[ib], wlo[ib]);
+        }
+#pragma unroll
+        for (int db = 0; db < ND16; ++db)
+#pragma unroll
+          for (int kb = 0; kb < NR16; ++kb) {
+            const u32x2 vvv = *(const u32x2*)(vv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+            acc.o[db] = mfma16(vvv, whi[kb], acc.o[db]);
+            acc.o[db] = mfma16(vvv, wlo[kb], acc.o[db]);
+          }
+      }
+    }
+  }
+
+  // ------------------------------------------- merge the 4 waves, write partial
+  if (hl < G) {
+    if (grp == 0) {
+      s_ml[wave][0][hl] = acc.m;
+      s_ml[wave][1][hl] = acc.l;
+    }
+#pragma unroll
+    for (int db = 0; db < ND16; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[wave][hl][16 * db + 4 * grp + r] = acc.o[db][r];
+  }
+  __syncthreads();
+  float* part = a.part + ((int64_t)lc * a.n_items + blockIdx.x) * G * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, dim = idx - h * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
+    float O = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_ml[w][0][h];
+      const float e = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+      O += e * s_o[w][h][dim];
+      L += e * s_ml[w][1][h];
+    }
+    part[h * (D + 2) + dim] = O;
+    if (dim == 0) {
+      part[h * (D + 2) + D] = M;
+      part[h * (D + 2) + D + 1] = L;
+    }
+  }
+}
+
+// Merge the partials of every item of (b, g) into out[b][lc][h][:].
+template <int D, int G>
+__global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
+  const int bg = blockIdx.x, lc = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int first = a.bg_first[bg];
+  const int count = a.items[first].part_count;
+  const float* base = a.part + ((int64_t)lc * a.n_items + first) * G * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, dim = idx - h * D;
+    float M = -INFINITY;
+    for (int i = 0; i < count; ++i) M = fmaxf(M, base[((int64_t)i * G + h) * (D + 2) + D]);
+    float O = 0.f, L = 0.f;
+    for (int i = 0; i < count; ++i) {
+      const float* p = base + ((int64_t)i * G + h) * (D + 2);
+      const float e = (p[D] == -INFINITY) ? 0.f : __expf(p[D] - M);
+      O += e * p[dim];
+      L += e * p[D + 1];
+    }
+    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
+  }
+}
+
+// ------------------------------------------------------------- dispatch
+#define SEKV_FOR_R(D, G)                                                     \
+  if (R == 16) return f(std::integral_constant<int, D>{}, std::integral_constant<int, G>{}, std::integral_constant<int, 16>{}); \
+  if (R == 32) return f(std::integral_constant<int, D>{}, std::integral_constant<int, G>{}, std::integral_constant<int, 32>{}); \
+  if (R == 64 && D >= 64) return f(std::integral_constant<int, D>{}, std::integral_constant<int, G>{}, std::integral_constant<int, 64>{});
+
+#define SEKV_FOR_G(D)   \
+  if (G == 1) { SEKV_FOR_R(D, 1) } \
+  if (G == 2) { SEKV_FOR_R(D, 2) } \
+  if (G == 4) { SEKV_FOR_R(D, 4) } \
+  if (G == 8) { SEKV_FOR_R(D, 8) }
+
+template <class F>
+static hipError_t dispatch(int D, int G, int R, F f) {
+  if (D == 64) { SEKV_FOR_G(64) }
+  if (D == 128) { SEKV_FOR_G(128) }
+  return hipErrorInvalidValue;
+}
+
+bool attend_supported(int D, int G, int R) {
+  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8) &&
+         (R == 16 || R == 32 || R == 64) && R <= D;
+}
+
+hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st) {
+  if (a.W > 1024) return hipErrorInvalidValue;
+  return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
+    hipLaunchKernelGGL((attend_kernel<decltype(d_)::value, decltype(g_)::value, decltype(r_)::value>),
+                       dim3(a.n_items, a.layer_count), dim3(256), 0, st, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int D, int G, hipStream_t st) {
+  return dispatch(D, G, 16, [&](auto d_, auto g_, auto) -> hipError_t {
+    hipLaunchKernelGGL((reduce_kernel<decltype(d_)::value, decltype(g_)::value>),
+                       dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace sekv

@@ -1,0 +1,213 @@
+// Internal definitions shared by the SeKV HIP kernels and the host runtime:
+// storage layouts in HBM, per-sequence metadata, kernel argument blocks and
+// launcher declarations.  Not part of the public ABI (include/sekv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sekv {
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------------------
+// Storage layouts.  Every matrix the decode kernel streams is stored in the
+// lane order of the MFMA operand that consumes it, so that one wave-wide
+// 16-byte (or 8-byte) load per lane reads 1 KB (512 B) of contiguous HBM.
+//
+// MFMA operand conventions used throughout (gfx950, wave64):
+//   v_mfma_f32_16x16x32_bf16  A[i][k]: lane = i + 16*(k/8), element k%8
+//                             B[k][j]: lane = j + 16*(k/8), element k%8
+//   v_mfma_f32_16x16x16_bf16  A[i][k]: lane = i + 16*(k/4), element k%4
+//                             B[k][j]: lane = j + 16*(k/4), element k%4
+//   both                      D[i][j]: lane = j + 16*(i/4), element i%4
+// ---------------------------------------------------------------------------
+
+// Row-major "K rows" (resident keys, and V^K^T of a span): A operand of
+// 16x16x32 with i = row within a 16-row block and k = dim within a 32-dim
+// slice.  Tiles ordered [row/16][dim/32][lane][8].
+__host__ __device__ inline int64_t krow_off(int64_t row, int dim, int D) {
+  const int i = (int)(row & 15), s = dim >> 5;
+  const int lane = i + 16 * ((dim & 31) >> 3), e = dim & 7;
+  return (row >> 4) * 16 * D + s * 512 + lane * 8 + e;
+}
+
+// Resident values: A operand of 16x16x32 computing O^T[dim][head] =
+// V^T[dim][rows] P[rows][head] over 32-row blocks.  k = 8*(lane/16) + e maps
+// to row 4*(lane/16) + e (e < 4) or 16 + 4*(lane/16) + e - 4 (e >= 4) of the
+// block, which is the row order in which the score MFMA leaves P in its
+// D operand.  Tiles ordered [row/32][dim/16][lane][8].
+__host__ __device__ inline int64_t vrow_off(int64_t row, int dim, int D) {
+  const int rr = (int)(row & 31), half = rr >> 4, rq = rr & 15;
+  const int lane = (dim & 15) + 16 * (rq >> 2), e = 4 * half + (rq & 3);
+  return (row >> 5) * 32 * D + (dim >> 4) * 512 + lane * 8 + e;
+}
+
+// A operand of 16x16x16 for a matrix with Kd columns (multiple of 16):
+// tiles ordered [i/16][k/16][lane][4].
+__host__ __device__ inline int64_t a16_off(int64_t i, int k, int Kd) {
+  const int lane = (int)(i & 15) + 16 * ((k & 15) >> 2), e = k & 3;
+  return ((i >> 4) * (Kd >> 4) + (k >> 4)) * 256 + lane * 4 + e;
+}
+
+// One span's factor blob (per layer and KV head), n_pad = n rounded up to 16:
+//   VKt  [R][d]   right key factors V^K^T        krow_off(i, dim, d)
+//   VV   [d][R]   right value factors V^V        a16_off(dim, i, R)
+//   smK  [R] fp32 sigma^K * m^K
+//   smV  [R] fp32 sigma^V * m^V
+//   UK   [n_pad][R] left key factors U^K         a16_off(t, i, R)
+//   UVt  [R][n_pad] left value factors U^V^T     a16_off(i, t, n_pad)
+// Rows/cols past n are zero.  Blobs start on 256-byte boundaries.
+struct Blob {
+  static __host__ __device__ inline int npad(int n) { return (n + 15) & ~15; }
+  static __host__ __device__ inline int64_t off_vkt(int, int) { return 0; }
+  static __host__ __device__ inline int64_t off_vv(int R, int D) { return 2LL * R * D; }
+  static __host__ __device__ inline int64_t off_smk(int R, int D) { return 4LL * R * D; }
+  static __host__ __device__ inline int64_t off_smv(int R, int D) { return 4LL * R * D + 4LL * R; }
+  static __host__ __device__ inline int64_t off_uk(int R, int D) { return 4LL * R * D + 8LL * R; }
+  static __host__ __device__ inline int64_t off_uvt(int R, int D, int n) {
+    return off_uk(R, D) + 2LL * npad(n) * R;
+  }
+  static __host__ __device__ inline int64_t bytes(int R, int D, int n) {
+    return (off_uvt(R, D, n) + 2LL * npad(n) * R + 255) & ~255LL;
+  }
+  // algorithmic bytes of one span: 4R(n + d) + 8R (no padding)
+  static __host__ __device__ inline int64_t alg_bytes(int R, int D, int n) {
+    return 4LL * R * (n + D) + 8LL * R;
+  }
+};
+
+// Per-sequence metadata (device copy used by every kernel).
+struct BMeta {
+  int32_t n_spans;      // N_S(b)
+  int32_t n_raw;        // N_raw(b)
+  int32_t n_res;        // N_raw + N_S
+  int32_t n_res_pad;    // n_res rounded up to 64
+  int32_t s_pad;        // N_S rounded up to 64 (stride of s rows)
+  int32_t pad_;
+  int64_t span_base;    // first span of b in the span tables
+  int64_t raw_base;     // first raw token of b in raw_pos
+  int64_t tok_base;     // first token of b's spans in the concatenated U order
+  int64_t res_base;     // element offset of (b, l=0, g=0) in K/V resident rows
+  int64_t s_base;       // element offset of (b, l=0, h=0) in s
+  int64_t pool_base;    // byte offset of (b, g=0) within a layer's factor region
+  int64_t pool_lg;      // bytes per (l, g) factor region of b; the region of
+                        // (b, l, g) starts at l * layer_bytes + pool_base + g * pool_lg
+};
+
+// Decode work: one workgroup of 4 waves per item.  kind 0: resident rows
+// tiles [j*tpw, (j+1)*tpw); kind 1: the j-th of nj shares of the union of
+// the routed spans of (b, l, g).
+struct WorkItem {
+  int32_t b, g, kind, j, nj;
+  int32_t part_first;   // first item of (b, g) (partials of (b, g) are contiguous)
+  int32_t part_count;   // items of (b, g)
+  int32_t pad_;
+};
+
+struct AttendArgs {
+  const bf16_t* q;          // [B][Lc][Hq][D]
+  const uint64_t* mask;     // [B][Lc][Hq][W]
+  const BMeta* meta;
+  const WorkItem* items;
+  const bf16_t* kres;
+  const bf16_t* vres;
+  const float* logn;        // [span] ln n_S
+  const int32_t* span_len;  // [span]
+  const int64_t* span_off;  // [span] byte offset of the blob in its (b, l, g) region
+  const uint8_t* pool;      // factor pool (HBM tier) or staging ring
+  const int64_t* ring_off;  // ring tier: [Lc][B][Hkv][max_spans] offset of the
+                            // k-th union span's blob in the ring, else NULL
+  float* part;              // [Lc][n_items][G][D + 2]
+  int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
+  int32_t layer_begin, layer_count, n_items;
+  int32_t B, L, Hq, Hkv, W, max_spans;
+  int32_t tpw;              // resident 64-row tiles per work item
+  float scale;              // 1/sqrt(d)
+};
+
+struct ReduceArgs {
+  const float* part;
+  const WorkItem* items;
+  const int32_t* bg_first;  // [B*Hkv] first item of (b, g)
+  float* out;               // [B][Lc][Hq][D]
+  int32_t layer_count, n_items, B, Hq, Hkv;
+};
+
+struct RouteArgs {
+  const bf16_t* q;          // [B][Lc][Hq][D]
+  const float* tau;         // [Lc][Hq]
+  const float* W;           // [L][Hq][dp][D]
+  const float* s;
+  const BMeta* meta;
+  uint64_t* mask;           // [B][Lc][Hq][Wd]
+  float* alpha;             // [B][Lc][Hq][Wd*64] (scratch or caller)
+  uint32_t* tickets;        // [B][Lc][Hq]
+  int32_t layer_begin, layer_count;
+  int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
+};
+
+struct CalibArgs {
+  const float* alpha;       // [B][Lc][Hq][Wd*64]
+  const BMeta* meta;
+  float* tau_out;           // [Lc][Hq]
+  int32_t layer_count, B, Hq, Wd;
+  float frac;
+};
+
+// ------------------------------------------------------------ launchers ---
+hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st);
+hipError_t launch_reduce(const ReduceArgs& a, int D, int G, hipStream_t st);
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st);
+bool attend_supported(int D, int G, int R);
+
+struct SplitArgs {
+  const float* H;           // [B][T]
+  int32_t* span_start;      // [B][S_max]
+  int32_t* span_len;        // [B][S_max]
+  float* span_logn;         // [B][S_max]
+  int32_t* raw_pos;         // [B][T]
+  int32_t* counts;          // [B][2] (N_S, N_raw)
+  int32_t* scratch;         // [B][2][T/2 + 2]
+  int32_t B, T, S_max, l_min;
+  double alpha_sp;
+};
+hipError_t launch_span_split(const SplitArgs& a, hipStream_t st);
+
+struct PackArgs {
+  const bf16_t* K;          // [B][L][Hkv][T][D]
+  const bf16_t* V;
+  const float* H;           // [B][T]
+  const float* W;           // [L][Hq][dp][D]
+  const float* gates;       // [B][L][Hkv][2][S_max][R] or NULL
+  const BMeta* meta;
+  const int32_t* span_start;  // concatenated over b
+  const int32_t* span_len;
+  const int32_t* raw_pos;
+  const int64_t* span_off;
+  bf16_t* kres;
+  bf16_t* vres;
+  float* s;
+  uint8_t* pool;            // device factor destination: one layer's region
+                            // (pool + layer * layer_bytes, or a staging buffer)
+  int32_t B, L, Hq, Hkv, D, T, R, dp, S_max;
+  int32_t layer;            // layer for the per-layer SVD launch
+  int32_t max_raw, max_spans;
+  int32_t oversample, power_iters;
+  uint64_t seed;
+  // batched mode (sekv_rsvd_batched): matrices given directly, fp32 outputs
+  const bf16_t* A;
+  const int64_t* mat_row_off;
+  const int32_t* mat_rows;
+  float* out_U;             // [count][max_rows][R]
+  float* out_S;             // [count][R]
+  float* out_Vt;            // [count][R][D]
+  int32_t count, max_rows;
+};
+hipError_t launch_pack_raw(const PackArgs& a, hipStream_t st);
+hipError_t launch_summaries(const PackArgs& a, hipStream_t st);
+hipError_t launch_rsvd(const PackArgs& a, hipStream_t st);
+hipError_t launch_rsvd_batched(const PackArgs& a, hipStream_t st);
+
+}  // namespace sekv

@@ -1,0 +1,231 @@
+// Stage 1 routing of the SeKV decode step, gfx950.
+//
+// SeKV article (aitrends.kr/articles/75020), section 방법론 (Method): the query
+// q^(l,h) is mapped by the routing projection W^(l,h), dotted with each span's
+// summary key, squashed by a sigmoid into alpha_S^(l,h) and compared with the
+// per-(layer, head) threshold tau^(l,h) to decide z_S^(l,h).  Section
+// 기술 상세 (Technical details): on budget overflow spans are taken in
+// descending alpha until the GPU budget holds (here a per-(layer, head) cap,
+// ties to the lower span index).
+//
+// One workgroup per (b, 256-span chunk, head, layer); each wave scores 64
+// spans, one per lane, and writes one mask word with a ballot.  When a cap is
+// given, the last workgroup of a (b, l, h) to finish (atomic ticket) counts
+// the expansions and, on overflow, keeps the cap largest alpha by a 4-pass
+// 8-bit radix select on the fp32 bit patterns (alpha >= 0, so bit order is
+// value order).
+#include "common.h"
+
+namespace sekv {
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+// Loads that bypass the (non-coherent) L1: data written by other workgroups
+// of the same launch, published by __threadfence() + the ticket atomic.
+__device__ __forceinline__ uint32_t ld_u32(const float* p) {
+  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
+  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block-wide inclusive scan of one int per thread (256 threads).
+__device__ int block_scan256(int v, int* s_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += s_tmp[w];
+  __syncthreads();
+  return v + add;
+}
+
+// Find the k-th largest key (1-based) among candidates; candidates are given
+// by the functor `cand(i, key&)` over i in [0, n).  Returns the key and sets
+// k to the rank of the answer among the keys equal to it (1-based).
+template <class Cand>
+__device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int* s_sel) {
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += 256) s_hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) {
+      uint32_t key;
+      if (cand(i, key) && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int cum = 0, digit = 0;
+      for (int bin = 255; bin >= 0; --bin) {
+        const int c = (int)s_hist[bin];
+        if (cum + c >= k) { digit = bin; break; }
+        cum += c;
+      }
+      s_sel[0] = digit;
+      s_sel[1] = k - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    pmask |= 255u << shift;
+    k = s_sel[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
+  __shared__ float s_u[256];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_tmp[8];
+  __shared__ int s_sel[2];
+  __shared__ int s_last;
+  const int nchunk = (a.Wd + 3) >> 2;
+  const int b = blockIdx.x / nchunk, chunk = blockIdx.x - b * nchunk;
+  const int h = blockIdx.y, lc = blockIdx.z, l = a.layer_begin + lc;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const BMeta bm = a.meta[b];
+  const int D = a.D, dp = a.dp;
+
+  // u = W^(l,h) q^(l,h), fp32
+  const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
+  const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
+  for (int j = wave; j < dp; j += 4) {
+    float acc = 0.f;
+    for (int d = lane; d < D; d += 64) acc += Wl[(int64_t)j * D + d] * bf16_to_f32(qp[d]);
+    acc = wave_sum(acc);
+    if (lane == 0) s_u[j] = acc;
+  }
+  __syncthreads();
+
+  const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
+  uint64_t* mrow = a.mask + row * a.Wd;
+  float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
+  const float tau = a.tau[lc * a.Hq + h];
+  const int wi = chunk * 4 + wave;
+  if (wi < a.Wd) {
+    const int S = 64 * wi + lane;
+    float alpha = 0.f;
+    bool z = false;
+    if (S < bm.n_spans) {
+      const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + S;
+      float dot = 0.f;
+      for (int j = 0; j < dp; ++j) dot += s_u[j] * sp[(int64_t)j * bm.s_pad];
+      alpha = 1.f / (1.f + expf(-dot));
+      z = alpha > tau;
+    }
+    const uint64_t word = __ballot(z);
+    if (lane == 0) mrow[wi] = word;
+    if (arow) arow[S] = alpha;
+  }
+  if (a.cap <= 0) return;
+
+  // ------------------------------------------------ budget cap (last block)
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = atomicAdd(&a.tickets[row], 1u);
+    s_last = (t == (uint32_t)nchunk - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  int cnt = 0;
+  for (int w = threadIdx.x; w < a.Wd; w += 256) cnt += __popcll(ld_u64(mrow + w));
+  cnt = block_scan256(cnt, s_tmp);
+  if (threadIdx.x == 255) s_sel[0] = cnt;
+  __syncthreads();
+  const int total = s_sel[0];
+  __syncthreads();
+  if (total > a.cap) {
+    int k = a.cap;
+    auto cand = [&](int S, uint32_t& key) -> bool {
+      const uint64_t word = ld_u64(mrow + (S >> 6));
+      if (!((word >> (S & 63)) & 1ull)) return false;
+      key = ld_u32(arow + S);
+      return true;
+    };
+    const uint32_t vstar = radix_select(bm.n_spans, k, cand, s_hist, s_sel);
+    // k = number of spans with alpha == vstar to keep, lowest span index first
+    int carry = 0;
+    for (int base = 0; base < a.Wd; base += 256) {
+      const int ww = base + threadIdx.x;
+      int tw = 0;
+      uint64_t zz = 0;
+      if (ww < a.Wd) {
+        zz = ld_u64(mrow + ww);
+        for (uint64_t bits = zz; bits; bits &= bits - 1)
+          tw += (ld_u32(arow + 64 * ww + __builtin_ctzll(bits)) == vstar);
+      }
+      const int incl = block_scan256(tw, s_tmp);
+      int rank = carry + incl - tw;
+      if (ww < a.Wd) {
+        uint64_t keep = 0;
+        for (uint64_t bits = zz; bits; bits &= bits - 1) {
+          const int bit = __builtin_ctzll(bits);
+          const uint32_t key = ld_u32(arow + 64 * ww + bit);
+          if (key > vstar) keep |= 1ull << bit;
+          else if (key == vstar) {
+            if (rank < k) keep |= 1ull << bit;
+            ++rank;
+          }
+        }
+        mrow[ww] = keep;
+      }
+      if (threadIdx.x == 255) s_sel[0] = incl;
+      __syncthreads();
+      carry += s_sel[0];
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) a.tickets[row] = 0u;
+}
+
+// tau^(l,h): midpoint of the k-th and (k+1)-th largest alpha over every
+// (b, span), k = round(frac * N) clipped to [1, N - 1].
+__global__ __launch_bounds__(256) void calibrate_kernel(const CalibArgs a) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_sel[2];
+  const int h = blockIdx.x, lc = blockIdx.y;
+  int64_t N = 0;
+  for (int b = 0; b < a.B; ++b) N += a.meta[b].n_spans;
+  int k = (int)floor((double)a.frac * (double)N + 0.5);
+  k = max(1, min(k, (int)N - 1));
+  // flatten (b, S) into one index range via a per-b walk
+  auto cand = [&](int i, uint32_t& key) -> bool {
+    int b = 0, rem = i;
+    while (b < a.B && rem >= a.meta[b].n_spans) { rem -= a.meta[b].n_spans; ++b; }
+    if (b >= a.B) return false;
+    key = __float_as_uint(a.alpha[(((int64_t)b * a.layer_count + lc) * a.Hq + h) * (int64_t)a.Wd * 64 + rem]);
+    return true;
+  };
+  int k1 = k, k2 = k + 1;
+  const uint32_t v1 = radix_select((int)N, k1, cand, s_hist, s_sel);
+  const uint32_t v2 = radix_select((int)N, k2, cand, s_hist, s_sel);
+  if (threadIdx.x == 0)
+    a.tau_out[lc * a.Hq + h] = 0.5f * (__uint_as_float(v1) + __uint_as_float(v2));
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  const int nchunk = (a.Wd + 3) >> 2;
+  hipLaunchKernelGGL(route_kernel, dim3(a.B * nchunk, a.Hq, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(calibrate_kernel, dim3(a.Hq, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sekv

@@ -1,0 +1,966 @@
+// Host runtime of the SeKV C ABI (include/sekv.h): contexts, index build /
+// import / export, routing and decode orchestration, and the pinned-tier
+// gather into the HBM staging ring.
+//
+// SeKV article (aitrends.kr/articles/75020): section 방법론 (Method) and its
+// Fig. 2 describe the two tiers (summaries and anchors on the GPU, truncated
+// SVD factors on the CPU) and the asynchronous CPU->GPU transfer of the routed
+// spans' factors; section 한계점 (Limitations) names the CPU-GPU bandwidth
+// dependency, which is why the gather is timed and counted on its own.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/sekv.h"
+#include "common.h"
+
+using namespace sekv;
+
+namespace {
+
+thread_local std::string g_err;
+
+sekv_status fail(sekv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(e_ == hipErrorOutOfMemory ? SEKV_ENOMEM : SEKV_EHIP, "%s: %s (%s:%d)", \
+                  #expr, hipGetErrorString(e_), __FILE__, __LINE__);                     \
+  } while (0)
+
+constexpr uint32_t CTX_MAGIC = 0x53454b43u;   // "SEKC"
+constexpr uint32_t IDX_MAGIC = 0x53454b49u;   // "SEKI"
+constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
+
+// Work decomposition of the decode kernel.
+constexpr int kTilesPerItem = 4;     // resident 64-row tiles per workgroup (1 per wave)
+constexpr int kSpansPerFacItem = 32; // factored workgroups per KV head = ceil(N_S / 32)
+
+// Device buffer owned by the library.
+struct DBuf {
+  void* p = nullptr;
+  size_t n = 0;
+  void release() {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+    n = 0;
+  }
+};
+
+hipError_t dalloc(DBuf& b, size_t bytes) {
+  b.release();
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(&b.p, bytes);
+  if (e == hipSuccess) b.n = bytes;
+  else b.p = nullptr;
+  return e;
+}
+
+hipError_t dgrow(DBuf& b, size_t bytes) {
+  if (b.p && b.n >= bytes) return hipSuccess;
+  return dalloc(b, bytes);
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+struct sekv_ctx {
+  uint32_t magic = CTX_MAGIC;
+  int device = 0;
+  hipStream_t stream = nullptr;
+};
+
+struct sekv_index {
+  uint32_t magic = IDX_MAGIC;
+  sekv_ctx* ctx = nullptr;
+  int B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, R = 0, dp = 0, G = 0, tier = 0;
+  int max_spans = 0, Wd = 0, max_raw = 0;
+  int64_t total_spans = 0, total_raw = 0, total_tok = 0;
+  int64_t layer_bytes = 0, pool_bytes = 0;
+  int64_t kres_elems = 0, s_elems = 0;
+  std::vector<BMeta> meta;
+  std::vector<int32_t> h_span_len;      // concatenated span lengths
+  std::vector<int64_t> h_span_off;      // concatenated blob offsets in the (b, l, g) region
+  // device
+  DBuf d_meta, d_span_start, d_span_len, d_logn, d_span_off, d_raw_pos;
+  DBuf d_kres, d_vres, d_s, d_W;
+  DBuf d_pool;                 // HBM tier
+  uint8_t* h_pool = nullptr;   // pinned tier
+  DBuf d_ring, d_ring_off;
+  int64_t ring_bytes = 0;
+  std::vector<int64_t> h_ring_off;
+  int64_t* h_ring_off_pinned = nullptr;
+  size_t h_ring_off_cap = 0;
+  uint64_t* h_mask_pinned = nullptr;
+  size_t h_mask_cap = 0;
+  // decode work
+  std::vector<WorkItem> items;
+  std::vector<int32_t> bg_first;
+  DBuf d_items, d_bg_first, d_part;
+  // routing scratch
+  DBuf d_alpha, d_tickets, d_tau_inf;
+  int tickets_lc = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+};
+
+namespace {
+
+sekv_status check_ctx(const sekv_ctx* c) {
+  if (!c) return fail(SEKV_EINVAL, "null context");
+  if (c->magic != CTX_MAGIC) return fail(SEKV_ESTATE, "context is not live");
+  return SEKV_OK;
+}
+
+sekv_status check_idx(const sekv_ctx* c, const sekv_index* x) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if (!x) return fail(SEKV_EINVAL, "null index");
+  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  if (x->ctx != c) return fail(SEKV_ESTATE, "index belongs to another context");
+  return SEKV_OK;
+}
+
+sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
+  if (!p) return fail(SEKV_EINVAL, "null params");
+  if (p->B < 1 || p->L < 1 || p->Hq < 1 || p->Hkv < 1 || p->T < 1)
+    return fail(SEKV_EINVAL, "B, L, Hq, Hkv, T must be >= 1");
+  if (p->Hq % p->Hkv) return fail(SEKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+  if (p->dprime < 1 || p->dprime > 256) return fail(SEKV_EINVAL, "dprime must be in [1, 256]");
+  if (p->R < 1 || p->R > p->d) return fail(SEKV_EINVAL, "R must be in [1, d]");
+  if (!attend_supported(p->d, p->Hq / p->Hkv, p->R))
+    return fail(SEKV_EUNSUPPORTED, "unsupported shape d=%d G=%d R=%d (d in {64,128}, G in {1,2,4,8}, R in {16,32,64})",
+                p->d, p->Hq / p->Hkv, p->R);
+  if (p->tier != SEKV_TIER_HBM && p->tier != SEKV_TIER_PINNED_HOST) return fail(SEKV_EINVAL, "bad tier");
+  if (p->ring_bytes < 0) return fail(SEKV_EINVAL, "ring_bytes < 0");
+  if (need_build_fields) {
+    if (p->l_min < 1) return fail(SEKV_EINVAL, "l_min must be >= 1");
+    if (!(p->alpha_sp == p->alpha_sp) || std::isinf(p->alpha_sp)) return fail(SEKV_EINVAL, "alpha_sp must be finite");
+    if (p->oversample < 0 || p->oversample > 16) return fail(SEKV_EINVAL, "oversample must be in [0, 16]");
+    if (p->power_iters < 0 || p->power_iters > 8) return fail(SEKV_EINVAL, "power_iters must be in [0, 8]");
+  }
+  const int64_t smax = (int64_t)(p->T + 1) / (p->l_min > 0 ? p->l_min + 1 : 2);
+  if ((smax + 63) / 64 > 1024) return fail(SEKV_EUNSUPPORTED, "T too large for l_min (more than 65536 spans possible)");
+  return SEKV_OK;
+}
+
+// Fill shape fields and the per-sequence layout from span counts/lengths.
+// n_spans, n_raw: per b; lens: concatenated span lengths.
+void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<int32_t>& n_spans,
+                 const std::vector<int32_t>& n_raw, const std::vector<int32_t>& lens) {
+  x->B = p->B; x->L = p->L; x->Hq = p->Hq; x->Hkv = p->Hkv; x->D = p->d; x->R = p->R;
+  x->dp = p->dprime; x->G = p->Hq / p->Hkv; x->tier = p->tier;
+  x->meta.assign(x->B, BMeta{});
+  x->h_span_len = lens;
+  x->h_span_off.assign(lens.size(), 0);
+  int64_t sb = 0, rb = 0, tb = 0, res = 0, sel = 0, pb = 0;
+  x->max_spans = 0; x->max_raw = 0;
+  for (int b = 0; b < x->B; ++b) {
+    BMeta& m = x->meta[b];
+    m.n_spans = n_spans[b];
+    m.n_raw = n_raw[b];
+    m.n_res = m.n_spans + m.n_raw;
+    m.n_res_pad = (int32_t)round_up(std::max(m.n_res, 1), 64);
+    m.s_pad = (int32_t)round_up(std::max(m.n_spans, 1), 64);
+    m.span_base = sb;
+    m.raw_base = rb;
+    m.tok_base = tb;
+    m.res_base = res;
+    m.s_base = sel;
+    int64_t off = 0;
+    for (int S = 0; S < m.n_spans; ++S) {
+      x->h_span_off[sb + S] = off;
+      off += Blob::bytes(x->R, x->D, lens[sb + S]);
+      tb += lens[sb + S];
+    }
+    m.pool_lg = off;
+    m.pool_base = pb;
+    pb += off * x->Hkv;
+    sb += m.n_spans;
+    rb += m.n_raw;
+    res += (int64_t)x->L * x->Hkv * m.n_res_pad * x->D;
+    sel += (int64_t)x->L * x->Hq * x->dp * m.s_pad;
+    x->max_spans = std::max(x->max_spans, m.n_spans);
+    x->max_raw = std::max(x->max_raw, m.n_raw);
+  }
+  x->total_spans = sb;
+  x->total_raw = rb;
+  x->total_tok = tb;
+  x->kres_elems = res;
+  x->s_elems = sel;
+  x->layer_bytes = pb;
+  x->pool_bytes = pb * x->L;
+  x->Wd = std::max(1, (x->max_spans + 63) / 64);
+  // decode work items, contiguous per (b, g)
+  x->items.clear();
+  x->bg_first.assign((size_t)x->B * x->Hkv, 0);
+  for (int b = 0; b < x->B; ++b) {
+    const BMeta& m = x->meta[b];
+    const int ntiles = m.n_res_pad / 64;
+    const int nres = (ntiles + kTilesPerItem - 1) / kTilesPerItem;
+    const int nfac = m.n_spans ? (m.n_spans + kSpansPerFacItem - 1) / kSpansPerFacItem : 0;
+    for (int g = 0; g < x->Hkv; ++g) {
+      const int first = (int)x->items.size();
+      x->bg_first[(size_t)b * x->Hkv + g] = first;
+      for (int j = 0; j < nres; ++j) x->items.push_back(WorkItem{b, g, 0, j, nres, first, nres + nfac, 0});
+      for (int j = 0; j < nfac; ++j) x->items.push_back(WorkItem{b, g, 1, j, nfac, first, nres + nfac, 0});
+    }
+  }
+}
+
+// Allocate and clear the device (and pinned) storage of a planned index.
+sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
+  const size_t nsp = (size_t)std::max<int64_t>(x->total_spans, 1);
+  HIP_TRY(dalloc(x->d_meta, sizeof(BMeta) * x->B));
+  HIP_TRY(dalloc(x->d_span_start, 4 * nsp));
+  HIP_TRY(dalloc(x->d_span_len, 4 * nsp));
+  HIP_TRY(dalloc(x->d_logn, 4 * nsp));
+  HIP_TRY(dalloc(x->d_span_off, 8 * nsp));
+  HIP_TRY(dalloc(x->d_raw_pos, 4 * (size_t)std::max<int64_t>(x->total_raw, 1)));
+  HIP_TRY(dalloc(x->d_kres, 2 * (size_t)x->kres_elems));
+  HIP_TRY(dalloc(x->d_vres, 2 * (size_t)x->kres_elems));
+  HIP_TRY(dalloc(x->d_s, 4 * (size_t)x->s_elems));
+  HIP_TRY(dalloc(x->d_W, 4 * (size_t)x->L * x->Hq * x->dp * x->D));
+  hipStream_t st = x->ctx->stream;
+  HIP_TRY(hipMemsetAsync(x->d_kres.p, 0, x->d_kres.n, st));
+  HIP_TRY(hipMemsetAsync(x->d_vres.p, 0, x->d_vres.n, st));
+  HIP_TRY(hipMemsetAsync(x->d_s.p, 0, x->d_s.n, st));
+  if (x->tier == SEKV_TIER_HBM) {
+    HIP_TRY(dalloc(x->d_pool, (size_t)x->pool_bytes));
+    HIP_TRY(hipMemsetAsync(x->d_pool.p, 0, x->d_pool.n, st));
+  } else {
+    const size_t pb = (size_t)std::max<int64_t>(x->pool_bytes, 256);
+    hipError_t e = hipHostMalloc((void**)&x->h_pool, pb, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      x->h_pool = nullptr;
+      return fail(SEKV_ENOMEM, "pinned host pool of %zu bytes: %s", pb, hipGetErrorString(e));
+    }
+    memset(x->h_pool, 0, pb);
+    x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : std::max<int64_t>(x->layer_bytes, 256);
+    HIP_TRY(dalloc(x->d_ring, (size_t)x->ring_bytes));
+  }
+  HIP_TRY(hipMemcpyAsync(x->d_meta.p, x->meta.data(), sizeof(BMeta) * x->B, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(x->d_span_len.p, x->h_span_len.data(), 4 * x->h_span_len.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(x->d_span_off.p, x->h_span_off.data(), 8 * x->h_span_off.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(dalloc(x->d_items, sizeof(WorkItem) * std::max<size_t>(x->items.size(), 1)));
+  HIP_TRY(dalloc(x->d_bg_first, 4 * x->bg_first.size()));
+  HIP_TRY(hipMemcpyAsync(x->d_items.p, x->items.data(), sizeof(WorkItem) * x->items.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(x->d_bg_first.p, x->bg_first.data(), 4 * x->bg_first.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventCreate(&x->ev0));
+  HIP_TRY(hipEventCreate(&x->ev1));
+  return SEKV_OK;
+}
+
+void free_index(sekv_index* x) {
+  if (!x) return;
+  if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
+  DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
+                  &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
+                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part,
+                  &x->d_alpha, &x->d_tickets, &x->d_tau_inf};
+  for (DBuf* b : bufs) b->release();
+  if (x->h_pool) (void)hipHostFree(x->h_pool);
+  if (x->h_ring_off_pinned) (void)hipHostFree(x->h_ring_off_pinned);
+  if (x->h_mask_pinned) (void)hipHostFree(x->h_mask_pinned);
+  if (x->ev0) (void)hipEventDestroy(x->ev0);
+  if (x->ev1) (void)hipEventDestroy(x->ev1);
+  x->magic = DEAD_MAGIC;
+  delete x;
+}
+
+struct IndexGuard {
+  sekv_index* x;
+  ~IndexGuard() { if (x) free_index(x); }
+};
+
+sekv_status set_device(sekv_ctx* c) {
+  HIP_TRY(hipSetDevice(c->device));
+  return SEKV_OK;
+}
+
+sekv_status ensure_route_scratch(sekv_index* x, int lc) {
+  const size_t rows = (size_t)x->B * lc * x->Hq;
+  HIP_TRY(dgrow(x->d_alpha, rows * x->Wd * 64 * sizeof(float)));
+  if (!x->d_tickets.p || x->tickets_lc < lc) {
+    HIP_TRY(dalloc(x->d_tickets, rows * sizeof(uint32_t)));
+    HIP_TRY(hipMemsetAsync(x->d_tickets.p, 0, x->d_tickets.n, x->ctx->stream));
+    x->tickets_lc = lc;
+  }
+  return SEKV_OK;
+}
+
+sekv_status check_layers(const sekv_index* x, int lb, int lc) {
+  if (lb < 0 || lc < 1 || lb + lc > x->L)
+    return fail(SEKV_EINVAL, "layer range [%d, %d) outside [0, %d)", lb, lb + lc, x->L);
+  return SEKV_OK;
+}
+
+}  // namespace
+
+// ============================================================== lifecycle ===
+
+extern "C" sekv_status sekv_create(int32_t device, void* stream, sekv_ctx** out) {
+  if (!out) return fail(SEKV_EINVAL, "null out");
+  *out = nullptr;
+  int n = 0;
+  HIP_TRY(hipGetDeviceCount(&n));
+  if (device < 0 || device >= n) return fail(SEKV_EINVAL, "device %d not in [0, %d)", device, n);
+  HIP_TRY(hipSetDevice(device));
+  sekv_ctx* c = new sekv_ctx();
+  c->device = device;
+  c->stream = (hipStream_t)stream;
+  *out = c;
+  return SEKV_OK;
+}
+
+extern "C" void sekv_destroy(sekv_ctx* c) {
+  if (!c || c->magic != CTX_MAGIC) return;
+  (void)hipSetDevice(c->device);
+  (void)hipStreamSynchronize(c->stream);
+  c->magic = DEAD_MAGIC;
+  delete c;
+}
+
+extern "C" const char* sekv_last_error(void) { return g_err.c_str(); }
+
+extern "C" int32_t sekv_max_spans(int32_t T, int32_t l_min) {
+  if (T < 1 || l_min < 1) return 0;
+  return (int32_t)(((int64_t)T + 1) / ((int64_t)l_min + 1));
+}
+
+extern "C" sekv_status sekv_validate_params(const sekv_build_params* p) { return check_shape(p, true); }
+
+extern "C" sekv_status sekv_rsvd_batched(sekv_ctx* c, int32_t count, const void* A, const int64_t* row_off,
+                                         const int32_t* rows, int32_t max_rows, int32_t d, int32_t R,
+                                         int32_t oversample, int32_t power_iters, uint64_t seed,
+                                         float* U, float* sigma, float* Vt) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if (count < 0) return fail(SEKV_EINVAL, "count < 0");
+  if (count == 0) return SEKV_OK;
+  if (!A || !row_off || !rows || !U || !sigma || !Vt) return fail(SEKV_EINVAL, "null pointer argument");
+  if (d != 64 && d != 128) return fail(SEKV_EUNSUPPORTED, "d must be 64 or 128");
+  if (R < 1 || R > 64 || R > d) return fail(SEKV_EINVAL, "R must be in [1, min(64, d)]");
+  if (oversample < 0 || oversample > 16) return fail(SEKV_EINVAL, "oversample must be in [0, 16]");
+  if (power_iters < 0 || power_iters > 8) return fail(SEKV_EINVAL, "power_iters must be in [0, 8]");
+  if (max_rows < 1) return fail(SEKV_EINVAL, "max_rows must be >= 1");
+  if ((st = set_device(c))) return st;
+  PackArgs pa{};
+  pa.A = (const bf16_t*)A;
+  pa.mat_row_off = row_off;
+  pa.mat_rows = rows;
+  pa.out_U = U;
+  pa.out_S = sigma;
+  pa.out_Vt = Vt;
+  pa.count = count;
+  pa.max_rows = max_rows;
+  pa.D = d;
+  pa.R = R;
+  pa.oversample = oversample;
+  pa.power_iters = power_iters;
+  pa.seed = seed;
+  HIP_TRY(launch_rsvd_batched(pa, c->stream));
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_index_get_info(const sekv_index* x, sekv_index_info* info) {
+  if (!x || !info) return fail(SEKV_EINVAL, "null argument");
+  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  info->B = x->B; info->L = x->L; info->Hq = x->Hq; info->Hkv = x->Hkv; info->d = x->D;
+  info->R = x->R; info->dprime = x->dp; info->tier = x->tier;
+  info->max_spans = x->max_spans;
+  info->mask_words = x->Wd;
+  info->total_spans = x->total_spans;
+  info->total_raw = x->total_raw;
+  info->total_span_tokens = x->total_tok;
+  info->resident_bytes = 2 * 2 * x->kres_elems + 4 * x->s_elems + 4LL * x->L * x->Hq * x->dp * x->D;
+  info->factor_bytes = x->pool_bytes;
+  info->ring_bytes = x->ring_bytes;
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_index_counts(const sekv_index* x, int32_t* n_spans, int32_t* n_raw) {
+  if (!x || !n_spans || !n_raw) return fail(SEKV_EINVAL, "null argument");
+  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  for (int b = 0; b < x->B; ++b) {
+    n_spans[b] = x->meta[b].n_spans;
+    n_raw[b] = x->meta[b].n_raw;
+  }
+  return SEKV_OK;
+}
+
+extern "C" void sekv_index_free(sekv_index* x) {
+  if (!x || x->magic != IDX_MAGIC) return;
+  if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipSetDevice(x->ctx->device);
+  free_index(x);
+}
+
+// ================================================================ prefill ===
+
+extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p, const void* K,
+                                        const void* V, const float* H, const float* W,
+                                        const float* gates, sekv_index** out) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if (!out) return fail(SEKV_EINVAL, "null out");
+  *out = nullptr;
+  if ((st = check_shape(p, true))) return st;
+  if (!K || !V || !H || !W) return fail(SEKV_EINVAL, "null K, V, H or W");
+  if ((st = set_device(c))) return st;
+  hipStream_t stream = c->stream;
+  const int B = p->B, T = p->T;
+  const int S_max = sekv_max_spans(T, p->l_min);
+
+  // ---- span split into scratch
+  DBuf sst, sln, slg, raw, cnt, scr;
+  struct Rel { DBuf* b[6]; ~Rel() { for (DBuf* x : b) x->release(); } } rel{{&sst, &sln, &slg, &raw, &cnt, &scr}};
+  HIP_TRY(dalloc(sst, 4 * (size_t)B * std::max(S_max, 1)));
+  HIP_TRY(dalloc(sln, 4 * (size_t)B * std::max(S_max, 1)));
+  HIP_TRY(dalloc(slg, 4 * (size_t)B * std::max(S_max, 1)));
+  HIP_TRY(dalloc(raw, 4 * (size_t)B * T));
+  HIP_TRY(dalloc(cnt, 8 * (size_t)B));
+  HIP_TRY(dalloc(scr, 4 * (size_t)B * 2 * (T / 2 + 2)));
+  SplitArgs sa{};
+  sa.H = H;
+  sa.span_start = (int32_t*)sst.p;
+  sa.span_len = (int32_t*)sln.p;
+  sa.span_logn = (float*)slg.p;
+  sa.raw_pos = (int32_t*)raw.p;
+  sa.counts = (int32_t*)cnt.p;
+  sa.scratch = (int32_t*)scr.p;
+  sa.B = B; sa.T = T; sa.S_max = S_max; sa.l_min = p->l_min; sa.alpha_sp = p->alpha_sp;
+  HIP_TRY(launch_span_split(sa, stream));
+  std::vector<int32_t> counts(2 * B);
+  HIP_TRY(hipMemcpyAsync(counts.data(), cnt.p, 8 * (size_t)B, hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  std::vector<int32_t> n_spans(B), n_raw(B);
+  int64_t tot_sp = 0;
+  for (int b = 0; b < B; ++b) {
+    n_spans[b] = counts[2 * b];
+    n_raw[b] = counts[2 * b + 1];
+    if (n_spans[b] < 0 || n_spans[b] > S_max || n_raw[b] < 0 || n_raw[b] > T)
+      return fail(SEKV_EHIP, "span split produced inconsistent counts for b=%d", b);
+    tot_sp += n_spans[b];
+  }
+  std::vector<int32_t> lens((size_t)tot_sp);
+  {
+    int64_t o = 0;
+    for (int b = 0; b < B; ++b) {
+      if (n_spans[b])
+        HIP_TRY(hipMemcpyAsync(lens.data() + o, (int32_t*)sln.p + (size_t)b * S_max, 4 * (size_t)n_spans[b],
+                               hipMemcpyDeviceToHost, stream));
+      o += n_spans[b];
+    }
+    HIP_TRY(hipStreamSynchronize(stream));
+  }
+  sekv_index* x = new sekv_index();
+  x->ctx = c;
+  IndexGuard guard{x};
+  plan_layout(x, p, n_spans, n_raw, lens);
+  if ((st = alloc_index(x, p->ring_bytes))) return st;
+  // compact span tables and raw positions
+  for (int b = 0; b < B; ++b) {
+    const BMeta& m = x->meta[b];
+    if (m.n_spans) {
+      HIP_TRY(hipMemcpyAsync((int32_t*)x->d_span_start.p + m.span_base, (int32_t*)sst.p + (size_t)b * S_max,
+                             4 * (size_t)m.n_spans, hipMemcpyDeviceToDevice, stream));
+      HIP_TRY(hipMemcpyAsync((float*)x->d_logn.p + m.span_base, (float*)slg.p + (size_t)b * S_max,
+                             4 * (size_t)m.n_spans, hipMemcpyDeviceToDevice, stream));
+    }
+    if (m.n_raw)
+      HIP_TRY(hipMemcpyAsync((int32_t*)x->d_raw_pos.p + m.raw_base, (int32_t*)raw.p + (size_t)b * T,
+                             4 * (size_t)m.n_raw, hipMemcpyDeviceToDevice, stream));
+  }
+  HIP_TRY(hipMemcpyAsync(x->d_W.p, W, x->d_W.n, hipMemcpyDeviceToDevice, stream));
+
+  PackArgs pa{};
+  pa.K = (const bf16_t*)K;
+  pa.V = (const bf16_t*)V;
+  pa.H = H;
+  pa.W = W;
+  pa.gates = gates;
+  pa.meta = (const BMeta*)x->d_meta.p;
+  pa.span_start = (const int32_t*)x->d_span_start.p;
+  pa.span_len = (const int32_t*)x->d_span_len.p;
+  pa.raw_pos = (const int32_t*)x->d_raw_pos.p;
+  pa.span_off = (const int64_t*)x->d_span_off.p;
+  pa.kres = (bf16_t*)x->d_kres.p;
+  pa.vres = (bf16_t*)x->d_vres.p;
+  pa.s = (float*)x->d_s.p;
+  pa.B = B; pa.L = p->L; pa.Hq = p->Hq; pa.Hkv = p->Hkv; pa.D = p->d; pa.T = T; pa.R = p->R;
+  pa.dp = p->dprime; pa.S_max = S_max; pa.max_raw = x->max_raw; pa.max_spans = x->max_spans;
+  pa.oversample = p->oversample; pa.power_iters = p->power_iters; pa.seed = p->seed;
+  HIP_TRY(launch_pack_raw(pa, stream));
+  HIP_TRY(launch_summaries(pa, stream));
+  DBuf stage;
+  struct Rel1 { DBuf* b; ~Rel1() { b->release(); } } rel1{&stage};
+  if (x->tier == SEKV_TIER_PINNED_HOST) {
+    HIP_TRY(dalloc(stage, (size_t)x->layer_bytes));
+  }
+  for (int l = 0; l < p->L; ++l) {
+    pa.layer = l;
+    if (x->tier == SEKV_TIER_HBM) {
+      pa.pool = (uint8_t*)x->d_pool.p + (size_t)l * x->layer_bytes;
+      HIP_TRY(launch_rsvd(pa, stream));
+    } else {
+      pa.pool = (uint8_t*)stage.p;
+      HIP_TRY(hipMemsetAsync(stage.p, 0, stage.n, stream));
+      HIP_TRY(launch_rsvd(pa, stream));
+      HIP_TRY(hipMemcpyAsync(x->h_pool + (size_t)l * x->layer_bytes, stage.p, (size_t)x->layer_bytes,
+                             hipMemcpyDeviceToHost, stream));
+    }
+  }
+  HIP_TRY(hipStreamSynchronize(stream));
+  guard.x = nullptr;
+  *out = x;
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p, const sekv_host_index* h,
+                                         sekv_index** out) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if (!out) return fail(SEKV_EINVAL, "null out");
+  *out = nullptr;
+  if ((st = check_shape(p, false))) return st;
+  if (!h || !h->n_spans || !h->n_raw || !h->k_res || !h->v_res || !h->s || !h->W)
+    return fail(SEKV_EINVAL, "null host index member");
+  const int B = p->B, T = p->T, D = p->d, R = p->R, L = p->L, Hkv = p->Hkv, Hq = p->Hq, dp = p->dprime;
+  std::vector<int32_t> n_spans(h->n_spans, h->n_spans + B), n_raw(h->n_raw, h->n_raw + B);
+  int64_t tot_sp = 0, tot_raw = 0;
+  for (int b = 0; b < B; ++b) {
+    if (n_spans[b] < 0 || n_raw[b] < 0) return fail(SEKV_EINVAL, "negative count at b=%d", b);
+    tot_sp += n_spans[b];
+    tot_raw += n_raw[b];
+  }
+  if (tot_sp && (!h->span_start || !h->span_len || !h->uk || !h->uv || !h->vkt || !h->vvt || !h->smk || !h->smv))
+    return fail(SEKV_EINVAL, "null span arrays");
+  if (tot_raw && !h->raw_pos) return fail(SEKV_EINVAL, "null raw_pos");
+  // the tables must partition [0, T) per sequence
+  {
+    int64_t so = 0, ro = 0;
+    std::vector<uint8_t> seen(T);
+    for (int b = 0; b < B; ++b) {
+      std::fill(seen.begin(), seen.end(), 0);
+      int64_t cov = 0;
+      for (int S = 0; S < n_spans[b]; ++S) {
+        const int a0 = h->span_start[so + S], n = h->span_len[so + S];
+        if (n < 1 || a0 < 0 || (int64_t)a0 + n > T) return fail(SEKV_EINVAL, "span %d of b=%d out of range", S, b);
+        for (int t = a0; t < a0 + n; ++t) {
+          if (seen[t]) return fail(SEKV_EINVAL, "token %d of b=%d covered twice", t, b);
+          seen[t] = 1;
+        }
+        cov += n;
+      }
+      for (int i = 0; i < n_raw[b]; ++i) {
+        const int t = h->raw_pos[ro + i];
+        if (t < 0 || t >= T || seen[t]) return fail(SEKV_EINVAL, "raw token %d of b=%d invalid", t, b);
+        seen[t] = 1;
+      }
+      if (cov + n_raw[b] != T) return fail(SEKV_EINVAL, "spans and raw tokens of b=%d do not cover T", b);
+      so += n_spans[b];
+      ro += n_raw[b];
+    }
+  }
+  if ((st = set_device(c))) return st;
+  std::vector<int32_t> lens(h->span_len, h->span_len + tot_sp);
+  sekv_index* x = new sekv_index();
+  x->ctx = c;
+  IndexGuard guard{x};
+  plan_layout(x, p, n_spans, n_raw, lens);
+  if ((st = alloc_index(x, p->ring_bytes))) return st;
+  hipStream_t stream = c->stream;
+  // pack into the native layouts on the host
+  std::vector<bf16_t> kres((size_t)x->kres_elems, 0), vres((size_t)x->kres_elems, 0);
+  std::vector<float> s((size_t)x->s_elems, 0.f), logn((size_t)std::max<int64_t>(tot_sp, 1));
+  std::vector<uint8_t> pool;
+  uint8_t* pool_dst;
+  if (x->tier == SEKV_TIER_HBM) {
+    pool.assign((size_t)x->pool_bytes, 0);
+    pool_dst = pool.data();
+  } else {
+    pool_dst = x->h_pool;
+  }
+  int64_t kro = 0, so = 0, tko = 0, spo = 0;
+  for (int b = 0; b < B; ++b) {
+    const BMeta& m = x->meta[b];
+    const int NS = m.n_spans, NR = m.n_res;
+    int64_t ntok = 0;
+    for (int S = 0; S < NS; ++S) ntok += lens[m.span_base + S];
+    for (int lg = 0; lg < L * Hkv; ++lg) {
+      const int64_t dst = m.res_base + (int64_t)lg * m.n_res_pad * D;
+      for (int r = 0; r < NR; ++r)
+        for (int d = 0; d < D; ++d) {
+          const int64_t src = kro + ((int64_t)lg * NR + r) * D + d;
+          kres[dst + krow_off(r, d, D)] = h->k_res[src];
+          vres[dst + vrow_off(r, d, D)] = h->v_res[src];
+        }
+    }
+    kro += (int64_t)L * Hkv * NR * D;
+    for (int lh = 0; lh < L * Hq; ++lh)
+      for (int j = 0; j < dp; ++j)
+        for (int S = 0; S < NS; ++S)
+          s[m.s_base + ((int64_t)lh * dp + j) * m.s_pad + S] = h->s[so + ((int64_t)lh * dp + j) * NS + S];
+    so += (int64_t)L * Hq * dp * NS;
+    for (int S = 0; S < NS; ++S) logn[m.span_base + S] = logf((float)lens[m.span_base + S]);
+    for (int l = 0; l < L; ++l)
+      for (int g = 0; g < Hkv; ++g) {
+        const int lg = l * Hkv + g;
+        int64_t toff = 0;
+        for (int S = 0; S < NS; ++S) {
+          const int n = lens[m.span_base + S], np = Blob::npad(n);
+          uint8_t* blob = pool_dst + (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg +
+                          x->h_span_off[m.span_base + S];
+          bf16_t* vkt = (bf16_t*)(blob + Blob::off_vkt(R, D));
+          bf16_t* vv = (bf16_t*)(blob + Blob::off_vv(R, D));
+          float* smk = (float*)(blob + Blob::off_smk(R, D));
+          float* smv = (float*)(blob + Blob::off_smv(R, D));
+          bf16_t* uk = (bf16_t*)(blob + Blob::off_uk(R, D));
+          bf16_t* uvt = (bf16_t*)(blob + Blob::off_uvt(R, D, n));
+          const int64_t rsp = spo + (int64_t)lg * NS + S;   // [L][Hkv][NS] index
+          for (int i = 0; i < R; ++i)
+            for (int d = 0; d < D; ++d) {
+              vkt[krow_off(i, d, D)] = h->vkt[(rsp * R + i) * D + d];
+              vv[a16_off(d, i, R)] = h->vvt[(rsp * R + i) * D + d];
+            }
+          for (int i = 0; i < R; ++i) {
+            smk[i] = h->smk[rsp * R + i];
+            smv[i] = h->smv[rsp * R + i];
+          }
+          const int64_t ub = tko + (int64_t)lg * ntok + toff;  // [L][Hkv][sum n][R] row
+          for (int t = 0; t < n; ++t)
+            for (int i = 0; i < R; ++i) {
+              uk[a16_off(t, i, R)] = h->uk[(ub + t) * R + i];
+              uvt[a16_off(i, t, np)] = h->uv[(ub + t) * R + i];
+            }
+          toff += n;
+        }
+      }
+    tko += (int64_t)L * Hkv * ntok;
+    spo += (int64_t)L * Hkv * NS;
+  }
+  HIP_TRY(hipMemcpyAsync(x->d_kres.p, kres.data(), 2 * kres.size(), hipMemcpyHostToDevice, stream));
+  HIP_TRY(hipMemcpyAsync(x->d_vres.p, vres.data(), 2 * vres.size(), hipMemcpyHostToDevice, stream));
+  HIP_TRY(hipMemcpyAsync(x->d_s.p, s.data(), 4 * s.size(), hipMemcpyHostToDevice, stream));
+  if (tot_sp) {
+    HIP_TRY(hipMemcpyAsync(x->d_span_start.p, h->span_start, 4 * (size_t)tot_sp, hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(x->d_logn.p, logn.data(), 4 * (size_t)tot_sp, hipMemcpyHostToDevice, stream));
+  }
+  if (tot_raw) HIP_TRY(hipMemcpyAsync(x->d_raw_pos.p, h->raw_pos, 4 * (size_t)tot_raw, hipMemcpyHostToDevice, stream));
+  HIP_TRY(hipMemcpyAsync(x->d_W.p, h->W, x->d_W.n, hipMemcpyHostToDevice, stream));
+  if (x->tier == SEKV_TIER_HBM)
+    HIP_TRY(hipMemcpyAsync(x->d_pool.p, pool.data(), pool.size(), hipMemcpyHostToDevice, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  guard.x = nullptr;
+  *out = x;
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const sekv_host_index_out* h) {
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if (!h) return fail(SEKV_EINVAL, "null host index");
+  if ((st = set_device(c))) return st;
+  hipStream_t stream = c->stream;
+  const int B = x->B, D = x->D, R = x->R, L = x->L, Hkv = x->Hkv, Hq = x->Hq, dp = x->dp;
+  std::vector<bf16_t> kres((size_t)x->kres_elems), vres((size_t)x->kres_elems);
+  std::vector<float> s((size_t)x->s_elems);
+  std::vector<int32_t> sst((size_t)std::max<int64_t>(x->total_spans, 1)), rp((size_t)std::max<int64_t>(x->total_raw, 1));
+  std::vector<uint8_t> pool;
+  const uint8_t* pool_src = x->h_pool;
+  if (x->tier == SEKV_TIER_HBM) {
+    pool.resize((size_t)x->pool_bytes);
+    HIP_TRY(hipMemcpyAsync(pool.data(), x->d_pool.p, pool.size(), hipMemcpyDeviceToHost, stream));
+    pool_src = pool.data();
+  }
+  HIP_TRY(hipMemcpyAsync(kres.data(), x->d_kres.p, 2 * kres.size(), hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipMemcpyAsync(vres.data(), x->d_vres.p, 2 * vres.size(), hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipMemcpyAsync(s.data(), x->d_s.p, 4 * s.size(), hipMemcpyDeviceToHost, stream));
+  if (x->total_spans)
+    HIP_TRY(hipMemcpyAsync(sst.data(), x->d_span_start.p, 4 * (size_t)x->total_spans, hipMemcpyDeviceToHost, stream));
+  if (x->total_raw)
+    HIP_TRY(hipMemcpyAsync(rp.data(), x->d_raw_pos.p, 4 * (size_t)x->total_raw, hipMemcpyDeviceToHost, stream));
+  HIP_TRY(hipStreamSynchronize(stream));
+  if (h->span_start) std::copy(sst.begin(), sst.begin() + x->total_spans, h->span_start);
+  if (h->span_len) std::copy(x->h_span_len.begin(), x->h_span_len.end(), h->span_len);
+  if (h->raw_pos) std::copy(rp.begin(), rp.begin() + x->total_raw, h->raw_pos);
+  int64_t kro = 0, so = 0, tko = 0, spo = 0;
+  for (int b = 0; b < B; ++b) {
+    const BMeta& m = x->meta[b];
+    const int NS = m.n_spans, NR = m.n_res;
+    int64_t ntok = 0;
+    for (int S = 0; S < NS; ++S) ntok += x->h_span_len[m.span_base + S];
+    for (int lg = 0; lg < L * Hkv; ++lg) {
+      const int64_t src = m.res_base + (int64_t)lg * m.n_res_pad * D;
+      for (int r = 0; r < NR; ++r)
+        for (int d = 0; d < D; ++d) {
+          const int64_t dst = kro + ((int64_t)lg * NR + r) * D + d;
+          if (h->k_res) h->k_res[dst] = kres[src + krow_off(r, d, D)];
+          if (h->v_res) h->v_res[dst] = vres[src + vrow_off(r, d, D)];
+        }
+    }
+    kro += (int64_t)L * Hkv * NR * D;
+    if (h->s)
+      for (int lh = 0; lh < L * Hq; ++lh)
+        for (int j = 0; j < dp; ++j)
+          for (int S = 0; S < NS; ++S)
+            h->s[so + ((int64_t)lh * dp + j) * NS + S] = s[m.s_base + ((int64_t)lh * dp + j) * m.s_pad + S];
+    so += (int64_t)L * Hq * dp * NS;
+    for (int l = 0; l < L; ++l)
+      for (int g = 0; g < Hkv; ++g) {
+        const int lg = l * Hkv + g;
+        int64_t toff = 0;
+        for (int S = 0; S < NS; ++S) {
+          const int n = x->h_span_len[m.span_base + S], np = Blob::npad(n);
+          const uint8_t* blob = pool_src + (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg +
+                                x->h_span_off[m.span_base + S];
+          const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt(R, D));
+          const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(R, D));
+          const float* smk = (const float*)(blob + Blob::off_smk(R, D));
+          const float* smv = (const float*)(blob + Blob::off_smv(R, D));
+          const bf16_t* uk = (const bf16_t*)(blob + Blob::off_uk(R, D));
+          const bf16_t* uvt = (const bf16_t*)(blob + Blob::off_uvt(R, D, n));
+          const int64_t rsp = spo + (int64_t)lg * NS + S;
+          for (int i = 0; i < R; ++i)
+            for (int d = 0; d < D; ++d) {
+              if (h->vkt) h->vkt[(rsp * R + i) * D + d] = vkt[krow_off(i, d, D)];
+              if (h->vvt) h->vvt[(rsp * R + i) * D + d] = vv[a16_off(d, i, R)];
+            }
+          for (int i = 0; i < R; ++i) {
+            if (h->smk) h->smk[rsp * R + i] = smk[i];
+            if (h->smv) h->smv[rsp * R + i] = smv[i];
+          }
+          const int64_t ub = tko + (int64_t)lg * ntok + toff;
+          for (int t = 0; t < n; ++t)
+            for (int i = 0; i < R; ++i) {
+              if (h->uk) h->uk[(ub + t) * R + i] = uk[a16_off(t, i, R)];
+              if (h->uv) h->uv[(ub + t) * R + i] = uvt[a16_off(i, t, np)];
+            }
+          toff += n;
+        }
+      }
+    tko += (int64_t)L * Hkv * ntok;
+    spo += (int64_t)L * Hkv * NS;
+  }
+  return SEKV_OK;
+}
+
+// ================================================================= decode ===
+
+extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc, const void* q,
+                                  const float* tau, int32_t cap, uint64_t* mask, float* alpha) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q || !tau || !mask) return fail(SEKV_EINVAL, "null q, tau or mask");
+  if (cap < 0) return fail(SEKV_EINVAL, "cap < 0");
+  if ((st = set_device(c))) return st;
+  if ((st = ensure_route_scratch(x, lc))) return st;
+  RouteArgs ra{};
+  ra.q = (const bf16_t*)q;
+  ra.tau = tau;
+  ra.W = (const float*)x->d_W.p;
+  ra.s = (const float*)x->d_s.p;
+  ra.meta = (const BMeta*)x->d_meta.p;
+  ra.mask = mask;
+  ra.alpha = alpha ? alpha : (cap > 0 ? (float*)x->d_alpha.p : nullptr);
+  ra.tickets = (uint32_t*)x->d_tickets.p;
+  ra.layer_begin = lb; ra.layer_count = lc;
+  ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
+  ra.cap = cap;
+  HIP_TRY(launch_route(ra, c->stream));
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
+                                          const void* q_cal, float frac, float* tau_out) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q_cal || !tau_out) return fail(SEKV_EINVAL, "null q_cal or tau_out");
+  if (!(frac >= 0.f && frac <= 1.f)) return fail(SEKV_EINVAL, "frac must be in [0, 1]");
+  if (x->total_spans < 2) return fail(SEKV_EINVAL, "calibration needs at least 2 spans");
+  if ((st = set_device(c))) return st;
+  if ((st = ensure_route_scratch(x, lc))) return st;
+  const size_t ntau = (size_t)lc * x->Hq;
+  if (!x->d_tau_inf.p || x->d_tau_inf.n < 4 * ntau) {
+    HIP_TRY(dalloc(x->d_tau_inf, 4 * ntau));
+    std::vector<float> inf(ntau, INFINITY);
+    HIP_TRY(hipMemcpyAsync(x->d_tau_inf.p, inf.data(), 4 * ntau, hipMemcpyHostToDevice, c->stream));
+    HIP_TRY(hipStreamSynchronize(c->stream));
+  }
+  DBuf mk;
+  struct Rel { DBuf* b; ~Rel() { b->release(); } } rel{&mk};
+  HIP_TRY(dalloc(mk, 8 * (size_t)x->B * lc * x->Hq * x->Wd));
+  RouteArgs ra{};
+  ra.q = (const bf16_t*)q_cal;
+  ra.tau = (const float*)x->d_tau_inf.p;
+  ra.W = (const float*)x->d_W.p;
+  ra.s = (const float*)x->d_s.p;
+  ra.meta = (const BMeta*)x->d_meta.p;
+  ra.mask = (uint64_t*)mk.p;
+  ra.alpha = (float*)x->d_alpha.p;
+  ra.tickets = (uint32_t*)x->d_tickets.p;
+  ra.layer_begin = lb; ra.layer_count = lc;
+  ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
+  ra.cap = 0;
+  HIP_TRY(launch_route(ra, c->stream));
+  CalibArgs ca{};
+  ca.alpha = (const float*)x->d_alpha.p;
+  ca.meta = (const BMeta*)x->d_meta.p;
+  ca.tau_out = tau_out;
+  ca.layer_count = lc; ca.B = x->B; ca.Hq = x->Hq; ca.Wd = x->Wd; ca.frac = frac;
+  HIP_TRY(launch_calibrate(ca, c->stream));
+  HIP_TRY(hipStreamSynchronize(c->stream));  // the temporary mask is freed on return
+  return SEKV_OK;
+}
+
+namespace {
+
+// Pinned tier: read the masks back, gather the union of every (b, l, g) into
+// the ring (coalescing spans that are adjacent in the pool), and publish the
+// ring offset of each union rank.
+sekv_status gather(sekv_index* x, int lb, int lc, const uint64_t* mask, sekv_stats* stats) {
+  hipStream_t st = x->ctx->stream;
+  const size_t nwords = (size_t)x->B * lc * x->Hq * x->Wd;
+  if (x->h_mask_cap < nwords) {
+    if (x->h_mask_pinned) (void)hipHostFree(x->h_mask_pinned);
+    x->h_mask_pinned = nullptr;
+    HIP_TRY(hipHostMalloc((void**)&x->h_mask_pinned, 8 * nwords, hipHostMallocDefault));
+    x->h_mask_cap = nwords;
+  }
+  HIP_TRY(hipMemcpyAsync(x->h_mask_pinned, mask, 8 * nwords, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  const size_t noff = (size_t)lc * x->B * x->Hkv * std::max(x->max_spans, 1);
+  if (x->h_ring_off_cap < noff) {
+    if (x->h_ring_off_pinned) (void)hipHostFree(x->h_ring_off_pinned);
+    x->h_ring_off_pinned = nullptr;
+    HIP_TRY(hipHostMalloc((void**)&x->h_ring_off_pinned, 8 * noff, hipHostMallocDefault));
+    x->h_ring_off_cap = noff;
+  }
+  HIP_TRY(dgrow(x->d_ring_off, 8 * noff));
+  // plan
+  struct Copy { int64_t src, dst, bytes; };
+  std::vector<Copy> copies;
+  int64_t ring_used = 0;
+  uint64_t unions = 0;
+  const int G = x->G, Wd = x->Wd;
+  for (int li = 0; li < lc; ++li) {
+    const int l = lb + li;
+    for (int b = 0; b < x->B; ++b) {
+      const BMeta& m = x->meta[b];
+      for (int g = 0; g < x->Hkv; ++g) {
+        int64_t* roff = x->h_ring_off_pinned + (((size_t)li * x->B + b) * x->Hkv + g) * std::max(x->max_spans, 1);
+        const uint64_t* mr = x->h_mask_pinned + (((size_t)b * lc + li) * x->Hq + (size_t)g * G) * Wd;
+        const int64_t region = (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg;
+        int k = 0;
+        for (int w = 0; w < Wd; ++w) {
+          uint64_t u = 0;
+          for (int h = 0; h < G; ++h) u |= mr[(size_t)h * Wd + w];
+          while (u) {
+            const int S = 64 * w + __builtin_ctzll(u);
+            u &= u - 1;
+            if (S >= m.n_spans) continue;
+            const int64_t src = region + x->h_span_off[m.span_base + S];
+            const int64_t bytes = Blob::bytes(x->R, x->D, x->h_span_len[m.span_base + S]);
+            if (ring_used + bytes > x->ring_bytes)
+              return fail(SEKV_ECAPACITY, "staging ring of %lld bytes too small for the routed union",
+                          (long long)x->ring_bytes);
+            if (!copies.empty() && copies.back().src + copies.back().bytes == src &&
+                copies.back().dst + copies.back().bytes == ring_used)
+              copies.back().bytes += bytes;
+            else
+              copies.push_back(Copy{src, ring_used, bytes});
+            roff[k++] = ring_used;
+            ring_used += bytes;
+            ++unions;
+          }
+        }
+      }
+    }
+  }
+  HIP_TRY(hipMemcpyAsync(x->d_ring_off.p, x->h_ring_off_pinned, 8 * noff, hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(x->ev0, st));
+  for (const Copy& cp : copies)
+    HIP_TRY(hipMemcpyAsync((uint8_t*)x->d_ring.p + cp.dst, x->h_pool + cp.src, (size_t)cp.bytes,
+                           hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(x->ev1, st));
+  if (stats) {
+    stats->union_spans = unions;
+    stats->pcie_bytes = (uint64_t)ring_used;
+    stats->pcie_copies = copies.size();
+    HIP_TRY(hipEventSynchronize(x->ev1));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, x->ev0, x->ev1));
+    stats->pcie_ms = ms;
+  }
+  return SEKV_OK;
+}
+
+}  // namespace
+
+extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
+                                          const void* q, const uint64_t* mask, float* out, sekv_stats* stats) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if ((st = set_device(c))) return st;
+  if (stats) memset(stats, 0, sizeof *stats);
+  const int n_items = (int)x->items.size();
+  HIP_TRY(dgrow(x->d_part, sizeof(float) * (size_t)lc * std::max(n_items, 1) * x->G * (x->D + 2)));
+  AttendArgs aa{};
+  aa.q = (const bf16_t*)q;
+  aa.mask = mask;
+  aa.meta = (const BMeta*)x->d_meta.p;
+  aa.items = (const WorkItem*)x->d_items.p;
+  aa.kres = (const bf16_t*)x->d_kres.p;
+  aa.vres = (const bf16_t*)x->d_vres.p;
+  aa.logn = (const float*)x->d_logn.p;
+  aa.span_len = (const int32_t*)x->d_span_len.p;
+  aa.span_off = (const int64_t*)x->d_span_off.p;
+  if (x->tier == SEKV_TIER_HBM) {
+    aa.pool = (const uint8_t*)x->d_pool.p;
+    aa.ring_off = nullptr;
+  } else {
+    if ((st = gather(x, lb, lc, mask, stats))) return st;
+    aa.pool = (const uint8_t*)x->d_ring.p;
+    aa.ring_off = (const int64_t*)x->d_ring_off.p;
+  }
+  aa.part = (float*)x->d_part.p;
+  aa.layer_bytes = x->layer_bytes;
+  aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
+  aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
+  aa.max_spans = std::max(x->max_spans, 1);
+  aa.tpw = kTilesPerItem;
+  aa.scale = 1.0f / sqrtf((float)x->D);
+  if (n_items > 0) HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
+  ReduceArgs rd{};
+  rd.part = (const float*)x->d_part.p;
+  rd.items = (const WorkItem*)x->d_items.p;
+  rd.bg_first = (const int32_t*)x->d_bg_first.p;
+  rd.out = out;
+  rd.layer_count = lc; rd.n_items = n_items; rd.B = x->B; rd.Hq = x->Hq; rd.Hkv = x->Hkv;
+  HIP_TRY(launch_reduce(rd, x->D, x->G, c->stream));
+  return SEKV_OK;
+}

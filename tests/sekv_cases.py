@@ -1,0 +1,150 @@
+"""Shared test machinery: seeded cases, oracle-built indexes in the library's
+import layout, mask packing and the comparison rules.
+
+Inputs come from compressed_kv_cache_sekv_amd.synth (the only code both sides
+share); expected values come from oracle/ only.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from oracle import sekv_oracle as O
+from compressed_kv_cache_sekv_amd import synth
+
+TIE = 1e-4          # |alpha - tau| below this is a tie, excluded from bit-exact checks
+REL_L2 = 5e-3       # decode outputs: max relative L2 error per (b, l, h)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """uint16 bit patterns of fp64 values that are bf16-representable."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bits_to_f64(u) -> np.ndarray:
+    return (np.asarray(u, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclass
+class Case:
+    w: synth.Workload
+    H: torch.Tensor          # [B, T] fp32 (cpu)
+    K: torch.Tensor          # [B, L, Hkv, T, d] bf16 (cpu)
+    V: torch.Tensor
+    W: torch.Tensor          # [L, Hq, d', d] fp32
+    gates: Optional[torch.Tensor]   # [B, L, Hkv, 2, S_max, R] or None
+    idxs: List[O.BatchIndex]
+    tau: np.ndarray          # [L, Hq] fp32 values (as fp64)
+
+    def q(self, step: int) -> torch.Tensor:
+        return synth.query(self.w, step)
+
+    @property
+    def s_max(self) -> int:
+        return synth.max_spans(self.w.T, self.w.l_min)
+
+
+def make_inputs(w: synth.Workload):
+    H, K, V = synth.kv_cache(w)
+    W = torch.stack([synth.routing_w(w, l) for l in range(w.L)])
+    S_max = synth.max_spans(w.T, w.l_min)
+    gl = []
+    for b in range(w.B):
+        gb = [synth.gates(w, b, l, S_max) for l in range(w.L)]
+        gl.append(None if gb[0] is None else torch.stack(gb))
+    gates = None if gl[0] is None else torch.stack(gl)
+    return H, K, V, W, gates
+
+
+def make_case(w: synth.Workload, store: bool = True) -> Case:
+    H, K, V, W, gates = make_inputs(w)
+    idxs = [O.build_index_b(H[b].numpy(), K[b].double().numpy(), V[b].double().numpy(),
+                            W.double().numpy(), None if gates is None else gates[b].double().numpy(),
+                            R=w.R, alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=w.Hq, store=store)
+            for b in range(w.B)]
+    if w.tau is not None:
+        tau = np.full((w.L, w.Hq), np.float32(w.tau), np.float64)
+    else:
+        tau = oracle_calibrated_tau(w, idxs, W)
+    return Case(w, H, K, V, W, gates, idxs, tau)
+
+
+def oracle_alpha(idxs, W, q, l: int, h: int) -> np.ndarray:
+    """alpha of every (b, span) for (l, h), concatenated over b (fp64)."""
+    Wn = W.double().numpy() if isinstance(W, torch.Tensor) else W
+    qn = q.double().numpy() if isinstance(q, torch.Tensor) else q
+    return np.concatenate([O.route_head(Wn[l, h], qn[b, l, h], idxs[b].s[l, h], 0.5)[0]
+                           for b in range(len(idxs))])
+
+
+def oracle_calibrated_tau(w, idxs, W) -> np.ndarray:
+    qc = synth.calibration_query(w)
+    tau = np.zeros((w.L, w.Hq))
+    for l in range(w.L):
+        for h in range(w.Hq):
+            tau[l, h] = np.float32(O.calibrate_tau(oracle_alpha(idxs, W, qc, l, h), w.frac))
+    return tau
+
+
+def import_arrays(case: Case) -> dict:
+    ix = case.idxs
+    cat = lambda f: np.concatenate([f(i).ravel() for i in ix]) if ix else np.zeros(0)
+    return dict(
+        n_spans=np.array([i.n_spans for i in ix], np.int32),
+        n_raw=np.array([i.n_raw for i in ix], np.int32),
+        span_start=cat(lambda i: i.split.spans[:, 0]).astype(np.int32),
+        span_len=cat(lambda i: i.split.spans[:, 1]).astype(np.int32),
+        raw_pos=cat(lambda i: i.split.raw).astype(np.int32),
+        k_res=bf16_bits(cat(lambda i: i.kres)), v_res=bf16_bits(cat(lambda i: i.vres)),
+        s=cat(lambda i: i.s).astype(np.float32),
+        uk=bf16_bits(cat(lambda i: i.uk)), uv=bf16_bits(cat(lambda i: i.uv)),
+        vkt=bf16_bits(cat(lambda i: i.vkt)), vvt=bf16_bits(cat(lambda i: i.vvt)),
+        smk=cat(lambda i: i.smk).astype(np.float32), smv=cat(lambda i: i.smv).astype(np.float32),
+        W=case.W.numpy().astype(np.float32),
+    )
+
+
+def pack_mask(z: dict, B: int, L: int, Hq: int, Wd: int) -> np.ndarray:
+    """z[(b, l, h)] bool [N_S(b)] -> uint64 [B, L, Hq, Wd] (bit j of word w is span 64w + j)."""
+    out = np.zeros((B, L, Hq, Wd), np.uint64)
+    for (b, l, h), zz in z.items():
+        bits = np.zeros(Wd * 64, np.uint8)
+        bits[:len(zz)] = zz
+        out[b, l, h] = np.packbits(bits.reshape(Wd, 64)[:, ::-1], axis=1).view(">u8").ravel().astype(np.uint64)
+    return out
+
+
+def unpack_mask(words: np.ndarray, n: int) -> np.ndarray:
+    w = np.asarray(words, np.uint64)
+    bits = np.unpackbits(w.astype(">u8").view(np.uint8).reshape(-1, 8), axis=1)[:, ::-1]
+    return bits.reshape(-1)[:n].astype(bool)
+
+
+def rel_l2(a, ref) -> float:
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def compare_masks(gpu_words, z_ref, alpha_ref, tau, cap_boundary=None):
+    """Bit-exact comparison excluding ties.  Returns (n_mismatch, n_ties)."""
+    n = len(z_ref)
+    zg = unpack_mask(gpu_words, n)
+    tie = np.abs(alpha_ref - tau) < TIE
+    if cap_boundary is not None:
+        tie |= np.abs(alpha_ref - cap_boundary) < TIE
+    bad = (zg != z_ref) & ~tie
+    extra = unpack_mask(gpu_words, len(np.asarray(gpu_words)) * 64)[n:]
+    return int(bad.sum()) + int(extra.sum()), int(tie.sum())
+
+
+def cap_boundary(alpha, z_pre, cap):
+    """alpha of the cap-th largest expansion (the budget boundary), or None."""
+    if cap <= 0 or z_pre.sum() <= cap:
+        return None
+    return float(np.sort(alpha[z_pre])[::-1][cap - 1])

@@ -1,0 +1,362 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Identical-index tier: the oracle builds the index, both sides route and
+attend over it.  End-to-end tier: the library builds its own index from the
+same synthetic inputs.  Bars: spans, raw positions and routing masks
+bit-exact (pairs with |alpha - tau| < 1e-4 excluded and counted); decode
+outputs within 5e-3 relative L2 per (b, l, h); summary keys within 1e-5
+relative L2; pseudo rows within one bf16 ulp; SVD error <= 1.05x the exact
+truncated-SVD optimum (+1e-5 ||A||_F) on the fp32 factors.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_kv_cache_sekv_amd import synth
+from oracle import sekv_oracle as O
+from tests import sekv_cases as SC
+
+pytestmark = pytest.mark.gpu
+
+W8 = synth.WORKLOADS
+
+
+def _wl(name, **kw):
+    return W8[name].scaled(**kw)
+
+
+CASE_SPECS = {
+    "tiny": _wl("tiny_2k"),
+    "8b_4k": _wl("llama8b_l1_32k", T=4096),
+    "8b_32k": _wl("llama8b_l1_32k"),                      # full config-2 size
+    "70b_b2": _wl("llama70b_b32_64k", B=2, T=8192),       # config-5 shape, 2 sequences
+    "8b_l2_cap": _wl("llama8b_l32_128k", L=2, T=16384),   # config-3 shape with the cap
+}
+_CACHE = {}
+
+
+def case(name):
+    if name not in _CACHE:
+        print(f"[case] building oracle index for {name}", flush=True)
+        _CACHE[name] = SC.make_case(CASE_SPECS[name])
+    return _CACHE[name]
+
+
+@pytest.fixture(scope="module")
+def sl():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from compressed_kv_cache_sekv_amd import lib
+    return lib
+
+
+@pytest.fixture(scope="module")
+def ctx(sl):
+    c = sl.Context(0)
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+def imported(ctx, sl, c, tier=0, ring_bytes=0):
+    return ctx.import_index(sl.build_params(c.w, tier=tier, ring_bytes=ring_bytes), SC.import_arrays(c))
+
+
+def dev(x, dtype=None):
+    t = torch.as_tensor(x)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous().cuda()
+
+
+def oracle_route_all(c, q, tau, cap=0):
+    w = c.w
+    return O.route_step(c.idxs, c.W.double().numpy(), q.double().numpy(), tau, cap)
+
+
+def gpu_route(idx, c, q, tau, cap=0):
+    w = c.w
+    Wd = idx.mask_words
+    mask = torch.zeros(w.B, w.L, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    alpha = torch.zeros(w.B, w.L, w.Hq, Wd * 64, dtype=torch.float32, device="cuda")
+    idx.route(0, w.L, dev(q), dev(tau, torch.float32), cap, mask, alpha)
+    torch.cuda.synchronize()
+    return mask.cpu().numpy().view(np.uint64), alpha.cpu().numpy()
+
+
+def gpu_decode(idx, c, q, mask_np, stats=False):
+    w = c.w
+    out = torch.zeros(w.B, w.L, w.Hq, w.d, dtype=torch.float32, device="cuda")
+    m = torch.from_numpy(np.ascontiguousarray(mask_np).view(np.int64)).cuda()
+    st = idx.decode_attend(0, w.L, dev(q), m, out, stats=stats)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), st
+
+
+# ----------------------------------------------------------- identical index
+
+def test_import_export_roundtrip(ctx, sl):
+    c = case("tiny")
+    arrays = SC.import_arrays(c)
+    idx = ctx.import_index(sl.build_params(c.w), arrays)
+    ex = idx.export()
+    for k, v in ex.items():
+        assert np.array_equal(v, arrays[k].ravel()), k
+    idx.free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2"])
+def test_route_identical_index(ctx, sl, name):
+    c = case(name)
+    idx = imported(ctx, sl, c)
+    for step in range(2):
+        q = c.q(step)
+        alpha_o, z_o = oracle_route_all(c, q, c.tau)
+        words, alpha_g = gpu_route(idx, c, q, c.tau)
+        bad = ties = 0
+        for (b, l, h), z in z_o.items():
+            n = len(z)
+            assert np.max(np.abs(alpha_g[b, l, h, :n] - alpha_o[b, l, h])) < 2e-5
+            m, t = SC.compare_masks(words[b, l, h], z, alpha_o[b, l, h], c.tau[l, h])
+            bad += m
+            ties += t
+        print(f"[route] {name} step {step}: mismatches {bad}, ties excluded {ties}")
+        assert bad == 0
+    idx.free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2"])
+def test_decode_identical_index(ctx, sl, name):
+    c = case(name)
+    w = c.w
+    idx = imported(ctx, sl, c)
+    worst = 0.0
+    for step in range(2):
+        q = c.q(step)
+        _, z_o = oracle_route_all(c, q, c.tau)
+        out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+        mask = SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words)
+        out_g, _ = gpu_decode(idx, c, q, mask)
+        for (b, l, h), ref in out_o.items():
+            worst = max(worst, SC.rel_l2(out_g[b, l, h], ref))
+    print(f"[decode] {name}: worst rel-L2 {worst:.3e}")
+    assert worst <= SC.REL_L2
+    idx.free()
+
+
+@pytest.mark.parametrize("tau_val", [-math.inf, math.inf])
+def test_decode_all_or_nothing(ctx, sl, tau_val):
+    c = case("8b_4k")
+    w = c.w
+    idx = imported(ctx, sl, c)
+    tau = np.full((w.L, w.Hq), tau_val)
+    q = c.q(0)
+    _, z_o = oracle_route_all(c, q, tau)
+    words, _ = gpu_route(idx, c, q, tau)
+    for (b, l, h), z in z_o.items():
+        assert np.array_equal(SC.unpack_mask(words[b, l, h], len(z)), z)
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, words)
+    worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+    print(f"[decode tau={tau_val}] worst rel-L2 {worst:.3e}")
+    assert worst <= SC.REL_L2
+    idx.free()
+
+
+def test_route_cap(ctx, sl):
+    c = case("8b_l2_cap")
+    w = c.w
+    idx = imported(ctx, sl, c)
+    cap = int(math.floor(w.cap_frac * c.idxs[0].n_spans))
+    for step in range(2):
+        q = c.q(step)
+        alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+        _, z_o = oracle_route_all(c, q, c.tau, cap)
+        words, _ = gpu_route(idx, c, q, c.tau, cap)
+        bad = ties = over = 0
+        for key, z in z_o.items():
+            b, l, h = key
+            bnd = SC.cap_boundary(alpha_o[key], z_pre[key], cap)
+            over += bnd is not None
+            m, t = SC.compare_masks(words[b, l, h], z, alpha_o[key], c.tau[l, h], bnd)
+            bad += m
+            ties += t
+            assert SC.unpack_mask(words[b, l, h], len(z)).sum() <= cap
+        print(f"[cap] step {step}: cap {cap}, heads over budget {over}, mismatches {bad}, ties {ties}")
+        assert bad == 0
+        # decode over the capped masks
+        out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+        out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words))
+        worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+        assert worst <= SC.REL_L2
+    idx.free()
+
+
+def test_pinned_tier_matches_hbm(ctx, sl):
+    c = case("8b_l2_cap")
+    w = c.w
+    hbm = imported(ctx, sl, c, tier=0)
+    pin = imported(ctx, sl, c, tier=1)
+    q = c.q(0)
+    _, z_o = oracle_route_all(c, q, c.tau)
+    mask = SC.pack_mask(z_o, w.B, w.L, w.Hq, hbm.mask_words)
+    out_h, _ = gpu_decode(hbm, c, q, mask)
+    out_p, st = gpu_decode(pin, c, q, mask, stats=True)
+    assert np.array_equal(out_h, out_p)
+    # bytes gathered = padded blobs of the union of every (b, l, g)
+    G = w.G
+    nu = 0
+    for l in range(w.L):
+        for g in range(w.Hkv):
+            u = np.zeros(c.idxs[0].n_spans, bool)
+            for h in range(g * G, (g + 1) * G):
+                u |= z_o[0, l, h]
+            nu += int(u.sum())
+    print(f"[pinned] union spans {st.union_spans}, PCIe bytes {st.pcie_bytes}, copies {st.pcie_copies}, "
+          f"{st.pcie_ms:.3f} ms")
+    assert st.union_spans == nu and st.pcie_bytes > 0 and st.pcie_copies >= 1
+    hbm.free()
+    pin.free()
+
+
+def test_pinned_ring_too_small(ctx, sl):
+    c = case("tiny")
+    pin = imported(ctx, sl, c, tier=1, ring_bytes=4096)
+    q = c.q(0)
+    w = c.w
+    mask = np.zeros((w.B, w.L, w.Hq, pin.mask_words), np.uint64)
+    mask[...] = np.uint64(0xFFFFFFFFFFFFFFFF)
+    out = torch.zeros(w.B, w.L, w.Hq, w.d, device="cuda")
+    with pytest.raises(sl.SekvError) as e:
+        pin.decode_attend(0, w.L, dev(q), torch.from_numpy(mask.view(np.int64)).cuda(), out)
+    assert e.value.status == 4
+    pin.free()
+
+
+def test_calibrate_tau(ctx, sl):
+    c = case("8b_4k")
+    w = c.w
+    idx = imported(ctx, sl, c)
+    qc = synth.calibration_query(w)
+    tau = torch.zeros(w.L, w.Hq, device="cuda")
+    idx.calibrate_tau(0, w.L, dev(qc), w.frac, tau)
+    torch.cuda.synchronize()
+    tau = tau.cpu().numpy()
+    N = sum(i.n_spans for i in c.idxs)
+    k = int(math.floor(w.frac * N + 0.5))
+    for l in range(w.L):
+        for h in range(w.Hq):
+            a = SC.oracle_alpha(c.idxs, c.W, qc, l, h)
+            near = np.abs(a - tau[l, h]) < SC.TIE
+            assert abs(int((a > tau[l, h]).sum()) - k) <= int(near.sum()), (l, h)
+    idx.free()
+
+
+# --------------------------------------------------------------- end to end
+
+def _gpu_build(ctx, sl, c, tier=0):
+    w = c.w
+    gates = None if c.gates is None else dev(c.gates)
+    return ctx.build_index(sl.build_params(w, tier=tier), dev(c.K), dev(c.V), dev(c.H), dev(c.W), gates)
+
+
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "70b_b2"])
+def test_build_index_spans_and_summaries(ctx, sl, name):
+    c = case(name)
+    w = c.w
+    idx = _gpu_build(ctx, sl, c)
+    assert list(idx.n_spans) == [i.n_spans for i in c.idxs]
+    assert list(idx.n_raw) == [i.n_raw for i in c.idxs]
+    ex = idx.export()
+    ref = SC.import_arrays(c)
+    for k in ("span_start", "span_len", "raw_pos"):
+        assert np.array_equal(ex[k], ref[k]), k
+    # resident rows: raw rows exact, pseudo rows within one bf16 ulp
+    off = 0
+    kg = SC.bits_to_f64(ex["k_res"])
+    vg = SC.bits_to_f64(ex["v_res"])
+    for i in c.idxs:
+        n = w.L * w.Hkv * (i.n_raw + i.n_spans) * w.d
+        for arr_g, arr_o in ((kg[off:off + n], i.kres), (vg[off:off + n], i.vres)):
+            a = arr_g.reshape(w.L, w.Hkv, -1, w.d)
+            assert np.array_equal(a[:, :, :i.n_raw], arr_o[:, :, :i.n_raw])
+            p, po = a[:, :, i.n_raw:], arr_o[:, :, i.n_raw:]
+            ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(po), 1e-30))[1] - 8)
+            assert np.all(np.abs(p - po) <= ulp * 1.0001)
+        off += n
+    # summary keys
+    so = 0
+    for i in c.idxs:
+        n = w.L * w.Hq * w.dprime * i.n_spans
+        sg = ex["s"][so:so + n].reshape(w.L, w.Hq, w.dprime, i.n_spans).astype(np.float64)
+        err = np.linalg.norm(sg - i.s, axis=2) / np.maximum(np.linalg.norm(i.s, axis=2), 1e-30)
+        assert err.max() <= 1e-5, err.max()
+        so += n
+    idx.free()
+
+
+def test_rsvd_batched_quality(ctx, sl):
+    """Randomized SVD on config-4-shaped span matrices (rank-16 blocks + noise,
+    R = 32, oversampling 8, 2 power iterations) against the exact optimum."""
+    w = _wl("prefill_8b_128k", T=8192, L=1, Hkv=2)
+    H, K, V = synth.kv_cache(w)
+    sp = O.span_split(H[0].numpy(), w.alpha_sp, w.l_min)
+    mats = []
+    for g in range(w.Hkv):
+        for X in (K, V):
+            for (a, n) in sp.spans:
+                mats.append(X[0, 0, g, a:a + n])
+    rows = torch.tensor([m.shape[0] for m in mats], dtype=torch.int32)
+    row_off = torch.cumsum(torch.cat([torch.zeros(1, dtype=torch.int64), rows[:-1].long()]), 0) * w.d
+    A = torch.cat(mats).contiguous()
+    mr = int(rows.max())
+    cnt = len(mats)
+    U = torch.zeros(cnt, mr, w.R, device="cuda")
+    S = torch.zeros(cnt, w.R, device="cuda")
+    Vt = torch.zeros(cnt, w.R, w.d, device="cuda")
+    ctx.rsvd_batched(A.cuda(), row_off.cuda(), rows.cuda(), mr, w.d, w.R, w.oversample, w.power_iters,
+                     w.seed, U, S, Vt)
+    torch.cuda.synchronize()
+    U, S, Vt = U.cpu().double().numpy(), S.cpu().double().numpy(), Vt.cpu().double().numpy()
+    worst, worst_orth = 0.0, 0.0
+    for m, Am in enumerate(mats):
+        Af = Am.double().numpy()
+        n = Af.shape[0]
+        r = min(w.R, n)
+        rec = U[m, :n] @ np.diag(S[m]) @ Vt[m]
+        err = np.linalg.norm(Af - rec)
+        opt = O.svd_optimum_error(Af, w.R)
+        worst = max(worst, err / (1.05 * opt + 1e-5 * np.linalg.norm(Af)))
+        assert np.all(np.diff(S[m, :r]) <= 1e-6 * S[m, 0]) and np.all(S[m] >= 0)
+        k = int((S[m] > 0).sum())
+        worst_orth = max(worst_orth, np.abs(U[m, :n, :k].T @ U[m, :n, :k] - np.eye(k)).max(),
+                         np.abs(Vt[m, :k] @ Vt[m, :k].T - np.eye(k)).max())
+    print(f"[rsvd] {cnt} matrices: worst err / (1.05 opt + 1e-5|A|) = {worst:.4f}; worst orthonormality {worst_orth:.2e}")
+    assert worst <= 1.0
+    assert worst_orth <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["tiny", "8b_4k"])
+def test_end_to_end_decode(ctx, sl, name):
+    """Library-built index and library routing against the oracle-built index
+    and oracle routing (factors differ by the randomized SVD and storage)."""
+    c = case(name)
+    w = c.w
+    idx = _gpu_build(ctx, sl, c)
+    worst = 0.0
+    q = c.q(0)
+    words, _ = gpu_route(idx, c, q, c.tau)
+    alpha_o, z_o = oracle_route_all(c, q, c.tau)
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, words)
+    flips = 0
+    for (b, l, h), ref in out_o.items():
+        zg = SC.unpack_mask(words[b, l, h], len(z_o[b, l, h]))
+        if not np.array_equal(zg, z_o[b, l, h]):
+            flips += 1
+            continue
+        worst = max(worst, SC.rel_l2(out_g[b, l, h], ref))
+    print(f"[end-to-end] {name}: worst rel-L2 {worst:.3e}; heads with routing ties skipped {flips}")
+    assert worst <= SC.REL_L2
+    idx.free()
