@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Decode throughput of the SeKV path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one decode token through every layer of the workload: per layer,
+routing (sekv_route) then attention over anchors, pseudo-tokens and the
+factored spans (sekv_decode_attend), launched layer by layer as a model's
+decode loop would.  Inputs (cache, index, queries, thresholds) are resident in
+HBM before the timed region.  Prints one JSON line on stdout.
+
+value       = decode query-tokens/s = B * K / (timed wall time of K steps)
+roofline    = the attention kernel's algorithmic bytes per launch (resident
+              K/V rows, the factor blobs of the routed union, queries, masks)
+              over its mean launch time from HIP events in the timed region,
+              against MI355X's 8 TB/s HBM peak
+cpu_baseline= the fp64 CPU oracle, single-threaded, on a bounded sample of the
+              same workload (one layer x one KV head), scaled to a full step
+pcie        = the same decode with span factors in pinned host memory and the
+              routed union gathered into an HBM ring (PCIe bytes and time per
+              step, reported beside the value, never as it)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "decode query-tokens/s at 128K ctx; achieved HBM GB/s vs peak (1 MI355X)"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def span_alg_bytes(R, d, n):
+    return 4 * R * (n + d) + 8 * R
+
+
+def kernel_source_hash():
+    p = os.path.join(ROOT, "compressed_kv_cache_sekv_amd", "csrc", "attend.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(bytes_per_launch_alg):
+    """HBM traffic per attention launch from the committed rocprofv3 PMC
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def union_alg_bytes(masks, n_spans, span_len, G, R, d):
+    """Algorithmic factor bytes of one attention launch: for every (b, g), the
+    blobs of the union over the G heads' routed spans.  masks: uint64 [B, Hq, Wd]."""
+    B, Hq, Wd = masks.shape
+    bits = np.unpackbits(masks.astype(">u8").view(np.uint8).reshape(B, Hq, Wd, 8), axis=3)[..., ::-1]
+    bits = bits.reshape(B, Hq, Wd * 64).astype(bool)
+    tot, nun = 0, 0
+    off = 0
+    for b in range(B):
+        ns = int(n_spans[b])
+        lens = span_len[off:off + ns]
+        blob = span_alg_bytes(R, d, lens.astype(np.int64))
+        for g in range(Hq // G):
+            u = bits[b, g * G:(g + 1) * G, :ns].any(0)
+            tot += int(blob[u].sum())
+            nun += int(u.sum())
+        off += ns
+    return tot, nun
+
+
+def cpu_baseline(w, H, K, V, W, gates, tau, cap, q_steps, budget_s=12.0):
+    """Time the oracle (one thread) on one (layer 0, KV head 0) unit of the
+    workload: build that unit's index (untimed), then route + attend for the
+    G query heads for as many decode steps as fit in ~budget_s."""
+    from threadpoolctl import threadpool_limits
+    from oracle import sekv_oracle as O
+    G = w.G
+    with threadpool_limits(1):
+        t0 = time.time()
+        gb = None if gates is None else gates[0][0:1, 0:1].double().numpy()
+        idx = O.build_index_b(H[0].numpy(), K[0][0:1, 0:1].double().numpy(),
+                              V[0][0:1, 0:1].double().numpy(), W[0:1, 0:G].double().numpy(), gb,
+                              R=w.R, alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=G)
+        log(f"[cpu] oracle index of one (layer, kv head) unit built in {time.time() - t0:.1f} s")
+        Wn = W[0, 0:G].double().numpy()
+        done, t0 = 0, time.time()
+        while True:
+            q = q_steps[done % len(q_steps)][0, 0, 0:G].double().numpy()   # [G, d]
+            for h in range(G):
+                _, z = O.route_head(Wn[h], q[h], idx.s[0, h], float(tau[0, h]), cap)
+                O.decode_head(q[h], idx, 0, 0, z)
+            done += 1
+            el = time.time() - t0
+            if el > budget_s or done >= 200:
+                break
+    per_unit = el / done
+    units = w.L * w.Hkv * w.B
+    step_s = per_unit * units
+    return {"value": w.B / step_s, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{done} decode steps of one (layer 0, KV head 0) unit (route + attend for its {G} "
+                       f"query heads over the oracle-built index of that unit at T={w.T}), "
+                       f"{per_unit * 1e3:.1f} ms per unit, scaled by {units} units per step")}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_l32_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pinned", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the SeKV decode path here has no multi-GPU mode "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        return 2
+
+    import torch
+    from compressed_kv_cache_sekv_amd import synth
+    from compressed_kv_cache_sekv_amd import lib as sl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    H, K, V = synth.kv_cache(w, device=dev)
+    W = torch.stack([synth.routing_w(w, l, dev) for l in range(w.L)])
+    S_max = synth.max_spans(w.T, w.l_min)
+    gl = [[synth.gates(w, b, l, S_max, dev) for l in range(w.L)] for b in range(w.B)]
+    gates = None if gl[0][0] is None else torch.stack([torch.stack(x) for x in gl])
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {w.name} generated on the GPU in {time.time() - t0:.1f} s")
+
+    ctx = sl.Context(0)
+    t0 = time.time()
+    idx = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM), K, V, H, W, gates)
+    build_s = time.time() - t0
+    info = idx.info
+    log(f"[bench] index built in {build_s:.2f} s: spans {list(idx.n_spans)[:4]} raw {list(idx.n_raw)[:4]} "
+        f"resident {info.resident_bytes / 1e9:.2f} GB factors {info.factor_bytes / 1e9:.2f} GB")
+    _, span_len, _ = idx.spans()
+
+    tau = torch.empty(w.L, w.Hq, device=dev)
+    if w.tau is not None:
+        tau.fill_(w.tau)
+    else:
+        idx.calibrate_tau(0, w.L, synth.calibration_query(w, dev), w.frac, tau)
+    cap = int(math.floor(w.cap_frac * int(idx.n_spans.min()))) if w.cap_frac else 0
+    L, B, Hq, d, Wd = w.L, w.B, w.Hq, w.d, idx.mask_words
+    nsteps = args.warmup + args.steps
+    qs = [[synth.query(w, s, dev, layers=[l]).contiguous() for l in range(L)] for s in range(nsteps)]
+    taus = [tau[l:l + 1].contiguous() for l in range(L)]
+    masks = torch.zeros(nsteps, L, B, 1, Hq, Wd, dtype=torch.int64, device=dev)
+    outs = [torch.zeros(B, 1, Hq, d, device=dev) for _ in range(L)]
+
+    def step(s, ix=idx):
+        for l in range(L):
+            ix.route(l, 1, qs[s][l], taus[l], cap, masks[s, l], None)
+            ix.decode_attend(l, 1, qs[s][l], masks[s, l], outs[l])
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ctx.timing(True)
+    ctx.timing_read()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(args.warmup, nsteps):
+        step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed_ms = e0.elapsed_time(e1)
+    route_ms, route_n, attend_ms, attend_n = ctx.timing_read()
+    ctx.timing(False)
+    assert attend_n == args.steps * L and route_n == args.steps * L
+    value = B * args.steps / (elapsed_ms / 1e3)
+    log(f"[bench] {args.steps} steps in {elapsed_ms:.2f} ms: {value:.1f} query-tokens/s; "
+        f"attend {attend_ms / attend_n * 1e3:.1f} us/launch, route {route_ms / route_n * 1e3:.1f} us/launch")
+
+    # algorithmic bytes of the timed launches
+    mk = masks[args.warmup:].cpu().numpy().view(np.uint64)     # [K, L, B, 1, Hq, Wd]
+    res_rows = int((idx.n_spans + idx.n_raw).sum())
+    res_bytes = w.Hkv * res_rows * d * 2 * 2
+    small = B * Hq * d * 2 + B * Hq * Wd * 8
+    fac_bytes, unions = 0, 0
+    for s in range(args.steps):
+        for l in range(L):
+            fb, nu = union_alg_bytes(mk[s, l][:, 0], idx.n_spans, span_len, w.G, w.R, d)
+            fac_bytes += fb
+            unions += nu
+    launches = args.steps * L
+    attend_bytes = launches * (res_bytes + small) + fac_bytes
+    per_launch = attend_bytes / launches
+    achieved = attend_bytes / (attend_ms / 1e3) / 1e9
+    route_bytes = launches * (Hq * w.dprime * int(idx.n_spans.sum()) * 4 + Hq * w.dprime * d * 4)
+    route_gbs = route_bytes / (route_ms / 1e3) / 1e9
+    traffic = traffic_from_profile(per_launch)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed_ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "query_heads": Hq, "kv_heads": w.Hkv, "head_dim": d,
+                   "batch": B, "context": w.T, "R": w.R, "dprime": w.dprime,
+                   "expand_frac_target": w.frac if w.tau is None else None, "tau": w.tau,
+                   "cap": cap, "factor_tier": "hbm", "launch": "per layer: route + decode_attend"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "attend_kernel", "alg_bytes_per_launch": int(per_launch),
+                     "mean_launch_us": round(attend_ms / attend_n * 1e3, 2)},
+        "route_roofline": {"achieved": round(route_gbs, 1), "unit": "GB/s",
+                           "mean_launch_us": round(route_ms / route_n * 1e3, 2)},
+        "index": {"build_s": round(build_s, 3), "spans": [int(x) for x in idx.n_spans[:4]],
+                  "raw": [int(x) for x in idx.n_raw[:4]], "union_spans_per_launch": round(unions / launches, 1),
+                  "resident_gb": round(info.resident_bytes / 1e9, 3),
+                  "factor_gb": round(info.factor_bytes / 1e9, 3)},
+    }
+
+    if not args.no_pinned and w.tier == "pinned":
+        # same decode with the factor pool in pinned host memory
+        del idx
+        torch.cuda.synchronize()
+        t0 = time.time()
+        pidx = ctx.build_index(sl.build_params(w, tier=sl.TIER_PINNED_HOST), K, V, H, W, gates)
+        log(f"[bench] pinned-tier index built in {time.time() - t0:.2f} s")
+        psteps = min(4, args.steps)
+        pb = pc = 0
+        pms = 0.0
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for s in range(args.warmup, args.warmup + psteps):
+            for l in range(L):
+                pidx.route(l, 1, qs[s][l], taus[l], cap, masks[s, l], None)
+                st = pidx.decode_attend(l, 1, qs[s][l], masks[s, l], outs[l], stats=True)
+                pb += st.pcie_bytes
+                pc += st.pcie_copies
+                pms += st.pcie_ms
+        torch.cuda.synchronize()
+        wall = time.time() - t0
+        result["pcie"] = {"steps": psteps, "bytes_per_step": int(pb / psteps),
+                          "copies_per_step": int(pc / psteps), "copy_ms_per_step": round(pms / psteps, 3),
+                          "GB_per_s": round(pb / (pms / 1e3) / 1e9, 2) if pms > 0 else None,
+                          "query_tokens_per_s_incl_pcie": round(B * psteps / wall, 3)}
+        log(f"[bench] pinned tier: {pb / psteps / 1e9:.3f} GB and {pc / psteps:.0f} copies per step, "
+            f"{pms / psteps:.1f} ms of copies per step, {B * psteps / wall:.2f} query-tokens/s with PCIe")
+        del pidx
+
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        Hc = H.cpu()
+        Kc = K[:, 0:1, 0:1].cpu()
+        Vc = V[:, 0:1, 0:1].cpu()
+        Wc = W.cpu()
+        gc = None if gates is None else gates[:, 0:1, 0:1].cpu()
+        qc = [qs[s][0].cpu() for s in range(args.warmup, nsteps)]
+        result["cpu_baseline"] = cpu_baseline(w, Hc, Kc, Vc, Wc, gc, tau.cpu().numpy(), cap, qc)
+        log(f"[bench] cpu baseline in {time.time() - t0:.1f} s: {result['cpu_baseline']['value']:.4f} query-tokens/s")
+
+    print(json.dumps(result), flush=True)
+    ctx.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

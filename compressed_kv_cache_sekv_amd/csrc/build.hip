@@ -186,12 +186,23 @@ hipError_t launch_pack_raw(const PackArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ summaries ---
-// One wave per (b, l, g, span): surprisal-weighted mean key/value (fp32
-// accumulation; uniform weights if the weights sum to zero), stored as the
-// span's pseudo row in bf16, and s^(l,h) = W^(l,h) kbar (unrounded kbar) for
-// the G query heads of KV head g.  grid (ceil(max_spans/4), B, L*Hkv).
+// Correctly rounded fp64 -> bf16 (round to nearest even): round to odd into
+// fp32 first (24 >= 8 + 2 bits), then round to nearest even; this composition
+// equals direct rounding (no double-rounding error).
+__device__ __forceinline__ bf16_t f64_to_bf16(double x) {
+  float f = __double2float_rz(x);
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x) u |= 1u;
+  return (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One wave per (b, l, g, span): surprisal-weighted mean key/value in fp64
+// (uniform weights if the weights sum to zero), stored as the span's pseudo
+// row in bf16, and s^(l,h) = W^(l,h) kbar in fp64 from the unrounded kbar,
+// stored fp32, for the G query heads of KV head g.  grid (ceil(max_spans/4),
+// B, L*Hkv).
 __global__ __launch_bounds__(256) void summaries_kernel(const PackArgs a) {
-  __shared__ float s_k[4][128];
+  __shared__ double s_k[4][128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int S = blockIdx.x * 4 + wave, b = blockIdx.y, lg = blockIdx.z;
   const int l = lg / a.Hkv, g = lg - l * a.Hkv, D = a.D;
@@ -204,32 +215,32 @@ __global__ __launch_bounds__(256) void summaries_kernel(const PackArgs a) {
     const bf16_t* K = a.K + src;
     const bf16_t* V = a.V + src;
     const int per = D >> 6;  // dims per lane: 1 (d=64) or 2 (d=128)
-    float ak[2] = {0.f, 0.f}, av[2] = {0.f, 0.f}, ws = 0.f;
+    double ak[2] = {0.0, 0.0}, av[2] = {0.0, 0.0}, ws = 0.0;
     for (int t = 0; t < n; ++t) {
-      const float w = H[t];
+      const double w = (double)H[t];
       ws += w;
       for (int e = 0; e < per; ++e) {
-        ak[e] += w * bf(K[(int64_t)t * D + per * lane + e]);
-        av[e] += w * bf(V[(int64_t)t * D + per * lane + e]);
+        ak[e] += w * (double)bf(K[(int64_t)t * D + per * lane + e]);
+        av[e] += w * (double)bf(V[(int64_t)t * D + per * lane + e]);
       }
     }
-    if (ws == 0.f) {
-      ws = (float)n;
-      ak[0] = ak[1] = av[0] = av[1] = 0.f;
+    if (ws == 0.0) {
+      ws = (double)n;
+      ak[0] = ak[1] = av[0] = av[1] = 0.0;
       for (int t = 0; t < n; ++t)
         for (int e = 0; e < per; ++e) {
-          ak[e] += bf(K[(int64_t)t * D + per * lane + e]);
-          av[e] += bf(V[(int64_t)t * D + per * lane + e]);
+          ak[e] += (double)bf(K[(int64_t)t * D + per * lane + e]);
+          av[e] += (double)bf(V[(int64_t)t * D + per * lane + e]);
         }
     }
     const int64_t dst = bm.res_base + (int64_t)lg * bm.n_res_pad * D;
     const int prow = bm.n_raw + S;
     for (int e = 0; e < per; ++e) {
       const int dim = per * lane + e;
-      const float kb = ak[e] / ws, vb = av[e] / ws;
+      const double kb = ak[e] / ws, vb = av[e] / ws;
       s_k[wave][dim] = kb;
-      a.kres[dst + krow_off(prow, dim, D)] = to_bf16(kb);
-      a.vres[dst + vrow_off(prow, dim, D)] = to_bf16(vb);
+      a.kres[dst + krow_off(prow, dim, D)] = f64_to_bf16(kb);
+      a.vres[dst + vrow_off(prow, dim, D)] = f64_to_bf16(vb);
     }
   }
   __syncthreads();
@@ -238,9 +249,9 @@ __global__ __launch_bounds__(256) void summaries_kernel(const PackArgs a) {
   for (int o = lane; o < G * a.dp; o += 64) {
     const int hh = g * G + o / a.dp, j = o - (o / a.dp) * a.dp;
     const float* w = a.W + (((int64_t)l * a.Hq + hh) * a.dp + j) * D;
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc += w[d] * s_k[wave][d];
-    a.s[bm.s_base + (((int64_t)l * a.Hq + hh) * a.dp + j) * bm.s_pad + S] = acc;
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += (double)w[d] * s_k[wave][d];
+    a.s[bm.s_base + (((int64_t)l * a.Hq + hh) * a.dp + j) * bm.s_pad + S] = (float)acc;
   }
 }
 

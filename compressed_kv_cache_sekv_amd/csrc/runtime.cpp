@@ -82,10 +82,52 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
+// Event pairs bracketing kernel launches (instrumentation).
+struct Timer {
+  std::vector<hipEvent_t> ev;   // 2 per launch, reused across periods
+  size_t used = 0;
+  hipError_t begin(hipStream_t st, size_t* slot) {
+    if (used + 2 > ev.size()) {
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t e;
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return r;
+        ev.push_back(e);
+      }
+    }
+    *slot = used;
+    used += 2;
+    return hipEventRecord(ev[*slot], st);
+  }
+  hipError_t end(hipStream_t st, size_t slot) { return hipEventRecord(ev[slot + 1], st); }
+  hipError_t drain(double* ms, int64_t* n) {
+    double t = 0.0;
+    for (size_t i = 0; i < used; i += 2) {
+      hipError_t r = hipEventSynchronize(ev[i + 1]);
+      if (r != hipSuccess) return r;
+      float x = 0.f;
+      r = hipEventElapsedTime(&x, ev[i], ev[i + 1]);
+      if (r != hipSuccess) return r;
+      t += x;
+    }
+    if (ms) *ms = t;
+    if (n) *n = (int64_t)(used / 2);
+    used = 0;
+    return hipSuccess;
+  }
+  void release() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    used = 0;
+  }
+};
+
 struct sekv_ctx {
   uint32_t magic = CTX_MAGIC;
   int device = 0;
   hipStream_t stream = nullptr;
+  bool timing = false;
+  Timer t_route, t_attend;
 };
 
 struct sekv_index {
@@ -334,8 +376,32 @@ extern "C" void sekv_destroy(sekv_ctx* c) {
   if (!c || c->magic != CTX_MAGIC) return;
   (void)hipSetDevice(c->device);
   (void)hipStreamSynchronize(c->stream);
+  c->t_route.release();
+  c->t_attend.release();
   c->magic = DEAD_MAGIC;
   delete c;
+}
+
+extern "C" sekv_status sekv_timing_enable(sekv_ctx* c, int32_t enable) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = set_device(c))) return st;
+  double ms;
+  int64_t n;
+  HIP_TRY(c->t_route.drain(&ms, &n));
+  HIP_TRY(c->t_attend.drain(&ms, &n));
+  c->timing = enable != 0;
+  return SEKV_OK;
+}
+
+extern "C" sekv_status sekv_timing_read(sekv_ctx* c, double* route_ms, int64_t* route_n, double* attend_ms,
+                                        int64_t* attend_n) {
+  sekv_status st = check_ctx(c);
+  if (st) return st;
+  if ((st = set_device(c))) return st;
+  HIP_TRY(c->t_route.drain(route_ms, route_n));
+  HIP_TRY(c->t_attend.drain(attend_ms, attend_n));
+  return SEKV_OK;
 }
 
 extern "C" const char* sekv_last_error(void) { return g_err.c_str(); }
@@ -680,19 +746,23 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
   if ((st = set_device(c))) return st;
   hipStream_t stream = c->stream;
   const int B = x->B, D = x->D, R = x->R, L = x->L, Hkv = x->Hkv, Hq = x->Hq, dp = x->dp;
-  std::vector<bf16_t> kres((size_t)x->kres_elems), vres((size_t)x->kres_elems);
-  std::vector<float> s((size_t)x->s_elems);
+  const bool want_res = h->k_res || h->v_res;
+  const bool want_fac = h->uk || h->uv || h->vkt || h->vvt || h->smk || h->smv;
+  std::vector<bf16_t> kres(want_res ? (size_t)x->kres_elems : 0), vres(want_res ? (size_t)x->kres_elems : 0);
+  std::vector<float> s(h->s ? (size_t)x->s_elems : 0);
   std::vector<int32_t> sst((size_t)std::max<int64_t>(x->total_spans, 1)), rp((size_t)std::max<int64_t>(x->total_raw, 1));
   std::vector<uint8_t> pool;
   const uint8_t* pool_src = x->h_pool;
-  if (x->tier == SEKV_TIER_HBM) {
+  if (x->tier == SEKV_TIER_HBM && want_fac) {
     pool.resize((size_t)x->pool_bytes);
     HIP_TRY(hipMemcpyAsync(pool.data(), x->d_pool.p, pool.size(), hipMemcpyDeviceToHost, stream));
     pool_src = pool.data();
   }
-  HIP_TRY(hipMemcpyAsync(kres.data(), x->d_kres.p, 2 * kres.size(), hipMemcpyDeviceToHost, stream));
-  HIP_TRY(hipMemcpyAsync(vres.data(), x->d_vres.p, 2 * vres.size(), hipMemcpyDeviceToHost, stream));
-  HIP_TRY(hipMemcpyAsync(s.data(), x->d_s.p, 4 * s.size(), hipMemcpyDeviceToHost, stream));
+  if (want_res) {
+    HIP_TRY(hipMemcpyAsync(kres.data(), x->d_kres.p, 2 * kres.size(), hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipMemcpyAsync(vres.data(), x->d_vres.p, 2 * vres.size(), hipMemcpyDeviceToHost, stream));
+  }
+  if (h->s) HIP_TRY(hipMemcpyAsync(s.data(), x->d_s.p, 4 * s.size(), hipMemcpyDeviceToHost, stream));
   if (x->total_spans)
     HIP_TRY(hipMemcpyAsync(sst.data(), x->d_span_start.p, 4 * (size_t)x->total_spans, hipMemcpyDeviceToHost, stream));
   if (x->total_raw)
@@ -707,7 +777,7 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
     const int NS = m.n_spans, NR = m.n_res;
     int64_t ntok = 0;
     for (int S = 0; S < NS; ++S) ntok += x->h_span_len[m.span_base + S];
-    for (int lg = 0; lg < L * Hkv; ++lg) {
+    for (int lg = 0; want_res && lg < L * Hkv; ++lg) {
       const int64_t src = m.res_base + (int64_t)lg * m.n_res_pad * D;
       for (int r = 0; r < NR; ++r)
         for (int d = 0; d < D; ++d) {
@@ -723,7 +793,7 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
           for (int S = 0; S < NS; ++S)
             h->s[so + ((int64_t)lh * dp + j) * NS + S] = s[m.s_base + ((int64_t)lh * dp + j) * m.s_pad + S];
     so += (int64_t)L * Hq * dp * NS;
-    for (int l = 0; l < L; ++l)
+    for (int l = 0; want_fac && l < L; ++l)
       for (int g = 0; g < Hkv; ++g) {
         const int lg = l * Hkv + g;
         int64_t toff = 0;
@@ -786,7 +856,10 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = cap;
+  size_t slot = 0;
+  if (c->timing) HIP_TRY(c->t_route.begin(c->stream, &slot));
   HIP_TRY(launch_route(ra, c->stream));
+  if (c->timing) HIP_TRY(c->t_route.end(c->stream, slot));
   return SEKV_OK;
 }
 
@@ -954,7 +1027,12 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   aa.max_spans = std::max(x->max_spans, 1);
   aa.tpw = kTilesPerItem;
   aa.scale = 1.0f / sqrtf((float)x->D);
-  if (n_items > 0) HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
+  if (n_items > 0) {
+    size_t slot = 0;
+    if (c->timing) HIP_TRY(c->t_attend.begin(c->stream, &slot));
+    HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
+    if (c->timing) HIP_TRY(c->t_attend.end(c->stream, slot));
+  }
   ReduceArgs rd{};
   rd.part = (const float*)x->d_part.p;
   rd.items = (const WorkItem*)x->d_items.p;

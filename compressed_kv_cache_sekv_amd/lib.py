@@ -28,7 +28,8 @@ STATUS = {0: "SEKV_OK", 1: "SEKV_EINVAL", 2: "SEKV_ENOMEM", 3: "SEKV_EHIP",
 EXPORTS = ("sekv_create", "sekv_destroy", "sekv_last_error", "sekv_max_spans",
            "sekv_validate_params", "sekv_rsvd_batched", "sekv_build_index", "sekv_index_import", "sekv_index_export",
            "sekv_index_get_info", "sekv_index_counts", "sekv_index_free",
-           "sekv_route", "sekv_calibrate_tau", "sekv_decode_attend")
+           "sekv_route", "sekv_calibrate_tau", "sekv_decode_attend",
+           "sekv_timing_enable", "sekv_timing_read")
 
 
 class SekvError(RuntimeError):
@@ -95,6 +96,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.sekv_route.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
     lib.sekv_calibrate_tau.argtypes = [vp, vp, i32, i32, vp, f32, vp]
     lib.sekv_decode_attend.argtypes = [vp, vp, i32, i32, vp, vp, vp, C.POINTER(Stats)]
+    lib.sekv_timing_enable.argtypes = [vp, i32]
+    lib.sekv_timing_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i64),
+                                     C.POINTER(C.c_double), C.POINTER(i64)]
     return lib
 
 
@@ -162,6 +166,17 @@ class Context:
         except Exception:
             pass
 
+    # -- instrumentation ------------------------------------------------------
+    def timing(self, enable: bool):
+        check(lib().sekv_timing_enable(self.h, 1 if enable else 0))
+
+    def timing_read(self):
+        """(route_ms, route_launches, attend_ms, attend_launches) since the last read."""
+        rm, rn = C.c_double(), C.c_int64()
+        am, an = C.c_double(), C.c_int64()
+        check(lib().sekv_timing_read(self.h, C.byref(rm), C.byref(rn), C.byref(am), C.byref(an)))
+        return rm.value, rn.value, am.value, an.value
+
     # -- prefill --------------------------------------------------------------
     def rsvd_batched(self, A, row_off, rows, max_rows, d, R, oversample, power_iters, seed, U, sigma, Vt):
         check(lib().sekv_rsvd_batched(self.h, int(rows.numel()), _ptr(A), _ptr(row_off), _ptr(rows),
@@ -223,6 +238,16 @@ class Index:
         check(lib().sekv_decode_attend(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q),
                                        _ptr(mask), _ptr(out), C.byref(st) if st is not None else None))
         return st
+
+    def spans(self):
+        """(span_start, span_len, raw_pos) of every sequence, concatenated over b."""
+        i = self.info
+        out = dict(span_start=np.zeros(int(i.total_spans), np.int32),
+                   span_len=np.zeros(int(i.total_spans), np.int32),
+                   raw_pos=np.zeros(int(i.total_raw), np.int32))
+        ho = HostIndexOut(**{k: (v.ctypes.data if v.size else None) for k, v in out.items()})
+        check(lib().sekv_index_export(self.ctx.h, self.h, C.byref(ho)))
+        return out["span_start"], out["span_len"], out["raw_pos"]
 
     def export(self) -> dict:
         """Logical-layout numpy arrays of the whole index."""

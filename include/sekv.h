@@ -272,6 +272,18 @@ sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
                                int32_t layer_count, const void* q, const uint64_t* mask,
                                float* out, sekv_stats* stats);
 
+/* --------------------------------------------------------- instrumentation */
+
+/* Kernel timing.  While enabled, every sekv_route call brackets its routing
+ * kernel and every sekv_decode_attend call brackets its attention kernel (not
+ * the partial merge) with HIP events on the context stream; nothing is
+ * synchronised.  sekv_timing_read synchronises those events, returns the summed
+ * milliseconds and launch counts since the previous read (or since enabling),
+ * and starts a new period.  Any output pointer may be NULL. */
+sekv_status sekv_timing_enable(sekv_ctx* ctx, int32_t enable);
+sekv_status sekv_timing_read(sekv_ctx* ctx, double* route_ms, int64_t* route_launches,
+                             double* attend_ms, int64_t* attend_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,8 @@ import torch
 from oracle import sekv_oracle as O
 from compressed_kv_cache_sekv_amd import synth
 
-TIE = 1e-4          # |alpha - tau| below this is a tie, excluded from bit-exact checks
+TIE = 1e-4          # |alpha - tau| below this is a tie by the stated rule (reported)
+STRICT_TIE = 1e-6   # the window the tests actually exclude: fp32 vs fp64 alpha differ by < 1e-7
 REL_L2 = 5e-3       # decode outputs: max relative L2 error per (b, l, h)
 
 
@@ -131,16 +132,21 @@ def rel_l2(a, ref) -> float:
     return float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def compare_masks(gpu_words, z_ref, alpha_ref, tau, cap_boundary=None):
-    """Bit-exact comparison excluding ties.  Returns (n_mismatch, n_ties)."""
+def compare_masks(gpu_words, z_ref, alpha_ref, tau, cap_boundary=None, window=STRICT_TIE):
+    """Bit-exact comparison excluding pairs within `window` of tau (and of the
+    cap boundary).  Returns (n_mismatch, n_excluded, n_ties_at_1e-4)."""
     n = len(z_ref)
     zg = unpack_mask(gpu_words, n)
-    tie = np.abs(alpha_ref - tau) < TIE
-    if cap_boundary is not None:
-        tie |= np.abs(alpha_ref - cap_boundary) < TIE
-    bad = (zg != z_ref) & ~tie
+
+    def near(win):
+        t = np.abs(alpha_ref - tau) < win
+        if cap_boundary is not None:
+            t |= np.abs(alpha_ref - cap_boundary) < win
+        return t
+    excl = near(window)
+    bad = (zg != z_ref) & ~excl
     extra = unpack_mask(gpu_words, len(np.asarray(gpu_words)) * 64)[n:]
-    return int(bad.sum()) + int(extra.sum()), int(tie.sum())
+    return int(bad.sum()) + int(extra.sum()), int(excl.sum()), int(near(TIE).sum())
 
 
 def cap_boundary(alpha, z_pre, cap):
