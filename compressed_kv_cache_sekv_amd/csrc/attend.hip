@@ -5,11 +5,10 @@
 // factors and merged into the attention output; section 기술 상세 (Technical
 // details) gives the reconstruction Khat_S = sum_i m_i sigma_i u_i v_i^T.
 //
-// One workgroup (4 waves) per work item, partials per item, then a merge
-// kernel.  Items of kind 0 stream 64-row tiles of resident rows (raw tokens,
-// then one pseudo row per span); items of kind 1 take an equal share of the
-// union over the G query heads of a KV head's routed spans.  Per span the
-// reconstruction is never materialised:
+// One workgroup (4 waves) per work item.  Items of kind 0 stream 64-row tiles
+// of resident rows (raw tokens, then one pseudo row per span); items of kind 1
+// take an equal share of the union over the G query heads of a KV head's
+// routed spans.  Per span the reconstruction is never materialised:
 //     t = V^K^T q                    (R)      MFMA 16x16x32, A = V^K^T tile
 //     scores = U^K (t . sigma m^K)/sqrt(d)    MFMA 16x16x16, A = U^K tile
 //     w = U^V^T p                    (R)      MFMA 16x16x16, A = U^V^T tile
@@ -19,6 +18,12 @@
 // occupy the 16 MFMA columns (G of them live).  fp32 operands that feed a
 // bf16 MFMA (softmax weights, scaled t, gated w) are split hi + lo into two
 // bf16 terms, which keeps ~16 mantissa bits; every accumulation is fp32.
+//
+// A span's factor blob is loaded in one round trip (all its loads issued
+// before any arithmetic); for R = 16 the next span's blob is in flight while
+// the current one is computed.  Each workgroup writes one softmax partial
+// (m, l, o) per head; the last workgroup of a (b, l, g) to finish (atomic
+// ticket) merges them into the output, so no second kernel is launched.
 #include "common.h"
 
 namespace sekv {
@@ -73,17 +78,10 @@ __device__ __forceinline__ float xsum4(float v) {
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Running softmax state of one lane: head hl = lane & 15; lanes that share hl
-// hold identical m and l.
-template <int ND16>
-struct Acc {
-  float m, l;
-  floatx4 o[ND16];  // o[dim = 16*db + 4*(lane/16) + r][head hl]
-};
-
-// Fold a block of scores (already scaled, masked to -inf) into the state and
-// return the softmax weights relative to the new running max.  `corr` is the
-// factor by which older accumulations must be scaled.
+// Fold a block of scores (already scaled, masked to -inf) into the running
+// softmax state (m, l) of this lane's head and turn them into weights
+// relative to the new running max.  Returns the factor by which older
+// accumulations must be scaled.
 template <int NB>
 __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, float& l) {
   float mx = -INFINITY;
@@ -112,14 +110,160 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
   return corr;
 }
 
+// Registers of one span blob: the fixed-size factors plus the first chunk
+// (up to 64 tokens) of the left factors.
+template <int D, int R>
+struct SpanRegs {
+  static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
+  u32x4 vkt[NR16][NS32];
+  u32x2 vv[ND16][NR16];
+  floatx4 smk[NR16], smv[NR16];
+  u32x2 uk[4][NR16];
+  u32x2 uvt[NR16][4];
+  const uint8_t* blob;
+  int n, hm;
+
+  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp) {
+    blob = b;
+    n = n_;
+    hm = hm_;
+    const bf16_t* pk = (const bf16_t*)(b + Blob::off_vkt(R, D));
+    const bf16_t* pv = (const bf16_t*)(b + Blob::off_vv(R, D));
+    const float* sk = (const float*)(b + Blob::off_smk(R, D));
+    const float* sv = (const float*)(b + Blob::off_smv(R, D));
+    const bf16_t* pu = (const bf16_t*)(b + Blob::off_uk(R, D));
+    const bf16_t* pw = (const bf16_t*)(b + Blob::off_uvt(R, D, n_));
+    const int ntb = Blob::npad(n_) >> 4;
+#pragma unroll
+    for (int ib = 0; ib < NR16; ++ib)
+#pragma unroll
+      for (int s = 0; s < NS32; ++s) vkt[ib][s] = *(const u32x4*)(pk + ib * 16 * D + s * 512 + lane * 8);
+#pragma unroll
+    for (int ib = 0; ib < NR16; ++ib) {
+      smk[ib] = *(const floatx4*)(sk + 16 * ib + 4 * grp);
+      smv[ib] = *(const floatx4*)(sv + 16 * ib + 4 * grp);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+      if (tb < ntb)
+#pragma unroll
+        for (int kb = 0; kb < NR16; ++kb)
+          uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tb * NR16 + kb) * 256 + lane * 4);
+#pragma unroll
+    for (int ib = 0; ib < NR16; ++ib)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (tb < ntb) uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tb) * 256 + lane * 4);
+#pragma unroll
+    for (int db = 0; db < ND16; ++db)
+#pragma unroll
+      for (int kb = 0; kb < NR16; ++kb) vv[db][kb] = *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+  }
+};
+
+// Attention over one routed span in factored form, folded into (m, l, o).
+template <int D, int G, int R>
+__device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 (&qB)[D / 32], float scale,
+                                          int lane, int hl, int grp, float& m, float& l,
+                                          floatx4 (&o)[D / 16]) {
+  constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
+  const int n = sr.n, npad = Blob::npad(n), ntb = npad >> 4;
+  // t = V^K^T q; c = t * sigma m^K / sqrt(d), split into bf16 hi + lo
+  u32x2 chi[NR16], clo[NR16];
+#pragma unroll
+  for (int ib = 0; ib < NR16; ++ib) {
+    floatx4 t = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < NS32; ++s) t = mfma32(sr.vkt[ib][s], qB[s], t);
+    pack4(t * sr.smk[ib] * scale, chi[ib], clo[ib]);
+  }
+  const bool act = (hl < G) && ((sr.hm >> hl) & 1);
+  const bf16_t* pu = (const bf16_t*)(sr.blob + Blob::off_uk(R, D));
+  const bf16_t* pw = (const bf16_t*)(sr.blob + Blob::off_uvt(R, D, n));
+  floatx4 wacc[NR16];
+#pragma unroll
+  for (int ib = 0; ib < NR16; ++ib) wacc[ib] = floatx4{0, 0, 0, 0};
+  for (int tb0 = 0; tb0 < ntb; tb0 += 4) {
+    const int nb = min(4, ntb - tb0);
+    u32x2 uk[4][NR16], uvt[NR16][4];
+    if (tb0 == 0) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int kb = 0; kb < NR16; ++kb) {
+          uk[tb][kb] = sr.uk[tb][kb];
+          uvt[kb][tb] = sr.uvt[kb][tb];
+        }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if (tb < nb)
+#pragma unroll
+          for (int kb = 0; kb < NR16; ++kb) {
+            uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4);
+            uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tb0 + tb) * 256 + lane * 4);
+          }
+    }
+    floatx4 sc[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      sc[tb] = floatx4{0, 0, 0, 0};
+      if (tb < nb) {
+#pragma unroll
+        for (int kb = 0; kb < NR16; ++kb) {
+          sc[tb] = mfma16(uk[tb][kb], chi[kb], sc[tb]);
+          sc[tb] = mfma16(uk[tb][kb], clo[kb], sc[tb]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = 16 * (tb0 + tb) + 4 * grp + r;
+          if (!act || tok >= n) sc[tb][r] = -INFINITY;
+        }
+      }
+    }
+    const float corr = online<4>(sc, nb, m, l);
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) o[db] *= corr;
+#pragma unroll
+    for (int ib = 0; ib < NR16; ++ib) wacc[ib] *= corr;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      if (tb < nb) {
+        u32x2 phi, plo;
+        pack4(sc[tb], phi, plo);
+#pragma unroll
+        for (int ib = 0; ib < NR16; ++ib) {
+          wacc[ib] = mfma16(uvt[ib][tb], phi, wacc[ib]);
+          wacc[ib] = mfma16(uvt[ib][tb], plo, wacc[ib]);
+        }
+      }
+    }
+  }
+  // o += V^V (sigma m^V . w)
+  u32x2 whi[NR16], wlo[NR16];
+#pragma unroll
+  for (int ib = 0; ib < NR16; ++ib) pack4(wacc[ib] * sr.smv[ib], whi[ib], wlo[ib]);
+#pragma unroll
+  for (int db = 0; db < ND16; ++db)
+#pragma unroll
+    for (int kb = 0; kb < NR16; ++kb) {
+      o[db] = mfma16(sr.vv[db][kb], whi[kb], o[db]);
+      o[db] = mfma16(sr.vv[db][kb], wlo[kb], o[db]);
+    }
+}
+
 template <int D, int G, int R>
 __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
-  constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
+  constexpr int NS32 = D / 32, ND16 = D / 16;
+  constexpr bool PREFETCH = (R <= 16);
   static_assert(G >= 1 && G <= 16, "G");
   __shared__ float s_ml[4][2][G];
   __shared__ float s_o[4][G][D];
   __shared__ uint64_t s_uw[1024];
   __shared__ int32_t s_pre[1025];
+  __shared__ float s_red[256];
+  __shared__ float s_M[G], s_L[G];
+  __shared__ int s_last;
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -139,11 +283,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   }
   const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + lc) * Hq + g * G) * Wd;
 
-  Acc<ND16> acc;
-  acc.m = -INFINITY;
-  acc.l = 0.f;
+  // running softmax state of this lane's head hl; o[dim = 16*db + 4*grp + r]
+  float m = -INFINITY, lsum = 0.f;
+  floatx4 o[ND16];
 #pragma unroll
-  for (int db = 0; db < ND16; ++db) acc.o[db] = floatx4{0, 0, 0, 0};
+  for (int db = 0; db < ND16; ++db) o[db] = floatx4{0, 0, 0, 0};
   const float scale = a.scale;
 
   if (it.kind == 0) {
@@ -190,17 +334,17 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
           }
           S[kb][r] = x;
         }
-      const float corr = online<4>(S, 4, acc.m, acc.l);
+      const float corr = online<4>(S, 4, m, lsum);
 #pragma unroll
-      for (int db = 0; db < ND16; ++db) acc.o[db] *= corr;
+      for (int db = 0; db < ND16; ++db) o[db] *= corr;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         u32x4 phi, plo;
         pack8(S[2 * rb], S[2 * rb + 1], phi, plo);
 #pragma unroll
         for (int db = 0; db < ND16; ++db) {
-          acc.o[db] = mfma32(vt[rb][db], phi, acc.o[db]);
-          acc.o[db] = mfma32(vt[rb][db], plo, acc.o[db]);
+          o[db] = mfma32(vt[rb][db], phi, o[db]);
+          o[db] = mfma32(vt[rb][db], plo, o[db]);
         }
       }
     }
@@ -237,7 +381,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     const int k0 = beg + (int)((int64_t)(end - beg) * wave / 4);
     const int k1 = beg + (int)((int64_t)(end - beg) * (wave + 1) / 4);
     if (k0 < k1) {
-      // locate rank k0: largest word w with s_pre[w] <= k0 and a set bit
+      // locate rank k0: largest word w with s_pre[w] <= k0 (it has a set bit)
       int lo = 0, hi = Wd - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -249,9 +393,11 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
       const int64_t* roff = a.ring_off
           ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans : nullptr;
-      for (int k = k0; k < k1; ++k) {
+      // next union span in rank order: its blob, length and active heads
+      int k_next = k0;
+      auto next_span = [&](SpanRegs<D, R>& sr) -> bool {
         while (bits == 0 && w + 1 < Wd) bits = s_uw[++w];
-        if (bits == 0) break;  // unreachable when the ranks are consistent
+        if (bits == 0) return false;  // unreachable when the ranks are consistent
         const int bit = __builtin_ctzll(bits);
         bits &= bits - 1;
         const int S = uni(64 * w + bit);
@@ -259,85 +405,26 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) hm |= (int)((mrow[(int64_t)h * Wd + w] >> bit) & 1ull) << h;
         const int n = uni(a.span_len[bm.span_base + S]);
-        const int npad = (n + 15) & ~15;
-        const uint8_t* blob = roff ? a.pool + roff[k] : region + a.span_off[bm.span_base + S];
-        const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt(R, D));
-        const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(R, D));
-        const float* smk = (const float*)(blob + Blob::off_smk(R, D));
-        const float* smv = (const float*)(blob + Blob::off_smv(R, D));
-        const bf16_t* uk = (const bf16_t*)(blob + Blob::off_uk(R, D));
-        const bf16_t* uvt = (const bf16_t*)(blob + Blob::off_uvt(R, D, n));
-
-        // t = V^K^T q, then c = t * sigma m^K / sqrt(d) split into bf16 hi + lo
-        u32x2 chi[NR16], clo[NR16];
-#pragma unroll
-        for (int ib = 0; ib < NR16; ++ib) {
-          floatx4 t = floatx4{0, 0, 0, 0};
-#pragma unroll
-          for (int s = 0; s < NS32; ++s)
-            t = mfma32(*(const u32x4*)(vkt + ib * 16 * D + s * 512 + lane * 8), qB[s], t);
-          const floatx4 sm = *(const floatx4*)(smk + 16 * ib + 4 * grp);
-          pack4(t * sm * scale, chi[ib], clo[ib]);
-        }
-        const bool act = (hl < G) && ((hm >> hl) & 1);
-        floatx4 wacc[NR16];
-#pragma unroll
-        for (int ib = 0; ib < NR16; ++ib) wacc[ib] = floatx4{0, 0, 0, 0};
-        const int ntb = npad >> 4;
-        for (int tb0 = 0; tb0 < ntb; tb0 += 4) {
-          const int nb = min(4, ntb - tb0);
-          floatx4 sc[4];
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            sc[tb] = floatx4{0, 0, 0, 0};
-            if (tb < nb) {
-#pragma unroll
-              for (int kb = 0; kb < NR16; ++kb) {
-                const u32x2 ukv = *(const u32x2*)(uk + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4);
-                sc[tb] = mfma16(ukv, chi[kb], sc[tb]);
-                sc[tb] = mfma16(ukv, clo[kb], sc[tb]);
-              }
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int tok = 16 * (tb0 + tb) + 4 * grp + r;
-                if (!act || tok >= n) sc[tb][r] = -INFINITY;
-              }
-            }
-          }
-          const float corr = online<4>(sc, nb, acc.m, acc.l);
-#pragma unroll
-          for (int db = 0; db < ND16; ++db) acc.o[db] *= corr;
-#pragma unroll
-          for (int ib = 0; ib < NR16; ++ib) wacc[ib] *= corr;
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            if (tb < nb) {
-              u32x2 phi, plo;
-              pack4(sc[tb], phi, plo);
-#pragma unroll
-              for (int ib = 0; ib < NR16; ++ib) {
-                const u32x2 uvv = *(const u32x2*)(uvt + ((int64_t)ib * ntb + tb0 + tb) * 256 + lane * 4);
-                wacc[ib] = mfma16(uvv, phi, wacc[ib]);
-                wacc[ib] = mfma16(uvv, plo, wacc[ib]);
-              }
-            }
+        const uint8_t* blob = roff ? a.pool + roff[k_next] : region + a.span_off[bm.span_base + S];
+        ++k_next;
+        sr.load(blob, n, hm, lane, grp);
+        return true;
+      };
+      SpanRegs<D, R> cur;
+      if (next_span(cur)) {
+        for (int k = k0; k < k1; ++k) {
+          const bool more = k + 1 < k1;
+          if (PREFETCH) {
+            SpanRegs<D, R> nxt;
+            const bool ok = more && next_span(nxt);
+            span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
+            if (!ok) break;
+            cur = nxt;
+          } else {
+            span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
+            if (!more || !next_span(cur)) break;
           }
         }
-        // o += V^V (sigma m^V . w)
-        u32x2 whi[NR16], wlo[NR16];
-#pragma unroll
-        for (int ib = 0; ib < NR16; ++ib) {
-          const floatx4 sm = *(const floatx4*)(smv + 16 * ib + 4 * grp);
-          pack4(wacc[ib] * sm, whi[ib], wlo[ib]);
-        }
-#pragma unroll
-        for (int db = 0; db < ND16; ++db)
-#pragma unroll
-          for (int kb = 0; kb < NR16; ++kb) {
-            const u32x2 vvv = *(const u32x2*)(vv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
-            acc.o[db] = mfma16(vvv, whi[kb], acc.o[db]);
-            acc.o[db] = mfma16(vvv, wlo[kb], acc.o[db]);
-          }
       }
     }
   }
@@ -345,16 +432,17 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   // ------------------------------------------- merge the 4 waves, write partial
   if (hl < G) {
     if (grp == 0) {
-      s_ml[wave][0][hl] = acc.m;
-      s_ml[wave][1][hl] = acc.l;
+      s_ml[wave][0][hl] = m;
+      s_ml[wave][1][hl] = lsum;
     }
 #pragma unroll
     for (int db = 0; db < ND16; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[wave][hl][16 * db + 4 * grp + r] = acc.o[db][r];
+      for (int r = 0; r < 4; ++r) s_o[wave][hl][16 * db + 4 * grp + r] = o[db][r];
   }
   __syncthreads();
-  float* part = a.part + ((int64_t)lc * a.n_items + blockIdx.x) * G * (D + 2);
+  const int64_t pstride = (int64_t)G * (D + 2);
+  float* part = a.part + ((int64_t)lc * a.n_items + blockIdx.x) * pstride;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, dim = idx - h * D;
     float M = -INFINITY;
@@ -374,29 +462,68 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
       part[h * (D + 2) + D + 1] = L;
     }
   }
-}
 
-// Merge the partials of every item of (b, g) into out[b][lc][h][:].
-template <int D, int G>
-__global__ __launch_bounds__(256) void reduce_kernel(const ReduceArgs a) {
-  const int bg = blockIdx.x, lc = blockIdx.y;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const int first = a.bg_first[bg];
-  const int count = a.items[first].part_count;
-  const float* base = a.part + ((int64_t)lc * a.n_items + first) * G * (D + 2);
+  // ------------------- the last workgroup of (b, l, g) merges the item partials
+  __threadfence();
+  __syncthreads();
+  uint32_t* ctr = a.counters + ((int64_t)b * a.layer_count + lc) * a.Hkv + g;
+  if (threadIdx.x == 0) s_last = (atomicAdd(ctr, 1u) == (uint32_t)it.part_count - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int P = it.part_count;
+  const float* base = a.part + ((int64_t)lc * a.n_items + it.part_first) * pstride;
+  {
+    // per-head max M and denominator L over the P partials
+    const int h = threadIdx.x % G, i0 = threadIdx.x / G, st = 256 / G;
+    float mx = -INFINITY;
+    for (int i = i0; i < P; i += st) mx = fmaxf(mx, base[i * pstride + h * (D + 2) + D]);
+    s_red[threadIdx.x] = mx;
+    __syncthreads();
+    if (threadIdx.x < G) {
+      float M = -INFINITY;
+      for (int j = threadIdx.x; j < st * G; j += G) M = fmaxf(M, s_red[j]);
+      s_M[threadIdx.x] = M;
+    }
+    __syncthreads();
+    const float M = s_M[h];
+    float ls = 0.f;
+    for (int i = i0; i < P; i += st) {
+      const float* p = base + i * pstride + h * (D + 2);
+      const float mi = p[D];
+      ls += (mi == -INFINITY) ? 0.f : __expf(mi - M) * p[D + 1];
+    }
+    __syncthreads();
+    s_red[threadIdx.x] = ls;
+    __syncthreads();
+    if (threadIdx.x < G) {
+      float L = 0.f;
+      for (int j = threadIdx.x; j < st * G; j += G) L += s_red[j];
+      s_L[threadIdx.x] = L;
+    }
+    __syncthreads();
+  }
+  // outputs: wave w sums the partials i = w (mod 4) for every (h, dim)
+  for (int idx = lane; idx < G * D; idx += 64) {
+    const int h = idx / D, dim = idx - h * D;
+    const float M = s_M[h];
+    float acc = 0.f;
+#pragma unroll 4
+    for (int i = wave; i < P; i += 4) {
+      const float* p = base + i * pstride + h * (D + 2);
+      const float mi = p[D];
+      acc += (mi == -INFINITY) ? 0.f : __expf(mi - M) * p[dim];
+    }
+    s_o[wave][h][dim] = acc;
+  }
+  __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, dim = idx - h * D;
-    float M = -INFINITY;
-    for (int i = 0; i < count; ++i) M = fmaxf(M, base[((int64_t)i * G + h) * (D + 2) + D]);
-    float O = 0.f, L = 0.f;
-    for (int i = 0; i < count; ++i) {
-      const float* p = base + ((int64_t)i * G + h) * (D + 2);
-      const float e = (p[D] == -INFINITY) ? 0.f : __expf(p[D] - M);
-      O += e * p[dim];
-      L += e * p[D + 1];
-    }
-    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
+    const float O = s_o[0][h][dim] + s_o[1][h][dim] + s_o[2][h][dim] + s_o[3][h][dim];
+    const float L = s_L[h];
+    a.out[(((int64_t)b * a.layer_count + lc) * Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
   }
+  if (threadIdx.x == 0) *ctr = 0u;
 }
 
 // ------------------------------------------------------------- dispatch
@@ -428,14 +555,6 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
   return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
     hipLaunchKernelGGL((attend_kernel<decltype(d_)::value, decltype(g_)::value, decltype(r_)::value>),
                        dim3(a.n_items, a.layer_count), dim3(256), 0, st, a);
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_reduce(const ReduceArgs& a, int D, int G, hipStream_t st) {
-  return dispatch(D, G, 16, [&](auto d_, auto g_, auto) -> hipError_t {
-    hipLaunchKernelGGL((reduce_kernel<decltype(d_)::value, decltype(g_)::value>),
-                       dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
     return hipGetLastError();
   });
 }

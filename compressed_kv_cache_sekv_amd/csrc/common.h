@@ -118,20 +118,14 @@ struct AttendArgs {
   const uint8_t* pool;      // factor pool (HBM tier) or staging ring
   const int64_t* ring_off;  // ring tier: [Lc][B][Hkv][max_spans] offset of the
                             // k-th union span's blob in the ring, else NULL
-  float* part;              // [Lc][n_items][G][D + 2]
+  float* part;              // [Lc][n_items][G][D + 2] softmax partials
+  uint32_t* counters;       // [B][Lc][Hkv] finished-item tickets (zero between launches)
+  float* out;               // [B][Lc][Hq][D]
   int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
   int32_t layer_begin, layer_count, n_items;
   int32_t B, L, Hq, Hkv, W, max_spans;
   int32_t tpw;              // resident 64-row tiles per work item
   float scale;              // 1/sqrt(d)
-};
-
-struct ReduceArgs {
-  const float* part;
-  const WorkItem* items;
-  const int32_t* bg_first;  // [B*Hkv] first item of (b, g)
-  float* out;               // [B][Lc][Hq][D]
-  int32_t layer_count, n_items, B, Hq, Hkv;
 };
 
 struct RouteArgs {
@@ -157,7 +151,6 @@ struct CalibArgs {
 
 // ------------------------------------------------------------ launchers ---
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st);
-hipError_t launch_reduce(const ReduceArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st);
 bool attend_supported(int D, int G, int R);

@@ -85,12 +85,16 @@ __device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int
   return prefix;
 }
 
+constexpr int kCapList = 2048;   // candidates ranked in LDS; more fall back to radix select
+
 __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[256];
   __shared__ uint32_t s_hist[256];
   __shared__ int s_tmp[8];
   __shared__ int s_sel[2];
-  __shared__ int s_last;
+  __shared__ int s_last, s_nc;
+  __shared__ uint64_t s_cand[kCapList];
+  __shared__ unsigned long long s_new[1024];
   const int nchunk = (a.Wd + 3) >> 2;
   const int b = blockIdx.x / nchunk, chunk = blockIdx.x - b * nchunk;
   const int h = blockIdx.y, lc = blockIdx.z, l = a.layer_begin + lc;
@@ -98,14 +102,24 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   const BMeta bm = a.meta[b];
   const int D = a.D, dp = a.dp;
 
-  // u = W^(l,h) q^(l,h), fp32
-  const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
-  const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
-  for (int j = wave; j < dp; j += 4) {
-    float acc = 0.f;
-    for (int d = lane; d < D; d += 64) acc += Wl[(int64_t)j * D + d] * bf16_to_f32(qp[d]);
-    acc = wave_sum(acc);
-    if (lane == 0) s_u[j] = acc;
+  // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims
+  {
+    const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
+    const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
+    const int qd = D >> 2, part = threadIdx.x & 3;
+    for (int j0 = 0; j0 < dp; j0 += 64) {
+      const int j = j0 + (threadIdx.x >> 2);
+      float acc = 0.f;
+      if (j < dp) {
+        const float* wr = Wl + (int64_t)j * D + part * qd;
+        const bf16_t* qq = qp + part * qd;
+#pragma unroll 8
+        for (int d = 0; d < qd; ++d) acc += wr[d] * bf16_to_f32(qq[d]);
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (part == 0 && j < dp) s_u[j] = acc;
+    }
   }
   __syncthreads();
 
@@ -120,8 +134,17 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
     bool z = false;
     if (S < bm.n_spans) {
       const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + S;
-      float dot = 0.f;
-      for (int j = 0; j < dp; ++j) dot += s_u[j] * sp[(int64_t)j * bm.s_pad];
+      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+      int j = 0;
+#pragma unroll 4
+      for (; j + 4 <= dp; j += 4) {
+        d0 += s_u[j] * sp[(int64_t)j * bm.s_pad];
+        d1 += s_u[j + 1] * sp[(int64_t)(j + 1) * bm.s_pad];
+        d2 += s_u[j + 2] * sp[(int64_t)(j + 2) * bm.s_pad];
+        d3 += s_u[j + 3] * sp[(int64_t)(j + 3) * bm.s_pad];
+      }
+      for (; j < dp; ++j) d0 += s_u[j] * sp[(int64_t)j * bm.s_pad];
+      const float dot = (d0 + d1) + (d2 + d3);
       alpha = 1.f / (1.f + expf(-dot));
       z = alpha > tau;
     }
@@ -137,18 +160,38 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   if (threadIdx.x == 0) {
     const uint32_t t = atomicAdd(&a.tickets[row], 1u);
     s_last = (t == (uint32_t)nchunk - 1);
+    s_nc = 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  int cnt = 0;
-  for (int w = threadIdx.x; w < a.Wd; w += 256) cnt += __popcll(ld_u64(mrow + w));
-  cnt = block_scan256(cnt, s_tmp);
-  if (threadIdx.x == 255) s_sel[0] = cnt;
+  __threadfence();  // acquire: the other blocks' masks and alphas are visible
+  // candidates: key = alpha bits (high) and the complemented span index (low),
+  // so key order is alpha descending, then span index ascending
+  for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = 0ull;
+  for (int S = threadIdx.x; S < bm.n_spans; S += 256) {
+    if ((mrow[S >> 6] >> (S & 63)) & 1ull) {
+      const int pos = atomicAdd(&s_nc, 1);
+      if (pos < kCapList)
+        s_cand[pos] = ((uint64_t)__float_as_uint(arow[S]) << 32) | (uint64_t)(~(uint32_t)S);
+    }
+  }
   __syncthreads();
-  const int total = s_sel[0];
-  __syncthreads();
-  if (total > a.cap) {
+  const int nc = s_nc;
+  if (nc > a.cap && nc <= kCapList) {
+    // rank of each candidate = number of larger keys (keys are distinct)
+    for (int i = threadIdx.x; i < nc; i += 256) {
+      const uint64_t ki = s_cand[i];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += s_cand[j] > ki;
+      if (rank < a.cap) {
+        const int S = (int)(~(uint32_t)(ki & 0xffffffffull));
+        atomicOr(&s_new[S >> 6], 1ull << (S & 63));
+      }
+    }
+    __syncthreads();
+    for (int w = threadIdx.x; w < a.Wd; w += 256) mrow[w] = s_new[w];
+  } else if (nc > a.cap) {
+    // large candidate sets: 4-pass radix select on alpha over global memory
     int k = a.cap;
     auto cand = [&](int S, uint32_t& key) -> bool {
       const uint64_t word = ld_u64(mrow + (S >> 6));

@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -49,9 +50,19 @@ constexpr uint32_t CTX_MAGIC = 0x53454b43u;   // "SEKC"
 constexpr uint32_t IDX_MAGIC = 0x53454b49u;   // "SEKI"
 constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
 
-// Work decomposition of the decode kernel.
-constexpr int kTilesPerItem = 4;     // resident 64-row tiles per workgroup (1 per wave)
-constexpr int kSpansPerFacItem = 32; // factored workgroups per KV head = ceil(N_S / 32)
+// Work decomposition of the decode kernel: resident 64-row tiles per
+// workgroup (default 4, one per wave) and spans per factored workgroup
+// (default 32: ceil(N_S / 32) workgroups share a KV head's routed union).
+// SEKV_TILES_PER_ITEM / SEKV_SPANS_PER_ITEM override them when an index is
+// created (tuning).
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = atoi(v);
+  return (x >= lo && x <= hi) ? x : dflt;
+}
+int tiles_per_item() { return env_int("SEKV_TILES_PER_ITEM", 4, 1, 1024); }
+int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 32, 1, 65536); }
 
 // Device buffer owned by the library.
 struct DBuf {
@@ -134,7 +145,7 @@ struct sekv_index {
   uint32_t magic = IDX_MAGIC;
   sekv_ctx* ctx = nullptr;
   int B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, R = 0, dp = 0, G = 0, tier = 0;
-  int max_spans = 0, Wd = 0, max_raw = 0;
+  int max_spans = 0, Wd = 0, max_raw = 0, tpw = 4;
   int64_t total_spans = 0, total_raw = 0, total_tok = 0;
   int64_t layer_bytes = 0, pool_bytes = 0;
   int64_t kres_elems = 0, s_elems = 0;
@@ -156,7 +167,8 @@ struct sekv_index {
   // decode work
   std::vector<WorkItem> items;
   std::vector<int32_t> bg_first;
-  DBuf d_items, d_bg_first, d_part;
+  DBuf d_items, d_bg_first, d_part, d_counters;
+  int counters_lc = 0;
   // routing scratch
   DBuf d_alpha, d_tickets, d_tau_inf;
   int tickets_lc = 0;
@@ -251,13 +263,15 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
   x->pool_bytes = pb * x->L;
   x->Wd = std::max(1, (x->max_spans + 63) / 64);
   // decode work items, contiguous per (b, g)
+  x->tpw = tiles_per_item();
+  const int spi = spans_per_item();
   x->items.clear();
   x->bg_first.assign((size_t)x->B * x->Hkv, 0);
   for (int b = 0; b < x->B; ++b) {
     const BMeta& m = x->meta[b];
     const int ntiles = m.n_res_pad / 64;
-    const int nres = (ntiles + kTilesPerItem - 1) / kTilesPerItem;
-    const int nfac = m.n_spans ? (m.n_spans + kSpansPerFacItem - 1) / kSpansPerFacItem : 0;
+    const int nres = (ntiles + x->tpw - 1) / x->tpw;
+    const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
     for (int g = 0; g < x->Hkv; ++g) {
       const int first = (int)x->items.size();
       x->bg_first[(size_t)b * x->Hkv + g] = first;
@@ -315,7 +329,7 @@ void free_index(sekv_index* x) {
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
-                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part,
+                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part, &x->d_counters,
                   &x->d_alpha, &x->d_tickets, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
@@ -1002,6 +1016,11 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (stats) memset(stats, 0, sizeof *stats);
   const int n_items = (int)x->items.size();
   HIP_TRY(dgrow(x->d_part, sizeof(float) * (size_t)lc * std::max(n_items, 1) * x->G * (x->D + 2)));
+  if (!x->d_counters.p || x->counters_lc < lc) {
+    HIP_TRY(dalloc(x->d_counters, sizeof(uint32_t) * (size_t)x->B * lc * x->Hkv));
+    HIP_TRY(hipMemsetAsync(x->d_counters.p, 0, x->d_counters.n, c->stream));
+    x->counters_lc = lc;
+  }
   AttendArgs aa{};
   aa.q = (const bf16_t*)q;
   aa.mask = mask;
@@ -1021,11 +1040,13 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     aa.ring_off = (const int64_t*)x->d_ring_off.p;
   }
   aa.part = (float*)x->d_part.p;
+  aa.counters = (uint32_t*)x->d_counters.p;
+  aa.out = out;
   aa.layer_bytes = x->layer_bytes;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
   aa.max_spans = std::max(x->max_spans, 1);
-  aa.tpw = kTilesPerItem;
+  aa.tpw = x->tpw;
   aa.scale = 1.0f / sqrtf((float)x->D);
   if (n_items > 0) {
     size_t slot = 0;
@@ -1033,12 +1054,5 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
     if (c->timing) HIP_TRY(c->t_attend.end(c->stream, slot));
   }
-  ReduceArgs rd{};
-  rd.part = (const float*)x->d_part.p;
-  rd.items = (const WorkItem*)x->d_items.p;
-  rd.bg_first = (const int32_t*)x->d_bg_first.p;
-  rd.out = out;
-  rd.layer_count = lc; rd.n_items = n_items; rd.B = x->B; rd.Hq = x->Hq; rd.Hkv = x->Hkv;
-  HIP_TRY(launch_reduce(rd, x->D, x->G, c->stream));
   return SEKV_OK;
 }

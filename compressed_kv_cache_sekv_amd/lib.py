@@ -16,7 +16,8 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsekv.so")
+# SEKV_LIB overrides the library path (e.g. to compare builds).
+LIB_PATH = os.environ.get("SEKV_LIB") or os.path.join(HERE, "libsekv.so")
 
 TIER_HBM = 0
 TIER_PINNED_HOST = 1
