@@ -22,8 +22,10 @@
 // A span's factor blob is loaded in one round trip (all its loads issued
 // before any arithmetic); for R = 16 the next span's blob is in flight while
 // the current one is computed.  Each workgroup writes one softmax partial
-// (m, l, o) per head; the last workgroup of a (b, l, g) to finish (atomic
-// ticket) merges them into the output, so no second kernel is launched.
+// (m, l, o) per head; merge_kernel combines them.  (A last-workgroup merge
+// inside this kernel would need a device-scope release per workgroup, which
+// on this GPU writes back the XCD's L2 each time; the kernel boundary is the
+// cheaper synchronisation.)
 #include "common.h"
 
 namespace sekv {
@@ -261,9 +263,6 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   __shared__ float s_o[4][G][D];
   __shared__ uint64_t s_uw[1024];
   __shared__ int32_t s_pre[1025];
-  __shared__ float s_red[256];
-  __shared__ float s_M[G], s_L[G];
-  __shared__ int s_last;
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -463,67 +462,74 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     }
   }
 
-  // ------------------- the last workgroup of (b, l, g) merges the item partials
-  __threadfence();
-  __syncthreads();
-  uint32_t* ctr = a.counters + ((int64_t)b * a.layer_count + lc) * a.Hkv + g;
-  if (threadIdx.x == 0) s_last = (atomicAdd(ctr, 1u) == (uint32_t)it.part_count - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int P = it.part_count;
-  const float* base = a.part + ((int64_t)lc * a.n_items + it.part_first) * pstride;
-  {
-    // per-head max M and denominator L over the P partials
-    const int h = threadIdx.x % G, i0 = threadIdx.x / G, st = 256 / G;
-    float mx = -INFINITY;
-    for (int i = i0; i < P; i += st) mx = fmaxf(mx, base[i * pstride + h * (D + 2) + D]);
-    s_red[threadIdx.x] = mx;
-    __syncthreads();
-    if (threadIdx.x < G) {
-      float M = -INFINITY;
-      for (int j = threadIdx.x; j < st * G; j += G) M = fmaxf(M, s_red[j]);
-      s_M[threadIdx.x] = M;
-    }
-    __syncthreads();
-    const float M = s_M[h];
-    float ls = 0.f;
-    for (int i = i0; i < P; i += st) {
-      const float* p = base + i * pstride + h * (D + 2);
-      const float mi = p[D];
-      ls += (mi == -INFINITY) ? 0.f : __expf(mi - M) * p[D + 1];
-    }
-    __syncthreads();
-    s_red[threadIdx.x] = ls;
-    __syncthreads();
-    if (threadIdx.x < G) {
-      float L = 0.f;
-      for (int j = threadIdx.x; j < st * G; j += G) L += s_red[j];
-      s_L[threadIdx.x] = L;
-    }
-    __syncthreads();
+}
+
+// Merge the partials of every item of (b, g) into out[b][lc][h][:]: per-head
+// max M over the partials, weights e = exp(m - M) and denominator
+// L = sum e * l in LDS, then each wave sums a quarter of the partials with
+// each lane owning G*D/64 contiguous outputs (vector loads), and the four
+// wave sums are added.  One workgroup per (b, lc, g).
+template <int D, int G>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  __shared__ float s_w[kMaxMergeWeights], s_wl[kMaxMergeWeights];
+  __shared__ float s_o[4][G * D];
+  __shared__ float s_M[G], s_L[G];
+  const int bg = blockIdx.x, lc = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int first = a.bg_first[bg];
+  const int P = a.items[first].part_count;
+  const int64_t pstride = (int64_t)G * (D + 2);
+  const float* base = a.part + ((int64_t)lc * a.n_items + first) * pstride;
+  for (int i = threadIdx.x; i < P * G; i += 256) {
+    const float* p = base + (i / G) * pstride + (i % G) * (D + 2) + D;
+    s_w[i] = p[0];
+    s_wl[i] = p[1];
   }
-  // outputs: wave w sums the partials i = w (mod 4) for every (h, dim)
-  for (int idx = lane; idx < G * D; idx += 64) {
-    const int h = idx / D, dim = idx - h * D;
-    const float M = s_M[h];
-    float acc = 0.f;
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY;
+    for (int i = 0; i < P; ++i) M = fmaxf(M, s_w[i * G + threadIdx.x]);
+    s_M[threadIdx.x] = M;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < P * G; i += 256) {
+    const float mi = s_w[i];
+    s_w[i] = (mi == -INFINITY) ? 0.f : __expf(mi - s_M[i % G]);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float L = 0.f;
+    for (int i = 0; i < P; ++i) L += s_w[i * G + threadIdx.x] * s_wl[i * G + threadIdx.x];
+    s_L[threadIdx.x] = L;
+  }
+  constexpr int NPL = G * D / 64;
+  {
+    const int o0 = lane * NPL, h = o0 / D;
+    float acc[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) acc[e] = 0.f;
 #pragma unroll 4
     for (int i = wave; i < P; i += 4) {
-      const float* p = base + i * pstride + h * (D + 2);
-      const float mi = p[D];
-      acc += (mi == -INFINITY) ? 0.f : __expf(mi - M) * p[dim];
+      const float wgt = s_w[i * G + h];
+      const float* p = base + i * pstride + h * (D + 2) + (o0 - h * D);
+#pragma unroll
+      for (int e = 0; e < NPL; e += 2) {
+        const float2 v = *(const float2*)(p + e);
+        acc[e] += wgt * v.x;
+        acc[e + 1] += wgt * v.y;
+      }
     }
-    s_o[wave][h][dim] = acc;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) s_o[wave][o0 + e] = acc[e];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, dim = idx - h * D;
-    const float O = s_o[0][h][dim] + s_o[1][h][dim] + s_o[2][h][dim] + s_o[3][h][dim];
+    const int h = idx / D;
+    const float O = s_o[0][idx] + s_o[1][idx] + s_o[2][idx] + s_o[3][idx];
     const float L = s_L[h];
-    a.out[(((int64_t)b * a.layer_count + lc) * Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
+    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G) * D + idx] = (L > 0.f) ? O / L : 0.f;
   }
-  if (threadIdx.x == 0) *ctr = 0u;
 }
 
 // ------------------------------------------------------------- dispatch
@@ -548,6 +554,14 @@ static hipError_t dispatch(int D, int G, int R, F f) {
 bool attend_supported(int D, int G, int R) {
   return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8) &&
          (R == 16 || R == 32 || R == 64) && R <= D;
+}
+
+hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
+  return dispatch(D, G, 16, [&](auto d_, auto g_, auto) -> hipError_t {
+    hipLaunchKernelGGL((merge_kernel<decltype(d_)::value, decltype(g_)::value>),
+                       dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st) {

@@ -95,6 +95,9 @@ struct BMeta {
                         // (b, l, g) starts at l * layer_bytes + pool_base + g * pool_lg
 };
 
+// Partials one merge can combine: items of a (b, g) times G (LDS bound).
+constexpr int kMaxMergeWeights = 2048;
+
 // Decode work: one workgroup of 4 waves per item.  kind 0: resident rows
 // tiles [j*tpw, (j+1)*tpw); kind 1: the j-th of nj shares of the union of
 // the routed spans of (b, l, g).
@@ -119,13 +122,19 @@ struct AttendArgs {
   const int64_t* ring_off;  // ring tier: [Lc][B][Hkv][max_spans] offset of the
                             // k-th union span's blob in the ring, else NULL
   float* part;              // [Lc][n_items][G][D + 2] softmax partials
-  uint32_t* counters;       // [B][Lc][Hkv] finished-item tickets (zero between launches)
-  float* out;               // [B][Lc][Hq][D]
   int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
   int32_t layer_begin, layer_count, n_items;
   int32_t B, L, Hq, Hkv, W, max_spans;
   int32_t tpw;              // resident 64-row tiles per work item
   float scale;              // 1/sqrt(d)
+};
+
+struct MergeArgs {
+  const float* part;
+  const WorkItem* items;
+  const int32_t* bg_first;  // [B*Hkv] first item of (b, g)
+  float* out;               // [B][Lc][Hq][D]
+  int32_t layer_count, n_items, B, Hq, Hkv;
 };
 
 struct RouteArgs {
@@ -136,7 +145,6 @@ struct RouteArgs {
   const BMeta* meta;
   uint64_t* mask;           // [B][Lc][Hq][Wd]
   float* alpha;             // [B][Lc][Hq][Wd*64] (scratch or caller)
-  uint32_t* tickets;        // [B][Lc][Hq]
   int32_t layer_begin, layer_count;
   int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
 };
@@ -151,7 +159,9 @@ struct CalibArgs {
 
 // ------------------------------------------------------------ launchers ---
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st);
 bool attend_supported(int D, int G, int R);
 

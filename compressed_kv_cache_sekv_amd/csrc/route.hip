@@ -9,11 +9,8 @@
 // ties to the lower span index).
 //
 // One workgroup per (b, 256-span chunk, head, layer); each wave scores 64
-// spans, one per lane, and writes one mask word with a ballot.  When a cap is
-// given, the last workgroup of a (b, l, h) to finish (atomic ticket) counts
-// the expansions and, on overflow, keeps the cap largest alpha by a 4-pass
-// 8-bit radix select on the fp32 bit patterns (alpha >= 0, so bit order is
-// value order).
+// spans, one per lane, and writes one mask word with a ballot.  The budget cap
+// runs as a second small kernel (route_cap_kernel) on the finished masks.
 #include "common.h"
 
 namespace sekv {
@@ -24,15 +21,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
   return v;
-}
-
-// Loads that bypass the (non-coherent) L1: data written by other workgroups
-// of the same launch, published by __threadfence() + the ticket atomic.
-__device__ __forceinline__ uint32_t ld_u32(const float* p) {
-  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
-  return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Block-wide inclusive scan of one int per thread (256 threads).
@@ -85,16 +73,8 @@ __device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int
   return prefix;
 }
 
-constexpr int kCapList = 2048;   // candidates ranked in LDS; more fall back to radix select
-
 __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[256];
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_tmp[8];
-  __shared__ int s_sel[2];
-  __shared__ int s_last, s_nc;
-  __shared__ uint64_t s_cand[kCapList];
-  __shared__ unsigned long long s_new[1024];
   const int nchunk = (a.Wd + 3) >> 2;
   const int b = blockIdx.x / nchunk, chunk = blockIdx.x - b * nchunk;
   const int h = blockIdx.y, lc = blockIdx.z, l = a.layer_begin + lc;
@@ -128,57 +108,81 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
   const float tau = a.tau[lc * a.Hq + h];
   const int wi = chunk * 4 + wave;
-  if (wi < a.Wd) {
-    const int S = 64 * wi + lane;
-    float alpha = 0.f;
-    bool z = false;
-    if (S < bm.n_spans) {
-      const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + S;
-      float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-      int j = 0;
-#pragma unroll 4
-      for (; j + 4 <= dp; j += 4) {
-        d0 += s_u[j] * sp[(int64_t)j * bm.s_pad];
-        d1 += s_u[j + 1] * sp[(int64_t)(j + 1) * bm.s_pad];
-        d2 += s_u[j + 2] * sp[(int64_t)(j + 2) * bm.s_pad];
-        d3 += s_u[j + 3] * sp[(int64_t)(j + 3) * bm.s_pad];
+  if (wi >= a.Wd) return;
+  const int S = 64 * wi + lane;
+  float alpha = 0.f;
+  bool z = false;
+  if (S < bm.n_spans) {
+    const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + S;
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+    for (int j0 = 0; j0 < dp; j0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = (j0 + k < dp) ? sp[(int64_t)(j0 + k) * bm.s_pad] : 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; k += 4) {
+        if (j0 + k < dp) d0 += s_u[j0 + k] * v[k];
+        if (j0 + k + 1 < dp) d1 += s_u[j0 + k + 1] * v[k + 1];
+        if (j0 + k + 2 < dp) d2 += s_u[j0 + k + 2] * v[k + 2];
+        if (j0 + k + 3 < dp) d3 += s_u[j0 + k + 3] * v[k + 3];
       }
-      for (; j < dp; ++j) d0 += s_u[j] * sp[(int64_t)j * bm.s_pad];
-      const float dot = (d0 + d1) + (d2 + d3);
-      alpha = 1.f / (1.f + expf(-dot));
-      z = alpha > tau;
     }
-    const uint64_t word = __ballot(z);
-    if (lane == 0) mrow[wi] = word;
-    if (arow) arow[S] = alpha;
+    const float dot = (d0 + d1) + (d2 + d3);
+    alpha = 1.f / (1.f + expf(-dot));
+    z = alpha > tau;
   }
-  if (a.cap <= 0) return;
+  const uint64_t word = __ballot(z);
+  if (lane == 0) mrow[wi] = word;
+  if (arow) arow[S] = alpha;
+}
 
-  // ------------------------------------------------ budget cap (last block)
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = atomicAdd(&a.tickets[row], 1u);
-    s_last = (t == (uint32_t)nchunk - 1);
-    s_nc = 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // acquire: the other blocks' masks and alphas are visible
-  // candidates: key = alpha bits (high) and the complemented span index (low),
-  // so key order is alpha descending, then span index ascending
+// Budget cap, one workgroup per (b, lc, h), after route_kernel: when more than
+// cap spans are expanded keep the cap largest alpha, ties to the lower span
+// index.  Expanded spans are collected into LDS with the key (alpha bits,
+// complemented span index), whose order is alpha descending then index
+// ascending and whose values are distinct; a span is kept iff fewer than cap
+// keys exceed its own.  Candidate sets above kCapList fall back to a 4-pass
+// radix select over global memory.
+constexpr int kCapList = 2048;
+
+__global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_tmp[8];
+  __shared__ int s_sel[2];
+  __shared__ int s_nc;
+  __shared__ uint64_t s_cand[kCapList];
+  __shared__ unsigned long long s_new[1024];
+  const int b = blockIdx.x, h = blockIdx.y, lc = blockIdx.z;
+  const BMeta bm = a.meta[b];
+  const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
+  uint64_t* mrow = a.mask + row * a.Wd;
+  const float* arow = a.alpha + row * (int64_t)a.Wd * 64;
+  if (threadIdx.x == 0) s_nc = 0;
   for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = 0ull;
-  for (int S = threadIdx.x; S < bm.n_spans; S += 256) {
-    if ((mrow[S >> 6] >> (S & 63)) & 1ull) {
-      const int pos = atomicAdd(&s_nc, 1);
-      if (pos < kCapList)
-        s_cand[pos] = ((uint64_t)__float_as_uint(arow[S]) << 32) | (uint64_t)(~(uint32_t)S);
+  __syncthreads();
+  for (int S0 = threadIdx.x; S0 < bm.n_spans; S0 += 1024) {
+    uint64_t wv[4];
+    float av[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int S = S0 + 256 * k;
+      wv[k] = (S < bm.n_spans) ? mrow[S >> 6] : 0ull;
+      av[k] = (S < bm.n_spans) ? arow[S] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int S = S0 + 256 * k;
+      if (S < bm.n_spans && ((wv[k] >> (S & 63)) & 1ull)) {
+        const int pos = atomicAdd(&s_nc, 1);
+        if (pos < kCapList)
+          s_cand[pos] = ((uint64_t)__float_as_uint(av[k]) << 32) | (uint64_t)(~(uint32_t)S);
+      }
     }
   }
   __syncthreads();
   const int nc = s_nc;
-  if (nc > a.cap && nc <= kCapList) {
-    // rank of each candidate = number of larger keys (keys are distinct)
+  if (nc <= a.cap) return;
+  if (nc <= kCapList) {
     for (int i = threadIdx.x; i < nc; i += 256) {
       const uint64_t ki = s_cand[i];
       int rank = 0;
@@ -190,49 +194,50 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
     }
     __syncthreads();
     for (int w = threadIdx.x; w < a.Wd; w += 256) mrow[w] = s_new[w];
-  } else if (nc > a.cap) {
-    // large candidate sets: 4-pass radix select on alpha over global memory
-    int k = a.cap;
-    auto cand = [&](int S, uint32_t& key) -> bool {
-      const uint64_t word = ld_u64(mrow + (S >> 6));
-      if (!((word >> (S & 63)) & 1ull)) return false;
-      key = ld_u32(arow + S);
-      return true;
-    };
-    const uint32_t vstar = radix_select(bm.n_spans, k, cand, s_hist, s_sel);
-    // k = number of spans with alpha == vstar to keep, lowest span index first
-    int carry = 0;
-    for (int base = 0; base < a.Wd; base += 256) {
-      const int ww = base + threadIdx.x;
-      int tw = 0;
-      uint64_t zz = 0;
-      if (ww < a.Wd) {
-        zz = ld_u64(mrow + ww);
-        for (uint64_t bits = zz; bits; bits &= bits - 1)
-          tw += (ld_u32(arow + 64 * ww + __builtin_ctzll(bits)) == vstar);
-      }
-      const int incl = block_scan256(tw, s_tmp);
-      int rank = carry + incl - tw;
-      if (ww < a.Wd) {
-        uint64_t keep = 0;
-        for (uint64_t bits = zz; bits; bits &= bits - 1) {
-          const int bit = __builtin_ctzll(bits);
-          const uint32_t key = ld_u32(arow + 64 * ww + bit);
-          if (key > vstar) keep |= 1ull << bit;
-          else if (key == vstar) {
-            if (rank < k) keep |= 1ull << bit;
-            ++rank;
-          }
-        }
-        mrow[ww] = keep;
-      }
-      if (threadIdx.x == 255) s_sel[0] = incl;
-      __syncthreads();
-      carry += s_sel[0];
-      __syncthreads();
-    }
+    return;
   }
-  if (threadIdx.x == 0) a.tickets[row] = 0u;
+  // large candidate sets: radix select on alpha, ties by span index
+  int k = a.cap;
+  auto cand = [&](int S, uint32_t& key) -> bool {
+    const uint64_t word = mrow[S >> 6];
+    if (!((word >> (S & 63)) & 1ull)) return false;
+    key = __float_as_uint(arow[S]);
+    return true;
+  };
+  const uint32_t vstar = radix_select(bm.n_spans, k, cand, s_hist, s_sel);
+  // k = number of spans with alpha == vstar to keep, lowest span index first
+  for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = mrow[w];
+  __syncthreads();
+  int carry = 0;
+  for (int base = 0; base < a.Wd; base += 256) {
+    const int ww = base + threadIdx.x;
+    int tw = 0;
+    uint64_t zz = 0;
+    if (ww < a.Wd) {
+      zz = s_new[ww];
+      for (uint64_t bits = zz; bits; bits &= bits - 1)
+        tw += (__float_as_uint(arow[64 * ww + __builtin_ctzll(bits)]) == vstar);
+    }
+    const int incl = block_scan256(tw, s_tmp);
+    int rank = carry + incl - tw;
+    if (ww < a.Wd) {
+      uint64_t keep = 0;
+      for (uint64_t bits = zz; bits; bits &= bits - 1) {
+        const int bit = __builtin_ctzll(bits);
+        const uint32_t key = __float_as_uint(arow[64 * ww + bit]);
+        if (key > vstar) keep |= 1ull << bit;
+        else if (key == vstar) {
+          if (rank < k) keep |= 1ull << bit;
+          ++rank;
+        }
+      }
+      mrow[ww] = keep;
+    }
+    if (threadIdx.x == 255) s_sel[0] = incl;
+    __syncthreads();
+    carry += s_sel[0];
+    __syncthreads();
+  }
 }
 
 // tau^(l,h): midpoint of the k-th and (k+1)-th largest alpha over every
@@ -263,6 +268,11 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const CalibArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nchunk = (a.Wd + 3) >> 2;
   hipLaunchKernelGGL(route_kernel, dim3(a.B * nchunk, a.Hq, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(route_cap_kernel, dim3(a.B, a.Hq, a.layer_count), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sekv.h"
+#include "sekv.h"
 #include "common.h"
 
 using namespace sekv;
@@ -167,11 +167,9 @@ struct sekv_index {
   // decode work
   std::vector<WorkItem> items;
   std::vector<int32_t> bg_first;
-  DBuf d_items, d_bg_first, d_part, d_counters;
-  int counters_lc = 0;
+  DBuf d_items, d_bg_first, d_part;
   // routing scratch
-  DBuf d_alpha, d_tickets, d_tau_inf;
-  int tickets_lc = 0;
+  DBuf d_alpha, d_tau_inf;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
 
@@ -267,11 +265,28 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
   const int spi = spans_per_item();
   x->items.clear();
   x->bg_first.assign((size_t)x->B * x->Hkv, 0);
+  // the merge combines at most kMaxMergeWeights / G partials per (b, g):
+  // widen the items of long sequences until they fit
+  const int max_items = kMaxMergeWeights / x->G;
   for (int b = 0; b < x->B; ++b) {
     const BMeta& m = x->meta[b];
     const int ntiles = m.n_res_pad / 64;
+    int tpw = x->tpw, sp = spi;
+    auto count = [&](int t, int s) {
+      return (ntiles + t - 1) / t + (m.n_spans ? (m.n_spans + s - 1) / s : 0);
+    };
+    while (count(tpw, sp) > max_items) {
+      tpw *= 2;
+      sp *= 2;
+    }
+    x->tpw = std::max(x->tpw, tpw);
+  }
+  for (int b = 0; b < x->B; ++b) {
+    const BMeta& m = x->meta[b];
+    const int ntiles = m.n_res_pad / 64;
+    const int sp = spi * (x->tpw / std::max(1, tiles_per_item()));
     const int nres = (ntiles + x->tpw - 1) / x->tpw;
-    const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
+    const int nfac = m.n_spans ? (m.n_spans + sp - 1) / sp : 0;
     for (int g = 0; g < x->Hkv; ++g) {
       const int first = (int)x->items.size();
       x->bg_first[(size_t)b * x->Hkv + g] = first;
@@ -329,8 +344,8 @@ void free_index(sekv_index* x) {
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
-                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part, &x->d_counters,
-                  &x->d_alpha, &x->d_tickets, &x->d_tau_inf};
+                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part,
+                  &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
   if (x->h_ring_off_pinned) (void)hipHostFree(x->h_ring_off_pinned);
@@ -354,11 +369,6 @@ sekv_status set_device(sekv_ctx* c) {
 sekv_status ensure_route_scratch(sekv_index* x, int lc) {
   const size_t rows = (size_t)x->B * lc * x->Hq;
   HIP_TRY(dgrow(x->d_alpha, rows * x->Wd * 64 * sizeof(float)));
-  if (!x->d_tickets.p || x->tickets_lc < lc) {
-    HIP_TRY(dalloc(x->d_tickets, rows * sizeof(uint32_t)));
-    HIP_TRY(hipMemsetAsync(x->d_tickets.p, 0, x->d_tickets.n, x->ctx->stream));
-    x->tickets_lc = lc;
-  }
   return SEKV_OK;
 }
 
@@ -866,13 +876,13 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   ra.meta = (const BMeta*)x->d_meta.p;
   ra.mask = mask;
   ra.alpha = alpha ? alpha : (cap > 0 ? (float*)x->d_alpha.p : nullptr);
-  ra.tickets = (uint32_t*)x->d_tickets.p;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = cap;
   size_t slot = 0;
   if (c->timing) HIP_TRY(c->t_route.begin(c->stream, &slot));
   HIP_TRY(launch_route(ra, c->stream));
+  if (cap > 0) HIP_TRY(launch_route_cap(ra, c->stream));
   if (c->timing) HIP_TRY(c->t_route.end(c->stream, slot));
   return SEKV_OK;
 }
@@ -906,7 +916,6 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
   ra.meta = (const BMeta*)x->d_meta.p;
   ra.mask = (uint64_t*)mk.p;
   ra.alpha = (float*)x->d_alpha.p;
-  ra.tickets = (uint32_t*)x->d_tickets.p;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = 0;
@@ -1016,11 +1025,6 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (stats) memset(stats, 0, sizeof *stats);
   const int n_items = (int)x->items.size();
   HIP_TRY(dgrow(x->d_part, sizeof(float) * (size_t)lc * std::max(n_items, 1) * x->G * (x->D + 2)));
-  if (!x->d_counters.p || x->counters_lc < lc) {
-    HIP_TRY(dalloc(x->d_counters, sizeof(uint32_t) * (size_t)x->B * lc * x->Hkv));
-    HIP_TRY(hipMemsetAsync(x->d_counters.p, 0, x->d_counters.n, c->stream));
-    x->counters_lc = lc;
-  }
   AttendArgs aa{};
   aa.q = (const bf16_t*)q;
   aa.mask = mask;
@@ -1040,8 +1044,6 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     aa.ring_off = (const int64_t*)x->d_ring_off.p;
   }
   aa.part = (float*)x->d_part.p;
-  aa.counters = (uint32_t*)x->d_counters.p;
-  aa.out = out;
   aa.layer_bytes = x->layer_bytes;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
@@ -1054,5 +1056,12 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
     if (c->timing) HIP_TRY(c->t_attend.end(c->stream, slot));
   }
+  MergeArgs mg{};
+  mg.part = (const float*)x->d_part.p;
+  mg.items = (const WorkItem*)x->d_items.p;
+  mg.bg_first = (const int32_t*)x->d_bg_first.p;
+  mg.out = out;
+  mg.layer_count = lc; mg.n_items = n_items; mg.B = x->B; mg.Hq = x->Hq; mg.Hkv = x->Hkv;
+  HIP_TRY(launch_merge(mg, x->D, x->G, c->stream));
   return SEKV_OK;
 }
