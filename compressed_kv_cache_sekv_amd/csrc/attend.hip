@@ -117,8 +117,9 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
 template <int D, int R>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
+  static constexpr bool VV_EARLY = (R <= 16);   // preload V^V (register budget)
   u32x4 vkt[NR16][NS32];
-  u32x2 vv[ND16][NR16];
+  u32x2 vv[VV_EARLY ? ND16 : 1][NR16];
   floatx4 smk[NR16], smv[NR16];
   u32x2 uk[4][NR16];
   u32x2 uvt[NR16][4];
@@ -156,12 +157,58 @@ struct SpanRegs {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         if (tb < ntb) uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tb) * 256 + lane * 4);
+    if (VV_EARLY) {
 #pragma unroll
-    for (int db = 0; db < ND16; ++db)
+      for (int db = 0; db < (VV_EARLY ? ND16 : 1); ++db)
 #pragma unroll
-      for (int kb = 0; kb < NR16; ++kb) vv[db][kb] = *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+        for (int kb = 0; kb < NR16; ++kb) vv[db][kb] = *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+    }
   }
 };
+
+// One chunk of up to 64 tokens of a routed span: scores, online softmax and
+// the U^V^T p accumulation.
+template <int D, int G, int R>
+__device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u32x2 (&uvt)[R / 16][4], int tb0,
+                                           int nb, int n, bool act, int grp, const u32x2 (&chi)[R / 16],
+                                           const u32x2 (&clo)[R / 16], float& m, float& l,
+                                           floatx4 (&o)[D / 16], floatx4 (&wacc)[R / 16]) {
+  constexpr int ND16 = D / 16, NR16 = R / 16;
+  floatx4 sc[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    sc[tb] = floatx4{0, 0, 0, 0};
+    if (tb < nb) {
+#pragma unroll
+      for (int kb = 0; kb < NR16; ++kb) {
+        sc[tb] = mfma16(uk[tb][kb], chi[kb], sc[tb]);
+        sc[tb] = mfma16(uk[tb][kb], clo[kb], sc[tb]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = 16 * (tb0 + tb) + 4 * grp + r;
+        if (!act || tok >= n) sc[tb][r] = -INFINITY;
+      }
+    }
+  }
+  const float corr = online<4>(sc, nb, m, l);
+#pragma unroll
+  for (int db = 0; db < ND16; ++db) o[db] *= corr;
+#pragma unroll
+  for (int ib = 0; ib < NR16; ++ib) wacc[ib] *= corr;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    if (tb < nb) {
+      u32x2 phi, plo;
+      pack4(sc[tb], phi, plo);
+#pragma unroll
+      for (int ib = 0; ib < NR16; ++ib) {
+        wacc[ib] = mfma16(uvt[ib][tb], phi, wacc[ib]);
+        wacc[ib] = mfma16(uvt[ib][tb], plo, wacc[ib]);
+      }
+    }
+  }
+}
 
 // Attention over one routed span in factored form, folded into (m, l, o).
 template <int D, int G, int R>
@@ -180,77 +227,42 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
     pack4(t * sr.smk[ib] * scale, chi[ib], clo[ib]);
   }
   const bool act = (hl < G) && ((sr.hm >> hl) & 1);
-  const bf16_t* pu = (const bf16_t*)(sr.blob + Blob::off_uk(R, D));
-  const bf16_t* pw = (const bf16_t*)(sr.blob + Blob::off_uvt(R, D, n));
   floatx4 wacc[NR16];
 #pragma unroll
   for (int ib = 0; ib < NR16; ++ib) wacc[ib] = floatx4{0, 0, 0, 0};
-  for (int tb0 = 0; tb0 < ntb; tb0 += 4) {
-    const int nb = min(4, ntb - tb0);
-    u32x2 uk[4][NR16], uvt[NR16][4];
-    if (tb0 == 0) {
+  // first 64 tokens from the preloaded registers, the rest streamed
+  span_chunk<D, G, R>(sr.uk, sr.uvt, 0, min(4, ntb), n, act, grp, chi, clo, m, l, o, wacc);
+  if (ntb > 4) {
+    const bf16_t* pu = (const bf16_t*)(sr.blob + Blob::off_uk(R, D));
+    const bf16_t* pw = (const bf16_t*)(sr.blob + Blob::off_uvt(R, D, n));
+    for (int tb0 = 4; tb0 < ntb; tb0 += 4) {
+      const int nb = min(4, ntb - tb0);
+      u32x2 uk[4][NR16], uvt[NR16][4];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int kb = 0; kb < NR16; ++kb) {
-          uk[tb][kb] = sr.uk[tb][kb];
-          uvt[kb][tb] = sr.uvt[kb][tb];
+          uk[tb][kb] = (tb < nb) ? *(const u32x2*)(pu + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4)
+                                 : u32x2{0, 0};
+          uvt[kb][tb] = (tb < nb) ? *(const u32x2*)(pw + ((int64_t)kb * ntb + tb0 + tb) * 256 + lane * 4)
+                                  : u32x2{0, 0};
         }
-    } else {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        if (tb < nb)
-#pragma unroll
-          for (int kb = 0; kb < NR16; ++kb) {
-            uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4);
-            uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tb0 + tb) * 256 + lane * 4);
-          }
-    }
-    floatx4 sc[4];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      sc[tb] = floatx4{0, 0, 0, 0};
-      if (tb < nb) {
-#pragma unroll
-        for (int kb = 0; kb < NR16; ++kb) {
-          sc[tb] = mfma16(uk[tb][kb], chi[kb], sc[tb]);
-          sc[tb] = mfma16(uk[tb][kb], clo[kb], sc[tb]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = 16 * (tb0 + tb) + 4 * grp + r;
-          if (!act || tok >= n) sc[tb][r] = -INFINITY;
-        }
-      }
-    }
-    const float corr = online<4>(sc, nb, m, l);
-#pragma unroll
-    for (int db = 0; db < ND16; ++db) o[db] *= corr;
-#pragma unroll
-    for (int ib = 0; ib < NR16; ++ib) wacc[ib] *= corr;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      if (tb < nb) {
-        u32x2 phi, plo;
-        pack4(sc[tb], phi, plo);
-#pragma unroll
-        for (int ib = 0; ib < NR16; ++ib) {
-          wacc[ib] = mfma16(uvt[ib][tb], phi, wacc[ib]);
-          wacc[ib] = mfma16(uvt[ib][tb], plo, wacc[ib]);
-        }
-      }
+      span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, chi, clo, m, l, o, wacc);
     }
   }
   // o += V^V (sigma m^V . w)
   u32x2 whi[NR16], wlo[NR16];
 #pragma unroll
   for (int ib = 0; ib < NR16; ++ib) pack4(wacc[ib] * sr.smv[ib], whi[ib], wlo[ib]);
+  const bf16_t* pv = (const bf16_t*)(sr.blob + Blob::off_vv(R, D));
 #pragma unroll
   for (int db = 0; db < ND16; ++db)
 #pragma unroll
     for (int kb = 0; kb < NR16; ++kb) {
-      o[db] = mfma16(sr.vv[db][kb], whi[kb], o[db]);
-      o[db] = mfma16(sr.vv[db][kb], wlo[kb], o[db]);
+      const u32x2 vvv = SpanRegs<D, R>::VV_EARLY ? sr.vv[SpanRegs<D, R>::VV_EARLY ? db : 0][kb]
+                                                 : *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+      o[db] = mfma16(vvv, whi[kb], o[db]);
+      o[db] = mfma16(vvv, wlo[kb], o[db]);
     }
 }
 
@@ -263,6 +275,8 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   __shared__ float s_o[4][G][D];
   __shared__ uint64_t s_uw[1024];
   __shared__ int32_t s_pre[1025];
+  __shared__ int32_t s_ln[kMaxSpanList];   // span length | active heads << 24
+  __shared__ int64_t s_off[kMaxSpanList];  // blob offset within the (b, l, g) region
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -309,6 +323,25 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int db = 0; db < ND16; ++db)
           vt[rb][db] = *(const u32x4*)(Vb + (int64_t)(2 * t + rb) * 32 * D + db * 512 + lane * 8);
+      // pseudo rows: the head's mask bit and the ln n_S bias, loaded with the tile
+      const int row0 = 64 * t;
+      const bool has_pseudo = row0 + 64 > bm.n_raw;
+      float bias[4][4];
+      if (has_pseudo) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
+            float bv = 0.f;
+            if (hl < G && sp >= 0 && sp < bm.n_spans) {
+              const uint64_t word = mh[sp >> 6];
+              const float lg_n = a.logn[bm.span_base + sp];
+              bv = ((word >> (sp & 63)) & 1ull) ? -INFINITY : lg_n;
+            }
+            bias[kb][r] = bv;
+          }
+      }
       floatx4 S[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -316,21 +349,14 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int s = 0; s < NS32; ++s) S[kb] = mfma32(kt[kb][s], qB[s], S[kb]);
       }
-      const int row0 = 64 * t;
-      const bool has_pseudo = row0 + 64 > bm.n_raw;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = row0 + 16 * kb + 4 * grp + r;
           float x = S[kb][r] * scale;
-          if (hl >= G || row >= bm.n_res) {
-            x = -INFINITY;
-          } else if (has_pseudo && row >= bm.n_raw) {
-            const int sp = row - bm.n_raw;
-            const uint64_t word = mh[sp >> 6];
-            x = ((word >> (sp & 63)) & 1ull) ? -INFINITY : x + a.logn[bm.span_base + sp];
-          }
+          if (hl >= G || row >= bm.n_res) x = -INFINITY;
+          else if (has_pseudo && row >= bm.n_raw) x += bias[kb][r];
           S[kb][r] = x;
         }
       const float corr = online<4>(S, 4, m, lsum);
@@ -377,52 +403,51 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     __syncthreads();
     const int U = s_pre[Wd];
     const int beg = (int)((int64_t)it.j * U / it.nj), end = (int)((int64_t)(it.j + 1) * U / it.nj);
-    const int k0 = beg + (int)((int64_t)(end - beg) * wave / 4);
-    const int k1 = beg + (int)((int64_t)(end - beg) * (wave + 1) / 4);
-    if (k0 < k1) {
-      // locate rank k0: largest word w with s_pre[w] <= k0 (it has a set bit)
-      int lo = 0, hi = Wd - 1;
+    const int cnt = min(end - beg, kMaxSpanList);   // the host keeps shares <= kMaxSpanList
+    // this workgroup's spans: rank -> (span, blob, length, active heads), all
+    // metadata loads issued in one parallel pass and kept in LDS
+    const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
+    const int64_t* roff = a.ring_off
+        ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans : nullptr;
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+      const int k = beg + i;
+      int lo = 0, hi = Wd - 1;   // largest word w with s_pre[w] <= k (it holds rank k)
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= k0) lo = mid; else hi = mid - 1;
+        if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
       }
-      int w = uni(lo);
-      uint64_t bits = s_uw[w];
-      for (int skip = k0 - s_pre[w]; skip > 0; --skip) bits &= bits - 1;
-      const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
-      const int64_t* roff = a.ring_off
-          ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans : nullptr;
-      // next union span in rank order: its blob, length and active heads
-      int k_next = k0;
-      auto next_span = [&](SpanRegs<D, R>& sr) -> bool {
-        while (bits == 0 && w + 1 < Wd) bits = s_uw[++w];
-        if (bits == 0) return false;  // unreachable when the ranks are consistent
-        const int bit = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        const int S = uni(64 * w + bit);
-        int hm = 0;
+      uint64_t bits = s_uw[lo];
+      for (int skip = k - s_pre[lo]; skip > 0; --skip) bits &= bits - 1;
+      const int bit = __builtin_ctzll(bits);
+      const int S = 64 * lo + bit;
+      int hm = 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h) hm |= (int)((mrow[(int64_t)h * Wd + w] >> bit) & 1ull) << h;
-        const int n = uni(a.span_len[bm.span_base + S]);
-        const uint8_t* blob = roff ? a.pool + roff[k_next] : region + a.span_off[bm.span_base + S];
-        ++k_next;
-        sr.load(blob, n, hm, lane, grp);
-        return true;
+      for (int h = 0; h < G; ++h) hm |= (int)((mrow[(int64_t)h * Wd + lo] >> bit) & 1ull) << h;
+      s_ln[i] = a.span_len[bm.span_base + S] | (hm << 24);
+      s_off[i] = roff ? roff[k] - ((int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg)
+                      : a.span_off[bm.span_base + S];
+    }
+    __syncthreads();
+    const int i0 = (int)((int64_t)cnt * wave / 4), i1 = (int)((int64_t)cnt * (wave + 1) / 4);
+    if (i0 < i1) {
+      const uint8_t* rbase = roff ? a.pool : region;
+      const int64_t rshift = roff ? ((int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg) : 0;
+      auto fetch = [&](SpanRegs<D, R>& sr, int i) {
+        const int ln = s_ln[i];
+        sr.load(rbase + rshift + s_off[i], uni(ln & 0xffffff), uni(ln >> 24), lane, grp);
       };
       SpanRegs<D, R> cur;
-      if (next_span(cur)) {
-        for (int k = k0; k < k1; ++k) {
-          const bool more = k + 1 < k1;
-          if (PREFETCH) {
-            SpanRegs<D, R> nxt;
-            const bool ok = more && next_span(nxt);
-            span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
-            if (!ok) break;
-            cur = nxt;
-          } else {
-            span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
-            if (!more || !next_span(cur)) break;
-          }
+      fetch(cur, i0);
+      for (int i = i0; i < i1; ++i) {
+        if (PREFETCH) {
+          SpanRegs<D, R> nxt;
+          if (i + 1 < i1) fetch(nxt, i + 1);
+          span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
+          if (i + 1 >= i1) break;
+          cur = nxt;
+        } else {
+          span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
+          if (i + 1 < i1) fetch(cur, i + 1);
         }
       }
     }
@@ -464,17 +489,28 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 
 }
 
-// Merge the partials of every item of (b, g) into out[b][lc][h][:]: per-head
-// max M over the partials, weights e = exp(m - M) and denominator
-// L = sum e * l in LDS, then each wave sums a quarter of the partials with
-// each lane owning G*D/64 contiguous outputs (vector loads), and the four
-// wave sums are added.  One workgroup per (b, lc, g).
+// Merge the partials of every item of (b, g) into out[b][lc][h][:].  Each
+// workgroup takes one slice of D / DSPLIT dims for all G heads: it reads the
+// (m, l) of every partial into LDS, forms the per-head max M, the weights
+// e = exp(m - M) and the denominator L = sum e * l, then each wave sums a
+// quarter of the partials (each lane owning NPL contiguous outputs) and the
+// four wave sums are added.  grid (B * Hkv * DSPLIT, Lc).
+template <int D, int G>
+struct MergeShape {
+  static constexpr int DSPLIT = (G * D >= 128) ? G * D / 128 : 1;
+  static constexpr int DS = D / DSPLIT;            // dims per workgroup
+  static constexpr int NPL = G * DS / 64;          // outputs per lane (1 or 2)
+};
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  using MS = MergeShape<D, G>;
+  constexpr int DS = MS::DS, NPL = MS::NPL;
+  static_assert(NPL == 1 || NPL == 2, "merge lane layout");
   __shared__ float s_w[kMaxMergeWeights], s_wl[kMaxMergeWeights];
-  __shared__ float s_o[4][G * D];
+  __shared__ float s_o[4][G * DS];
   __shared__ float s_M[G], s_L[G];
-  const int bg = blockIdx.x, lc = blockIdx.y;
+  const int bg = blockIdx.x / MS::DSPLIT, z = blockIdx.x - bg * MS::DSPLIT, lc = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int first = a.bg_first[bg];
@@ -503,32 +539,31 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     for (int i = 0; i < P; ++i) L += s_w[i * G + threadIdx.x] * s_wl[i * G + threadIdx.x];
     s_L[threadIdx.x] = L;
   }
-  constexpr int NPL = G * D / 64;
   {
-    const int o0 = lane * NPL, h = o0 / D;
-    float acc[NPL];
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) acc[e] = 0.f;
-#pragma unroll 4
+    const int o0 = lane * NPL, h = o0 / DS, dim = z * DS + (o0 - h * DS);
+    float acc0 = 0.f, acc1 = 0.f;
+    const float* p0 = base + h * (D + 2) + dim;
+#pragma unroll 8
     for (int i = wave; i < P; i += 4) {
       const float wgt = s_w[i * G + h];
-      const float* p = base + i * pstride + h * (D + 2) + (o0 - h * D);
-#pragma unroll
-      for (int e = 0; e < NPL; e += 2) {
-        const float2 v = *(const float2*)(p + e);
-        acc[e] += wgt * v.x;
-        acc[e + 1] += wgt * v.y;
+      const float* p = p0 + i * pstride;
+      if (NPL == 2) {
+        const float2 v = *(const float2*)p;
+        acc0 += wgt * v.x;
+        acc1 += wgt * v.y;
+      } else {
+        acc0 += wgt * p[0];
       }
     }
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) s_o[wave][o0 + e] = acc[e];
+    s_o[wave][o0] = acc0;
+    if (NPL == 2) s_o[wave][o0 + 1] = acc1;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D;
+  for (int idx = threadIdx.x; idx < G * DS; idx += 256) {
+    const int h = idx / DS, dim = z * DS + (idx - h * DS);
     const float O = s_o[0][idx] + s_o[1][idx] + s_o[2][idx] + s_o[3][idx];
     const float L = s_L[h];
-    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G) * D + idx] = (L > 0.f) ? O / L : 0.f;
+    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
   }
 }
 
@@ -558,8 +593,9 @@ bool attend_supported(int D, int G, int R) {
 
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
   return dispatch(D, G, 16, [&](auto d_, auto g_, auto) -> hipError_t {
-    hipLaunchKernelGGL((merge_kernel<decltype(d_)::value, decltype(g_)::value>),
-                       dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
+    constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value;
+    hipLaunchKernelGGL((merge_kernel<D_, G_>), dim3(a.B * a.Hkv * MergeShape<D_, G_>::DSPLIT, a.layer_count),
+                       dim3(256), 0, st, a);
     return hipGetLastError();
   });
 }

@@ -97,6 +97,8 @@ struct BMeta {
 
 // Partials one merge can combine: items of a (b, g) times G (LDS bound).
 constexpr int kMaxMergeWeights = 2048;
+// Routed spans one factored work item may take (its LDS span list).
+constexpr int kMaxSpanList = 512;
 
 // Decode work: one workgroup of 4 waves per item.  kind 0: resident rows
 // tiles [j*tpw, (j+1)*tpw); kind 1: the j-th of nj shares of the union of

@@ -73,15 +73,31 @@ __device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int
   return prefix;
 }
 
+// Summary-key dimensions held in registers per lane (d' <= kMaxDp; entries
+// past d' are zero, and s_u is zero there, so they add nothing).
+constexpr int kMaxDp = 64;
+
 __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
-  __shared__ float s_u[256];
+  __shared__ float s_u[kMaxDp];
   const int nchunk = (a.Wd + 3) >> 2;
   const int b = blockIdx.x / nchunk, chunk = blockIdx.x - b * nchunk;
   const int h = blockIdx.y, lc = blockIdx.z, l = a.layer_begin + lc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const BMeta bm = a.meta[b];
   const int D = a.D, dp = a.dp;
-
+  if (threadIdx.x < kMaxDp) s_u[threadIdx.x] = 0.f;
+  __syncthreads();
+  const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
+  const int wi = chunk * 4 + wave;
+  const int S = 64 * wi + lane;
+  const bool live = wi < a.Wd && S < bm.n_spans;
+  // summary keys of this lane's span, all loads in flight before u is needed
+  float v[kMaxDp];
+  {
+    const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + (live ? S : 0);
+#pragma unroll
+    for (int j = 0; j < kMaxDp; ++j) v[j] = (live && j < dp) ? sp[(int64_t)j * bm.s_pad] : 0.f;
+  }
   // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims
   {
     const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
@@ -102,30 +118,20 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
     }
   }
   __syncthreads();
-
-  const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
+  if (wi >= a.Wd) return;
   uint64_t* mrow = a.mask + row * a.Wd;
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
   const float tau = a.tau[lc * a.Hq + h];
-  const int wi = chunk * 4 + wave;
-  if (wi >= a.Wd) return;
-  const int S = 64 * wi + lane;
   float alpha = 0.f;
   bool z = false;
-  if (S < bm.n_spans) {
-    const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + S;
+  if (live) {
     float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-    for (int j0 = 0; j0 < dp; j0 += 16) {
-      float v[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = (j0 + k < dp) ? sp[(int64_t)(j0 + k) * bm.s_pad] : 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; k += 4) {
-        if (j0 + k < dp) d0 += s_u[j0 + k] * v[k];
-        if (j0 + k + 1 < dp) d1 += s_u[j0 + k + 1] * v[k + 1];
-        if (j0 + k + 2 < dp) d2 += s_u[j0 + k + 2] * v[k + 2];
-        if (j0 + k + 3 < dp) d3 += s_u[j0 + k + 3] * v[k + 3];
-      }
+    for (int j = 0; j < kMaxDp; j += 4) {
+      d0 += s_u[j] * v[j];
+      d1 += s_u[j + 1] * v[j + 1];
+      d2 += s_u[j + 2] * v[j + 2];
+      d3 += s_u[j + 3] * v[j + 3];
     }
     const float dot = (d0 + d1) + (d2 + d3);
     alpha = 1.f / (1.f + expf(-dot));
@@ -140,9 +146,10 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
 // cap spans are expanded keep the cap largest alpha, ties to the lower span
 // index.  Expanded spans are collected into LDS with the key (alpha bits,
 // complemented span index), whose order is alpha descending then index
-// ascending and whose values are distinct; a span is kept iff fewer than cap
-// keys exceed its own.  Candidate sets above kCapList fall back to a 4-pass
-// radix select over global memory.
+// ascending and whose values are distinct; an 8-pass radix select in LDS
+// finds the cap-th largest key and every key at or above it is kept.
+// Candidate sets above kCapList fall back to a 4-pass radix select on alpha
+// over global memory.
 constexpr int kCapList = 2048;
 
 __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
@@ -160,20 +167,28 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   if (threadIdx.x == 0) s_nc = 0;
   for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = 0ull;
   __syncthreads();
-  for (int S0 = threadIdx.x; S0 < bm.n_spans; S0 += 1024) {
-    uint64_t wv[4];
-    float av[4];
+  for (int S0 = threadIdx.x; S0 < bm.n_spans; S0 += 256 * 16) {
+    // 16 spans per thread per round trip: all loads issued before any use
+    uint64_t wv[16];
+    float av[16];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 16; ++k) {
       const int S = S0 + 256 * k;
       wv[k] = (S < bm.n_spans) ? mrow[S >> 6] : 0ull;
       av[k] = (S < bm.n_spans) ? arow[S] : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 16; ++k) {
       const int S = S0 + 256 * k;
-      if (S < bm.n_spans && ((wv[k] >> (S & 63)) & 1ull)) {
-        const int pos = atomicAdd(&s_nc, 1);
+      const bool on = S < bm.n_spans && ((wv[k] >> (S & 63)) & 1ull);
+      // one LDS atomic per wave: reserve the wave's slots, then place by rank
+      const uint64_t bal = __ballot(on);
+      const int lane = threadIdx.x & 63;
+      int basepos = 0;
+      if (lane == 0 && bal) basepos = atomicAdd(&s_nc, (int)__popcll(bal));
+      basepos = __shfl(basepos, 0);
+      if (on) {
+        const int pos = basepos + (int)__popcll(bal & ((1ull << lane) - 1));
         if (pos < kCapList)
           s_cand[pos] = ((uint64_t)__float_as_uint(av[k]) << 32) | (uint64_t)(~(uint32_t)S);
       }
@@ -183,12 +198,58 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   const int nc = s_nc;
   if (nc <= a.cap) return;
   if (nc <= kCapList) {
+    // the cap-th largest composite key K* by an 8-pass radix select (8 bits a
+    // pass, histograms in LDS); keys are distinct, so exactly cap keys are >= K*
+    uint64_t prefix = 0, pmask = 0;
+    int k = a.cap;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      s_hist[threadIdx.x] = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < nc; i += 256) {
+        const uint64_t key = s_cand[i];
+        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane owns bins 255-4*lane .. 252-4*lane (descending); inclusive scan
+        int c[4], tot = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[e] = (int)s_hist[255 - 4 * lane - e];
+          tot += c[e];
+        }
+        int inc = tot;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(inc, d);
+          if (lane >= d) inc += y;
+        }
+        const int exc = inc - tot;
+        if (exc < k && k <= inc) {   // exactly one lane holds the k-th key
+          int cum = exc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (cum + c[e] >= k) {
+              s_sel[0] = 255 - 4 * lane - e;
+              s_sel[1] = k - cum;
+              break;
+            }
+            cum += c[e];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= (uint64_t)s_sel[0] << shift;
+      pmask |= 255ull << shift;
+      k = s_sel[1];
+      __syncthreads();
+    }
     for (int i = threadIdx.x; i < nc; i += 256) {
-      const uint64_t ki = s_cand[i];
-      int rank = 0;
-      for (int j = 0; j < nc; ++j) rank += s_cand[j] > ki;
-      if (rank < a.cap) {
-        const int S = (int)(~(uint32_t)(ki & 0xffffffffull));
+      const uint64_t key = s_cand[i];
+      if (key >= prefix) {
+        const int S = (int)(~(uint32_t)(key & 0xffffffffull));
         atomicOr(&s_new[S >> 6], 1ull << (S & 63));
       }
     }

@@ -62,7 +62,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   return (x >= lo && x <= hi) ? x : dflt;
 }
 int tiles_per_item() { return env_int("SEKV_TILES_PER_ITEM", 4, 1, 1024); }
-int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 32, 1, 65536); }
+int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 32, 1, kMaxSpanList); }
 
 // Device buffer owned by the library.
 struct DBuf {
@@ -195,7 +195,7 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
   if (p->B < 1 || p->L < 1 || p->Hq < 1 || p->Hkv < 1 || p->T < 1)
     return fail(SEKV_EINVAL, "B, L, Hq, Hkv, T must be >= 1");
   if (p->Hq % p->Hkv) return fail(SEKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
-  if (p->dprime < 1 || p->dprime > 256) return fail(SEKV_EINVAL, "dprime must be in [1, 256]");
+  if (p->dprime < 1 || p->dprime > 64) return fail(SEKV_EUNSUPPORTED, "dprime must be in [1, 64]");
   if (p->R < 1 || p->R > p->d) return fail(SEKV_EINVAL, "R must be in [1, d]");
   if (!attend_supported(p->d, p->Hq / p->Hkv, p->R))
     return fail(SEKV_EUNSUPPORTED, "unsupported shape d=%d G=%d R=%d (d in {64,128}, G in {1,2,4,8}, R in {16,32,64})",
@@ -277,14 +277,14 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
     };
     while (count(tpw, sp) > max_items) {
       tpw *= 2;
-      sp *= 2;
+      sp = std::min(2 * sp, kMaxSpanList);
     }
     x->tpw = std::max(x->tpw, tpw);
   }
   for (int b = 0; b < x->B; ++b) {
     const BMeta& m = x->meta[b];
     const int ntiles = m.n_res_pad / 64;
-    const int sp = spi * (x->tpw / std::max(1, tiles_per_item()));
+    const int sp = std::min(kMaxSpanList, spi * (x->tpw / std::max(1, tiles_per_item())));
     const int nres = (ntiles + x->tpw - 1) / x->tpw;
     const int nfac = m.n_spans ? (m.n_spans + sp - 1) / sp : 0;
     for (int g = 0; g < x->Hkv; ++g) {

@@ -61,7 +61,7 @@ typedef struct sekv_ctx sekv_ctx;
 typedef struct sekv_index sekv_index;
 
 /* Shapes and prefill settings.  Supported: d in {64, 128}; G in {1, 2, 4, 8};
- * R in {16, 32, 64} with R <= d; 1 <= dprime <= 256; l_min >= 1. */
+ * R in {16, 32, 64} with R <= d; 1 <= dprime <= 64; l_min >= 1. */
 typedef struct {
   int32_t B, L, Hq, Hkv, d, T;
   int32_t R;            /* max SVD rank per span                                  */

@@ -71,7 +71,7 @@ def test_validate_accepts_every_workload(L):
 @pytest.mark.parametrize("field,value,status", [
     ("Hkv", 7, 1), ("d", 96, 6), ("R", 256, 1), ("R", 48, 6), ("Hkv", 2, 6),
     ("l_min", 0, 1), ("oversample", 17, 1), ("power_iters", -1, 1), ("alpha_sp", float("nan"), 1),
-    ("alpha_sp", float("inf"), 1), ("dprime", 0, 1), ("T", 0, 1), ("B", 0, 1), ("tier", 5, 1),
+    ("alpha_sp", float("inf"), 1), ("dprime", 0, 6), ("dprime", 65, 6), ("T", 0, 1), ("B", 0, 1), ("tier", 5, 1),
     ("ring_bytes", -1, 1), ("T", 2_000_000, 6),
 ])
 def test_validate_rejects(L, field, value, status):
