@@ -126,6 +126,7 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama8b_l32_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pinned", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="time a HIP graph replay of the step instead of eager launches")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the SeKV decode path here has no multi-GPU mode "
@@ -140,6 +141,10 @@ def main(argv=None):
     w = synth.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)
+    # one default-priority stream for everything: the library context, the
+    # timed region and the graph capture
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     t0 = time.time()
     H, K, V = synth.kv_cache(w, device=dev)
     W = torch.stack([synth.routing_w(w, l, dev) for l in range(w.L)])
@@ -149,7 +154,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"[bench] inputs for {w.name} generated on the GPU in {time.time() - t0:.1f} s")
 
-    ctx = sl.Context(0)
+    ctx = sl.Context(0, stream=stream)
     t0 = time.time()
     idx = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM), K, V, H, W, gates)
     build_s = time.time() - t0
@@ -179,23 +184,60 @@ def main(argv=None):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+
+    # kernel durations: an instrumented eager pass over the timed steps
     ctx.timing(True)
     ctx.timing_read()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
     for s in range(args.warmup, nsteps):
         step(s)
-    e1.record()
     torch.cuda.synchronize()
-    elapsed_ms = e0.elapsed_time(e1)
     route_ms, route_n, attend_ms, attend_n = ctx.timing_read()
     ctx.timing(False)
     assert attend_n == args.steps * L and route_n == args.steps * L
+
+    # whole-step throughput: the step (copy of the step's queries into the
+    # captured buffers, then route + attend for every layer) replayed as one
+    # HIP graph, or launched eagerly with --eager
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    if not args.graph:
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(args.warmup, nsteps):
+            step(s)
+        e1.record()
+        torch.cuda.synchronize()
+    else:
+        # the captured step reads its queries from fixed buffers; each timed
+        # step first copies its own queries there (part of the timed work)
+        qbuf = [torch.empty_like(qs[0][l]) for l in range(L)]
+        mbuf = torch.zeros_like(masks[0])
+        for l in range(L):
+            qbuf[l].copy_(qs[args.warmup][l])
+
+        def gstep():
+            for l in range(L):
+                idx.route(l, 1, qbuf[l], taus[l], cap, mbuf[l], None)
+                idx.decode_attend(l, 1, qbuf[l], mbuf[l], outs[l])
+        gstep()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            gstep()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(args.warmup, nsteps):
+            for l in range(L):
+                qbuf[l].copy_(qs[s][l])
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+    elapsed_ms = e0.elapsed_time(e1)
     value = B * args.steps / (elapsed_ms / 1e3)
-    log(f"[bench] {args.steps} steps in {elapsed_ms:.2f} ms: {value:.1f} query-tokens/s; "
-        f"attend {attend_ms / attend_n * 1e3:.1f} us/launch, route {route_ms / route_n * 1e3:.1f} us/launch")
+    log(f"[bench] {args.steps} steps in {elapsed_ms:.2f} ms ({'graph' if args.graph else 'eager'}): "
+        f"{value:.1f} query-tokens/s; attend {attend_ms / attend_n * 1e3:.1f} us/launch, "
+        f"route {route_ms / route_n * 1e3:.1f} us/launch")
 
     # algorithmic bytes of the timed launches
     mk = masks[args.warmup:].cpu().numpy().view(np.uint64)     # [K, L, B, 1, Hq, Wd]

@@ -146,17 +146,21 @@ struct SpanRegs {
       smk[ib] = *(const floatx4*)(sk + 16 * ib + 4 * grp);
       smv[ib] = *(const floatx4*)(sv + 16 * ib + 4 * grp);
     }
+    // token blocks past ntb read block ntb - 1 again (in range; never used)
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-      if (tb < ntb)
+    for (int tb = 0; tb < 4; ++tb) {
+      const int tbc = min(tb, ntb - 1);
 #pragma unroll
-        for (int kb = 0; kb < NR16; ++kb)
-          uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tb * NR16 + kb) * 256 + lane * 4);
+      for (int kb = 0; kb < NR16; ++kb)
+        uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
+    }
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        if (tb < ntb) uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tb) * 256 + lane * 4);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int tbc = min(tb, ntb - 1);
+        uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
+      }
     if (VV_EARLY) {
 #pragma unroll
       for (int db = 0; db < (VV_EARLY ? ND16 : 1); ++db)
@@ -239,14 +243,14 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
       const int nb = min(4, ntb - tb0);
       u32x2 uk[4][NR16], uvt[NR16][4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) {
+        const int tbc = tb0 + min(tb, nb - 1);
 #pragma unroll
         for (int kb = 0; kb < NR16; ++kb) {
-          uk[tb][kb] = (tb < nb) ? *(const u32x2*)(pu + ((int64_t)(tb0 + tb) * NR16 + kb) * 256 + lane * 4)
-                                 : u32x2{0, 0};
-          uvt[kb][tb] = (tb < nb) ? *(const u32x2*)(pw + ((int64_t)kb * ntb + tb0 + tb) * 256 + lane * 4)
-                                  : u32x2{0, 0};
+          uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
+          uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tbc) * 256 + lane * 4);
         }
+      }
       span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, chi, clo, m, l, o, wacc);
     }
   }
@@ -325,21 +329,30 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
           vt[rb][db] = *(const u32x4*)(Vb + (int64_t)(2 * t + rb) * 32 * D + db * 512 + lane * 8);
       // pseudo rows: the head's mask bit and the ln n_S bias, loaded with the tile
       const int row0 = 64 * t;
-      const bool has_pseudo = row0 + 64 > bm.n_raw;
+      const bool has_pseudo = row0 + 64 > bm.n_raw && bm.n_spans > 0;
       float bias[4][4];
       if (has_pseudo) {
+        // branch-free: every lane loads from a clamped in-range span, all 32
+        // loads are in flight together, invalid rows are masked afterwards
+        uint64_t word[4][4];
+        float lgn[4][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
-            float bv = 0.f;
-            if (hl < G && sp >= 0 && sp < bm.n_spans) {
-              const uint64_t word = mh[sp >> 6];
-              const float lg_n = a.logn[bm.span_base + sp];
-              bv = ((word >> (sp & 63)) & 1ull) ? -INFINITY : lg_n;
-            }
-            bias[kb][r] = bv;
+            const int spc = min(max(sp, 0), bm.n_spans - 1);
+            word[kb][r] = mh[spc >> 6];
+            lgn[kb][r] = a.logn[bm.span_base + spc];
+          }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
+            const bool valid = hl < G && sp >= 0 && sp < bm.n_spans;
+            const bool expanded = (word[kb][r] >> (sp & 63)) & 1ull;
+            bias[kb][r] = !valid ? 0.f : (expanded ? -INFINITY : lgn[kb][r]);
           }
       }
       floatx4 S[4];
@@ -490,13 +503,12 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 }
 
 // Merge the partials of every item of (b, g) into out[b][lc][h][:].  Each
-// workgroup takes one slice of D / DSPLIT dims for all G heads: it reads the
-// (m, l) of every partial into LDS, forms the per-head max M, the weights
-// e = exp(m - M) and the denominator L = sum e * l, then each wave sums a
-// quarter of the partials (each lane owning NPL contiguous outputs) and the
-// four wave sums are added.  grid (B * Hkv * DSPLIT, Lc).
+// workgroup takes one slice of D / DSPLIT dims for all G heads; each wave
+// folds a quarter of the partials into a running (max, denominator, sum)
+// with every load of a 16-partial chunk issued before any use, and the four
+// wave states are combined in LDS.  grid (B * Hkv * DSPLIT, Lc).
 template <int D, int G>
-struct MergeShape {
+struct MergeShape {   // lane layout of the merge
   static constexpr int DSPLIT = (G * D >= 128) ? G * D / 128 : 1;
   static constexpr int DS = D / DSPLIT;            // dims per workgroup
   static constexpr int NPL = G * DS / 64;          // outputs per lane (1 or 2)
@@ -506,10 +518,10 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   using MS = MergeShape<D, G>;
   constexpr int DS = MS::DS, NPL = MS::NPL;
+  constexpr int CH = 16;                       // partials per wave per round trip
   static_assert(NPL == 1 || NPL == 2, "merge lane layout");
-  __shared__ float s_w[kMaxMergeWeights], s_wl[kMaxMergeWeights];
   __shared__ float s_o[4][G * DS];
-  __shared__ float s_M[G], s_L[G];
+  __shared__ float s_m[4][G], s_l[4][G];
   const int bg = blockIdx.x / MS::DSPLIT, z = blockIdx.x - bg * MS::DSPLIT, lc = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -517,53 +529,69 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int P = a.items[first].part_count;
   const int64_t pstride = (int64_t)G * (D + 2);
   const float* base = a.part + ((int64_t)lc * a.n_items + first) * pstride;
-  for (int i = threadIdx.x; i < P * G; i += 256) {
-    const float* p = base + (i / G) * pstride + (i % G) * (D + 2) + D;
-    s_w[i] = p[0];
-    s_wl[i] = p[1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float M = -INFINITY;
-    for (int i = 0; i < P; ++i) M = fmaxf(M, s_w[i * G + threadIdx.x]);
-    s_M[threadIdx.x] = M;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < P * G; i += 256) {
-    const float mi = s_w[i];
-    s_w[i] = (mi == -INFINITY) ? 0.f : __expf(mi - s_M[i % G]);
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float L = 0.f;
-    for (int i = 0; i < P; ++i) L += s_w[i * G + threadIdx.x] * s_wl[i * G + threadIdx.x];
-    s_L[threadIdx.x] = L;
-  }
-  {
-    const int o0 = lane * NPL, h = o0 / DS, dim = z * DS + (o0 - h * DS);
-    float acc0 = 0.f, acc1 = 0.f;
-    const float* p0 = base + h * (D + 2) + dim;
-#pragma unroll 8
-    for (int i = wave; i < P; i += 4) {
-      const float wgt = s_w[i * G + h];
-      const float* p = p0 + i * pstride;
+  const int o0 = lane * NPL, h = o0 / DS, dim = z * DS + (o0 - h * DS);
+  // online merge over this wave's partials i = wave (mod 4), CH at a time
+  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int c0 = wave; c0 < P; c0 += 4 * CH) {
+    float mv[CH], lv[CH], v0[CH], v1[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = c0 + 4 * c;
+      const float* p = base + i * pstride + h * (D + 2);
+      const bool ok = i < P;
+      mv[c] = ok ? p[D] : -INFINITY;
+      lv[c] = ok ? p[D + 1] : 0.f;
       if (NPL == 2) {
-        const float2 v = *(const float2*)p;
-        acc0 += wgt * v.x;
-        acc1 += wgt * v.y;
+        const float2 v = ok ? *(const float2*)(p + dim) : float2{0.f, 0.f};
+        v0[c] = v.x;
+        v1[c] = v.y;
       } else {
-        acc0 += wgt * p[0];
+        v0[c] = ok ? p[dim] : 0.f;
+        v1[c] = 0.f;
       }
     }
-    s_o[wave][o0] = acc0;
-    if (NPL == 2) s_o[wave][o0 + 1] = acc1;
+    float mx = M;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) mx = fmaxf(mx, mv[c]);
+    const float corr = (M == -INFINITY) ? 0.f : __expf(M - mx);
+    L *= corr;
+    acc0 *= corr;
+    acc1 *= corr;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const float e = (mv[c] == -INFINITY) ? 0.f : __expf(mv[c] - mx);
+      L += e * lv[c];
+      acc0 += e * v0[c];
+      acc1 += e * v1[c];
+    }
+    M = mx;
+  }
+  // combine the four waves
+  if ((o0 - h * DS) == 0) {
+    s_m[wave][h] = M;
+    s_l[wave][h] = L;
   }
   __syncthreads();
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, s_m[w][h]);
+  const float sc = (M == -INFINITY) ? 0.f : __expf(M - Mt);
+  s_o[wave][o0] = acc0 * sc;
+  if (NPL == 2) s_o[wave][o0 + 1] = acc1 * sc;
+  __syncthreads();
   for (int idx = threadIdx.x; idx < G * DS; idx += 256) {
-    const int h = idx / DS, dim = z * DS + (idx - h * DS);
+    const int hh = idx / DS, dd = z * DS + (idx - hh * DS);
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
+    float Lh = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = s_m[w][hh];
+      Lh += (mw == -INFINITY) ? 0.f : __expf(mw - Mh) * s_l[w][hh];
+    }
     const float O = s_o[0][idx] + s_o[1][idx] + s_o[2][idx] + s_o[3][idx];
-    const float L = s_L[h];
-    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G + h) * D + dim] = (L > 0.f) ? O / L : 0.f;
+    a.out[(((int64_t)b * a.layer_count + lc) * a.Hq + g * G + hh) * D + dd] = (Lh > 0.f) ? O / Lh : 0.f;
   }
 }
 

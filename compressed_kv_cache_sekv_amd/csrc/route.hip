@@ -96,7 +96,9 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   {
     const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + (live ? S : 0);
 #pragma unroll
-    for (int j = 0; j < kMaxDp; ++j) v[j] = (live && j < dp) ? sp[(int64_t)j * bm.s_pad] : 0.f;
+    for (int j = 0; j < kMaxDp; ++j) v[j] = sp[(int64_t)min(j, dp - 1) * bm.s_pad];   // in range
+#pragma unroll
+    for (int j = 0; j < kMaxDp; ++j) v[j] = (live && j < dp) ? v[j] : 0.f;
   }
   // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims
   {
@@ -172,10 +174,10 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
     uint64_t wv[16];
     float av[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int S = S0 + 256 * k;
-      wv[k] = (S < bm.n_spans) ? mrow[S >> 6] : 0ull;
-      av[k] = (S < bm.n_spans) ? arow[S] : 0.f;
+    for (int k = 0; k < 16; ++k) {   // branch-free: clamped in-range loads
+      const int S = min(S0 + 256 * k, bm.n_spans - 1);
+      wv[k] = mrow[S >> 6];
+      av[k] = arow[S];
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -207,9 +209,22 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       const int shift = 56 - 8 * pass;
       s_hist[threadIdx.x] = 0;
       __syncthreads();
-      for (int i = threadIdx.x; i < nc; i += 256) {
-        const uint64_t key = s_cand[i];
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+      for (int i0 = 0; i0 < nc; i0 += 256) {
+        // lanes with equal digits are counted with 8 ballots and only the
+        // lowest such lane updates the bin (keys share their top bytes, so
+        // per-lane atomics would all hit one bin)
+        const int i = i0 + threadIdx.x;
+        const uint64_t key = (i < nc) ? s_cand[i] : 0ull;
+        const bool on = (i < nc) && (key & pmask) == prefix;
+        const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+        uint64_t peers = __ballot(on);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const uint64_t bal = __ballot((digit >> bit) & 1u);
+          peers &= ((digit >> bit) & 1u) ? bal : ~bal;
+        }
+        if (on && (peers & ((1ull << lane) - 1)) == 0)
+          atomicAdd(&s_hist[digit], (uint32_t)__popcll(peers));
       }
       __syncthreads();
       if (wave == 0) {
