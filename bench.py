@@ -127,6 +127,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pinned", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time a HIP graph replay of the step instead of eager launches")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 4 plain device copies of MIB MiB each (a known-size kernel that scales "
+                         "rocprofv3's FETCH_SIZE / WRITE_SIZE readings) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the SeKV decode path here has no multi-GPU mode "
@@ -138,6 +141,15 @@ def main(argv=None):
     from compressed_kv_cache_sekv_amd import lib as sl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        n = args.copy_probe << 18   # fp32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 4}), flush=True)
+        return 0
     w = synth.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)

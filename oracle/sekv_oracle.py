@@ -13,7 +13,7 @@ of it:
   [Tech]     기술 상세 (Technical details), including the reconstruction sum
              that the Method section calls Eq. 8
 Where the article leaves a step open, the reading taken is stated at the
-function (readings R1..R17 are collected in the design doc's readings table).
+function that takes it.
 
 Everything is fp64 numpy; inputs arrive in their storage precision (bf16 K, V,
 q; fp32 H, W, gates) and are widened exactly.  No blocking, fusion or
