@@ -79,6 +79,11 @@ __device__ __forceinline__ float xsum4(float v) {
 }
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Fold a block of scores (already scaled, masked to -inf) into the running
 // softmax state (m, l) of this lane's head and turn them into weights
@@ -117,7 +122,7 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
 template <int D, int R>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
-  static constexpr bool VV_EARLY = (R <= 16);   // preload V^V (register budget)
+  static constexpr bool VV_EARLY = false;   // preload V^V (register budget)
   u32x4 vkt[NR16][NS32];
   u32x2 vv[VV_EARLY ? ND16 : 1][NR16];
   floatx4 smk[NR16], smv[NR16];
@@ -271,16 +276,16 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
 }
 
 template <int D, int G, int R>
-__global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 16 ? 3 : (R <= 32 ? 2 : 1))))
+void attend_kernel(const AttendArgs a) {
   constexpr int NS32 = D / 32, ND16 = D / 16;
-  constexpr bool PREFETCH = (R <= 16);
+  constexpr bool PREFETCH = false;
   static_assert(G >= 1 && G <= 16, "G");
   __shared__ float s_ml[4][2][G];
   __shared__ float s_o[4][G][D];
-  __shared__ uint64_t s_uw[1024];
-  __shared__ int32_t s_pre[1025];
-  __shared__ int32_t s_ln[kMaxSpanList];   // span length | active heads << 24
-  __shared__ int64_t s_off[kMaxSpanList];  // blob offset within the (b, l, g) region
+  __shared__ uint64_t s_uw[kMaxWords];     // union of the G heads' mask words
+  __shared__ int32_t s_pre[kMaxWords + 1];
+  __shared__ int32_t s_ln[kMaxSpanList];   // span id | active heads << 24
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -309,35 +314,33 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
 
   if (it.kind == 0) {
     // ------------------------------------------------------ resident rows
+    // 32-row steps: two 16-row key blocks and one 32-row value block
     const int64_t lg = (int64_t)l * a.Hkv + g;
     const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
     const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
     const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
-    const int ntiles = bm.n_res_pad >> 6;
-    const int t_end = min(ntiles, (it.j + 1) * a.tpw);
-    for (int t = it.j * a.tpw + wave; t < t_end; t += 4) {
-      u32x4 kt[4][NS32], vt[2][ND16];
+    const int nsteps = bm.n_res_pad >> 5;
+    const int s_end = min(nsteps, 2 * (it.j + 1) * a.tpw);
+    for (int t = 2 * it.j * a.tpw + wave; t < s_end; t += 4) {
+      u32x4 kt[2][NS32], vt[ND16];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s = 0; s < NS32; ++s)
-          kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(4 * t + kb) * 16 * D + s * 512 + lane * 8);
+          kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int db = 0; db < ND16; ++db)
-          vt[rb][db] = *(const u32x4*)(Vb + (int64_t)(2 * t + rb) * 32 * D + db * 512 + lane * 8);
-      // pseudo rows: the head's mask bit and the ln n_S bias, loaded with the tile
-      const int row0 = 64 * t;
-      const bool has_pseudo = row0 + 64 > bm.n_raw && bm.n_spans > 0;
-      float bias[4][4];
+      for (int db = 0; db < ND16; ++db) vt[db] = *(const u32x4*)(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
+      // pseudo rows: the head's mask bit and the ln n_S bias, loaded with the step
+      const int row0 = 32 * t;
+      const bool has_pseudo = row0 + 32 > bm.n_raw && bm.n_spans > 0;
+      float bias[2][4];
       if (has_pseudo) {
-        // branch-free: every lane loads from a clamped in-range span, all 32
+        // branch-free: every lane loads from a clamped in-range span, the
         // loads are in flight together, invalid rows are masked afterwards
-        uint64_t word[4][4];
-        float lgn[4][4];
+        uint64_t word[2][4];
+        float lgn[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
             lgn[kb][r] = a.logn[bm.span_base + spc];
           }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
@@ -355,15 +358,15 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
             bias[kb][r] = !valid ? 0.f : (expanded ? -INFINITY : lgn[kb][r]);
           }
       }
-      floatx4 S[4];
+      floatx4 S[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
         S[kb] = floatx4{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < NS32; ++s) S[kb] = mfma32(kt[kb][s], qB[s], S[kb]);
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = row0 + 16 * kb + 4 * grp + r;
@@ -372,30 +375,38 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
           else if (has_pseudo && row >= bm.n_raw) x += bias[kb][r];
           S[kb][r] = x;
         }
-      const float corr = online<4>(S, 4, m, lsum);
+      const float corr = online<2>(S, 2, m, lsum);
 #pragma unroll
       for (int db = 0; db < ND16; ++db) o[db] *= corr;
+      u32x4 phi, plo;
+      pack8(S[0], S[1], phi, plo);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        u32x4 phi, plo;
-        pack8(S[2 * rb], S[2 * rb + 1], phi, plo);
-#pragma unroll
-        for (int db = 0; db < ND16; ++db) {
-          o[db] = mfma32(vt[rb][db], phi, o[db]);
-          o[db] = mfma32(vt[rb][db], plo, o[db]);
-        }
+      for (int db = 0; db < ND16; ++db) {
+        o[db] = mfma32(vt[db], phi, o[db]);
+        o[db] = mfma32(vt[db], plo, o[db]);
       }
     }
   } else {
     // --------------------------------------------------- routed spans
-    // union over the G heads of this KV head, and its prefix counts
-    // (bits at or past N_S(b) are ignored, whatever the caller's mask holds)
-    for (int w = threadIdx.x; w < Wd; w += 256) {
-      uint64_t u = 0;
+    // per-head mask words and their union over the G heads of this KV head
+    // (bits at or past N_S(b) are ignored, whatever the caller's mask
+    // holds), prefix counts of the union words
+    // (word w = threadIdx.x + 256 k of every head stays in this thread's registers)
+    uint64_t hw[kMaxWords / 256][G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) u |= mrow[(int64_t)h * Wd + w];
-      const int left = bm.n_spans - 64 * w;
-      s_uw[w] = left >= 64 ? u : (left > 0 ? u & ((1ull << left) - 1) : 0ull);
+    for (int k = 0; k < kMaxWords / 256; ++k) {
+      const int w = threadIdx.x + 256 * k;
+      if (w < Wd) {
+        const int left = bm.n_spans - 64 * w;
+        const uint64_t valid = left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
+        uint64_t u = 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          hw[k][h] = mrow[(int64_t)h * Wd + w] & valid;
+          u |= hw[k][h];
+        }
+        s_uw[w] = u;
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -417,51 +428,63 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
     const int U = s_pre[Wd];
     const int beg = (int)((int64_t)it.j * U / it.nj), end = (int)((int64_t)(it.j + 1) * U / it.nj);
     const int cnt = min(end - beg, kMaxSpanList);   // the host keeps shares <= kMaxSpanList
-    // this workgroup's spans: rank -> (span, blob, length, active heads), all
-    // metadata loads issued in one parallel pass and kept in LDS
-    const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
-    const int64_t* roff = a.ring_off
-        ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans : nullptr;
-    for (int i = threadIdx.x; i < cnt; i += 256) {
-      const int k = beg + i;
-      int lo = 0, hi = Wd - 1;   // largest word w with s_pre[w] <= k (it holds rank k)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
-      }
-      uint64_t bits = s_uw[lo];
-      for (int skip = k - s_pre[lo]; skip > 0; --skip) bits &= bits - 1;
-      const int bit = __builtin_ctzll(bits);
-      const int S = 64 * lo + bit;
-      int hm = 0;
+    // this item's spans in union order (span id | active heads << 24), one
+    // thread per mask word
 #pragma unroll
-      for (int h = 0; h < G; ++h) hm |= (int)((mrow[(int64_t)h * Wd + lo] >> bit) & 1ull) << h;
-      s_ln[i] = a.span_len[bm.span_base + S] | (hm << 24);
-      s_off[i] = roff ? roff[k] - ((int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg)
-                      : a.span_off[bm.span_base + S];
+    for (int kw = 0; kw < kMaxWords / 256; ++kw) {
+      const int w = threadIdx.x + 256 * kw;
+      if (w >= Wd) continue;
+      int k = s_pre[w];
+      if (k >= beg + cnt || s_pre[w + 1] <= beg) continue;
+      uint64_t bits = s_uw[w];
+      while (bits && k < beg + cnt) {
+        const int bit = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (k >= beg) {
+          int hm = 0;
+#pragma unroll
+          for (int h = 0; h < G; ++h) hm |= (int)((hw[kw][h] >> bit) & 1ull) << h;
+          s_ln[k - beg] = (64 * w + bit) | (hm << 24);
+        }
+        ++k;
+      }
     }
     __syncthreads();
     const int i0 = (int)((int64_t)cnt * wave / 4), i1 = (int)((int64_t)cnt * (wave + 1) / 4);
     if (i0 < i1) {
-      const uint8_t* rbase = roff ? a.pool : region;
-      const int64_t rshift = roff ? ((int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg) : 0;
-      auto fetch = [&](SpanRegs<D, R>& sr, int i) {
-        const int ln = s_ln[i];
-        sr.load(rbase + rshift + s_off[i], uni(ln & 0xffffff), uni(ln >> 24), lane, grp);
+      // blob address of span rank i: the factor pool, or the staging ring
+      const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
+      const int64_t* roff = a.ring_off
+          ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + beg : nullptr;
+      // metadata of rank i (wave-uniform): length, active heads, blob offset;
+      // loaded one span ahead of the blob that needs it
+      struct Meta { int n, hm; int64_t off; };
+      auto meta = [&](int i) {
+        const int e = s_ln[min(i, i1 - 1)];
+        const int S = e & 0xffffff;
+        Meta mt;
+        mt.hm = e >> 24;
+        mt.n = a.span_len[bm.span_base + S];
+        mt.off = roff ? roff[min(i, i1 - 1)] : (int64_t)(region - a.pool) + a.span_off[bm.span_base + S];
+        return mt;
       };
+      Meta mc = meta(i0);
+      Meta mn = meta(i0 + 1);
       SpanRegs<D, R> cur;
-      fetch(cur, i0);
+      cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp);
       for (int i = i0; i < i1; ++i) {
+        const Meta mnn = meta(i + 2);
         if (PREFETCH) {
           SpanRegs<D, R> nxt;
-          if (i + 1 < i1) fetch(nxt, i + 1);
+          if (i + 1 < i1) nxt.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp);
           span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
           if (i + 1 >= i1) break;
           cur = nxt;
         } else {
           span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
-          if (i + 1 < i1) fetch(cur, i + 1);
+          if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp);
         }
+        mn = mnn;
       }
     }
   }
@@ -479,7 +502,7 @@ __global__ __launch_bounds__(256) void attend_kernel(const AttendArgs a) {
   }
   __syncthreads();
   const int64_t pstride = (int64_t)G * (D + 2);
-  float* part = a.part + ((int64_t)lc * a.n_items + blockIdx.x) * pstride;
+  float* part = a.part + ((int64_t)lc * a.n_items + it.slot) * pstride;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, dim = idx - h * D;
     float M = -INFINITY;
@@ -525,8 +548,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int bg = blockIdx.x / MS::DSPLIT, z = blockIdx.x - bg * MS::DSPLIT, lc = blockIdx.y;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int first = a.bg_first[bg];
-  const int P = a.items[first].part_count;
+  const int first = a.bg_first[2 * bg];
+  const int P = a.bg_first[2 * bg + 1];
   const int64_t pstride = (int64_t)G * (D + 2);
   const float* base = a.part + ((int64_t)lc * a.n_items + first) * pstride;
   const int o0 = lane * NPL, h = o0 / DS, dim = z * DS + (o0 - h * DS);

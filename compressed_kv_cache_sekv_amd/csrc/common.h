@@ -99,15 +99,19 @@ struct BMeta {
 constexpr int kMaxMergeWeights = 2048;
 // Routed spans one factored work item may take (its LDS span list).
 constexpr int kMaxSpanList = 512;
+// Mask words per (b, l, h) the decode kernel handles (65536 spans).
+constexpr int kMaxWords = 1024;
 
 // Decode work: one workgroup of 4 waves per item.  kind 0: resident rows
 // tiles [j*tpw, (j+1)*tpw); kind 1: the j-th of nj shares of the union of
-// the routed spans of (b, l, g).
+// the routed spans of (b, l, g).  Items are launched span shares first; each
+// writes its softmax partial to `slot` (the slots of one (b, g) are
+// contiguous).
 struct WorkItem {
   int32_t b, g, kind, j, nj;
-  int32_t part_first;   // first item of (b, g) (partials of (b, g) are contiguous)
-  int32_t part_count;   // items of (b, g)
-  int32_t pad_;
+  int32_t part_first;   // first slot of (b, g)
+  int32_t part_count;   // slots of (b, g)
+  int32_t slot;
 };
 
 struct AttendArgs {
@@ -134,7 +138,7 @@ struct AttendArgs {
 struct MergeArgs {
   const float* part;
   const WorkItem* items;
-  const int32_t* bg_first;  // [B*Hkv] first item of (b, g)
+  const int32_t* bg_first;  // [B*Hkv][2]: first partial slot of (b, g), slot count
   float* out;               // [B][Lc][Hq][D]
   int32_t layer_count, n_items, B, Hq, Hkv;
 };

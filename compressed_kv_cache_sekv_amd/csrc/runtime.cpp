@@ -209,7 +209,7 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
     if (p->power_iters < 0 || p->power_iters > 8) return fail(SEKV_EINVAL, "power_iters must be in [0, 8]");
   }
   const int64_t smax = (int64_t)(p->T + 1) / (p->l_min > 0 ? p->l_min + 1 : 2);
-  if ((smax + 63) / 64 > 1024) return fail(SEKV_EUNSUPPORTED, "T too large for l_min (more than 65536 spans possible)");
+  if ((smax + 63) / 64 > kMaxWords) return fail(SEKV_EUNSUPPORTED, "T too large for l_min (more than 65536 spans possible)");
   return SEKV_OK;
 }
 
@@ -260,11 +260,11 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
   x->layer_bytes = pb;
   x->pool_bytes = pb * x->L;
   x->Wd = std::max(1, (x->max_spans + 63) / 64);
-  // decode work items, contiguous per (b, g)
+  // decode work items; the partial slots of one (b, g) are contiguous
   x->tpw = tiles_per_item();
   const int spi = spans_per_item();
   x->items.clear();
-  x->bg_first.assign((size_t)x->B * x->Hkv, 0);
+  x->bg_first.assign((size_t)2 * x->B * x->Hkv, 0);
   // the merge combines at most kMaxMergeWeights / G partials per (b, g):
   // widen the items of long sequences until they fit
   const int max_items = kMaxMergeWeights / x->G;
@@ -281,6 +281,9 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
     }
     x->tpw = std::max(x->tpw, tpw);
   }
+  // span shares of every (b, g) first (they run longest), then resident tiles
+  std::vector<WorkItem> res_items;
+  int slot = 0;
   for (int b = 0; b < x->B; ++b) {
     const BMeta& m = x->meta[b];
     const int ntiles = m.n_res_pad / 64;
@@ -288,12 +291,14 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
     const int nres = (ntiles + x->tpw - 1) / x->tpw;
     const int nfac = m.n_spans ? (m.n_spans + sp - 1) / sp : 0;
     for (int g = 0; g < x->Hkv; ++g) {
-      const int first = (int)x->items.size();
-      x->bg_first[(size_t)b * x->Hkv + g] = first;
-      for (int j = 0; j < nres; ++j) x->items.push_back(WorkItem{b, g, 0, j, nres, first, nres + nfac, 0});
-      for (int j = 0; j < nfac; ++j) x->items.push_back(WorkItem{b, g, 1, j, nfac, first, nres + nfac, 0});
+      const int first = slot;
+      x->bg_first[2 * ((size_t)b * x->Hkv + g)] = first;
+      x->bg_first[2 * ((size_t)b * x->Hkv + g) + 1] = nres + nfac;
+      for (int j = 0; j < nfac; ++j) x->items.push_back(WorkItem{b, g, 1, j, nfac, first, nres + nfac, slot++});
+      for (int j = 0; j < nres; ++j) res_items.push_back(WorkItem{b, g, 0, j, nres, first, nres + nfac, slot++});
     }
   }
+  x->items.insert(x->items.end(), res_items.begin(), res_items.end());
 }
 
 // Allocate and clear the device (and pinned) storage of a planned index.
