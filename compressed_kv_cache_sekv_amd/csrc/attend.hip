@@ -118,25 +118,27 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
 }
 
 // Registers of one span blob: the fixed-size factors plus the first chunk
-// (up to 64 tokens) of the left factors.
+// (up to 64 tokens) of the left factors.  V^V, needed only at the end of the
+// span, goes to the wave's LDS buffer instead: asynchronous global->LDS loads
+// (16 bytes per lane, 1 KB per instruction, lane i's bytes land at 16 i)
+// issued with the rest, so it costs no registers and no second round trip.
 template <int D, int R>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
-  static constexpr bool VV_EARLY = false;   // preload V^V (register budget)
+  static constexpr int VV_BYTES = 2 * D * R;
   u32x4 vkt[NR16][NS32];
-  u32x2 vv[VV_EARLY ? ND16 : 1][NR16];
   floatx4 smk[NR16], smv[NR16];
   u32x2 uk[4][NR16];
   u32x2 uvt[NR16][4];
   const uint8_t* blob;
   int n, hm;
 
-  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp) {
+  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp, uint8_t* lds_vv) {
     blob = b;
     n = n_;
     hm = hm_;
     const bf16_t* pk = (const bf16_t*)(b + Blob::off_vkt(R, D));
-    const bf16_t* pv = (const bf16_t*)(b + Blob::off_vv(R, D));
+    const uint8_t* pv = b + Blob::off_vv(R, D);
     const float* sk = (const float*)(b + Blob::off_smk(R, D));
     const float* sv = (const float*)(b + Blob::off_smv(R, D));
     const bf16_t* pu = (const bf16_t*)(b + Blob::off_uk(R, D));
@@ -166,12 +168,10 @@ struct SpanRegs {
         const int tbc = min(tb, ntb - 1);
         uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
       }
-    if (VV_EARLY) {
 #pragma unroll
-      for (int db = 0; db < (VV_EARLY ? ND16 : 1); ++db)
-#pragma unroll
-        for (int kb = 0; kb < NR16; ++kb) vv[db][kb] = *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
-    }
+    for (int c = 0; c < VV_BYTES / 1024; ++c)
+      __builtin_amdgcn_global_load_lds((const void*)(pv + c * 1024 + lane * 16),
+                                       (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, 0);
   }
 };
 
@@ -223,7 +223,7 @@ __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u
 template <int D, int G, int R>
 __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 (&qB)[D / 32], float scale,
                                           int lane, int hl, int grp, float& m, float& l,
-                                          floatx4 (&o)[D / 16]) {
+                                          floatx4 (&o)[D / 16], const uint8_t* lds_vv) {
   constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
   const int n = sr.n, npad = Blob::npad(n), ntb = npad >> 4;
   // t = V^K^T q; c = t * sigma m^K / sqrt(d), split into bf16 hi + lo
@@ -263,13 +263,15 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
   u32x2 whi[NR16], wlo[NR16];
 #pragma unroll
   for (int ib = 0; ib < NR16; ++ib) pack4(wacc[ib] * sr.smv[ib], whi[ib], wlo[ib]);
-  const bf16_t* pv = (const bf16_t*)(sr.blob + Blob::off_vv(R, D));
+  // V^V from the wave's LDS copy: wait for every outstanding load of the
+  // wave, the asynchronous copies included
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const bf16_t* pv = (const bf16_t*)lds_vv;
 #pragma unroll
   for (int db = 0; db < ND16; ++db)
 #pragma unroll
     for (int kb = 0; kb < NR16; ++kb) {
-      const u32x2 vvv = SpanRegs<D, R>::VV_EARLY ? sr.vv[SpanRegs<D, R>::VV_EARLY ? db : 0][kb]
-                                                 : *(const u32x2*)(pv + ((int64_t)db * NR16 + kb) * 256 + lane * 4);
+      const u32x2 vvv = *(const u32x2*)(pv + ((db * NR16 + kb) * 256 + lane * 4));
       o[db] = mfma16(vvv, whi[kb], o[db]);
       o[db] = mfma16(vvv, wlo[kb], o[db]);
     }
@@ -279,13 +281,13 @@ template <int D, int G, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 16 ? 3 : (R <= 32 ? 2 : 1))))
 void attend_kernel(const AttendArgs a) {
   constexpr int NS32 = D / 32, ND16 = D / 16;
-  constexpr bool PREFETCH = false;
   static_assert(G >= 1 && G <= 16, "G");
   __shared__ float s_ml[4][2][G];
   __shared__ float s_o[4][G][D];
   __shared__ uint64_t s_uw[kMaxWords];     // union of the G heads' mask words
   __shared__ int32_t s_pre[kMaxWords + 1];
   __shared__ int32_t s_ln[kMaxSpanList];   // span id | active heads << 24
+  __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -471,19 +473,11 @@ void attend_kernel(const AttendArgs a) {
       Meta mc = meta(i0);
       Meta mn = meta(i0 + 1);
       SpanRegs<D, R> cur;
-      cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp);
+      cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp, s_vv[wave]);
       for (int i = i0; i < i1; ++i) {
         const Meta mnn = meta(i + 2);
-        if (PREFETCH) {
-          SpanRegs<D, R> nxt;
-          if (i + 1 < i1) nxt.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp);
-          span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
-          if (i + 1 >= i1) break;
-          cur = nxt;
-        } else {
-          span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o);
-          if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp);
-        }
+        span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave]);
+        if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp, s_vv[wave]);
         mn = mnn;
       }
     }
@@ -528,7 +522,7 @@ void attend_kernel(const AttendArgs a) {
 // Merge the partials of every item of (b, g) into out[b][lc][h][:].  Each
 // workgroup takes one slice of D / DSPLIT dims for all G heads; each wave
 // folds a quarter of the partials into a running (max, denominator, sum)
-// with every load of a 16-partial chunk issued before any use, and the four
+// with every load of a 32-partial chunk issued before any use, and the four
 // wave states are combined in LDS.  grid (B * Hkv * DSPLIT, Lc).
 template <int D, int G>
 struct MergeShape {   // lane layout of the merge
@@ -541,7 +535,7 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   using MS = MergeShape<D, G>;
   constexpr int DS = MS::DS, NPL = MS::NPL;
-  constexpr int CH = 16;                       // partials per wave per round trip
+  constexpr int CH = 32;                       // partials per wave per round trip
   static_assert(NPL == 1 || NPL == 2, "merge lane layout");
   __shared__ float s_o[4][G * DS];
   __shared__ float s_m[4][G], s_l[4][G];

@@ -79,9 +79,16 @@ constexpr int kMaxDp = 64;
 
 __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[kMaxDp];
+  // workgroup id -> (b, chunk, h) so that every chunk of one (b, h) lands on
+  // the same XCD (consecutive ids go round-robin over the 8 XCDs): W^(l,h)
+  // and q are then fetched once into that XCD's L2
   const int nchunk = (a.Wd + 3) >> 2;
-  const int b = blockIdx.x / nchunk, chunk = blockIdx.x - b * nchunk;
-  const int h = blockIdx.y, lc = blockIdx.z, l = a.layer_begin + lc;
+  const int id = blockIdx.x, x8 = id & 7, rest = id >> 3;
+  const int chunk = rest % nchunk, bh8 = rest / nchunk;
+  const int bh = bh8 * 8 + x8;                 // (b, h) pair, b major
+  const int b = bh / a.Hq, h = bh - b * a.Hq;
+  if (b >= a.B) return;
+  const int lc = blockIdx.y, l = a.layer_begin + lc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const BMeta bm = a.meta[b];
   const int D = a.D, dp = a.dp;
@@ -157,7 +164,7 @@ constexpr int kCapList = 2048;
 __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   __shared__ uint32_t s_hist[256];
   __shared__ int s_tmp[8];
-  __shared__ int s_sel[2];
+  __shared__ int s_sel[3];
   __shared__ int s_nc;
   __shared__ uint64_t s_cand[kCapList];
   __shared__ unsigned long long s_new[1024];
@@ -249,6 +256,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
             if (cum + c[e] >= k) {
               s_sel[0] = 255 - 4 * lane - e;
               s_sel[1] = k - cum;
+              s_sel[2] = (k - cum == c[e]);   // every key of the bin is kept
               break;
             }
             cum += c[e];
@@ -259,7 +267,11 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       prefix |= (uint64_t)s_sel[0] << shift;
       pmask |= 255ull << shift;
       k = s_sel[1];
+      const bool whole_bin = s_sel[2] != 0;
       __syncthreads();
+      // the cap-th largest key is the smallest of its bin and the whole bin
+      // is kept: every key >= prefix (lower bytes zero) is exactly the top cap
+      if (whole_bin) break;
     }
     for (int i = threadIdx.x; i < nc; i += 256) {
       const uint64_t key = s_cand[i];
@@ -343,7 +355,8 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const CalibArgs a) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nchunk = (a.Wd + 3) >> 2;
-  hipLaunchKernelGGL(route_kernel, dim3(a.B * nchunk, a.Hq, a.layer_count), dim3(256), 0, st, a);
+  const int nbh8 = (a.B * a.Hq + 7) / 8;
+  hipLaunchKernelGGL(route_kernel, dim3(nbh8 * 8 * nchunk, a.layer_count), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
