@@ -1,0 +1,167 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (one layer per call, the 8B-shaped 128K layer of the 32-layer stack).
+
+* 8B-shaped layer at 131072 tokens (32 query / 8 KV heads, R = 16, 10% cap):
+  the oracle builds the index, the library imports it; every head is routed
+  (masks bit-exact, ties at the threshold and at the cap boundary excluded)
+  and decoded (5e-3 relative L2).  The library's own index from the same
+  inputs: span table and raw positions bit-exact.
+* 70B-shaped layer, 32 sequences of 65536 tokens (64 query / 8 KV heads,
+  R = 64): the library builds the whole index on the GPU from inputs drawn on
+  the GPU; the span table of every sequence is checked against the oracle's
+  split, and for sampled (sequence, KV head) units the oracle builds that
+  unit's index from the same inputs and routes and decodes its query heads
+  (masks bit-exact; outputs within the end-to-end bound, since the two sides
+  hold different rank-R factors of spans longer than R).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_kv_cache_sekv_amd import synth
+from oracle import sekv_oracle as O
+from tests import sekv_cases as SC
+from tests.test_gpu_parity import dev, gpu_decode, gpu_route, imported, oracle_route_all
+
+pytestmark = pytest.mark.gpu
+
+END_TO_END = 2e-2
+
+
+@pytest.fixture(scope="module")
+def sl():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from compressed_kv_cache_sekv_amd import lib
+    return lib
+
+
+@pytest.fixture(scope="module")
+def ctx(sl):
+    c = sl.Context(0)
+    yield c
+    torch.cuda.synchronize()
+    c.close()
+
+
+@pytest.fixture(scope="module")
+def case_128k():
+    w = synth.WORKLOADS["llama8b_l32_128k"].scaled(L=1, tier="hbm")
+    print(f"[case] building the oracle index of one 128K layer", flush=True)
+    return SC.make_case(w)
+
+
+def test_128k_layer_identical_index(ctx, sl, case_128k):
+    c = case_128k
+    w = c.w
+    idx = imported(ctx, sl, c)
+    cap = int(math.floor(w.cap_frac * c.idxs[0].n_spans))
+    q = c.q(0)
+    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+    _, z_o = oracle_route_all(c, q, c.tau, cap)
+    words, _ = gpu_route(idx, c, q, c.tau, cap)
+    bad = excl = ties = over = 0
+    for key, z in z_o.items():
+        b, l, h = key
+        bnd = SC.cap_boundary(alpha_o[key], z_pre[key], cap)
+        over += bnd is not None
+        m, e, t = SC.compare_masks(words[b, l, h], z, alpha_o[key], c.tau[l, h], bnd)
+        bad += m
+        excl += e
+        ties += t
+        assert SC.unpack_mask(words[b, l, h], len(z)).sum() <= cap
+    print(f"[128k] N_S {c.idxs[0].n_spans}, cap {cap}, heads over budget {over}, mask mismatches {bad}, "
+          f"excluded {excl}, ties at 1e-4 {ties}", flush=True)
+    assert bad == 0
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words))
+    worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+    print(f"[128k] decode over {len(out_o)} heads: worst rel-L2 {worst:.3e}", flush=True)
+    assert worst <= SC.REL_L2
+    idx.free()
+
+
+def test_128k_layer_build_spans(ctx, sl, case_128k):
+    c = case_128k
+    w = c.w
+    idx = ctx.build_index(sl.build_params(w), dev(c.K), dev(c.V), dev(c.H), dev(c.W), None)
+    assert list(idx.n_spans) == [c.idxs[0].n_spans] and list(idx.n_raw) == [c.idxs[0].n_raw]
+    start, length, raw = idx.spans()
+    ref = SC.import_arrays(c)
+    assert np.array_equal(start, ref["span_start"]) and np.array_equal(length, ref["span_len"])
+    assert np.array_equal(raw, ref["raw_pos"])
+    idx.free()
+
+
+def _tau_for(alpha, frac):
+    """Midpoint of the k-th and (k+1)-th largest alpha, k = round(frac * N)."""
+    a = np.sort(np.asarray(alpha, np.float64))[::-1]
+    k = min(max(int(math.floor(frac * len(a) + 0.5)), 1), len(a) - 1)
+    return float(np.float32(0.5 * (a[k - 1] + a[k])))
+
+
+def test_70b_batch32_64k_sampled(ctx, sl):
+    w = synth.WORKLOADS["llama70b_b32_64k"]
+    G = w.G
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, l, "cuda") for l in range(w.L)])
+    S_max = synth.max_spans(w.T, w.l_min)
+    gates = torch.stack([torch.stack([synth.gates(w, b, l, S_max, "cuda") for l in range(w.L)])
+                         for b in range(w.B)])
+    q = synth.query(w, 0, "cuda")
+    idx = ctx.build_index(sl.build_params(w), K, V, H, W, gates)
+    Hc = H.cpu()
+    # span tables of every sequence
+    start, length, raw = idx.spans()
+    so = ro = 0
+    for b in range(w.B):
+        sp = O.span_split(Hc[b].numpy(), w.alpha_sp, w.l_min)
+        n, r = len(sp.spans), len(sp.raw)
+        assert idx.n_spans[b] == n and idx.n_raw[b] == r, b
+        assert np.array_equal(start[so:so + n], sp.spans[:, 0]) and np.array_equal(length[so:so + n], sp.spans[:, 1])
+        assert np.array_equal(raw[ro:ro + r], sp.raw)
+        so += n
+        ro += r
+    # sampled units: the oracle's own index of (sequence b, KV head g)
+    Wn = W.cpu().double().numpy()
+    qn = q.cpu().double().numpy()
+    units = [(0, 0), (17, 3), (31, 7)]
+    refs = {}
+    tau = np.full((w.L, w.Hq), 0.5, np.float64)
+    for b, g in units:
+        ix = O.build_index_b(Hc[b].numpy(), K[b, :, g:g + 1].cpu().double().numpy(),
+                             V[b, :, g:g + 1].cpu().double().numpy(), Wn[:, g * G:(g + 1) * G],
+                             gates[b, :, g:g + 1].cpu().double().numpy(), R=w.R, alpha_sp=w.alpha_sp,
+                             l_min=w.l_min, Hq=G)
+        refs[(b, g)] = ix
+        for hh in range(G):
+            a, _ = O.route_head(Wn[0, g * G + hh], qn[b, 0, g * G + hh], ix.s[0, hh], 0.5)
+            tau[0, g * G + hh] = _tau_for(a, w.frac)
+    Wd = idx.mask_words
+    mask = torch.zeros(w.B, w.L, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    idx.route(0, w.L, q, dev(tau, torch.float32), 0, mask, None)
+    out = torch.zeros(w.B, w.L, w.Hq, w.d, device="cuda")
+    idx.decode_attend(0, w.L, q, mask, out)
+    torch.cuda.synchronize()
+    words = mask.cpu().numpy().view(np.uint64)
+    out = out.cpu().double().numpy()
+    worst = 0.0
+    bad = skipped = 0
+    for (b, g), ix in refs.items():
+        for hh in range(G):
+            h = g * G + hh
+            alpha, z = O.route_head(Wn[0, h], qn[b, 0, h], ix.s[0, hh], tau[0, h])
+            m, _, _ = SC.compare_masks(words[b, 0, h], z, alpha, tau[0, h])
+            bad += m
+            if not np.array_equal(SC.unpack_mask(words[b, 0, h], len(z)), z):
+                skipped += 1   # a pair within the tie window decided the other way
+                continue
+            ref = O.decode_head(qn[b, 0, h], ix, 0, 0, z)
+            worst = max(worst, SC.rel_l2(out[b, 0, h], ref))
+    print(f"[70b b32] spans per sequence {list(idx.n_spans[:4])}..., sampled heads {len(units) * G}, "
+          f"mask mismatches {bad}, heads skipped for ties {skipped}, worst end-to-end rel-L2 {worst:.3e}",
+          flush=True)
+    assert bad == 0
+    assert worst <= END_TO_END
+    idx.free()
