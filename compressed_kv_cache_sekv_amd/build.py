@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsekv.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["runtime.cpp", "attend.hip", "route.hip", "build.hip", "rsvd.hip"]
+SOURCES = ["runtime.cpp", "attend.hip", "route.hip", "build.hip", "rsvd.hip", "gather.hip"]
 ARCH = "gfx950"
 
 

@@ -163,6 +163,21 @@ struct CalibArgs {
   float frac;
 };
 
+// Pinned-tier gather (see gather.hip).
+struct GatherArgs {
+  const uint64_t* mask;      // [B][Lc][Hq][W]
+  const BMeta* meta;
+  const int32_t* span_len;
+  const int64_t* span_off;
+  const uint8_t* host_pool;  // device address of the mapped pinned factor pool
+  uint8_t* ring;             // HBM staging ring
+  int64_t* usize;            // [Lc][B][Hkv][2]: union spans, union blob bytes
+  const int64_t* ubase;      // [Lc][B][Hkv]: ring offset of each (l, b, g) region
+  int64_t* ring_off;         // [Lc][B][Hkv][max_spans]: ring offset of the k-th union blob
+  int64_t layer_bytes;
+  int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, R, D, max_spans, nsplit;
+};
+
 // ------------------------------------------------------------ launchers ---
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st);
@@ -218,5 +233,8 @@ hipError_t launch_pack_raw(const PackArgs& a, hipStream_t st);
 hipError_t launch_summaries(const PackArgs& a, hipStream_t st);
 hipError_t launch_rsvd(const PackArgs& a, hipStream_t st);
 hipError_t launch_rsvd_batched(const PackArgs& a, hipStream_t st);
+hipError_t launch_union_size(const GatherArgs& a, hipStream_t st);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+int gather_share();   // union spans per gather workgroup
 
 }  // namespace sekv

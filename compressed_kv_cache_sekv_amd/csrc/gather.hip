@@ -1,0 +1,177 @@
+// Pinned-host factor tier: gather the routed spans' factor blobs into the HBM
+// staging ring, gfx950.
+//
+// SeKV article (aitrends.kr/articles/75020), section 방법론 (Method): the span
+// factors live in CPU memory and, for the spans the router expands, U, Sigma
+// and V are transferred asynchronously to the GPU before reconstruction;
+// section 한계점 (Limitations): this CPU-GPU bandwidth is the method's stated
+// cost.
+//
+// The pinned pool is mapped into the device address space and read by the
+// kernel over PCIe.  Two passes per call:
+//   union_size_kernel  per (layer, b, KV head): number and bytes of the blobs
+//                      of the union over the G heads' masks (the host turns
+//                      these into ring offsets and checks the ring capacity);
+//   gather_kernel      per (layer, b, KV head, share): copies its share of
+//                      the union, in union order, to consecutive ring
+//                      addresses and records each blob's ring offset.
+#include "common.h"
+
+namespace sekv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint64_t valid_bits(int n_spans, int w) {
+  const int left = n_spans - 64 * w;
+  return left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
+}
+
+__global__ __launch_bounds__(256) void union_size_kernel(const GatherArgs a) {
+  __shared__ int64_t s_red[2][4];
+  const int bg = blockIdx.x, li = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const BMeta bm = a.meta[b];
+  const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + li) * a.Hq + (int64_t)g * a.G) * a.W;
+  int64_t cnt = 0, bytes = 0;
+  for (int w = threadIdx.x; w < a.W; w += 256) {
+    uint64_t u = 0;
+    for (int h = 0; h < a.G; ++h) u |= mrow[(int64_t)h * a.W + w];
+    u &= valid_bits(bm.n_spans, w);
+    cnt += __popcll(u);
+    for (; u; u &= u - 1) {
+      const int S = 64 * w + __builtin_ctzll(u);
+      bytes += Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    cnt += __shfl_xor(cnt, o);
+    bytes += __shfl_xor(bytes, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_red[0][wave] = cnt;
+    s_red[1][wave] = bytes;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t* o = a.usize + 2 * (((int64_t)li * a.B + b) * a.Hkv + g);
+    o[0] = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+    o[1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  }
+}
+
+constexpr int kShare = 128;   // union spans one gather workgroup copies
+
+__global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
+  __shared__ uint64_t s_uw[kMaxWords];
+  __shared__ int32_t s_pre[kMaxWords + 1];      // union spans before word w
+  __shared__ int64_t s_bpre[kMaxWords + 1];     // union bytes before word w
+  __shared__ int64_t s_src[kShare];
+  __shared__ int64_t s_dst[kShare];
+  __shared__ int32_t s_len[kShare];             // 16-byte chunks
+  const int li = blockIdx.y, l = a.layer_begin + li;
+  const int j = blockIdx.x % a.nsplit, bg = blockIdx.x / a.nsplit;
+  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+  const BMeta bm = a.meta[b];
+  const int64_t rid = ((int64_t)li * a.B + b) * a.Hkv + g;
+  const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + li) * a.Hq + (int64_t)g * a.G) * a.W;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int w = threadIdx.x; w < a.W; w += 256) {
+    uint64_t u = 0;
+    for (int h = 0; h < a.G; ++h) u |= mrow[(int64_t)h * a.W + w];
+    u &= valid_bits(bm.n_spans, w);
+    s_uw[w] = u;
+    int64_t by = 0;
+    for (uint64_t v = u; v; v &= v - 1)
+      by += Blob::bytes(a.R, a.D, a.span_len[bm.span_base + 64 * w + __builtin_ctzll(v)]);
+    s_bpre[w + 1] = by;
+    s_pre[w + 1] = __popcll(u);
+  }
+  __syncthreads();
+  if (wave == 0) {   // inclusive scans of the per-word counts and bytes
+    int carry = 0;
+    int64_t bcarry = 0;
+    for (int base = 0; base < a.W; base += 64) {
+      const int w = base + lane;
+      int v = (w < a.W) ? s_pre[w + 1] : 0;
+      int64_t by = (w < a.W) ? s_bpre[w + 1] : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(v, d);
+        const int64_t yb = __shfl_up(by, d);
+        if (lane >= d) {
+          v += y;
+          by += yb;
+        }
+      }
+      if (w < a.W) {
+        s_pre[w + 1] = carry + v;
+        s_bpre[w + 1] = bcarry + by;
+      }
+      carry += __shfl(v, 63);
+      bcarry += __shfl(by, 63);
+    }
+    if (lane == 0) {
+      s_pre[0] = 0;
+      s_bpre[0] = 0;
+    }
+  }
+  __syncthreads();
+  const int U = s_pre[a.W];
+  const int beg = (int)((int64_t)j * U / a.nsplit), end = (int)((int64_t)(j + 1) * U / a.nsplit);
+  const int cnt = min(end - beg, kShare);   // the host keeps shares <= kShare
+  const int64_t base = a.ubase[rid];
+  const int64_t region = (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
+  int64_t* roff = a.ring_off + rid * a.max_spans;
+  // this share's blobs: source in the pinned pool, ring destination
+  for (int w = threadIdx.x; w < a.W; w += 256) {
+    int k = s_pre[w];
+    if (k >= beg + cnt || s_pre[w + 1] <= beg) continue;
+    int64_t off = s_bpre[w];
+    for (uint64_t u = s_uw[w]; u && k < beg + cnt; u &= u - 1) {
+      const int S = 64 * w + __builtin_ctzll(u);
+      const int64_t by = Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]);
+      if (k >= beg) {
+        s_src[k - beg] = region + a.span_off[bm.span_base + S];
+        s_dst[k - beg] = base + off;
+        s_len[k - beg] = (int32_t)(by >> 4);
+        roff[k] = base + off;
+      }
+      off += by;
+      ++k;
+    }
+  }
+  __syncthreads();
+  // copy, 16 bytes per lane, four loads in flight per lane
+  for (int e = 0; e < cnt; ++e) {
+    const u32x4* src = (const u32x4*)(a.host_pool + s_src[e]);
+    u32x4* dst = (u32x4*)(a.ring + s_dst[e]);
+    const int nch = s_len[e];
+    for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
+      u32x4 v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = src[min(c0 + 256 * r, nch - 1)];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (c0 + 256 * r < nch) dst[c0 + 256 * r] = v[r];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_union_size(const GatherArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(union_size_kernel, dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(gather_kernel, dim3(a.B * a.Hkv * a.nsplit, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+int gather_share() { return kShare; }
+
+}  // namespace sekv

@@ -1,6 +1,8 @@
 // Host runtime of the SeKV C ABI (include/sekv.h): contexts, index build /
 // import / export, routing and decode orchestration, and the pinned-tier
-// gather into the HBM staging ring.
+// gather into the HBM staging ring (sizing on the device, placement and
+// capacity check on the host, the copy itself by a kernel reading the mapped
+// pinned pool).
 //
 // SeKV article (aitrends.kr/articles/75020): section 방법론 (Method) and its
 // Fig. 2 describe the two tiers (summaries and anchors on the GPU, truncated
@@ -156,14 +158,13 @@ struct sekv_index {
   DBuf d_meta, d_span_start, d_span_len, d_logn, d_span_off, d_raw_pos;
   DBuf d_kres, d_vres, d_s, d_W;
   DBuf d_pool;                 // HBM tier
-  uint8_t* h_pool = nullptr;   // pinned tier
-  DBuf d_ring, d_ring_off;
+  uint8_t* h_pool = nullptr;   // pinned tier (host address)
+  const uint8_t* d_host_pool = nullptr;   // the same pool's device address
+  DBuf d_ring, d_ring_off, d_usize, d_ubase;
   int64_t ring_bytes = 0;
-  std::vector<int64_t> h_ring_off;
-  int64_t* h_ring_off_pinned = nullptr;
-  size_t h_ring_off_cap = 0;
-  uint64_t* h_mask_pinned = nullptr;
-  size_t h_mask_cap = 0;
+  int64_t* h_usize = nullptr;  // pinned [Lc][B][Hkv][2]
+  int64_t* h_ubase = nullptr;  // pinned [Lc][B][Hkv]
+  size_t h_gather_cap = 0;     // (l, b, g) regions the two buffers hold
   // decode work
   std::vector<WorkItem> items;
   std::vector<int32_t> bg_first;
@@ -323,12 +324,15 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
     HIP_TRY(hipMemsetAsync(x->d_pool.p, 0, x->d_pool.n, st));
   } else {
     const size_t pb = (size_t)std::max<int64_t>(x->pool_bytes, 256);
-    hipError_t e = hipHostMalloc((void**)&x->h_pool, pb, hipHostMallocDefault);
+    hipError_t e = hipHostMalloc((void**)&x->h_pool, pb, hipHostMallocPortable | hipHostMallocMapped);
     if (e != hipSuccess) {
       x->h_pool = nullptr;
       return fail(SEKV_ENOMEM, "pinned host pool of %zu bytes: %s", pb, hipGetErrorString(e));
     }
     memset(x->h_pool, 0, pb);
+    void* dp = nullptr;
+    HIP_TRY(hipHostGetDevicePointer(&dp, x->h_pool, 0));
+    x->d_host_pool = (const uint8_t*)dp;
     x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : std::max<int64_t>(x->layer_bytes, 256);
     HIP_TRY(dalloc(x->d_ring, (size_t)x->ring_bytes));
   }
@@ -349,12 +353,12 @@ void free_index(sekv_index* x) {
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
-                  &x->d_ring, &x->d_ring_off, &x->d_items, &x->d_bg_first, &x->d_part,
-                  &x->d_alpha, &x->d_tau_inf};
+                  &x->d_ring, &x->d_ring_off, &x->d_usize, &x->d_ubase, &x->d_items, &x->d_bg_first,
+                  &x->d_part, &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
-  if (x->h_ring_off_pinned) (void)hipHostFree(x->h_ring_off_pinned);
-  if (x->h_mask_pinned) (void)hipHostFree(x->h_mask_pinned);
+  if (x->h_usize) (void)hipHostFree(x->h_usize);
+  if (x->h_ubase) (void)hipHostFree(x->h_ubase);
   if (x->ev0) (void)hipEventDestroy(x->ev0);
   if (x->ev1) (void)hipEventDestroy(x->ev1);
   x->magic = DEAD_MAGIC;
@@ -937,78 +941,62 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
 
 namespace {
 
-// Pinned tier: read the masks back, gather the union of every (b, l, g) into
-// the ring (coalescing spans that are adjacent in the pool), and publish the
-// ring offset of each union rank.
+// Pinned tier: size the union of every (l, b, g) on the device, read the
+// sizes back (one synchronisation), place the regions in the ring (capacity
+// check), then gather the blobs with one kernel that reads the mapped pinned
+// pool and records each union rank's ring offset.
 sekv_status gather(sekv_index* x, int lb, int lc, const uint64_t* mask, sekv_stats* stats) {
   hipStream_t st = x->ctx->stream;
-  const size_t nwords = (size_t)x->B * lc * x->Hq * x->Wd;
-  if (x->h_mask_cap < nwords) {
-    if (x->h_mask_pinned) (void)hipHostFree(x->h_mask_pinned);
-    x->h_mask_pinned = nullptr;
-    HIP_TRY(hipHostMalloc((void**)&x->h_mask_pinned, 8 * nwords, hipHostMallocDefault));
-    x->h_mask_cap = nwords;
+  const size_t nreg = (size_t)lc * x->B * x->Hkv;
+  if (x->h_gather_cap < nreg) {
+    if (x->h_usize) (void)hipHostFree(x->h_usize);
+    if (x->h_ubase) (void)hipHostFree(x->h_ubase);
+    x->h_usize = nullptr;
+    x->h_ubase = nullptr;
+    x->h_gather_cap = 0;
+    HIP_TRY(hipHostMalloc((void**)&x->h_usize, 16 * nreg, hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void**)&x->h_ubase, 8 * nreg, hipHostMallocDefault));
+    x->h_gather_cap = nreg;
   }
-  HIP_TRY(hipMemcpyAsync(x->h_mask_pinned, mask, 8 * nwords, hipMemcpyDeviceToHost, st));
+  HIP_TRY(dgrow(x->d_usize, 16 * nreg));
+  HIP_TRY(dgrow(x->d_ubase, 8 * nreg));
+  HIP_TRY(dgrow(x->d_ring_off, 8 * nreg * std::max(x->max_spans, 1)));
+  GatherArgs ga{};
+  ga.mask = mask;
+  ga.meta = (const BMeta*)x->d_meta.p;
+  ga.span_len = (const int32_t*)x->d_span_len.p;
+  ga.span_off = (const int64_t*)x->d_span_off.p;
+  ga.host_pool = x->d_host_pool;
+  ga.ring = (uint8_t*)x->d_ring.p;
+  ga.usize = (int64_t*)x->d_usize.p;
+  ga.ubase = (const int64_t*)x->d_ubase.p;
+  ga.ring_off = (int64_t*)x->d_ring_off.p;
+  ga.layer_bytes = x->layer_bytes;
+  ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
+  ga.W = x->Wd; ga.G = x->G; ga.R = x->R; ga.D = x->D;
+  ga.max_spans = std::max(x->max_spans, 1);
+  ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
+  HIP_TRY(launch_union_size(ga, st));
+  HIP_TRY(hipMemcpyAsync(x->h_usize, x->d_usize.p, 16 * nreg, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
-  const size_t noff = (size_t)lc * x->B * x->Hkv * std::max(x->max_spans, 1);
-  if (x->h_ring_off_cap < noff) {
-    if (x->h_ring_off_pinned) (void)hipHostFree(x->h_ring_off_pinned);
-    x->h_ring_off_pinned = nullptr;
-    HIP_TRY(hipHostMalloc((void**)&x->h_ring_off_pinned, 8 * noff, hipHostMallocDefault));
-    x->h_ring_off_cap = noff;
-  }
-  HIP_TRY(dgrow(x->d_ring_off, 8 * noff));
-  // plan
-  struct Copy { int64_t src, dst, bytes; };
-  std::vector<Copy> copies;
-  int64_t ring_used = 0;
+  int64_t used = 0;
   uint64_t unions = 0;
-  const int G = x->G, Wd = x->Wd;
-  for (int li = 0; li < lc; ++li) {
-    const int l = lb + li;
-    for (int b = 0; b < x->B; ++b) {
-      const BMeta& m = x->meta[b];
-      for (int g = 0; g < x->Hkv; ++g) {
-        int64_t* roff = x->h_ring_off_pinned + (((size_t)li * x->B + b) * x->Hkv + g) * std::max(x->max_spans, 1);
-        const uint64_t* mr = x->h_mask_pinned + (((size_t)b * lc + li) * x->Hq + (size_t)g * G) * Wd;
-        const int64_t region = (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg;
-        int k = 0;
-        for (int w = 0; w < Wd; ++w) {
-          uint64_t u = 0;
-          for (int h = 0; h < G; ++h) u |= mr[(size_t)h * Wd + w];
-          while (u) {
-            const int S = 64 * w + __builtin_ctzll(u);
-            u &= u - 1;
-            if (S >= m.n_spans) continue;
-            const int64_t src = region + x->h_span_off[m.span_base + S];
-            const int64_t bytes = Blob::bytes(x->R, x->D, x->h_span_len[m.span_base + S]);
-            if (ring_used + bytes > x->ring_bytes)
-              return fail(SEKV_ECAPACITY, "staging ring of %lld bytes too small for the routed union",
-                          (long long)x->ring_bytes);
-            if (!copies.empty() && copies.back().src + copies.back().bytes == src &&
-                copies.back().dst + copies.back().bytes == ring_used)
-              copies.back().bytes += bytes;
-            else
-              copies.push_back(Copy{src, ring_used, bytes});
-            roff[k++] = ring_used;
-            ring_used += bytes;
-            ++unions;
-          }
-        }
-      }
-    }
+  for (size_t r = 0; r < nreg; ++r) {
+    x->h_ubase[r] = used;
+    unions += (uint64_t)x->h_usize[2 * r];
+    used += x->h_usize[2 * r + 1];
   }
-  HIP_TRY(hipMemcpyAsync(x->d_ring_off.p, x->h_ring_off_pinned, 8 * noff, hipMemcpyHostToDevice, st));
+  if (used > x->ring_bytes)
+    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes too small for the routed union (%lld bytes)",
+                (long long)x->ring_bytes, (long long)used);
+  HIP_TRY(hipMemcpyAsync(x->d_ubase.p, x->h_ubase, 8 * nreg, hipMemcpyHostToDevice, st));
   HIP_TRY(hipEventRecord(x->ev0, st));
-  for (const Copy& cp : copies)
-    HIP_TRY(hipMemcpyAsync((uint8_t*)x->d_ring.p + cp.dst, x->h_pool + cp.src, (size_t)cp.bytes,
-                           hipMemcpyHostToDevice, st));
+  HIP_TRY(launch_gather(ga, st));
   HIP_TRY(hipEventRecord(x->ev1, st));
   if (stats) {
     stats->union_spans = unions;
-    stats->pcie_bytes = (uint64_t)ring_used;
-    stats->pcie_copies = copies.size();
+    stats->pcie_bytes = (uint64_t)used;
+    stats->pcie_copies = 1;
     HIP_TRY(hipEventSynchronize(x->ev1));
     float ms = 0.f;
     HIP_TRY(hipEventElapsedTime(&ms, x->ev0, x->ev1));

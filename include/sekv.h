@@ -141,9 +141,9 @@ typedef struct {
  * tier only (zero for the HBM tier). */
 typedef struct {
   uint64_t union_spans;    /* sum over (b, l, g) of |union of the G heads' z|   */
-  uint64_t pcie_bytes;     /* bytes copied host -> HBM ring                      */
-  uint64_t pcie_copies;    /* hipMemcpyAsync calls issued                        */
-  double pcie_ms;          /* stream time of the gather copies (HIP events)      */
+  uint64_t pcie_bytes;     /* bytes moved host -> HBM ring (padded blobs)        */
+  uint64_t pcie_copies;    /* gather kernel launches                             */
+  double pcie_ms;          /* stream time of the gather kernel (HIP events)      */
 } sekv_stats;
 
 /* ---------------------------------------------------------------- lifecycle */
@@ -265,9 +265,11 @@ sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
  *          the caller)
  *   out    device fp32 [B][layer_count][Hq][d]
  *   stats  host, or NULL
- * Pinned tier: reads the mask back, synchronising the stream, and gathers the
- * union of the routed spans into the HBM ring with hipMemcpyAsync before the
- * kernels (SEKV_ECAPACITY if it does not fit). */
+ * Pinned tier: sizes the union of the routed spans of every (b, l, KV head)
+ * on the device, reads those sizes back (synchronising the stream once),
+ * places the unions in the HBM ring (SEKV_ECAPACITY if they do not fit) and
+ * gathers the factor blobs with a kernel that reads the mapped pinned pool
+ * over PCIe, before the attention kernels. */
 sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                                int32_t layer_count, const void* q, const uint64_t* mask,
                                float* out, sekv_stats* stats);
