@@ -107,24 +107,38 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
 #pragma unroll
     for (int j = 0; j < kMaxDp; ++j) v[j] = (live && j < dp) ? v[j] : 0.f;
   }
-  // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims
+  // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims;
+  // the thread's W row slice and q slice are loaded with 16-byte loads, all
+  // issued together (with the key loads still in flight)
   {
     const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
     const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
     const int qd = D >> 2, part = threadIdx.x & 3;
-    for (int j0 = 0; j0 < dp; j0 += 64) {
-      const int j = j0 + (threadIdx.x >> 2);
-      float acc = 0.f;
-      if (j < dp) {
-        const float* wr = Wl + (int64_t)j * D + part * qd;
-        const bf16_t* qq = qp + part * qd;
-#pragma unroll 8
-        for (int d = 0; d < qd; ++d) acc += wr[d] * bf16_to_f32(qq[d]);
+    const int j = threadIdx.x >> 2;   // dp <= kMaxDp = 64 outputs
+    float acc = 0.f;
+    if (D == 128) {
+      float4 wv[8];
+      uint4 qv[4];
+      const float* wr = Wl + (int64_t)min(j, dp - 1) * D + part * 32;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wv[k] = *(const float4*)(wr + 4 * k);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qv[k] = *(const uint4*)(qp + part * 32 + 8 * k);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t q0 = (k & 1) ? qv[k >> 1].z : qv[k >> 1].x;
+        const uint32_t q1 = (k & 1) ? qv[k >> 1].w : qv[k >> 1].y;
+        acc += wv[k].x * __uint_as_float(q0 << 16) + wv[k].y * __uint_as_float(q0 & 0xffff0000u) +
+               wv[k].z * __uint_as_float(q1 << 16) + wv[k].w * __uint_as_float(q1 & 0xffff0000u);
       }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (part == 0 && j < dp) s_u[j] = acc;
+    } else {
+      const float* wr = Wl + (int64_t)min(j, dp - 1) * D + part * qd;
+      const bf16_t* qq = qp + part * qd;
+      for (int d = 0; d < qd; ++d) acc += wr[d] * bf16_to_f32(qq[d]);
     }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (part == 0 && j < dp) s_u[j] = acc;
   }
   __syncthreads();
   if (wi >= a.Wd) return;
