@@ -118,6 +118,77 @@ def cpu_baseline(w, H, K, V, W, gates, tau, cap, q_steps, budget_s=12.0):
                        f"{per_unit * 1e3:.1f} ms per unit, scaled by {units} units per step")}
 
 
+def prefill(args) -> int:
+    """Prefill leg: index build of the 128K single-layer workload, then the
+    randomized SVD (sekv_rsvd_batched) of every span's K and V of that layer,
+    timed with HIP events on the library's stream.  GEMM work per matrix
+    (n x d, sketch width l = min(R + p, n, d)): A Omega, q power steps of two
+    products each, and the final projection, 2 n d l flops apiece."""
+    import torch
+    from compressed_kv_cache_sekv_amd import synth
+    from compressed_kv_cache_sekv_amd import lib as sl
+    w = synth.WORKLOADS["prefill_8b_128k"]
+    dev = "cuda"
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    H, K, V = synth.kv_cache(w, device=dev)
+    W = torch.stack([synth.routing_w(w, l, dev) for l in range(w.L)])
+    ctx = sl.Context(0, stream=stream)
+    reps = 3
+    build_ms = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        idx = ctx.build_index(sl.build_params(w), K, V, H, W, None)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            build_ms.append(e0.elapsed_time(e1))
+        start, length, _ = idx.spans()
+        idx.free()
+    # every span's K and V rows of the layer, for each KV head, as one batch
+    st = torch.from_numpy(start.astype(np.int64)).to(dev)
+    ln = torch.from_numpy(length.astype(np.int64)).to(dev)
+    tok = torch.repeat_interleave(st, ln) + (torch.arange(int(ln.sum()), device=dev)
+                                             - torch.repeat_interleave(torch.cumsum(ln, 0) - ln, ln))
+    mats = [X[0, 0, g].index_select(0, tok) for g in range(w.Hkv) for X in (K, V)]
+    A = torch.cat(mats).contiguous()
+    nspan = len(length)
+    rows = torch.from_numpy(np.tile(length.astype(np.int32), 2 * w.Hkv)).to(dev)
+    row_off = (torch.cumsum(rows.long(), 0) - rows.long()) * w.d
+    cnt, mr = int(rows.numel()), int(length.max())
+    U = torch.empty(cnt, mr, w.R, device=dev)
+    S = torch.empty(cnt, w.R, device=dev)
+    Vt = torch.empty(cnt, w.R, w.d, device=dev)
+    rsvd_ms = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ctx.rsvd_batched(A, row_off, rows, mr, w.d, w.R, w.oversample, w.power_iters, w.seed, U, S, Vt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            rsvd_ms.append(e0.elapsed_time(e1))
+    n = np.tile(length.astype(np.int64), 2 * w.Hkv)
+    lw = np.minimum(np.minimum(w.R + w.oversample, n), w.d)
+    flops = float(np.sum(2 * n * w.d * lw * (2 + 2 * w.power_iters)))
+    t = float(np.median(rsvd_ms))
+    tflops = flops / (t * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "prefill: randomized SVD of every span K/V of one 128K layer (R=32, oversampling 8, "
+                  "2 power iterations)",
+        "value": round(t, 3), "unit": "ms", "higher_is_better": False, "dtype": "bf16 MFMA / fp32, fp64",
+        "data": "synthetic", "matrices": cnt, "spans": nspan,
+        "build_index_ms": round(float(np.median(build_ms)), 3),
+        "gemm_gflop": round(flops / 1e9, 2),
+        "mfma": {"achieved": round(tflops, 3), "peak": 2500.0, "unit": "TFLOP/s",
+                 "frac": round(tflops / 2500.0, 5)},
+        "config": {"workload": w.name, "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "R": w.R}}),
+        flush=True)
+    ctx.close()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +198,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pinned", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time a HIP graph replay of the step instead of eager launches")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the prefill side instead: the index build of one 128K layer (R = 32) and the "
+                         "randomized SVD of all its span matrices alone; prints one JSON line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 4 plain device copies of MIB MiB each (a known-size kernel that scales "
                          "rocprofv3's FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -150,6 +224,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 4}), flush=True)
         return 0
+    if args.prefill:
+        return prefill(args)
     w = synth.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)
