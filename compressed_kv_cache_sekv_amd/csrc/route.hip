@@ -165,137 +165,244 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   if (arow) arow[S] = alpha;
 }
 
-// Budget cap, one workgroup per (b, lc, h), after route_kernel: when more than
+// Budget cap, one workgroup per (b, h, lc), after route_kernel: when more than
 // cap spans are expanded keep the cap largest alpha, ties to the lower span
-// index.  Expanded spans are collected into LDS with the key (alpha bits,
-// complemented span index), whose order is alpha descending then index
-// ascending and whose values are distinct; an 8-pass radix select in LDS
-// finds the cap-th largest key and every key at or above it is kept.
-// Candidate sets above kCapList fall back to a 4-pass radix select on alpha
-// over global memory.
+// index.  Each candidate is keyed (alpha bits, complemented span index): the
+// key order is alpha descending then index ascending, and keys are distinct,
+// so the kept set is exactly the keys at or above the cap-th largest key K*.
+//  * Collect: thread t takes spans 32t .. 32t+31 (half a mask word and eight
+//    16-byte alpha loads, all issued together); a block scan of the per-thread
+//    counts places the candidates in LDS in span order.
+//  * Select: one histogram of the alpha bits over the candidates' own range
+//    (1024 bins by a shift of (bits - min); alpha >= 0, so the bits order like
+//    the values and the binning is monotone) finds the bin holding K* and how
+//    many of its keys are kept; only that bin's keys are then ranked against
+//    each other.  A boundary bin of more than kCapRank keys (alpha saturated
+//    at one value) falls back to an 8-pass radix select of the composite keys.
+//  * Candidate sets above kCapList fall back to a 4-pass radix select on alpha
+//    over global memory.
 constexpr int kCapList = 2048;
+constexpr int kCapBins = 1024;
+constexpr int kCapRank = 256;
+
+// block_scan256 that also returns the block total.
+__device__ int block_scan256_total(int v, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += s_tmp[w];
+  total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  __syncthreads();
+  return v + add;
+}
+
+__device__ __forceinline__ float f4_at(const float4& v, int c) {
+  return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
+}
+
+// K* by an 8-pass radix select over the nc composite keys in s_cand (8 bits a
+// pass, histograms in LDS).  Returns a threshold T with exactly k keys >= T:
+// K* itself, or K*'s leading bytes when the bin of K* is kept whole.
+__device__ uint64_t radix_select_keys(const uint64_t* s_cand, int nc, int k, uint32_t* s_hist,
+                                      int* s_sel) {
+  uint64_t prefix = 0, pmask = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    s_hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < nc; i0 += 256) {
+      // lanes with equal digits are counted with 8 ballots and only the
+      // lowest such lane updates the bin (keys share their top bytes, so
+      // per-lane atomics would all hit one bin)
+      const int i = i0 + threadIdx.x;
+      const uint64_t key = (i < nc) ? s_cand[i] : 0ull;
+      const bool on = (i < nc) && (key & pmask) == prefix;
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+      uint64_t peers = __ballot(on);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const uint64_t bal = __ballot((digit >> bit) & 1u);
+        peers &= ((digit >> bit) & 1u) ? bal : ~bal;
+      }
+      if (on && (peers & ((1ull << lane) - 1)) == 0) atomicAdd(&s_hist[digit], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane owns bins 255-4*lane .. 252-4*lane (descending); inclusive scan
+      int c[4], tot = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = (int)s_hist[255 - 4 * lane - e];
+        tot += c[e];
+      }
+      int inc = tot;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+      }
+      const int exc = inc - tot;
+      if (exc < k && k <= inc) {   // exactly one lane holds the k-th key
+        int cum = exc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (cum + c[e] >= k) {
+            s_sel[0] = 255 - 4 * lane - e;
+            s_sel[1] = k - cum;
+            s_sel[2] = (k - cum == c[e]);   // every key of the bin is kept
+            break;
+          }
+          cum += c[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_sel[0] << shift;
+    pmask |= 255ull << shift;
+    k = s_sel[1];
+    const bool whole_bin = s_sel[2] != 0;
+    __syncthreads();
+    // the cap-th largest key is the smallest of its bin and the whole bin
+    // is kept: every key >= prefix (lower bytes zero) is exactly the top cap
+    if (whole_bin) break;
+  }
+  return prefix;
+}
 
 __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
-  __shared__ uint32_t s_hist[256];
+  __shared__ uint64_t s_cand[kCapList];
+  __shared__ uint32_t s_hist[kCapBins];
+  __shared__ unsigned long long s_new[kMaxWords];
+  __shared__ uint64_t s_bnd[kCapRank];
+  __shared__ uint64_t s_kstar;
+  __shared__ uint32_t s_rng[8];
   __shared__ int s_tmp[8];
   __shared__ int s_sel[3];
-  __shared__ int s_nc;
-  __shared__ uint64_t s_cand[kCapList];
-  __shared__ unsigned long long s_new[1024];
+  __shared__ int s_nb;
   const int b = blockIdx.x, h = blockIdx.y, lc = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const BMeta bm = a.meta[b];
   const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
   uint64_t* mrow = a.mask + row * a.Wd;
   const float* arow = a.alpha + row * (int64_t)a.Wd * 64;
-  if (threadIdx.x == 0) s_nc = 0;
-  for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = 0ull;
-  __syncthreads();
-  for (int S0 = threadIdx.x; S0 < bm.n_spans; S0 += 256 * 16) {
-    // 16 spans per thread per round trip: all loads issued before any use
-    uint64_t wv[16];
-    float av[16];
+  for (int w = tid; w < a.Wd; w += 256) s_new[w] = 0ull;
+  if (tid == 0) s_nb = 0;
+  // collect (mask bits at or past N_S are 0, so their alpha is never used)
+  const int nh = 2 * a.Wd;
+  int nc = 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int base = 0; base < nh; base += 256) {
+    const int t = min(base + tid, nh - 1);
+    const uint64_t word = mrow[t >> 1];
+    const float4* ap = (const float4*)(arow + 32 * (int64_t)t);
+    float4 av[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {   // branch-free: clamped in-range loads
-      const int S = min(S0 + 256 * k, bm.n_spans - 1);
-      wv[k] = mrow[S >> 6];
-      av[k] = arow[S];
-    }
+    for (int k = 0; k < 8; ++k) av[k] = ap[k];
+    const uint32_t bits = (base + tid < nh) ? (uint32_t)(word >> (32 * (t & 1))) : 0u;
+    const int c = __popc(bits);
+    int total;
+    const int incl = block_scan256_total(c, s_tmp, total);
+    int pos = nc + incl - c;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int S = S0 + 256 * k;
-      const bool on = S < bm.n_spans && ((wv[k] >> (S & 63)) & 1ull);
-      // one LDS atomic per wave: reserve the wave's slots, then place by rank
-      const uint64_t bal = __ballot(on);
-      const int lane = threadIdx.x & 63;
-      int basepos = 0;
-      if (lane == 0 && bal) basepos = atomicAdd(&s_nc, (int)__popcll(bal));
-      basepos = __shfl(basepos, 0);
-      if (on) {
-        const int pos = basepos + (int)__popcll(bal & ((1ull << lane) - 1));
-        if (pos < kCapList)
-          s_cand[pos] = ((uint64_t)__float_as_uint(av[k]) << 32) | (uint64_t)(~(uint32_t)S);
+    for (int j = 0; j < 32; ++j) {
+      if ((bits >> j) & 1u) {
+        const uint32_t ab = __float_as_uint(f4_at(av[j >> 2], j & 3));
+        if (pos < kCapList) s_cand[pos] = ((uint64_t)ab << 32) | (uint64_t)(~(uint32_t)(32 * t + j));
+        ++pos;
+        lo = min(lo, ab);
+        hi = max(hi, ab);
       }
     }
+    nc += total;
   }
-  __syncthreads();
-  const int nc = s_nc;
   if (nc <= a.cap) return;
   if (nc <= kCapList) {
-    // the cap-th largest composite key K* by an 8-pass radix select (8 bits a
-    // pass, histograms in LDS); keys are distinct, so exactly cap keys are >= K*
-    uint64_t prefix = 0, pmask = 0;
-    int k = a.cap;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      s_hist[threadIdx.x] = 0;
-      __syncthreads();
-      for (int i0 = 0; i0 < nc; i0 += 256) {
-        // lanes with equal digits are counted with 8 ballots and only the
-        // lowest such lane updates the bin (keys share their top bytes, so
-        // per-lane atomics would all hit one bin)
-        const int i = i0 + threadIdx.x;
-        const uint64_t key = (i < nc) ? s_cand[i] : 0ull;
-        const bool on = (i < nc) && (key & pmask) == prefix;
-        const uint32_t digit = (uint32_t)(key >> shift) & 255u;
-        uint64_t peers = __ballot(on);
+    // range of the candidates' alpha bits
 #pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-          const uint64_t bal = __ballot((digit >> bit) & 1u);
-          peers &= ((digit >> bit) & 1u) ? bal : ~bal;
-        }
-        if (on && (peers & ((1ull << lane) - 1)) == 0)
-          atomicAdd(&s_hist[digit], (uint32_t)__popcll(peers));
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane owns bins 255-4*lane .. 252-4*lane (descending); inclusive scan
-        int c[4], tot = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c[e] = (int)s_hist[255 - 4 * lane - e];
-          tot += c[e];
-        }
-        int inc = tot;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(inc, d);
-          if (lane >= d) inc += y;
-        }
-        const int exc = inc - tot;
-        if (exc < k && k <= inc) {   // exactly one lane holds the k-th key
-          int cum = exc;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (cum + c[e] >= k) {
-              s_sel[0] = 255 - 4 * lane - e;
-              s_sel[1] = k - cum;
-              s_sel[2] = (k - cum == c[e]);   // every key of the bin is kept
-              break;
-            }
-            cum += c[e];
-          }
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)s_sel[0] << shift;
-      pmask |= 255ull << shift;
-      k = s_sel[1];
-      const bool whole_bin = s_sel[2] != 0;
-      __syncthreads();
-      // the cap-th largest key is the smallest of its bin and the whole bin
-      // is kept: every key >= prefix (lower bytes zero) is exactly the top cap
-      if (whole_bin) break;
+    for (int d = 32; d >= 1; d >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, d));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, d));
     }
-    for (int i = threadIdx.x; i < nc; i += 256) {
+    if (lane == 0) {
+      s_rng[wave] = lo;
+      s_rng[4 + wave] = hi;
+    }
+    for (int i = tid; i < kCapBins; i += 256) s_hist[i] = 0;
+    __syncthreads();
+    lo = min(min(s_rng[0], s_rng[1]), min(s_rng[2], s_rng[3]));
+    hi = max(max(s_rng[4], s_rng[5]), max(s_rng[6], s_rng[7]));
+    const uint32_t range = hi - lo;
+    const int sh = max(0, 22 - (int)__clz((int)range));   // (range >> sh) < kCapBins
+    auto bin_of = [&](uint64_t key) -> uint32_t { return ((uint32_t)(key >> 32) - lo) >> sh; };
+    for (int i = tid; i < nc; i += 256) atomicAdd(&s_hist[bin_of(s_cand[i])], 1u);
+    __syncthreads();
+    // descending scan: thread t owns bins kCapBins-1-4t .. kCapBins-4-4t
+    int cnt[4], tot = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cnt[e] = (int)s_hist[kCapBins - 1 - 4 * tid - e];
+      tot += cnt[e];
+    }
+    int total;
+    const int inc = block_scan256_total(tot, s_tmp, total);
+    const int exc = inc - tot;
+    if (exc < a.cap && a.cap <= inc) {   // exactly one thread holds K*
+      int cum = exc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (cum + cnt[e] >= a.cap) {
+          s_sel[0] = kCapBins - 1 - 4 * tid - e;
+          s_sel[1] = a.cap - cum;   // keys of that bin to keep
+          s_sel[2] = cnt[e];
+          break;
+        }
+        cum += cnt[e];
+      }
+    }
+    __syncthreads();
+    const uint32_t bstar = (uint32_t)s_sel[0];
+    const int r = s_sel[1], m = s_sel[2];
+    // keep: bin > bstar, or bin == bstar and key >= kth (kth = 0: whole bin)
+    uint64_t kth = 0;
+    bool by_bin = true;
+    if (r < m) {
+      if (m <= kCapRank) {
+        for (int i = tid; i < nc; i += 256) {
+          const uint64_t key = s_cand[i];
+          if (bin_of(key) == bstar) s_bnd[atomicAdd(&s_nb, 1)] = key;
+        }
+        __syncthreads();
+        if (tid < m) {
+          const uint64_t e = s_bnd[tid];
+          int rank = 0;
+          for (int j = 0; j < m; ++j) rank += s_bnd[j] > e;
+          if (rank == r - 1) s_kstar = e;
+        }
+        __syncthreads();
+        kth = s_kstar;
+      } else {
+        kth = radix_select_keys(s_cand, nc, a.cap, s_hist, s_sel);
+        by_bin = false;
+      }
+    }
+    for (int i = tid; i < nc; i += 256) {
       const uint64_t key = s_cand[i];
-      if (key >= prefix) {
+      const uint32_t bk = bin_of(key);
+      const bool keep = by_bin ? (bk > bstar || (bk == bstar && key >= kth)) : key >= kth;
+      if (keep) {
         const int S = (int)(~(uint32_t)(key & 0xffffffffull));
         atomicOr(&s_new[S >> 6], 1ull << (S & 63));
       }
     }
     __syncthreads();
-    for (int w = threadIdx.x; w < a.Wd; w += 256) mrow[w] = s_new[w];
+    for (int w = tid; w < a.Wd; w += 256) mrow[w] = s_new[w];
     return;
   }
   // large candidate sets: radix select on alpha, ties by span index
@@ -308,11 +415,11 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   };
   const uint32_t vstar = radix_select(bm.n_spans, k, cand, s_hist, s_sel);
   // k = number of spans with alpha == vstar to keep, lowest span index first
-  for (int w = threadIdx.x; w < a.Wd; w += 256) s_new[w] = mrow[w];
+  for (int w = tid; w < a.Wd; w += 256) s_new[w] = mrow[w];
   __syncthreads();
   int carry = 0;
   for (int base = 0; base < a.Wd; base += 256) {
-    const int ww = base + threadIdx.x;
+    const int ww = base + tid;
     int tw = 0;
     uint64_t zz = 0;
     if (ww < a.Wd) {
@@ -320,7 +427,8 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       for (uint64_t bits = zz; bits; bits &= bits - 1)
         tw += (__float_as_uint(arow[64 * ww + __builtin_ctzll(bits)]) == vstar);
     }
-    const int incl = block_scan256(tw, s_tmp);
+    int total;
+    const int incl = block_scan256_total(tw, s_tmp, total);
     int rank = carry + incl - tw;
     if (ww < a.Wd) {
       uint64_t keep = 0;
@@ -335,10 +443,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       }
       mrow[ww] = keep;
     }
-    if (threadIdx.x == 255) s_sel[0] = incl;
-    __syncthreads();
-    carry += s_sel[0];
-    __syncthreads();
+    carry += total;
   }
 }
 

@@ -875,6 +875,7 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !tau || !mask) return fail(SEKV_EINVAL, "null q, tau or mask");
   if (cap < 0) return fail(SEKV_EINVAL, "cap < 0");
+  if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
   if ((st = ensure_route_scratch(x, lc))) return st;
   RouteArgs ra{};

@@ -239,8 +239,9 @@ void sekv_index_free(sekv_index* idx);
  *   tau    device fp32 [layer_count][Hq]  (+-inf allowed)
  *   mask   device uint64 [B][layer_count][Hq][mask_words]; bit j of word w is
  *          z of span 64w + j; bits at or past N_S(b) are 0
- *   alpha  device fp32 [B][layer_count][Hq][mask_words * 64] or NULL; entries
- *          at or past N_S(b) are unspecified */
+ *   alpha  device fp32 [B][layer_count][Hq][mask_words * 64], 16-byte
+ *          aligned (SEKV_EINVAL otherwise), or NULL; entries at or past N_S(b)
+ *          are unspecified */
 sekv_status sekv_route(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                        int32_t layer_count, const void* q, const float* tau,
                        int32_t cap, uint64_t* mask, float* alpha);

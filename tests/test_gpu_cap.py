@@ -1,0 +1,135 @@
+"""Budget-cap selection paths of the routing kernels, on one 8B-shaped layer at
+131072 tokens (N_S = 2628 spans) whose index the library builds on the GPU.
+
+The cap rule (SeKV article, section 기술 상세 (Technical details): spans taken
+in descending alpha until the budget holds; ties here to the lower span index)
+is checked as a property of one routing call's own outputs: with the pre-cap
+mask z and the fp32 alpha of the same call, the capped mask must be exactly
+the cap largest (alpha, then lower span index) members of z, and z must be
+exactly [alpha > tau].  Both sides take the decision on the same fp32 alpha.
+Parity of the cap against the fp64 oracle is in test_gpu_parity and
+test_gpu_fullsize; this file makes every selection path of the kernel run:
+  bin     one histogram over the candidates' alpha range (boundary bin kept
+          whole, or its keys ranked against each other)
+  radix   a boundary bin of more than 256 keys (alpha saturated at 1.0f)
+  global  more than 2048 candidates
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_kv_cache_sekv_amd import synth
+from tests import sekv_cases as SC
+
+pytestmark = pytest.mark.gpu
+
+CAP_LIST, CAP_BINS, CAP_RANK = 2048, 1024, 256
+
+
+@pytest.fixture(scope="module")
+def setup():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from compressed_kv_cache_sekv_amd import lib as sl
+    ctx = sl.Context(0)
+    w = synth.WORKLOADS["llama8b_l32_128k"].scaled(L=1, tier="hbm")
+    print("[cap paths] building the 128K layer index on the GPU", flush=True)
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, 0, "cuda")])
+    idx = ctx.build_index(sl.build_params(w), K, V, H, W, None)
+    del H, K, V
+    yield w, idx
+    torch.cuda.synchronize()
+    idx.free()
+    ctx.close()
+
+
+def _route(idx, w, q, tau, cap):
+    Wd = idx.mask_words
+    mask = torch.zeros(w.B, 1, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    alpha = torch.zeros(w.B, 1, w.Hq, Wd * 64, dtype=torch.float32, device="cuda")
+    idx.route(0, 1, q, torch.as_tensor(tau, dtype=torch.float32).reshape(1, w.Hq).cuda(), cap, mask, alpha)
+    torch.cuda.synchronize()
+    return mask.cpu().numpy().view(np.uint64), alpha.cpu().numpy()
+
+
+def _path(a, z, cap):
+    """Which selection the kernel takes for this head (for coverage only)."""
+    nc = int(z.sum())
+    if nc <= cap:
+        return "none"
+    if nc > CAP_LIST:
+        return "global"
+    bits = a[z].view(np.uint32).astype(np.int64)
+    lo, hi = int(bits.min()), int(bits.max())
+    sh = max(0, (hi - lo).bit_length() - 10)
+    cnt = np.bincount((bits - lo) >> sh, minlength=CAP_BINS)[::-1]
+    cum = np.cumsum(cnt)
+    i = int(np.searchsorted(cum, cap))
+    m, r = int(cnt[i]), cap - (int(cum[i - 1]) if i else 0)
+    if r == m:
+        return "bin-whole"
+    return "bin-rank" if m <= CAP_RANK else "radix"
+
+
+def _expected(a, z, cap):
+    idx = np.nonzero(z)[0]
+    if len(idx) <= cap:
+        return z.copy()
+    order = np.lexsort((idx, -a[idx].astype(np.float64)))   # alpha desc, then index asc
+    keep = np.zeros_like(z)
+    keep[idx[order[:cap]]] = True
+    return keep
+
+
+def _tau_kth(a, k):
+    s = np.sort(a)[::-1]
+    return float(np.float32(0.5 * (float(s[k - 1]) + float(s[k]))))
+
+
+def _check(idx, w, q, tau, cap, paths, label):
+    n = int(idx.n_spans[0])
+    pre, a0 = _route(idx, w, q, tau, 0)
+    got, a1 = _route(idx, w, q, tau, cap)
+    assert np.array_equal(a0[0, 0, :, :n], a1[0, 0, :, :n])
+    for h in range(w.Hq):
+        a = a0[0, 0, h, :n]
+        z = SC.unpack_mask(pre[0, 0, h], n)
+        assert np.array_equal(z, a > np.float32(tau[h])), (label, h)
+        zc = SC.unpack_mask(got[0, 0, h], n)
+        exp = _expected(a, z, cap)
+        assert np.array_equal(zc, exp), (label, h, int(z.sum()), int(zc.sum()), int((zc != exp).sum()))
+        p = _path(a, z, cap)
+        paths[p] = paths.get(p, 0) + 1
+    print(f"[cap paths] {label}: cap {cap}, paths so far {paths}", flush=True)
+
+
+def test_cap_selection_paths(setup):
+    w, idx = setup
+    n = int(idx.n_spans[0])
+    cap = int(np.floor(w.cap_frac * n))
+    assert n > CAP_LIST
+    q = synth.query(w, 0, "cuda")
+    paths = {}
+    # alpha of every span at the plain query
+    _, a_all = _route(idx, w, q, np.full(w.Hq, -np.inf), 0)
+    a_all = a_all[0, 0, :, :n]
+    # bin: about 20% routed, twice the cap
+    tau = np.array([_tau_kth(a_all[h], int(0.2 * n)) for h in range(w.Hq)])
+    _check(idx, w, q, tau, cap, paths, "20% routed")
+    # global: everything routed
+    _check(idx, w, q, np.full(w.Hq, -np.inf), cap, paths, "all routed")
+    # radix: scale q by 2^k (exact in bf16 and in u = W q) until a few hundred
+    # spans per head saturate at alpha = 1.0f, then route about 1800 spans
+    x = np.log(a_all.astype(np.float64)) - np.log1p(-a_all.astype(np.float64))
+    best = min(range(0, 16), key=lambda k: abs(np.median((x * 2.0 ** k > 17.5).sum(axis=1)) - 600))
+    qs = q * (2.0 ** best)
+    _, a_sc = _route(idx, w, qs, np.full(w.Hq, -np.inf), 0)
+    a_sc = a_sc[0, 0, :, :n]
+    sat = (a_sc == 1.0).sum(axis=1)
+    print(f"[cap paths] q scaled by 2^{best}: saturated spans per head median {int(np.median(sat))}, "
+          f"min {int(sat.min())}, max {int(sat.max())}", flush=True)
+    tau = np.array([_tau_kth(a_sc[h], 1800) if sat[h] < 1800 else 0.5 for h in range(w.Hq)])
+    _check(idx, w, qs, tau, cap, paths, "saturated")
+    assert paths.get("global", 0) >= 1
+    assert paths.get("bin-whole", 0) + paths.get("bin-rank", 0) >= 1
+    assert paths.get("radix", 0) >= 1
