@@ -5,10 +5,13 @@
 // factors and merged into the attention output; section 기술 상세 (Technical
 // details) gives the reconstruction Khat_S = sum_i m_i sigma_i u_i v_i^T.
 //
-// One workgroup (4 waves) per work item.  Items of kind 0 stream 64-row tiles
-// of resident rows (raw tokens, then one pseudo row per span); items of kind 1
-// take an equal share of the union over the G query heads of a KV head's
-// routed spans.  Per span the reconstruction is never materialised:
+// One workgroup (4 waves) per work item.  Item j of nj for a KV head (b, g)
+// streams a slice of its resident rows (raw tokens, then one pseudo row per
+// span) in 32-row steps and takes share j of nj of the union over the G query
+// heads of that KV head's routed spans: every item of a launch has the same
+// shape, so one launch fits the GPU in a single wave of workgroups and the
+// resident loads overlap the span bookkeeping.  For the union share of the
+// item's spans the reconstruction is never materialised:
 //     t = V^K^T q                    (R)      MFMA 16x16x32, A = V^K^T tile
 //     scores = U^K (t . sigma m^K)/sqrt(d)    MFMA 16x16x16, A = U^K tile
 //     w = U^V^T p                    (R)      MFMA 16x16x16, A = U^V^T tile
@@ -20,8 +23,7 @@
 // bf16 terms, which keeps ~16 mantissa bits; every accumulation is fp32.
 //
 // A span's factor blob is loaded in one round trip (all its loads issued
-// before any arithmetic); for R = 16 the next span's blob is in flight while
-// the current one is computed.  Each workgroup writes one softmax partial
+// before any arithmetic).  Each workgroup writes one softmax partial
 // (m, l, o) per head; merge_kernel combines them.  (A last-workgroup merge
 // inside this kernel would need a device-scope release per workgroup, which
 // on this GPU writes back the XCD's L2 each time; the kernel boundary is the
@@ -277,6 +279,84 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
     }
 }
 
+// One 32-row step of resident rows for the lane's head: two 16-row key
+// blocks, one 32-row value block, and for pseudo rows the head's mask bit
+// and the ln n_S bias, all loaded in one round trip (branch-free: clamped
+// in-range loads, invalid rows masked afterwards).
+template <int D, int G>
+struct ResStep {
+  static constexpr int NS32 = D / 32, ND16 = D / 16;
+  u32x4 kt[2][NS32], vt[ND16];
+  uint64_t word[2][4];
+  float lgn[2][4];
+  int t;
+
+  __device__ __forceinline__ void load(const bf16_t* Kb, const bf16_t* Vb, const uint64_t* mh, const float* logn,
+                                       const BMeta& bm, int t_, int lane, int grp) {
+    t = t_;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < NS32; ++s)
+        kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) vt[db] = *(const u32x4*)(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
+    if (32 * t + 32 > bm.n_raw && bm.n_spans > 0) {   // wave-uniform
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sp = 32 * t + 16 * kb + 4 * grp + r - bm.n_raw;
+          const int spc = min(max(sp, 0), bm.n_spans - 1);
+          word[kb][r] = mh[spc >> 6];
+          lgn[kb][r] = logn[bm.span_base + spc];
+        }
+    }
+  }
+
+  // scores, online softmax and o += V p for this step
+  __device__ __forceinline__ void fold(const u32x4 (&qB)[NS32], const BMeta& bm, float scale, int hl, int grp,
+                                       float& m, float& l, floatx4 (&o)[ND16]) const {
+    const int row0 = 32 * t;
+    const bool has_pseudo = row0 + 32 > bm.n_raw && bm.n_spans > 0;
+    floatx4 S[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      S[kb] = floatx4{0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < NS32; ++s) S[kb] = mfma32(kt[kb][s], qB[s], S[kb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + 16 * kb + 4 * grp + r;
+        float x = S[kb][r] * scale;
+        if (hl >= G || row >= bm.n_res) x = -INFINITY;
+        else if (has_pseudo && row >= bm.n_raw) {
+          // a span expanded by this head is attended through its factors
+          const int sp = row - bm.n_raw;
+          x = ((word[kb][r] >> (sp & 63)) & 1ull) ? -INFINITY : x + lgn[kb][r];
+        }
+        S[kb][r] = x;
+      }
+    const float corr = online<2>(S, 2, m, l);
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) o[db] *= corr;
+    u32x4 phi, plo;
+    pack8(S[0], S[1], phi, plo);
+#pragma unroll
+    for (int db = 0; db < ND16; ++db) {
+      o[db] = mfma32(vt[db], phi, o[db]);
+      o[db] = mfma32(vt[db], plo, o[db]);
+    }
+  }
+};
+
+// Dynamic LDS of attend_kernel: the union of the G heads' mask words, then
+// the G heads' words, [(G + 1)][W] uint64.
+inline size_t attend_dyn_lds(int G, int W) { return (size_t)(G + 1) * W * sizeof(uint64_t); }
+
 template <int D, int G, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 16 ? 3 : (R <= 32 ? 2 : 1))))
 void attend_kernel(const AttendArgs a) {
@@ -284,10 +364,10 @@ void attend_kernel(const AttendArgs a) {
   static_assert(G >= 1 && G <= 16, "G");
   __shared__ float s_ml[4][2][G];
   __shared__ float s_o[4][G][D];
-  __shared__ uint64_t s_uw[kMaxWords];     // union of the G heads' mask words
-  __shared__ int32_t s_pre[kMaxWords + 1];
   __shared__ int32_t s_ln[kMaxSpanList];   // span id | active heads << 24
+  __shared__ int32_t s_share[2];           // first union rank, span count
   __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
+  extern __shared__ uint64_t s_dyn[];
 
   const WorkItem it = a.items[blockIdx.x];
   const int lc = blockIdx.y, l = a.layer_begin + lc;
@@ -296,6 +376,8 @@ void attend_kernel(const AttendArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hl = lane & 15, grp = lane >> 4;
   const int Hq = a.Hq, Wd = a.W;
+  uint64_t* s_uw = s_dyn;        // [Wd] union words
+  uint64_t* s_hw = s_dyn + Wd;   // [G][Wd] head words
 
   // query operand: B[k = dim][j = head]
   u32x4 qB[NS32];
@@ -314,172 +396,120 @@ void attend_kernel(const AttendArgs a) {
   for (int db = 0; db < ND16; ++db) o[db] = floatx4{0, 0, 0, 0};
   const float scale = a.scale;
 
-  if (it.kind == 0) {
-    // ------------------------------------------------------ resident rows
-    // 32-row steps: two 16-row key blocks and one 32-row value block
-    const int64_t lg = (int64_t)l * a.Hkv + g;
-    const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
-    const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
-    const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
-    const int nsteps = bm.n_res_pad >> 5;
-    const int s_end = min(nsteps, 2 * (it.j + 1) * a.tpw);
-    for (int t = 2 * it.j * a.tpw + wave; t < s_end; t += 4) {
-      u32x4 kt[2][NS32], vt[ND16];
+  // ---------------------------------------------- resident slice: first step
+  // wave w takes steps step_begin + w, + 4, ...; the first one's loads are in
+  // flight during the span bookkeeping below
+  const int64_t lg = (int64_t)l * a.Hkv + g;
+  const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
+  const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
+  const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
+  ResStep<D, G> rs;
+  int t = it.step_begin + wave;
+  if (t < it.step_end) rs.load(Kb, Vb, mh, a.logn, bm, t, lane, grp);
+
+  // ------------------------------------------- span share: union bookkeeping
+  // (bits at or past N_S(b) are ignored, whatever the caller's mask holds)
+  int beg = 0, cnt = 0;
+  if (bm.n_spans > 0) {
+    for (int w = threadIdx.x; w < Wd; w += 256) {
+      const int left = bm.n_spans - 64 * w;
+      const uint64_t valid = left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
+      uint64_t u = 0;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < NS32; ++s)
-          kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
-#pragma unroll
-      for (int db = 0; db < ND16; ++db) vt[db] = *(const u32x4*)(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
-      // pseudo rows: the head's mask bit and the ln n_S bias, loaded with the step
-      const int row0 = 32 * t;
-      const bool has_pseudo = row0 + 32 > bm.n_raw && bm.n_spans > 0;
-      float bias[2][4];
-      if (has_pseudo) {
-        // branch-free: every lane loads from a clamped in-range span, the
-        // loads are in flight together, invalid rows are masked afterwards
-        uint64_t word[2][4];
-        float lgn[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
-            const int spc = min(max(sp, 0), bm.n_spans - 1);
-            word[kb][r] = mh[spc >> 6];
-            lgn[kb][r] = a.logn[bm.span_base + spc];
-          }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sp = row0 + 16 * kb + 4 * grp + r - bm.n_raw;
-            const bool valid = hl < G && sp >= 0 && sp < bm.n_spans;
-            const bool expanded = (word[kb][r] >> (sp & 63)) & 1ull;
-            bias[kb][r] = !valid ? 0.f : (expanded ? -INFINITY : lgn[kb][r]);
-          }
+      for (int h = 0; h < G; ++h) {
+        const uint64_t x = mrow[(int64_t)h * Wd + w] & valid;
+        s_hw[h * Wd + w] = x;
+        u |= x;
       }
-      floatx4 S[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        S[kb] = floatx4{0, 0, 0, 0};
-#pragma unroll
-        for (int s = 0; s < NS32; ++s) S[kb] = mfma32(kt[kb][s], qB[s], S[kb]);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = row0 + 16 * kb + 4 * grp + r;
-          float x = S[kb][r] * scale;
-          if (hl >= G || row >= bm.n_res) x = -INFINITY;
-          else if (has_pseudo && row >= bm.n_raw) x += bias[kb][r];
-          S[kb][r] = x;
-        }
-      const float corr = online<2>(S, 2, m, lsum);
-#pragma unroll
-      for (int db = 0; db < ND16; ++db) o[db] *= corr;
-      u32x4 phi, plo;
-      pack8(S[0], S[1], phi, plo);
-#pragma unroll
-      for (int db = 0; db < ND16; ++db) {
-        o[db] = mfma32(vt[db], phi, o[db]);
-        o[db] = mfma32(vt[db], plo, o[db]);
-      }
-    }
-  } else {
-    // --------------------------------------------------- routed spans
-    // per-head mask words and their union over the G heads of this KV head
-    // (bits at or past N_S(b) are ignored, whatever the caller's mask
-    // holds), prefix counts of the union words
-    // (word w = threadIdx.x + 256 k of every head stays in this thread's registers)
-    uint64_t hw[kMaxWords / 256][G];
-#pragma unroll
-    for (int k = 0; k < kMaxWords / 256; ++k) {
-      const int w = threadIdx.x + 256 * k;
-      if (w < Wd) {
-        const int left = bm.n_spans - 64 * w;
-        const uint64_t valid = left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
-        uint64_t u = 0;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          hw[k][h] = mrow[(int64_t)h * Wd + w] & valid;
-          u |= hw[k][h];
-        }
-        s_uw[w] = u;
-      }
+      s_uw[w] = u;
     }
     __syncthreads();
     if (wave == 0) {
+      // union size U, this item's ranks [beg, end) = share j of nj, then the
+      // spans of those ranks in union order: a ballot picks the words that
+      // overlap the share and each lane places the bit of its own position
+      int U = 0;
+      for (int w = lane; w < Wd; w += 64) U += __popcll(s_uw[w]);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) U += __shfl_xor(U, d);
+      const int b0 = (int)((int64_t)it.j * U / it.nj);
+      const int b1 = min((int)((int64_t)(it.j + 1) * U / it.nj), b0 + kMaxSpanList);
       int carry = 0;
-      for (int base = 0; base < Wd; base += 64) {
+      for (int base = 0; base < Wd && carry < b1; base += 64) {
         const int w = base + lane;
-        int v = (w < Wd) ? __popcll(s_uw[w]) : 0;
+        const uint64_t u = (w < Wd) ? s_uw[w] : 0ull;
+        const int c = __popcll(u);
+        int incl = c;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(v, d);
-          if (lane >= d) v += y;
+          const int y = __shfl_up(incl, d);
+          if (lane >= d) incl += y;
         }
-        if (w < Wd) s_pre[w + 1] = carry + v;
-        carry += __shfl(v, 63);
+        const int pre = carry + incl - c;
+        uint64_t hit = __ballot(c > 0 && pre < b1 && pre + c > b0);
+        while (hit) {
+          const int src = __builtin_ctzll(hit);
+          hit &= hit - 1;
+          const int ww = base + src;
+          const uint32_t ulo = __shfl((uint32_t)u, src), uhi = __shfl((uint32_t)(u >> 32), src);
+          const uint64_t uw = ((uint64_t)uhi << 32) | ulo;
+          const int r = __shfl(pre, src) + (int)__popcll(uw & ((1ull << lane) - 1));
+          if (((uw >> lane) & 1ull) && r >= b0 && r < b1) {
+            int hm = 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) hm |= (int)((s_hw[h * Wd + ww] >> lane) & 1ull) << h;
+            s_ln[r - b0] = (64 * ww + lane) | (hm << 24);
+          }
+        }
+        carry += __shfl(incl, 63);
       }
-      if (lane == 0) s_pre[0] = 0;
-    }
-    __syncthreads();
-    const int U = s_pre[Wd];
-    const int beg = (int)((int64_t)it.j * U / it.nj), end = (int)((int64_t)(it.j + 1) * U / it.nj);
-    const int cnt = min(end - beg, kMaxSpanList);   // the host keeps shares <= kMaxSpanList
-    // this item's spans in union order (span id | active heads << 24), one
-    // thread per mask word
-#pragma unroll
-    for (int kw = 0; kw < kMaxWords / 256; ++kw) {
-      const int w = threadIdx.x + 256 * kw;
-      if (w >= Wd) continue;
-      int k = s_pre[w];
-      if (k >= beg + cnt || s_pre[w + 1] <= beg) continue;
-      uint64_t bits = s_uw[w];
-      while (bits && k < beg + cnt) {
-        const int bit = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        if (k >= beg) {
-          int hm = 0;
-#pragma unroll
-          for (int h = 0; h < G; ++h) hm |= (int)((hw[kw][h] >> bit) & 1ull) << h;
-          s_ln[k - beg] = (64 * w + bit) | (hm << 24);
-        }
-        ++k;
+      if (lane == 0) {
+        s_share[0] = b0;
+        s_share[1] = b1 - b0;
       }
     }
     __syncthreads();
-    const int i0 = (int)((int64_t)cnt * wave / 4), i1 = (int)((int64_t)cnt * (wave + 1) / 4);
-    if (i0 < i1) {
-      // blob address of span rank i: the factor pool, or the staging ring
-      const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
-      const int64_t* roff = a.ring_off
-          ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + beg : nullptr;
-      // metadata of rank i (wave-uniform): length, active heads, blob offset;
-      // loaded one span ahead of the blob that needs it
-      struct Meta { int n, hm; int64_t off; };
-      auto meta = [&](int i) {
-        const int e = s_ln[min(i, i1 - 1)];
-        const int S = e & 0xffffff;
-        Meta mt;
-        mt.hm = e >> 24;
-        mt.n = a.span_len[bm.span_base + S];
-        mt.off = roff ? roff[min(i, i1 - 1)] : (int64_t)(region - a.pool) + a.span_off[bm.span_base + S];
-        return mt;
-      };
-      Meta mc = meta(i0);
-      Meta mn = meta(i0 + 1);
-      SpanRegs<D, R> cur;
-      cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp, s_vv[wave]);
-      for (int i = i0; i < i1; ++i) {
-        const Meta mnn = meta(i + 2);
-        span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave]);
-        if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp, s_vv[wave]);
-        mn = mnn;
-      }
+    beg = s_share[0];
+    cnt = s_share[1];
+  }
+
+  // ------------------------------------------------ resident slice: fold
+  if (t < it.step_end) {
+    rs.fold(qB, bm, scale, hl, grp, m, lsum, o);
+    for (t += 4; t < it.step_end; t += 4) {
+      rs.load(Kb, Vb, mh, a.logn, bm, t, lane, grp);
+      rs.fold(qB, bm, scale, hl, grp, m, lsum, o);
+    }
+  }
+
+  // --------------------------------------------------------- routed spans
+  const int i0 = (int)((int64_t)cnt * wave / 4), i1 = (int)((int64_t)cnt * (wave + 1) / 4);
+  if (i0 < i1) {
+    // blob address of span rank i: the factor pool, or the staging ring
+    const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
+    const int64_t* roff = a.ring_off
+        ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + beg : nullptr;
+    // metadata of rank i (wave-uniform): length, active heads, blob offset;
+    // loaded one span ahead of the blob that needs it
+    struct Meta { int n, hm; int64_t off; };
+    auto meta = [&](int i) {
+      const int e = s_ln[min(i, i1 - 1)];
+      const int S = e & 0xffffff;
+      Meta mt;
+      mt.hm = e >> 24;
+      mt.n = a.span_len[bm.span_base + S];
+      mt.off = roff ? roff[min(i, i1 - 1)] : (int64_t)(region - a.pool) + a.span_off[bm.span_base + S];
+      return mt;
+    };
+    Meta mc = meta(i0);
+    Meta mn = meta(i0 + 1);
+    SpanRegs<D, R> cur;
+    cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp, s_vv[wave]);
+    for (int i = i0; i < i1; ++i) {
+      const Meta mnn = meta(i + 2);
+      span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave]);
+      if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp, s_vv[wave]);
+      mn = mnn;
     }
   }
 
@@ -648,8 +678,17 @@ hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st) {
   if (a.W > 1024) return hipErrorInvalidValue;
   return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
-    hipLaunchKernelGGL((attend_kernel<decltype(d_)::value, decltype(g_)::value, decltype(r_)::value>),
-                       dim3(a.n_items, a.layer_count), dim3(256), 0, st, a);
+    constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
+    auto kern = attend_kernel<D_, G_, R_>;
+    const size_t dyn = attend_dyn_lds(G_, a.W);
+    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * (kMaxSpanList + 2) +
+                             4 * SpanRegs<D_, R_>::VV_BYTES;
+    if (fixed + dyn > 160 * 1024) return hipErrorInvalidValue;
+    if (dyn > 32 * 1024) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), dyn, st, a);
     return hipGetLastError();
   });
 }

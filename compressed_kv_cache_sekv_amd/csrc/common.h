@@ -102,16 +102,17 @@ constexpr int kMaxSpanList = 512;
 // Mask words per (b, l, h) the decode kernel handles (65536 spans).
 constexpr int kMaxWords = 1024;
 
-// Decode work: one workgroup of 4 waves per item.  kind 0: resident rows
-// tiles [j*tpw, (j+1)*tpw); kind 1: the j-th of nj shares of the union of
-// the routed spans of (b, l, g).  Items are launched span shares first; each
-// writes its softmax partial to `slot` (the slots of one (b, g) are
+// Decode work: one workgroup of 4 waves per item.  Item j of the nj items of
+// a KV head (b, g) takes the resident 32-row steps [step_begin, step_end) and
+// the j-th of nj equal shares of the union of the routed spans of (b, l, g);
+// it writes its softmax partial to `slot` (the slots of one (b, g) are
 // contiguous).
 struct WorkItem {
-  int32_t b, g, kind, j, nj;
-  int32_t part_first;   // first slot of (b, g)
-  int32_t part_count;   // slots of (b, g)
-  int32_t slot;
+  int32_t b, g;
+  int32_t j, nj;                    // union share j of nj of (b, g)
+  int32_t step_begin, step_end;     // resident 32-row steps of (b, g)
+  int32_t slot;                     // partial slot
+  int32_t pad;
 };
 
 struct AttendArgs {
@@ -131,7 +132,6 @@ struct AttendArgs {
   int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
   int32_t layer_begin, layer_count, n_items;
   int32_t B, L, Hq, Hkv, W, max_spans;
-  int32_t tpw;              // resident 64-row tiles per work item
   float scale;              // 1/sqrt(d)
 };
 

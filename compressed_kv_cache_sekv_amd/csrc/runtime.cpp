@@ -63,7 +63,7 @@ int env_int(const char* name, int dflt, int lo, int hi) {
   const int x = atoi(v);
   return (x >= lo && x <= hi) ? x : dflt;
 }
-int tiles_per_item() { return env_int("SEKV_TILES_PER_ITEM", 4, 1, 1024); }
+int steps_per_item() { return env_int("SEKV_STEPS_PER_ITEM", 8, 1, 1 << 20); }
 int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 32, 1, kMaxSpanList); }
 
 // Device buffer owned by the library.
@@ -147,7 +147,7 @@ struct sekv_index {
   uint32_t magic = IDX_MAGIC;
   sekv_ctx* ctx = nullptr;
   int B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, R = 0, dp = 0, G = 0, tier = 0;
-  int max_spans = 0, Wd = 0, max_raw = 0, tpw = 4;
+  int max_spans = 0, Wd = 0, max_raw = 0;
   int64_t total_spans = 0, total_raw = 0, total_tok = 0;
   int64_t layer_bytes = 0, pool_bytes = 0;
   int64_t kres_elems = 0, s_elems = 0;
@@ -216,7 +216,7 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
 
 // Fill shape fields and the per-sequence layout from span counts/lengths.
 // n_spans, n_raw: per b; lens: concatenated span lengths.
-void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<int32_t>& n_spans,
+sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<int32_t>& n_spans,
                  const std::vector<int32_t>& n_raw, const std::vector<int32_t>& lens) {
   x->B = p->B; x->L = p->L; x->Hq = p->Hq; x->Hkv = p->Hkv; x->D = p->d; x->R = p->R;
   x->dp = p->dprime; x->G = p->Hq / p->Hkv; x->tier = p->tier;
@@ -261,45 +261,32 @@ void plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<in
   x->layer_bytes = pb;
   x->pool_bytes = pb * x->L;
   x->Wd = std::max(1, (x->max_spans + 63) / 64);
-  // decode work items; the partial slots of one (b, g) are contiguous
-  x->tpw = tiles_per_item();
-  const int spi = spans_per_item();
+  // decode work items: nj per (b, g), each with an equal slice of the
+  // resident steps and an equal share of the routed union; nj covers the
+  // larger of the two (at most spans_per_item union spans and
+  // steps_per_item steps an item, unless the merge bound caps nj)
+  const int spi = spans_per_item(), spw = steps_per_item();
+  const int max_items = kMaxMergeWeights / x->G;
   x->items.clear();
   x->bg_first.assign((size_t)2 * x->B * x->Hkv, 0);
-  // the merge combines at most kMaxMergeWeights / G partials per (b, g):
-  // widen the items of long sequences until they fit
-  const int max_items = kMaxMergeWeights / x->G;
-  for (int b = 0; b < x->B; ++b) {
-    const BMeta& m = x->meta[b];
-    const int ntiles = m.n_res_pad / 64;
-    int tpw = x->tpw, sp = spi;
-    auto count = [&](int t, int s) {
-      return (ntiles + t - 1) / t + (m.n_spans ? (m.n_spans + s - 1) / s : 0);
-    };
-    while (count(tpw, sp) > max_items) {
-      tpw *= 2;
-      sp = std::min(2 * sp, kMaxSpanList);
-    }
-    x->tpw = std::max(x->tpw, tpw);
-  }
-  // span shares of every (b, g) first (they run longest), then resident tiles
-  std::vector<WorkItem> res_items;
   int slot = 0;
   for (int b = 0; b < x->B; ++b) {
     const BMeta& m = x->meta[b];
-    const int ntiles = m.n_res_pad / 64;
-    const int sp = std::min(kMaxSpanList, spi * (x->tpw / std::max(1, tiles_per_item())));
-    const int nres = (ntiles + x->tpw - 1) / x->tpw;
-    const int nfac = m.n_spans ? (m.n_spans + sp - 1) / sp : 0;
+    const int nsteps = m.n_res_pad / 32;
+    const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
+    const int nres = (nsteps + spw - 1) / spw;
+    const int nj = std::min(std::max(std::max(nfac, nres), 1), max_items);
+    if ((m.n_spans + nj - 1) / nj > kMaxSpanList)
+      return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d exceed the decode work plan", m.n_spans, b);
     for (int g = 0; g < x->Hkv; ++g) {
-      const int first = slot;
-      x->bg_first[2 * ((size_t)b * x->Hkv + g)] = first;
-      x->bg_first[2 * ((size_t)b * x->Hkv + g) + 1] = nres + nfac;
-      for (int j = 0; j < nfac; ++j) x->items.push_back(WorkItem{b, g, 1, j, nfac, first, nres + nfac, slot++});
-      for (int j = 0; j < nres; ++j) res_items.push_back(WorkItem{b, g, 0, j, nres, first, nres + nfac, slot++});
+      x->bg_first[2 * ((size_t)b * x->Hkv + g)] = slot;
+      x->bg_first[2 * ((size_t)b * x->Hkv + g) + 1] = nj;
+      for (int j = 0; j < nj; ++j)
+        x->items.push_back(WorkItem{b, g, j, nj, (int)((int64_t)j * nsteps / nj),
+                                    (int)((int64_t)(j + 1) * nsteps / nj), slot++, 0});
     }
   }
-  x->items.insert(x->items.end(), res_items.begin(), res_items.end());
+  return SEKV_OK;
 }
 
 // Allocate and clear the device (and pinned) storage of a planned index.
@@ -572,7 +559,7 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   sekv_index* x = new sekv_index();
   x->ctx = c;
   IndexGuard guard{x};
-  plan_layout(x, p, n_spans, n_raw, lens);
+  if ((st = plan_layout(x, p, n_spans, n_raw, lens))) return st;
   if ((st = alloc_index(x, p->ring_bytes))) return st;
   // compact span tables and raw positions
   for (int b = 0; b < B; ++b) {
@@ -683,7 +670,7 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
   sekv_index* x = new sekv_index();
   x->ctx = c;
   IndexGuard guard{x};
-  plan_layout(x, p, n_spans, n_raw, lens);
+  if ((st = plan_layout(x, p, n_spans, n_raw, lens))) return st;
   if ((st = alloc_index(x, p->ring_bytes))) return st;
   hipStream_t stream = c->stream;
   // pack into the native layouts on the host
@@ -1042,7 +1029,6 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
   aa.max_spans = std::max(x->max_spans, 1);
-  aa.tpw = x->tpw;
   aa.scale = 1.0f / sqrtf((float)x->D);
   if (n_items > 0) {
     size_t slot = 0;
