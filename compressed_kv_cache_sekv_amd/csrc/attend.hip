@@ -282,12 +282,15 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
 // One 32-row step of resident rows for the lane's head: two 16-row key
 // blocks, one 32-row value block, and for pseudo rows the head's mask bit
 // and the ln n_S bias, all loaded in one round trip (branch-free: clamped
-// in-range loads, invalid rows masked afterwards).
+// in-range loads, invalid rows masked afterwards).  Every global load from
+// here to the first fold is issued without a branch: the wait before the
+// fold then counts only the loads issued after this step's, which stay in
+// flight.
 template <int D, int G>
 struct ResStep {
   static constexpr int NS32 = D / 32, ND16 = D / 16;
   u32x4 kt[2][NS32], vt[ND16];
-  uint64_t word[2][4];
+  uint32_t word[2][4];   // the 32-bit half of the mask word holding the row's bit
   float lgn[2][4];
   int t;
 
@@ -301,17 +304,17 @@ struct ResStep {
         kt[kb][s] = *(const u32x4*)(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
 #pragma unroll
     for (int db = 0; db < ND16; ++db) vt[db] = *(const u32x4*)(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
-    if (32 * t + 32 > bm.n_raw && bm.n_spans > 0) {   // wave-uniform
+    // pseudo-row inputs, loaded for every step (no branch, so that later
+    // waits can count these loads); raw rows read span 0 and are masked
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int sp = 32 * t + 16 * kb + 4 * grp + r - bm.n_raw;
-          const int spc = min(max(sp, 0), bm.n_spans - 1);
-          word[kb][r] = mh[spc >> 6];
-          lgn[kb][r] = logn[bm.span_base + spc];
-        }
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int sp = 32 * t + 16 * kb + 4 * grp + r - bm.n_raw;
+        const int spc = max(min(sp, bm.n_spans - 1), 0);
+        word[kb][r] = ((const uint32_t*)mh)[spc >> 5];
+        lgn[kb][r] = logn[bm.n_spans > 0 ? bm.span_base + spc : 0];
+      }
   }
 
   // scores, online softmax and o += V p for this step
@@ -336,7 +339,7 @@ struct ResStep {
         else if (has_pseudo && row >= bm.n_raw) {
           // a span expanded by this head is attended through its factors
           const int sp = row - bm.n_raw;
-          x = ((word[kb][r] >> (sp & 63)) & 1ull) ? -INFINITY : x + lgn[kb][r];
+          x = ((word[kb][r] >> (sp & 31)) & 1u) ? -INFINITY : x + lgn[kb][r];
         }
         S[kb][r] = x;
       }
@@ -364,8 +367,12 @@ void attend_kernel(const AttendArgs a) {
   static_assert(G >= 1 && G <= 16, "G");
   __shared__ float s_ml[4][2][G];
   __shared__ float s_o[4][G][D];
-  __shared__ int32_t s_ln[kMaxSpanList];   // span id | active heads << 24
-  __shared__ int32_t s_share[2];           // first union rank, span count
+  // per wave: the item's share of the union (span id | active heads << 24
+  // by rank within the share), then the wave's own spans in the order it
+  // takes them: blob offset, length, active heads
+  __shared__ int32_t s_ln[4][kMaxSpanList];
+  __shared__ int64_t s_woff[4][kMaxSpanList];
+  __shared__ int32_t s_wn[4][kMaxSpanList];
   __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
   extern __shared__ uint64_t s_dyn[];
 
@@ -379,15 +386,19 @@ void attend_kernel(const AttendArgs a) {
   uint64_t* s_uw = s_dyn;        // [Wd] union words
   uint64_t* s_hw = s_dyn + Wd;   // [G][Wd] head words
 
-  // query operand: B[k = dim][j = head]
+  // query operand: B[k = dim][j = head] (lanes of absent heads load head 0
+  // and zero it)
   u32x4 qB[NS32];
   {
-    const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * Hq + g * G + hl) * D;
+    const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * Hq + g * G + (hl < G ? hl : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < NS32; ++s)
-      qB[s] = (hl < G) ? *(const u32x4*)(qp + 32 * s + 8 * grp) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < NS32; ++s) {
+      const u32x4 v = *(const u32x4*)(qp + 32 * s + 8 * grp);
+      qB[s] = (hl < G) ? v : u32x4{0, 0, 0, 0};
+    }
   }
   const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + lc) * Hq + g * G) * Wd;
+  const bool spans = bm.n_spans > 0;   // uniform
 
   // running softmax state of this lane's head hl; o[dim = 16*db + 4*grp + r]
   float m = -INFINITY, lsum = 0.f;
@@ -396,84 +407,100 @@ void attend_kernel(const AttendArgs a) {
   for (int db = 0; db < ND16; ++db) o[db] = floatx4{0, 0, 0, 0};
   const float scale = a.scale;
 
-  // ---------------------------------------------- resident slice: first step
-  // wave w takes steps step_begin + w, + 4, ...; the first one's loads are in
-  // flight during the span bookkeeping below
+  // the G heads' mask words of word threadIdx.x (more words below)
+  const int w0 = min((int)threadIdx.x, Wd - 1);
+  uint64_t mw[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) mw[h] = mrow[(int64_t)h * Wd + w0];
+
+  // resident slice: wave w takes steps step_begin + w, + 4, ...; the first
+  // one's loads stay in flight during the span bookkeeping below
   const int64_t lg = (int64_t)l * a.Hkv + g;
   const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
   const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
   const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
-  ResStep<D, G> rs;
   int t = it.step_begin + wave;
-  if (t < it.step_end) rs.load(Kb, Vb, mh, a.logn, bm, t, lane, grp);
+  ResStep<D, G> rs;
+  rs.load(Kb, Vb, mh, a.logn, bm, (it.step_begin < it.step_end) ? min(t, it.step_end - 1) : 0, lane, grp);
 
-  // ------------------------------------------- span share: union bookkeeping
-  // (bits at or past N_S(b) are ignored, whatever the caller's mask holds)
-  int beg = 0, cnt = 0;
-  if (bm.n_spans > 0) {
-    for (int w = threadIdx.x; w < Wd; w += 256) {
-      const int left = bm.n_spans - 64 * w;
-      const uint64_t valid = left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
-      uint64_t u = 0;
+  // union of the G heads' mask words (bits at or past N_S(b) ignored,
+  // whatever the caller's mask holds) and the heads' words, in LDS
+  auto put_word = [&](int w, const uint64_t (&x)[G]) {
+    const int left = bm.n_spans - 64 * w;
+    const uint64_t valid = left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
+    uint64_t u = 0;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint64_t x = mrow[(int64_t)h * Wd + w] & valid;
-        s_hw[h * Wd + w] = x;
-        u |= x;
-      }
-      s_uw[w] = u;
+    for (int h = 0; h < G; ++h) {
+      s_hw[h * Wd + w] = x[h] & valid;
+      u |= x[h] & valid;
     }
-    __syncthreads();
-    if (wave == 0) {
-      // union size U, this item's ranks [beg, end) = share j of nj, then the
-      // spans of those ranks in union order: a ballot picks the words that
-      // overlap the share and each lane places the bit of its own position
-      int U = 0;
-      for (int w = lane; w < Wd; w += 64) U += __popcll(s_uw[w]);
+    s_uw[w] = u;
+  };
+  put_word(w0, mw);   // threads past Wd rewrite word Wd - 1 with the same values
+  for (int w = threadIdx.x + 256; w < Wd; w += 256) {
+    uint64_t x[G];
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) U += __shfl_xor(U, d);
-      const int b0 = (int)((int64_t)it.j * U / it.nj);
-      const int b1 = min((int)((int64_t)(it.j + 1) * U / it.nj), b0 + kMaxSpanList);
-      int carry = 0;
-      for (int base = 0; base < Wd && carry < b1; base += 64) {
-        const int w = base + lane;
-        const uint64_t u = (w < Wd) ? s_uw[w] : 0ull;
-        const int c = __popcll(u);
-        int incl = c;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(incl, d);
-          if (lane >= d) incl += y;
-        }
-        const int pre = carry + incl - c;
-        uint64_t hit = __ballot(c > 0 && pre < b1 && pre + c > b0);
-        while (hit) {
-          const int src = __builtin_ctzll(hit);
-          hit &= hit - 1;
-          const int ww = base + src;
-          const uint32_t ulo = __shfl((uint32_t)u, src), uhi = __shfl((uint32_t)(u >> 32), src);
-          const uint64_t uw = ((uint64_t)uhi << 32) | ulo;
-          const int r = __shfl(pre, src) + (int)__popcll(uw & ((1ull << lane) - 1));
-          if (((uw >> lane) & 1ull) && r >= b0 && r < b1) {
-            int hm = 0;
-#pragma unroll
-            for (int h = 0; h < G; ++h) hm |= (int)((s_hw[h * Wd + ww] >> lane) & 1ull) << h;
-            s_ln[r - b0] = (64 * ww + lane) | (hm << 24);
-          }
-        }
-        carry += __shfl(incl, 63);
-      }
-      if (lane == 0) {
-        s_share[0] = b0;
-        s_share[1] = b1 - b0;
-      }
-    }
-    __syncthreads();
-    beg = s_share[0];
-    cnt = s_share[1];
+    for (int h = 0; h < G; ++h) x[h] = mrow[(int64_t)h * Wd + w];
+    put_word(w, x);
   }
+  __syncthreads();
 
-  // ------------------------------------------------ resident slice: fold
+  // every wave: union size U, the item's ranks [b0, b1) = share j of nj, and
+  // the spans of those ranks (a ballot picks the words that overlap the
+  // share, each lane places the bit of its own position); lane k then holds
+  // the share's k-th span: id | active heads << 24, length, blob offset
+  int U = 0;
+  for (int w = lane; w < Wd; w += 64) U += __popcll(s_uw[w]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) U += __shfl_xor(U, d);
+  const int b0 = spans ? (int)((int64_t)it.j * U / it.nj) : 0;
+  const int b1 = spans ? min((int)((int64_t)(it.j + 1) * U / it.nj), b0 + kMaxSpanList) : 0;
+  const int nsh = b1 - b0;
+  {
+    int carry = 0;
+    for (int base = 0; base < Wd && carry < b1; base += 64) {
+      const int w = base + lane;
+      const uint64_t u = (w < Wd) ? s_uw[w] : 0ull;
+      const int c = __popcll(u);
+      int incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      const int pre = carry + incl - c;
+      uint64_t hit = __ballot(c > 0 && pre < b1 && pre + c > b0);
+      while (hit) {
+        const int src = __builtin_ctzll(hit);
+        hit &= hit - 1;
+        const int ww = base + src;
+        const uint32_t ulo = __shfl((uint32_t)u, src), uhi = __shfl((uint32_t)(u >> 32), src);
+        const uint64_t uw = ((uint64_t)uhi << 32) | ulo;
+        const int r = __shfl(pre, src) + (int)__popcll(uw & ((1ull << lane) - 1));
+        if (((uw >> lane) & 1ull) && r >= b0 && r < b1) {
+          int hm = 0;
+#pragma unroll
+          for (int h = 0; h < G; ++h) hm |= (int)((s_hw[h * Wd + ww] >> lane) & 1ull) << h;
+          s_ln[wave][r - b0] = (64 * ww + lane) | (hm << 24);
+        }
+      }
+      carry += __shfl(incl, 63);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // (clamped, branch-free: a lane past the share, or an empty share, reads a
+  // valid span and is ignored)
+  const int ek = (nsh > 0) ? s_ln[wave][min(lane, nsh - 1)] : 0;
+  const int Sk = spans ? bm.span_base + (ek & 0xffffff) : 0;
+  const int nk = a.span_len[Sk];
+  const bool ring = a.ring_off != nullptr;
+  const int64_t* okp = ring
+      ? a.ring_off + ((((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + b0 + min(lane, max(nsh - 1, 0)))
+      : a.span_off + Sk;
+  const int64_t ok = *okp + (ring ? 0 : (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg);
+
+  // resident slice: fold (the span metadata loads are in flight)
   if (t < it.step_end) {
     rs.fold(qB, bm, scale, hl, grp, m, lsum, o);
     for (t += 4; t < it.step_end; t += 4) {
@@ -482,34 +509,49 @@ void attend_kernel(const AttendArgs a) {
     }
   }
 
-  // --------------------------------------------------------- routed spans
-  const int i0 = (int)((int64_t)cnt * wave / 4), i1 = (int)((int64_t)cnt * (wave + 1) / 4);
-  if (i0 < i1) {
-    // blob address of span rank i: the factor pool, or the staging ring
-    const uint8_t* region = a.pool + (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
-    const int64_t* roff = a.ring_off
-        ? a.ring_off + (((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + beg : nullptr;
-    // metadata of rank i (wave-uniform): length, active heads, blob offset;
-    // loaded one span ahead of the blob that needs it
-    struct Meta { int n, hm; int64_t off; };
-    auto meta = [&](int i) {
-      const int e = s_ln[min(i, i1 - 1)];
-      const int S = e & 0xffffff;
-      Meta mt;
-      mt.hm = e >> 24;
-      mt.n = a.span_len[bm.span_base + S];
-      mt.off = roff ? roff[min(i, i1 - 1)] : (int64_t)(region - a.pool) + a.span_off[bm.span_base + S];
-      return mt;
-    };
-    Meta mc = meta(i0);
-    Meta mn = meta(i0 + 1);
-    SpanRegs<D, R> cur;
-    cur.load(a.pool + uni64(mc.off), uni(mc.n), uni(mc.hm), lane, grp, s_vv[wave]);
-    for (int i = i0; i < i1; ++i) {
-      const Meta mnn = meta(i + 2);
+  // routed spans: longest first, each to the wave with the least work so far
+  // (greedy LPT; cost in round trips: the blob with its first 64 tokens, one
+  // per further 64 tokens, and one for the compute).  Every wave computes the
+  // same assignment from the lengths alone, so results do not depend on
+  // timing.
+  if (nsh > 0) {
+    const int nv = (lane < nsh) ? nk : -1;
+    int rank = 0;
+    for (int j = 0; j < nsh; ++j) {
+      const int nj = __shfl(nv, j);
+      rank += (nj > nv) || (nj == nv && j < lane);
+    }
+    int er = 0;   // lane r: the share index of the rank-r span
+    for (int j = 0; j < nsh; ++j) er = (__shfl(rank, j) == lane) ? j : er;
+    const int cr = 1 + (__shfl(nv, er) + 63) / 64;
+    int load0 = 0, load1 = 0, load2 = 0, load3 = 0, wr = 0;
+    for (int r = 0; r < nsh; ++r) {
+      const int c = __shfl(cr, r);
+      int w = 0, lw = load0;
+      if (load1 < lw) { w = 1; lw = load1; }
+      if (load2 < lw) { w = 2; lw = load2; }
+      if (load3 < lw) { w = 3; lw = load3; }
+      if (w == 0) load0 += c; else if (w == 1) load1 += c; else if (w == 2) load2 += c; else load3 += c;
+      if (lane == r) wr = w;
+    }
+    // this wave's spans, longest first, into its LDS list
+    const uint64_t mine = __ballot(lane < nsh && wr == wave);
+    const uint32_t olo = __shfl((uint32_t)ok, er), ohi = __shfl((uint32_t)((uint64_t)ok >> 32), er);
+    const int ne = __shfl(nk, er), he = (int)((uint32_t)__shfl(ek, er) >> 24);
+    if ((mine >> lane) & 1ull) {
+      const int pos = (int)__popcll(mine & ((1ull << lane) - 1));
+      s_woff[wave][pos] = (int64_t)(((uint64_t)ohi << 32) | olo);
+      s_wn[wave][pos] = ne | (he << 24);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int nw = (int)__popcll(mine);
+    for (int i = 0; i < nw; ++i) {
+      const int nh = s_wn[wave][i];
+      SpanRegs<D, R> cur;
+      cur.load(a.pool + uni64(s_woff[wave][i]), uni(nh & 0xffffff), uni((int)((uint32_t)nh >> 24)), lane, grp,
+               s_vv[wave]);
       span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave]);
-      if (i + 1 < i1) cur.load(a.pool + uni64(mn.off), uni(mn.n), uni(mn.hm), lane, grp, s_vv[wave]);
-      mn = mnn;
     }
   }
 

@@ -97,8 +97,8 @@ struct BMeta {
 
 // Partials one merge can combine: items of a (b, g) times G (LDS bound).
 constexpr int kMaxMergeWeights = 2048;
-// Routed spans one factored work item may take (its LDS span list).
-constexpr int kMaxSpanList = 512;
+// Routed spans one work item may take (one per lane of a wave).
+constexpr int kMaxSpanList = 64;
 // Mask words per (b, l, h) the decode kernel handles (65536 spans).
 constexpr int kMaxWords = 1024;
 

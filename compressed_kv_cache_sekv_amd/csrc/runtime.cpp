@@ -264,9 +264,8 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   // decode work items: nj per (b, g), each with an equal slice of the
   // resident steps and an equal share of the routed union; nj covers the
   // larger of the two (at most spans_per_item union spans and
-  // steps_per_item steps an item, unless the merge bound caps nj)
+  // steps_per_item steps an item)
   const int spi = spans_per_item(), spw = steps_per_item();
-  const int max_items = kMaxMergeWeights / x->G;
   x->items.clear();
   x->bg_first.assign((size_t)2 * x->B * x->Hkv, 0);
   int slot = 0;
@@ -275,7 +274,7 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
     const int nsteps = m.n_res_pad / 32;
     const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
     const int nres = (nsteps + spw - 1) / spw;
-    const int nj = std::min(std::max(std::max(nfac, nres), 1), max_items);
+    const int nj = std::max(std::max(nfac, nres), 1);
     if ((m.n_spans + nj - 1) / nj > kMaxSpanList)
       return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d exceed the decode work plan", m.n_spans, b);
     for (int g = 0; g < x->Hkv; ++g) {
