@@ -128,6 +128,11 @@ template <int D, int R>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
   static constexpr int VV_BYTES = 2 * D * R;
+  // tokens 64..127 of the left factors (U^K and U^V^T, 4 token blocks each)
+  // also go to the wave's LDS with the blob, so a span of up to 128 tokens
+  // is one round trip; longer spans stream their further chunks
+  static constexpr bool CK = R <= 32;
+  static constexpr int CK_BYTES = CK ? 2 * 4 * NR16 * 512 : 16;
   u32x4 vkt[NR16][NS32];
   floatx4 smk[NR16], smv[NR16];
   u32x2 uk[4][NR16];
@@ -135,7 +140,8 @@ struct SpanRegs {
   const uint8_t* blob;
   int n, hm;
 
-  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp, uint8_t* lds_vv) {
+  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp, uint8_t* lds_vv,
+                                       uint8_t* lds_ck) {
     blob = b;
     n = n_;
     hm = hm_;
@@ -174,6 +180,29 @@ struct SpanRegs {
     for (int c = 0; c < VV_BYTES / 1024; ++c)
       __builtin_amdgcn_global_load_lds((const void*)(pv + c * 1024 + lane * 16),
                                        (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, 0);
+    if (CK && ntb > 4) {   // wave-uniform
+      // 512-byte blocks: U^K (tb, kb) at (tb' NR16 + kb), then U^V^T (ib, tb)
+      // at 4 NR16 + ib 4 + tb', tb' = tb - 4; blocks past the span re-read
+      // its last block (in range, multiplied by zero weights)
+      const uint8_t* uk8 = (const uint8_t*)pu;
+      const uint8_t* uv8 = (const uint8_t*)pw;
+#pragma unroll
+      for (int c = 0; c < 4 * NR16; ++c) {
+        const int blk = 2 * c + (lane >> 5);
+        int64_t src;
+        if (blk < 4 * NR16) {
+          const int tb = 4 + blk / NR16, kb = blk % NR16;
+          src = (int64_t)(min(tb, ntb - 1) * NR16 + kb) * 512;
+          src += (int64_t)(uk8 - b);
+        } else {
+          const int ib = (blk - 4 * NR16) >> 2, tb = 4 + ((blk - 4 * NR16) & 3);
+          src = (int64_t)(ib * ntb + min(tb, ntb - 1)) * 512;
+          src += (int64_t)(uv8 - b);
+        }
+        __builtin_amdgcn_global_load_lds((const void*)(b + src + (lane & 31) * 16),
+                                         (__attribute__((address_space(3))) void*)(lds_ck + c * 1024), 16, 0, 0);
+      }
+    }
   }
 };
 
@@ -225,7 +254,7 @@ __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u
 template <int D, int G, int R>
 __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 (&qB)[D / 32], float scale,
                                           int lane, int hl, int grp, float& m, float& l,
-                                          floatx4 (&o)[D / 16], const uint8_t* lds_vv) {
+                                          floatx4 (&o)[D / 16], const uint8_t* lds_vv, const uint8_t* lds_ck) {
   constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
   const int n = sr.n, npad = Blob::npad(n), ntb = npad >> 4;
   // t = V^K^T q; c = t * sigma m^K / sqrt(d), split into bf16 hi + lo
@@ -249,13 +278,26 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
     for (int tb0 = 4; tb0 < ntb; tb0 += 4) {
       const int nb = min(4, ntb - tb0);
       u32x2 uk[4][NR16], uvt[NR16][4];
+      if (SpanRegs<D, R>::CK && tb0 == 4) {
+        // from the wave's LDS copy (wait for the wave's outstanding loads,
+        // the asynchronous copies included)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int tbc = tb0 + min(tb, nb - 1);
+        for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int kb = 0; kb < NR16; ++kb) {
-          uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
-          uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tbc) * 256 + lane * 4);
+          for (int kb = 0; kb < NR16; ++kb) {
+            uk[tb][kb] = *(const u32x2*)(lds_ck + (tb * NR16 + kb) * 512 + lane * 8);
+            uvt[kb][tb] = *(const u32x2*)(lds_ck + (4 * NR16 + kb * 4 + tb) * 512 + lane * 8);
+          }
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int tbc = tb0 + min(tb, nb - 1);
+#pragma unroll
+          for (int kb = 0; kb < NR16; ++kb) {
+            uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
+            uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tbc) * 256 + lane * 4);
+          }
         }
       }
       span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, chi, clo, m, l, o, wacc);
@@ -374,6 +416,7 @@ void attend_kernel(const AttendArgs a) {
   __shared__ int64_t s_woff[4][kMaxSpanList];
   __shared__ int32_t s_wn[4][kMaxSpanList];
   __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t s_ck[4][SpanRegs<D, R>::CK_BYTES];   // per wave
   extern __shared__ uint64_t s_dyn[];
 
   const WorkItem it = a.items[blockIdx.x];
@@ -550,8 +593,8 @@ void attend_kernel(const AttendArgs a) {
       const int nh = s_wn[wave][i];
       SpanRegs<D, R> cur;
       cur.load(a.pool + uni64(s_woff[wave][i]), uni(nh & 0xffffff), uni((int)((uint32_t)nh >> 24)), lane, grp,
-               s_vv[wave]);
-      span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave]);
+               s_vv[wave], s_ck[wave]);
+      span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave], s_ck[wave]);
     }
   }
 
@@ -723,8 +766,8 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
     auto kern = attend_kernel<D_, G_, R_>;
     const size_t dyn = attend_dyn_lds(G_, a.W);
-    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * (kMaxSpanList + 2) +
-                             4 * SpanRegs<D_, R_>::VV_BYTES;
+    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * 16 * kMaxSpanList +
+                             4 * (SpanRegs<D_, R_>::VV_BYTES + SpanRegs<D_, R_>::CK_BYTES);
     if (fixed + dyn > 160 * 1024) return hipErrorInvalidValue;
     if (dyn > 32 * 1024) {
       const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
