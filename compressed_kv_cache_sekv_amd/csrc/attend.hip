@@ -398,6 +398,27 @@ struct ResStep {
   }
 };
 
+// Wave-wide sum, and inclusive prefix over lanes, of per-lane counts below
+// 2^11, by bit-sliced ballots (scalar popcounts, no lane-to-lane moves).
+__device__ __forceinline__ int wave_sum_small(int c) {
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 11; ++i) s += (int)__popcll(__ballot((c >> i) & 1)) << i;
+  return s;
+}
+__device__ __forceinline__ int wave_prefix_small(int c, int lane, int& total) {
+  const uint64_t le = (2ull << lane) - 1;   // lanes <= lane (all 64 for lane 63)
+  int s = 0, t = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {   // counts of one mask word: at most 64
+    const uint64_t bal = __ballot((c >> i) & 1);
+    s += (int)__popcll(bal & le) << i;
+    t += (int)__popcll(bal) << i;
+  }
+  total = t;
+  return s;
+}
+
 // Dynamic LDS of attend_kernel: the union of the G heads' mask words, then
 // the G heads' words, [(G + 1)][W] uint64.
 inline size_t attend_dyn_lds(int G, int W) { return (size_t)(G + 1) * W * sizeof(uint64_t); }
@@ -494,10 +515,10 @@ void attend_kernel(const AttendArgs a) {
   // the share's k-th span: id | active heads << 24, length, blob offset
   int U = 0;
   for (int w = lane; w < Wd; w += 64) U += __popcll(s_uw[w]);
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) U += __shfl_xor(U, d);
-  const int b0 = spans ? (int)((int64_t)it.j * U / it.nj) : 0;
-  const int b1 = spans ? min((int)((int64_t)(it.j + 1) * U / it.nj), b0 + kMaxSpanList) : 0;
+  U = wave_sum_small(U);
+  // 32-bit: the plan keeps nj * N_S below 2^31
+  const int b0 = spans ? (int)((uint32_t)it.j * (uint32_t)U / (uint32_t)it.nj) : 0;
+  const int b1 = spans ? min((int)((uint32_t)(it.j + 1) * (uint32_t)U / (uint32_t)it.nj), b0 + kMaxSpanList) : 0;
   const int nsh = b1 - b0;
   {
     int carry = 0;
@@ -505,21 +526,17 @@ void attend_kernel(const AttendArgs a) {
       const int w = base + lane;
       const uint64_t u = (w < Wd) ? s_uw[w] : 0ull;
       const int c = __popcll(u);
-      int incl = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
-      const int pre = carry + incl - c;
+      int tot;
+      const int pre = carry + wave_prefix_small(c, lane, tot) - c;
       uint64_t hit = __ballot(c > 0 && pre < b1 && pre + c > b0);
       while (hit) {
         const int src = __builtin_ctzll(hit);
         hit &= hit - 1;
         const int ww = base + src;
-        const uint32_t ulo = __shfl((uint32_t)u, src), uhi = __shfl((uint32_t)(u >> 32), src);
+        const uint32_t ulo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+        const uint32_t uhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
         const uint64_t uw = ((uint64_t)uhi << 32) | ulo;
-        const int r = __shfl(pre, src) + (int)__popcll(uw & ((1ull << lane) - 1));
+        const int r = __builtin_amdgcn_readlane(pre, src) + (int)__popcll(uw & ((1ull << lane) - 1));
         if (((uw >> lane) & 1ull) && r >= b0 && r < b1) {
           int hm = 0;
 #pragma unroll
@@ -527,7 +544,7 @@ void attend_kernel(const AttendArgs a) {
           s_ln[wave][r - b0] = (64 * ww + lane) | (hm << 24);
         }
       }
-      carry += __shfl(incl, 63);
+      carry += tot;
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -561,15 +578,15 @@ void attend_kernel(const AttendArgs a) {
     const int nv = (lane < nsh) ? nk : -1;
     int rank = 0;
     for (int j = 0; j < nsh; ++j) {
-      const int nj = __shfl(nv, j);
+      const int nj = __builtin_amdgcn_readlane(nv, j);
       rank += (nj > nv) || (nj == nv && j < lane);
     }
     int er = 0;   // lane r: the share index of the rank-r span
-    for (int j = 0; j < nsh; ++j) er = (__shfl(rank, j) == lane) ? j : er;
+    for (int j = 0; j < nsh; ++j) er = (__builtin_amdgcn_readlane(rank, j) == lane) ? j : er;
     const int cr = 1 + (__shfl(nv, er) + 63) / 64;
     int load0 = 0, load1 = 0, load2 = 0, load3 = 0, wr = 0;
     for (int r = 0; r < nsh; ++r) {
-      const int c = __shfl(cr, r);
+      const int c = __builtin_amdgcn_readlane(cr, r);
       int w = 0, lw = load0;
       if (load1 < lw) { w = 1; lw = load1; }
       if (load2 < lw) { w = 2; lw = load2; }

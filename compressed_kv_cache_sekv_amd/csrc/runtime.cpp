@@ -275,7 +275,7 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
     const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
     const int nres = (nsteps + spw - 1) / spw;
     const int nj = std::max(std::max(nfac, nres), 1);
-    if ((m.n_spans + nj - 1) / nj > kMaxSpanList)
+    if ((m.n_spans + nj - 1) / nj > kMaxSpanList || (int64_t)nj * m.n_spans >= (1LL << 31))
       return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d exceed the decode work plan", m.n_spans, b);
     for (int g = 0; g < x->Hkv; ++g) {
       x->bg_first[2 * ((size_t)b * x->Hkv + g)] = slot;
