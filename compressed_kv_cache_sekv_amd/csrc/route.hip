@@ -77,6 +77,7 @@ __device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int
 // past d' are zero, and s_u is zero there, so they add nothing).
 constexpr int kMaxDp = 64;
 
+template <int D>
 __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[kMaxDp];
   // workgroup id -> (b, chunk, h) so that every chunk of one (b, h) lands on
@@ -91,56 +92,50 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   const int lc = blockIdx.y, l = a.layer_begin + lc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const BMeta bm = a.meta[b];
-  const int D = a.D, dp = a.dp;
-  if (threadIdx.x < kMaxDp) s_u[threadIdx.x] = 0.f;
-  __syncthreads();
+  const int dp = a.dp;
   const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
   const int wi = chunk * 4 + wave;
   const int S = 64 * wi + lane;
   const bool live = wi < a.Wd && S < bm.n_spans;
-  // summary keys of this lane's span, all loads in flight before u is needed
+  // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims.
+  // The thread's W row slice and q slice (16-byte loads) are issued first,
+  // then the summary keys of this lane's span: u is reduced while the keys
+  // are still in flight.
+  const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
+  const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
+  constexpr int QD = D / 4;           // dims per thread
+  const int part = threadIdx.x & 3;
+  const int j = threadIdx.x >> 2;      // dp <= kMaxDp = 64 outputs
+  const float* wr = Wl + (int64_t)min(j, dp - 1) * D + part * QD;
+  float4 wv[QD / 4];
+  uint4 qv[QD / 8];
+#pragma unroll
+  for (int k = 0; k < QD / 4; ++k) wv[k] = *(const float4*)(wr + 4 * k);
+#pragma unroll
+  for (int k = 0; k < QD / 8; ++k) qv[k] = *(const uint4*)(qp + part * QD + 8 * k);
   float v[kMaxDp];
   {
     const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + (live ? S : 0);
 #pragma unroll
-    for (int j = 0; j < kMaxDp; ++j) v[j] = sp[(int64_t)min(j, dp - 1) * bm.s_pad];   // in range
-#pragma unroll
-    for (int j = 0; j < kMaxDp; ++j) v[j] = (live && j < dp) ? v[j] : 0.f;
+    for (int jj = 0; jj < kMaxDp; ++jj) v[jj] = sp[(int64_t)min(jj, dp - 1) * bm.s_pad];   // in range
   }
-  // u = W^(l,h) q^(l,h), fp32: 4 threads per output, each over D/4 dims;
-  // the thread's W row slice and q slice are loaded with 16-byte loads, all
-  // issued together (with the key loads still in flight)
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
   {
-    const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
-    const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
-    const int qd = D >> 2, part = threadIdx.x & 3;
-    const int j = threadIdx.x >> 2;   // dp <= kMaxDp = 64 outputs
     float acc = 0.f;
-    if (D == 128) {
-      float4 wv[8];
-      uint4 qv[4];
-      const float* wr = Wl + (int64_t)min(j, dp - 1) * D + part * 32;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) wv[k] = *(const float4*)(wr + 4 * k);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qv[k] = *(const uint4*)(qp + part * 32 + 8 * k);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t q0 = (k & 1) ? qv[k >> 1].z : qv[k >> 1].x;
-        const uint32_t q1 = (k & 1) ? qv[k >> 1].w : qv[k >> 1].y;
-        acc += wv[k].x * __uint_as_float(q0 << 16) + wv[k].y * __uint_as_float(q0 & 0xffff0000u) +
-               wv[k].z * __uint_as_float(q1 << 16) + wv[k].w * __uint_as_float(q1 & 0xffff0000u);
-      }
-    } else {
-      const float* wr = Wl + (int64_t)min(j, dp - 1) * D + part * qd;
-      const bf16_t* qq = qp + part * qd;
-      for (int d = 0; d < qd; ++d) acc += wr[d] * bf16_to_f32(qq[d]);
+    for (int k = 0; k < QD / 4; ++k) {
+      const uint32_t q0 = (k & 1) ? qv[k >> 1].z : qv[k >> 1].x;
+      const uint32_t q1 = (k & 1) ? qv[k >> 1].w : qv[k >> 1].y;
+      acc += wv[k].x * __uint_as_float(q0 << 16) + wv[k].y * __uint_as_float(q0 & 0xffff0000u) +
+             wv[k].z * __uint_as_float(q1 << 16) + wv[k].w * __uint_as_float(q1 & 0xffff0000u);
     }
     acc += __shfl_xor(acc, 1);
     acc += __shfl_xor(acc, 2);
-    if (part == 0 && j < dp) s_u[j] = acc;
+    if (part == 0) s_u[j] = (j < dp) ? acc : 0.f;   // entries past d' are zero
   }
   __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < kMaxDp; ++jj) v[jj] = (live && jj < dp) ? v[jj] : 0.f;
   if (wi >= a.Wd) return;
   uint64_t* mrow = a.mask + row * a.Wd;
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
@@ -475,7 +470,10 @@ __global__ __launch_bounds__(256) void calibrate_kernel(const CalibArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nchunk = (a.Wd + 3) >> 2;
   const int nbh8 = (a.B * a.Hq + 7) / 8;
-  hipLaunchKernelGGL(route_kernel, dim3(nbh8 * 8 * nchunk, a.layer_count), dim3(256), 0, st, a);
+  const dim3 grid(nbh8 * 8 * nchunk, a.layer_count);
+  if (a.D == 128) hipLaunchKernelGGL(route_kernel<128>, grid, dim3(256), 0, st, a);
+  else if (a.D == 64) hipLaunchKernelGGL(route_kernel<64>, grid, dim3(256), 0, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
