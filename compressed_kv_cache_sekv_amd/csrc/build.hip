@@ -251,7 +251,8 @@ __global__ __launch_bounds__(256) void summaries_kernel(const PackArgs a) {
     const float* w = a.W + (((int64_t)l * a.Hq + hh) * a.dp + j) * D;
     double acc = 0.0;
     for (int d = 0; d < D; ++d) acc += (double)w[d] * s_k[wave][d];
-    a.s[bm.s_base + (((int64_t)l * a.Hq + hh) * a.dp + j) * bm.s_pad + S] = (float)acc;
+    const int d4 = dp_pad4(a.dp);
+    a.s[bm.s_base + ((int64_t)l * a.Hq + hh) * d4 * bm.s_pad + skey_index(S, j, d4)] = (float)acc;
   }
 }
 

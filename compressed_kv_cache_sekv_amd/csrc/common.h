@@ -78,12 +78,21 @@ struct Blob {
 };
 
 // Per-sequence metadata (device copy used by every kernel).
+// Summary keys s of one (b, l, h): s_pad span slots x d4 = d' rounded up to 4
+// dims (zeros past d'), in blocks of 64 spans x 4 dims: lane S % 64 of a
+// routing wave reads its span's 4 dims as one 16-byte load, and the wave's
+// 64 loads are 1 KB contiguous.
+__host__ __device__ inline int dp_pad4(int dp) { return (dp + 3) & ~3; }
+__host__ __device__ inline int64_t skey_index(int S, int j, int d4) {
+  return ((int64_t)(S >> 6) * (d4 >> 2) + (j >> 2)) * 256 + (S & 63) * 4 + (j & 3);
+}
+
 struct BMeta {
   int32_t n_spans;      // N_S(b)
   int32_t n_raw;        // N_raw(b)
   int32_t n_res;        // N_raw + N_S
   int32_t n_res_pad;    // n_res rounded up to 64
-  int32_t s_pad;        // N_S rounded up to 64 (stride of s rows)
+  int32_t s_pad;        // N_S rounded up to 64 (span slots of one (l, h) of s)
   int32_t pad_;
   int64_t span_base;    // first span of b in the span tables
   int64_t raw_base;     // first raw token of b in raw_pos

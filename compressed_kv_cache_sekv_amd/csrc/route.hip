@@ -113,11 +113,15 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   for (int k = 0; k < QD / 4; ++k) wv[k] = *(const float4*)(wr + 4 * k);
 #pragma unroll
   for (int k = 0; k < QD / 8; ++k) qv[k] = *(const uint4*)(qp + part * QD + 8 * k);
-  float v[kMaxDp];
+  // the lane's span's summary key, 4 dims per 16-byte load (clamped in
+  // range; dims past d' meet zeros of u)
+  float4 v4[kMaxDp / 4];
   {
-    const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * dp * bm.s_pad + (live ? S : 0);
+    const int d4 = dp_pad4(dp);
+    const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * d4 * bm.s_pad;
+    const int Sc = live ? S : 0;
 #pragma unroll
-    for (int jj = 0; jj < kMaxDp; ++jj) v[jj] = sp[(int64_t)min(jj, dp - 1) * bm.s_pad];   // in range
+    for (int k = 0; k < kMaxDp / 4; ++k) v4[k] = *(const float4*)(sp + skey_index(Sc, 4 * min(k, (d4 >> 2) - 1), d4));
   }
   __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
   {
@@ -134,8 +138,6 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
     if (part == 0) s_u[j] = (j < dp) ? acc : 0.f;   // entries past d' are zero
   }
   __syncthreads();
-#pragma unroll
-  for (int jj = 0; jj < kMaxDp; ++jj) v[jj] = (live && jj < dp) ? v[jj] : 0.f;
   if (wi >= a.Wd) return;
   uint64_t* mrow = a.mask + row * a.Wd;
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
@@ -145,11 +147,11 @@ __global__ __launch_bounds__(256) void route_kernel(const RouteArgs a) {
   if (live) {
     float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
-    for (int j = 0; j < kMaxDp; j += 4) {
-      d0 += s_u[j] * v[j];
-      d1 += s_u[j + 1] * v[j + 1];
-      d2 += s_u[j + 2] * v[j + 2];
-      d3 += s_u[j + 3] * v[j + 3];
+    for (int k = 0; k < kMaxDp / 4; ++k) {
+      d0 += s_u[4 * k] * v4[k].x;
+      d1 += s_u[4 * k + 1] * v4[k].y;
+      d2 += s_u[4 * k + 2] * v4[k].z;
+      d3 += s_u[4 * k + 3] * v4[k].w;
     }
     const float dot = (d0 + d1) + (d2 + d3);
     alpha = 1.f / (1.f + expf(-dot));

@@ -249,7 +249,7 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
     sb += m.n_spans;
     rb += m.n_raw;
     res += (int64_t)x->L * x->Hkv * m.n_res_pad * x->D;
-    sel += (int64_t)x->L * x->Hq * x->dp * m.s_pad;
+    sel += (int64_t)x->L * x->Hq * dp_pad4(x->dp) * m.s_pad;
     x->max_spans = std::max(x->max_spans, m.n_spans);
     x->max_raw = std::max(x->max_raw, m.n_raw);
   }
@@ -702,7 +702,8 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
     for (int lh = 0; lh < L * Hq; ++lh)
       for (int j = 0; j < dp; ++j)
         for (int S = 0; S < NS; ++S)
-          s[m.s_base + ((int64_t)lh * dp + j) * m.s_pad + S] = h->s[so + ((int64_t)lh * dp + j) * NS + S];
+          s[m.s_base + (int64_t)lh * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))] =
+              h->s[so + ((int64_t)lh * dp + j) * NS + S];
     so += (int64_t)L * Hq * dp * NS;
     for (int S = 0; S < NS; ++S) logn[m.span_base + S] = logf((float)lens[m.span_base + S]);
     for (int l = 0; l < L; ++l)
@@ -810,7 +811,8 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
       for (int lh = 0; lh < L * Hq; ++lh)
         for (int j = 0; j < dp; ++j)
           for (int S = 0; S < NS; ++S)
-            h->s[so + ((int64_t)lh * dp + j) * NS + S] = s[m.s_base + ((int64_t)lh * dp + j) * m.s_pad + S];
+            h->s[so + ((int64_t)lh * dp + j) * NS + S] =
+                s[m.s_base + (int64_t)lh * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))];
     so += (int64_t)L * Hq * dp * NS;
     for (int l = 0; want_fac && l < L; ++l)
       for (int g = 0; g < Hkv; ++g) {
