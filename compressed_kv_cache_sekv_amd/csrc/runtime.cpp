@@ -52,10 +52,10 @@ constexpr uint32_t CTX_MAGIC = 0x53454b43u;   // "SEKC"
 constexpr uint32_t IDX_MAGIC = 0x53454b49u;   // "SEKI"
 constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
 
-// Work decomposition of the decode kernel: resident 64-row tiles per
-// workgroup (default 4, one per wave) and spans per factored workgroup
-// (default 32: ceil(N_S / 32) workgroups share a KV head's routed union).
-// SEKV_TILES_PER_ITEM / SEKV_SPANS_PER_ITEM override them when an index is
+// Work decomposition of the decode kernel: at most this many resident 32-row
+// steps (default 8, two per wave) and compressed spans of the sequence
+// (default 32) per workgroup; the larger count sets the items of a KV head.
+// SEKV_STEPS_PER_ITEM / SEKV_SPANS_PER_ITEM override them when an index is
 // created (tuning).
 int env_int(const char* name, int dflt, int lo, int hi) {
   const char* v = getenv(name);
