@@ -148,6 +148,47 @@ def test_decode_identical_index(ctx, sl, name):
     idx.free()
 
 
+def _case_with_all_raw_sequence():
+    """Two 8B-shaped sequences at 4K; the second has a surprisal spike every
+    6th token (10, else 0: mu + 2 sigma = 9.1 < 10), so every run between
+    anchors is shorter than l_min and the sequence has no compressed span."""
+    w = W8["llama8b_l1_32k"].scaled(T=4096, B=2)
+    H, K, V, W, gates = SC.make_inputs(w)
+    H = H.clone()
+    H[1] = torch.where(torch.arange(w.T) % 6 == 0, torch.tensor(10.0), torch.tensor(0.0))
+    idxs = [O.build_index_b(H[b].numpy(), K[b].double().numpy(), V[b].double().numpy(), W.double().numpy(),
+                            None if gates is None else gates[b].double().numpy(), R=w.R,
+                            alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=w.Hq) for b in range(w.B)]
+    return SC.Case(w, H, K, V, W, gates, idxs, SC.oracle_calibrated_tau(w, idxs, W))
+
+
+def test_decode_sequence_without_spans(ctx, sl):
+    c = _case_with_all_raw_sequence()
+    w = c.w
+    assert c.idxs[0].n_spans > 0 and c.idxs[1].n_spans == 0 and c.idxs[1].n_raw == w.T
+    # the library's own split agrees
+    built = ctx.build_index(sl.build_params(w), dev(c.K), dev(c.V), dev(c.H), dev(c.W),
+                            None if c.gates is None else dev(c.gates))
+    assert list(built.n_spans) == [c.idxs[0].n_spans, 0] and list(built.n_raw) == [c.idxs[0].n_raw, w.T]
+    built.free()
+    idx = imported(ctx, sl, c)
+    q = c.q(0)
+    alpha_o, z_o = oracle_route_all(c, q, c.tau)
+    words, _ = gpu_route(idx, c, q, c.tau)
+    bad = 0
+    for (b, l, h), z in z_o.items():
+        m, _, _ = SC.compare_masks(words[b, l, h], z, alpha_o[(b, l, h)], c.tau[l, h])
+        bad += m
+    assert bad == 0
+    assert not words[1].any()
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words))
+    worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+    print(f"[no-span sequence] N_S {[i.n_spans for i in c.idxs]}, worst rel-L2 {worst:.3e}")
+    assert worst <= SC.REL_L2
+    idx.free()
+
+
 @pytest.mark.parametrize("tau_val", [-math.inf, math.inf])
 def test_decode_all_or_nothing(ctx, sl, tau_val):
     c = case("8b_4k")
