@@ -667,7 +667,8 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   using MS = MergeShape<D, G>;
   constexpr int DS = MS::DS, NPL = MS::NPL;
-  constexpr int CH = 32;                       // partials per wave per round trip
+  constexpr int CH = 24;                       // partials per wave per round trip (2 loads each:
+                                               // at most 63 loads in flight per wave)
   static_assert(NPL == 1 || NPL == 2, "merge lane layout");
   __shared__ float s_o[4][G * DS];
   __shared__ float s_m[4][G], s_l[4][G];
@@ -685,15 +686,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     float mv[CH], lv[CH], v0[CH], v1[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
+      // branch-free: partials past P re-read partial P - 1 and are ignored
       const int i = c0 + 4 * c;
-      const float* p = base + i * pstride + h * (D + 2);
       const bool ok = i < P;
-      mv[c] = ok ? p[D] : -INFINITY;
-      lv[c] = ok ? p[D + 1] : 0.f;
+      const float* p = base + min(i, P - 1) * pstride + h * (D + 2);
+      const float2 ml = *(const float2*)(p + D);
+      mv[c] = ok ? ml.x : -INFINITY;
+      lv[c] = ok ? ml.y : 0.f;
       if (NPL == 2) {
-        const float2 v = ok ? *(const float2*)(p + dim) : float2{0.f, 0.f};
-        v0[c] = v.x;
-        v1[c] = v.y;
+        const float2 v = *(const float2*)(p + dim);
+        v0[c] = ok ? v.x : 0.f;
+        v1[c] = ok ? v.y : 0.f;
       } else {
         v0[c] = ok ? p[dim] : 0.f;
         v1[c] = 0.f;
