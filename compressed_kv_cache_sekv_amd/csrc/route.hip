@@ -199,6 +199,30 @@ __device__ int block_scan256_total(int v, int* s_tmp, int& total) {
   return v + add;
 }
 
+// Block-wide inclusive scan of one count per thread (256 threads, counts
+// below 2^BITS): wave prefixes by bit-sliced ballots, wave totals through
+// s_tmp (4 ints; callers alternate two buffers between consecutive calls, so
+// one barrier suffices).
+template <int BITS>
+__device__ __forceinline__ int block_scan_small(int v, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t le = (2ull << lane) - 1;   // lanes <= lane
+  int incl = 0, wt = 0;
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) {
+    const uint64_t bal = __ballot((v >> i) & 1);
+    incl += (int)__popcll(bal & le) << i;
+    wt += (int)__popcll(bal) << i;
+  }
+  if (lane == 0) s_tmp[wave] = wt;
+  __syncthreads();
+  int add = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) add += (w < wave) ? s_tmp[w] : 0;
+  total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  return incl + add;
+}
+
 __device__ __forceinline__ float f4_at(const float4& v, int c) {
   return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
 }
@@ -295,7 +319,8 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   const int nh = 2 * a.Wd;
   int nc = 0;
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int base = 0; base < nh; base += 256) {
+  int par = 0;
+  for (int base = 0; base < nh; base += 256, par ^= 1) {
     const int t = min(base + tid, nh - 1);
     const uint64_t word = mrow[t >> 1];
     const float4* ap = (const float4*)(arow + 32 * (int64_t)t);
@@ -305,7 +330,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
     const uint32_t bits = (base + tid < nh) ? (uint32_t)(word >> (32 * (t & 1))) : 0u;
     const int c = __popc(bits);
     int total;
-    const int incl = block_scan256_total(c, s_tmp, total);
+    const int incl = block_scan_small<6>(c, s_tmp + 4 * par, total);
     int pos = nc + incl - c;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
@@ -322,11 +347,8 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   if (nc <= a.cap) return;
   if (nc <= kCapList) {
     // range of the candidates' alpha bits
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, d));
-      hi = max(hi, (uint32_t)__shfl_xor((int)hi, d));
-    }
+    lo = __reduce_min_sync(~0ull, lo);
+    hi = __reduce_max_sync(~0ull, hi);
     if (lane == 0) {
       s_rng[wave] = lo;
       s_rng[4 + wave] = hi;
@@ -348,7 +370,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       tot += cnt[e];
     }
     int total;
-    const int inc = block_scan256_total(tot, s_tmp, total);
+    const int inc = block_scan_small<12>(tot, s_tmp + 4 * par, total);   // tot <= kCapList
     const int exc = inc - tot;
     if (exc < a.cap && a.cap <= inc) {   // exactly one thread holds K*
       int cum = exc;
