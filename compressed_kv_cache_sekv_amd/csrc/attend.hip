@@ -28,6 +28,8 @@
 // inside this kernel would need a device-scope release per workgroup, which
 // on this GPU writes back the XCD's L2 each time; the kernel boundary is the
 // cheaper synchronisation.)
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace sekv {
@@ -780,7 +782,8 @@ hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
   });
 }
 
-hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st) {
+hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
   if (a.W > 1024) return hipErrorInvalidValue;
   return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
@@ -793,7 +796,11 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
       const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), dyn, st, a);
+    if (ev_start)
+      hipExtLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), (uint32_t)dyn, st, ev_start, ev_stop, 0u,
+                            a);
+    else
+      hipLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), dyn, st, a);
     return hipGetLastError();
   });
 }

@@ -188,7 +188,10 @@ struct GatherArgs {
 };
 
 // ------------------------------------------------------------ launchers ---
-hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st);
+// With ev_start / ev_stop the launch records them in its dispatch packet
+// (hipExtLaunchKernel): their interval is the kernel's own execution.
+hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st);

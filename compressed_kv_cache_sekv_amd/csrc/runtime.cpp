@@ -113,6 +113,20 @@ struct Timer {
     return hipEventRecord(ev[*slot], st);
   }
   hipError_t end(hipStream_t st, size_t slot) { return hipEventRecord(ev[slot + 1], st); }
+  // two events for a launch that records them itself
+  hipError_t reserve(size_t* slot) {
+    if (used + 2 > ev.size()) {
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t e;
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return r;
+        ev.push_back(e);
+      }
+    }
+    *slot = used;
+    used += 2;
+    return hipSuccess;
+  }
   hipError_t drain(double* ms, int64_t* n) {
     double t = 0.0;
     for (size_t i = 0; i < used; i += 2) {
@@ -1033,9 +1047,12 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   aa.scale = 1.0f / sqrtf((float)x->D);
   if (n_items > 0) {
     size_t slot = 0;
-    if (c->timing) HIP_TRY(c->t_attend.begin(c->stream, &slot));
-    HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
-    if (c->timing) HIP_TRY(c->t_attend.end(c->stream, slot));
+    if (c->timing) {
+      HIP_TRY(c->t_attend.reserve(&slot));
+      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream, c->t_attend.ev[slot], c->t_attend.ev[slot + 1]));
+    } else {
+      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
+    }
   }
   MergeArgs mg{};
   mg.part = (const float*)x->d_part.p;

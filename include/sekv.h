@@ -278,9 +278,11 @@ sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
 /* --------------------------------------------------------- instrumentation */
 
 /* Kernel timing.  While enabled, every sekv_route call brackets its routing
- * kernel and every sekv_decode_attend call brackets its attention kernel (not
- * the partial merge) with HIP events on the context stream; nothing is
- * synchronised.  sekv_timing_read synchronises those events, returns the summed
+ * kernels with HIP events on the context stream, and every sekv_decode_attend
+ * call times its attention kernel (not the partial merge) with HIP events that
+ * the launch itself records in its dispatch packet (hipExtLaunchKernel), so
+ * their interval is the kernel's execution without the dispatch gap; nothing
+ * is synchronised.  sekv_timing_read synchronises those events, returns the summed
  * milliseconds and launch counts since the previous read (or since enabling),
  * and starts a new period.  Any output pointer may be NULL. */
 sekv_status sekv_timing_enable(sekv_ctx* ctx, int32_t enable);
