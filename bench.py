@@ -372,7 +372,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         t0 = time.time()
         pidx = ctx.build_index(sl.build_params(w, tier=sl.TIER_PINNED_HOST), K, V, H, W, gates)
-        log(f"[bench] pinned-tier index built in {time.time() - t0:.2f} s")
+        pbuild_s = time.time() - t0
+        log(f"[bench] pinned-tier index built in {pbuild_s:.2f} s")
         psteps = min(4, args.steps)
         pb = pc = 0
         pms = 0.0
@@ -387,7 +388,7 @@ def main(argv=None):
                 pms += st.pcie_ms
         torch.cuda.synchronize()
         wall = time.time() - t0
-        result["pcie"] = {"steps": psteps, "bytes_per_step": int(pb / psteps),
+        result["pcie"] = {"build_s": round(pbuild_s, 3), "steps": psteps, "bytes_per_step": int(pb / psteps),
                           "copies_per_step": int(pc / psteps), "copy_ms_per_step": round(pms / psteps, 3),
                           "GB_per_s": round(pb / (pms / 1e3) / 1e9, 2) if pms > 0 else None,
                           "query_tokens_per_s_incl_pcie": round(B * psteps / wall, 3)}

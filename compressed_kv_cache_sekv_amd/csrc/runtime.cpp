@@ -608,25 +608,55 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   pa.oversample = p->oversample; pa.power_iters = p->power_iters; pa.seed = p->seed;
   HIP_TRY(launch_pack_raw(pa, stream));
   HIP_TRY(launch_summaries(pa, stream));
-  DBuf stage;
-  struct Rel1 { DBuf* b; ~Rel1() { b->release(); } } rel1{&stage};
-  if (x->tier == SEKV_TIER_PINNED_HOST) {
-    HIP_TRY(dalloc(stage, (size_t)x->layer_bytes));
-  }
-  for (int l = 0; l < p->L; ++l) {
-    pa.layer = l;
-    if (x->tier == SEKV_TIER_HBM) {
+  if (x->tier == SEKV_TIER_HBM) {
+    for (int l = 0; l < p->L; ++l) {
+      pa.layer = l;
       pa.pool = (uint8_t*)x->d_pool.p + (size_t)l * x->layer_bytes;
       HIP_TRY(launch_rsvd(pa, stream));
-    } else {
-      pa.pool = (uint8_t*)stage.p;
-      HIP_TRY(hipMemsetAsync(stage.p, 0, stage.n, stream));
-      HIP_TRY(launch_rsvd(pa, stream));
-      HIP_TRY(hipMemcpyAsync(x->h_pool + (size_t)l * x->layer_bytes, stage.p, (size_t)x->layer_bytes,
-                             hipMemcpyDeviceToHost, stream));
     }
+    HIP_TRY(hipStreamSynchronize(stream));
+  } else {
+    // pinned tier: layer l's factors go to HBM stage l % 2 and are copied to
+    // the pinned pool on a second stream while layer l + 1 is factored into
+    // the other stage (blob padding is the same in every layer, so the stages
+    // are cleared once)
+    struct Overlap {
+      DBuf stage[2];
+      hipStream_t copy = nullptr;
+      hipEvent_t done[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
+      ~Overlap() {
+        if (copy) (void)hipStreamSynchronize(copy);
+        for (int k = 0; k < 2; ++k) {
+          if (done[k]) (void)hipEventDestroy(done[k]);
+          if (copied[k]) (void)hipEventDestroy(copied[k]);
+          stage[k].release();
+        }
+        if (copy) (void)hipStreamDestroy(copy);
+      }
+    } ov;
+    const int nst = p->L > 1 ? 2 : 1;
+    for (int k = 0; k < nst; ++k) {
+      HIP_TRY(dalloc(ov.stage[k], (size_t)x->layer_bytes));
+      HIP_TRY(hipMemsetAsync(ov.stage[k].p, 0, ov.stage[k].n, stream));
+      HIP_TRY(hipEventCreateWithFlags(&ov.done[k], hipEventDisableTiming));
+      HIP_TRY(hipEventCreateWithFlags(&ov.copied[k], hipEventDisableTiming));
+    }
+    HIP_TRY(hipStreamCreateWithFlags(&ov.copy, hipStreamNonBlocking));
+    for (int l = 0; l < p->L; ++l) {
+      const int k = l % nst;
+      pa.layer = l;
+      pa.pool = (uint8_t*)ov.stage[k].p;
+      if (l >= nst) HIP_TRY(hipStreamWaitEvent(stream, ov.copied[k], 0));   // stage k drained
+      HIP_TRY(launch_rsvd(pa, stream));
+      HIP_TRY(hipEventRecord(ov.done[k], stream));
+      HIP_TRY(hipStreamWaitEvent(ov.copy, ov.done[k], 0));
+      HIP_TRY(hipMemcpyAsync(x->h_pool + (size_t)l * x->layer_bytes, ov.stage[k].p, (size_t)x->layer_bytes,
+                             hipMemcpyDeviceToHost, ov.copy));
+      HIP_TRY(hipEventRecord(ov.copied[k], ov.copy));
+    }
+    HIP_TRY(hipStreamSynchronize(ov.copy));
+    HIP_TRY(hipStreamSynchronize(stream));
   }
-  HIP_TRY(hipStreamSynchronize(stream));
   guard.x = nullptr;
   *out = x;
   return SEKV_OK;

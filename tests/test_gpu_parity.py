@@ -266,6 +266,35 @@ def test_pinned_tier_matches_hbm(ctx, sl):
     pin.free()
 
 
+def test_pinned_build_matches_hbm(ctx, sl):
+    """The pinned-tier build (factor layers staged through two HBM buffers and
+    copied to the pinned pool on a second stream while the next layer is
+    factored) stores exactly the factors of the HBM-tier build, and decodes to
+    the same outputs."""
+    w = W8["llama8b_l32_128k"].scaled(L=3, T=8192)
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, l, "cuda") for l in range(w.L)])
+    hbm = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM), K, V, H, W, None)
+    pin = ctx.build_index(sl.build_params(w, tier=sl.TIER_PINNED_HOST, ring_bytes=1 << 27), K, V, H, W, None)
+    eh, ep = hbm.export(), pin.export()
+    for k in eh:
+        assert np.array_equal(eh[k], ep[k]), k
+    q = synth.query(w, 0, "cuda")
+    tau = torch.full((w.L, w.Hq), 0.5, device="cuda")
+    mask = torch.zeros(w.B, w.L, w.Hq, hbm.mask_words, dtype=torch.int64, device="cuda")
+    hbm.route(0, w.L, q, tau, 0, mask, None)
+    outs = []
+    for idx in (hbm, pin):
+        out = torch.zeros(w.B, w.L, w.Hq, w.d, device="cuda")
+        idx.decode_attend(0, w.L, q, mask, out)
+        outs.append(out.cpu())
+    torch.cuda.synchronize()
+    assert int(mask.count_nonzero()) > 0
+    assert torch.equal(outs[0], outs[1])
+    hbm.free()
+    pin.free()
+
+
 def test_pinned_ring_too_small(ctx, sl):
     c = case("tiny")
     pin = imported(ctx, sl, c, tier=1, ring_bytes=4096)
