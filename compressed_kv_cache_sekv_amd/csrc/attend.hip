@@ -22,8 +22,11 @@
 // bf16 MFMA (softmax weights, scaled t, gated w) are split hi + lo into two
 // bf16 terms, which keeps ~16 mantissa bits; every accumulation is fp32.
 //
-// A span's factor blob is loaded in one round trip (all its loads issued
-// before any arithmetic).  Each workgroup writes one softmax partial
+// A span's factor blob, with the second 64-token chunk of its left factors,
+// is loaded in one round trip (all its loads issued before any arithmetic;
+// V^V and that chunk go to LDS).  Each wave takes its spans longest first,
+// from a greedy assignment every wave computes alike from the span lengths,
+// so results do not depend on timing.  Each workgroup writes one softmax partial
 // (m, l, o) per head; merge_kernel combines them.  (A last-workgroup merge
 // inside this kernel would need a device-scope release per workgroup, which
 // on this GPU writes back the XCD's L2 each time; the kernel boundary is the

@@ -104,8 +104,6 @@ struct BMeta {
                         // (b, l, g) starts at l * layer_bytes + pool_base + g * pool_lg
 };
 
-// Partials one merge can combine: items of a (b, g) times G (LDS bound).
-constexpr int kMaxMergeWeights = 2048;
 // Routed spans one work item may take (one per lane of a wave).
 constexpr int kMaxSpanList = 64;
 // Mask words per (b, l, h) the decode kernel handles (65536 spans).
