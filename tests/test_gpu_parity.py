@@ -33,6 +33,9 @@ CASE_SPECS = {
     "8b_32k": _wl("llama8b_l1_32k"),                      # full config-2 size
     "70b_b2": _wl("llama70b_b32_64k", B=2, T=8192),       # config-5 shape, 2 sequences
     "8b_l2_cap": _wl("llama8b_l32_128k", L=2, T=16384),   # config-3 shape with the cap
+    # the other GQA group sizes the kernels are built for (G = 1, 2; d = 64)
+    "g1_4k": _wl("llama8b_l1_32k", T=4096, Hq=8, Hkv=8),
+    "g2_d64_4k": _wl("llama8b_l1_32k", T=4096, Hq=16, Hkv=8, d=64),
 }
 _CACHE = {}
 
@@ -106,7 +109,7 @@ def test_import_export_roundtrip(ctx, sl):
     idx.free()
 
 
-@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2"])
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2", "g1_4k", "g2_d64_4k"])
 def test_route_identical_index(ctx, sl, name):
     c = case(name)
     idx = imported(ctx, sl, c)
@@ -129,7 +132,7 @@ def test_route_identical_index(ctx, sl, name):
     idx.free()
 
 
-@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2"])
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "8b_32k", "70b_b2", "g1_4k", "g2_d64_4k"])
 def test_decode_identical_index(ctx, sl, name):
     c = case(name)
     w = c.w
