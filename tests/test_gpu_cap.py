@@ -133,3 +133,29 @@ def test_cap_selection_paths(setup):
     assert paths.get("global", 0) >= 1
     assert paths.get("bin-whole", 0) + paths.get("bin-rank", 0) >= 1
     assert paths.get("radix", 0) >= 1
+
+
+def test_cap_repeated_calls(setup):
+    """The cap over the library's own alpha scratch, in consecutive calls whose
+    queries differ: each call's capped mask must follow that call's alpha,
+    never values left in the scratch by the call before."""
+    w, idx = setup
+    n = int(idx.n_spans[0])
+    cap = int(np.floor(w.cap_frac * n))
+    ref = []
+    for s in (0, 1, 2):
+        q = synth.query(w, s, "cuda")
+        _, a_all = _route(idx, w, q, np.full(w.Hq, -np.inf), 0)
+        tau = np.array([_tau_kth(a_all[0, 0, h, :n], int(0.2 * n)) for h in range(w.Hq)])
+        pre, a0 = _route(idx, w, q, tau, 0)
+        exp = [_expected(a0[0, 0, h, :n], SC.unpack_mask(pre[0, 0, h], n), cap) for h in range(w.Hq)]
+        ref.append((q, torch.as_tensor(tau, dtype=torch.float32).reshape(1, w.Hq).cuda(), exp))
+    mask = torch.zeros(w.B, 1, w.Hq, idx.mask_words, dtype=torch.int64, device="cuda")
+    for rep in range(3):
+        for i, (q, tau, exp) in enumerate(ref):
+            idx.route(0, 1, q, tau, cap, mask, None)
+            torch.cuda.synchronize()
+            got = mask.cpu().numpy().view(np.uint64)
+            for h in range(w.Hq):
+                assert np.array_equal(SC.unpack_mask(got[0, 0, h], n), exp[h]), (rep, i, h)
+    print(f"[cap paths] 9 consecutive capped calls over 3 queries: all {w.Hq} heads exact", flush=True)
