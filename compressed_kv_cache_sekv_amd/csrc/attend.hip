@@ -776,6 +776,21 @@ bool attend_supported(int D, int G, int R) {
          (R == 16 || R == 32 || R == 64) && R <= D;
 }
 
+hipError_t attend_slots(int D, int G, int R, int W, int device, int* slots) {
+  *slots = 0;
+  return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
+    constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
+    int per_cu = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<D_, G_, R_>, 256,
+                                                                attend_dyn_lds(G_, W));
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return e;
+    *slots = per_cu * cus;
+    return hipSuccess;
+  });
+}
+
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
   return dispatch(D, G, 16, [&](auto d_, auto g_, auto) -> hipError_t {
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value;

@@ -195,6 +195,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st);
 bool attend_supported(int D, int G, int R);
+// Workgroups of the attention kernel for (D, G, R) with W mask words that the
+// device can hold resident at once (CUs x workgroups per CU).
+hipError_t attend_slots(int D, int G, int R, int W, int device, int* slots);
 
 struct SplitArgs {
   const float* H;           // [B][T]

@@ -54,9 +54,11 @@ constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
 
 // Work decomposition of the decode kernel: at most this many resident 32-row
 // steps (default 8, two per wave) and compressed spans of the sequence
-// (default 32) per workgroup; the larger count sets the items of a KV head.
-// SEKV_STEPS_PER_ITEM / SEKV_SPANS_PER_ITEM override them when an index is
-// created (tuning).
+// (default 32) per workgroup; the larger count sets the items of a KV head,
+// raised (SEKV_FILL_SLOTS, default on) until the items fill the attention
+// kernel's resident workgroup slots, keeping at least kMinFillSpans spans of
+// the sequence per item.  SEKV_STEPS_PER_ITEM / SEKV_SPANS_PER_ITEM /
+// SEKV_FILL_SLOTS override them when an index is created (tuning).
 int env_int(const char* name, int dflt, int lo, int hi) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
@@ -65,6 +67,8 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 }
 int steps_per_item() { return env_int("SEKV_STEPS_PER_ITEM", 8, 1, 1 << 20); }
 int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 32, 1, kMaxSpanList); }
+bool fill_slots() { return env_int("SEKV_FILL_SLOTS", 1, 0, 1) != 0; }
+constexpr int kMinFillSpans = 16;
 
 // Device buffer owned by the library.
 struct DBuf {
@@ -280,6 +284,17 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   // larger of the two (at most spans_per_item union spans and
   // steps_per_item steps an item)
   const int spi = spans_per_item(), spw = steps_per_item();
+  // workgroups of the attention kernel resident at once on this device: the
+  // items of one launch (one layer) share them out per (b, g).  One wave of
+  // workgroups that fills them measured fastest (items of fewer routed spans
+  // shorten each wave's chain of blob round trips; a second wave of
+  // workgroups costs more than it saves).
+  int fill = 0;
+  if (fill_slots() && attend_supported(x->D, x->G, x->R)) {
+    int slots = 0;
+    HIP_TRY(attend_slots(x->D, x->G, x->R, x->Wd, x->ctx->device, &slots));
+    fill = slots / std::max(1, x->B * x->Hkv);
+  }
   x->items.clear();
   x->bg_first.assign((size_t)2 * x->B * x->Hkv, 0);
   int slot = 0;
@@ -288,7 +303,8 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
     const int nsteps = m.n_res_pad / 32;
     const int nfac = m.n_spans ? (m.n_spans + spi - 1) / spi : 0;
     const int nres = (nsteps + spw - 1) / spw;
-    const int nj = std::max(std::max(nfac, nres), 1);
+    const int nfill = std::min(fill, (m.n_spans + kMinFillSpans - 1) / kMinFillSpans);
+    const int nj = std::max(std::max(std::max(nfac, nres), nfill), 1);
     if ((m.n_spans + nj - 1) / nj > kMaxSpanList || (int64_t)nj * m.n_spans >= (1LL << 31))
       return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d exceed the decode work plan", m.n_spans, b);
     for (int g = 0; g < x->Hkv; ++g) {
