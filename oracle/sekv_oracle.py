@@ -23,7 +23,8 @@ Parity pins (tests/test_oracle_pins.py): full-rank + tau=-inf equals full
 attention; tau=+inf equals full attention over span-mean-replaced rows; brute
 force span split on tiny inputs; SVD against an eigen-decomposition of A^T A;
 routing against the (W^T W) identity and a sign test at tau=0.5; the cap rule
-against brute force; calibration by counting.  Unpinned: absolute decode
+against brute force; the pooled budget against brute force and against the
+per-head cap on a one-head pool; calibration by counting.  Unpinned: absolute decode
 outputs at generic tau (no worked example is printed on the pages); they stand
 on the pinned pieces.
 """
@@ -279,6 +280,32 @@ def route_head(W_h, q_h, s_h, tau: float, cap: int = 0):
         keep[order[:cap]] = True
         z = keep
     return alpha, z
+
+
+def pool_budget(alpha, z, budget: int):
+    """The budget rule of [Tech] (expand in descending alpha until the budget
+    holds) read over a pool instead of one (layer, head): every (layer, head,
+    span) triple of one sequence that a routing call covers.  alpha, z: dicts
+    keyed (b, l, h) -> [N_S(b)] arrays, the pre-budget routing.  For each b,
+    keep the `budget` largest alpha among the routed triples, ties broken
+    toward the lower (l, h, span) position (R26); budget 0 = no budget.
+    Returns the new z dict."""
+    out = {k: np.array(v, bool) for k, v in z.items()}
+    if budget <= 0:
+        return out
+    for b in sorted({k[0] for k in z}):
+        keys = sorted(k for k in z if k[0] == b)
+        cand = [(-float(alpha[k][S]), k[1], k[2], int(S)) for k in keys for S in np.nonzero(z[k])[0]]
+        if len(cand) <= budget:
+            continue
+        cand.sort()
+        kept = {(l, h, S) for _, l, h, S in cand[:budget]}
+        for k in keys:
+            m = np.zeros(len(z[k]), bool)
+            for S in np.nonzero(z[k])[0]:
+                m[S] = (k[1], k[2], int(S)) in kept
+            out[k] = m
+    return out
 
 
 def calibrate_tau(alphas, frac: float) -> float:

@@ -246,6 +246,85 @@ def test_route_cap_brute_force_with_ties(seed):
         assert z.sum() == min(cap, z0.sum()) and not (z & ~z0).any()
 
 
+def _brute_pool(alpha, z, budget):
+    """Every budget-subset of the routed triples of one sequence; the kept set
+    is the one subset that beats every triple it leaves out, comparing alpha
+    first and the lower (l, h, span) position second.  Returns it, checking
+    that exactly one subset has that property."""
+    cand = [(k[1], k[2], int(S)) for k in sorted(z) for S in np.nonzero(z[k])[0]]
+    a = {(k[1], k[2], int(S)): float(alpha[k][S]) for k in z for S in np.nonzero(z[k])[0]}
+
+    def beats(x, y):   # x kept ahead of y
+        return a[x] > a[y] or (a[x] == a[y] and x < y)
+
+    found = []
+    for keep in itertools.combinations(cand, min(budget, len(cand))):
+        ks = set(keep)
+        if all(beats(x, y) for x in ks for y in cand if y not in ks):
+            found.append(ks)
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pool_budget_brute_force_with_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    L, Hq, N, dp, d = 2, 2, 5, 3, 4
+    W = rng.standard_normal((L, Hq, dp, d))
+    q = rng.standard_normal((L, Hq, d))
+    s = rng.standard_normal((L, Hq, dp, N))
+    s[1, 0] = s[0, 1]                      # one head repeats another: equal alphas across heads
+    s[0, 0, :, 3] = s[0, 0, :, 1]          # and within a head
+    q[1, 0] = q[0, 1]
+    W[1, 0] = W[0, 1]
+    alpha, z = {}, {}
+    for l in range(L):
+        for h in range(Hq):
+            alpha[0, l, h], z[0, l, h] = O.route_head(W[l, h], q[l, h], s[l, h], 0.2)
+    total = sum(int(v.sum()) for v in z.values())
+    for budget in range(1, total + 2):
+        zp = O.pool_budget(alpha, z, budget)
+        kept = {(k[1], k[2], int(S)) for k in zp for S in np.nonzero(zp[k])[0]}
+        assert kept == _brute_pool(alpha, z, budget)
+        assert len(kept) == min(budget, total)
+        assert all(not (zp[k] & ~z[k]).any() for k in z)
+
+
+def test_pool_budget_one_head_is_the_cap():
+    rng = np.random.default_rng(7)
+    dp, d, N = 4, 6, 40
+    W = rng.standard_normal((dp, d))
+    q = rng.standard_normal(d)
+    s = rng.standard_normal((dp, N))
+    alpha, z = O.route_head(W, q, s, 0.4)
+    for cap in (1, 3, 7, int(z.sum()) - 1):
+        _, zc = O.route_head(W, q, s, 0.4, cap)
+        zp = O.pool_budget({(0, 0, 0): alpha}, {(0, 0, 0): z}, cap)
+        assert np.array_equal(zp[0, 0, 0], zc)
+
+
+def test_pool_budget_sequences_are_separate_and_monotone():
+    rng = np.random.default_rng(9)
+    B, L, Hq, N = 2, 2, 3, 30
+    alpha = {(b, l, h): rng.random(N) for b in range(B) for l in range(L) for h in range(Hq)}
+    z = {k: v > 0.5 for k, v in alpha.items()}
+    per_b = {b: sum(int(z[k].sum()) for k in z if k[0] == b) for b in range(B)}
+    prev = None
+    for budget in (0, 1, 5, 12, 20, max(per_b.values()), max(per_b.values()) + 3):
+        zp = O.pool_budget(alpha, z, budget)
+        for b in range(B):
+            n = sum(int(zp[k].sum()) for k in zp if k[0] == b)
+            assert n == (per_b[b] if budget == 0 else min(budget, per_b[b]))
+            # every kept alpha of b is at least every dropped one
+            kept = [alpha[k][S] for k in zp if k[0] == b for S in np.nonzero(zp[k])[0]]
+            drop = [alpha[k][S] for k in zp if k[0] == b for S in np.nonzero(z[k] & ~zp[k])[0]]
+            if kept and drop:
+                assert min(kept) >= max(drop)
+        if prev is not None and budget > 0 and prev[0] > 0:
+            assert all(not (prev[1][k] & ~zp[k]).any() for k in z)   # a larger budget keeps a superset
+        prev = (budget, zp)
+
+
 def test_calibrate_tau_counts():
     rng = np.random.default_rng(11)
     a = rng.uniform(0, 1, 1000)
