@@ -198,6 +198,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pinned", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time a HIP graph replay of the step instead of eager launches")
+    ap.add_argument("--pooled", action="store_true",
+                    help="replace the per-(layer, head) cap with one budget per layer pooled over its heads "
+                         "(sekv_route_pooled, budget = cap x query heads); workloads with a cap only")
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill side instead: the index build of one 128K layer (R = 32) and the "
                          "randomized SVD of all its span matrices alone; prints one JSON line")
@@ -264,9 +267,17 @@ def main(argv=None):
     masks = torch.zeros(nsteps, L, B, 1, Hq, Wd, dtype=torch.int64, device=dev)
     outs = [torch.zeros(B, 1, Hq, d, device=dev) for _ in range(L)]
 
+    if args.pooled and cap <= 0:
+        log("[bench] --pooled needs a workload with a cap")
+        return 2
+    budget = cap * Hq if args.pooled else 0
+
     def step(s, ix=idx):
         for l in range(L):
-            ix.route(l, 1, qs[s][l], taus[l], cap, masks[s, l], None)
+            if args.pooled:
+                ix.route_pooled(l, 1, qs[s][l], taus[l], budget, masks[s, l], None)
+            else:
+                ix.route(l, 1, qs[s][l], taus[l], cap, masks[s, l], None)
             ix.decode_attend(l, 1, qs[s][l], masks[s, l], outs[l])
 
     for s in range(args.warmup):
@@ -305,7 +316,10 @@ def main(argv=None):
 
         def gstep():
             for l in range(L):
-                idx.route(l, 1, qbuf[l], taus[l], cap, mbuf[l], None)
+                if args.pooled:
+                    idx.route_pooled(l, 1, qbuf[l], taus[l], budget, mbuf[l], None)
+                else:
+                    idx.route(l, 1, qbuf[l], taus[l], cap, mbuf[l], None)
                 idx.decode_attend(l, 1, qbuf[l], mbuf[l], outs[l])
         gstep()
         torch.cuda.synchronize()
@@ -353,7 +367,8 @@ def main(argv=None):
         "config": {"workload": w.name, "layers": L, "query_heads": Hq, "kv_heads": w.Hkv, "head_dim": d,
                    "batch": B, "context": w.T, "R": w.R, "dprime": w.dprime,
                    "expand_frac_target": w.frac if w.tau is None else None, "tau": w.tau,
-                   "cap": cap, "factor_tier": "hbm", "launch": "per layer: route + decode_attend"},
+                   "cap": 0 if args.pooled else cap, "pooled_budget_per_layer": budget or None,
+                   "factor_tier": "hbm", "launch": "per layer: route + decode_attend"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attend_kernel", "alg_bytes_per_launch": int(per_launch),

@@ -160,6 +160,7 @@ struct RouteArgs {
   float* alpha;             // [B][Lc][Hq][Wd*64] (scratch or caller)
   int32_t layer_begin, layer_count;
   int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
+  int32_t budget;           // pooled budget per sequence (route_pool_kernel)
 };
 
 struct CalibArgs {
@@ -193,6 +194,7 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st);
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_pool(const RouteArgs& a, hipStream_t st);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t st);
 bool attend_supported(int D, int G, int R);
 // Workgroups of the attention kernel for (D, G, R) with W mask words that the

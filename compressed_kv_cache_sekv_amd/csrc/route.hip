@@ -467,6 +467,210 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   }
 }
 
+// Budget pooled over a routing call, one 1024-thread workgroup per sequence b,
+// after route_kernel: among the routed (layer, head, span) triples of b in the
+// call, keep the `budget` largest alpha, ties to the lower (layer, head,
+// span) position (the flat order of the mask words).  The budget rule of the
+// Technical-details section of the SeKV article, read over the whole call
+// instead of one (layer, head).
+//  * Collect: threads take 32-span halves of the mask words in flat order,
+//    each with its 32 alpha as eight 16-byte loads, chunk by chunk; a block
+//    scan of the per-half counts places each routed triple (alpha bits, flat
+//    position) in an LDS list in flat order, and the same sweep builds the
+//    first histogram and counts the triples.  A sequence within its budget
+//    stops there.
+//  * Radix select of the budget-th largest alpha bits (alpha >= 0, so the bits
+//    order like the values): histogram passes of 11, 11 and 10 bits in LDS.
+//  * Keys equal to the selected one are kept lowest position first (a block
+//    scan over the list, or over the halves, in flat order).
+// When the routed triples or the halves do not fit in LDS, every pass sweeps
+// the mask words and alpha in global memory instead.
+constexpr int kPoolThreads = 1024;
+constexpr int kPoolBins = 2048;
+constexpr int kPoolList = 12288;    // routed triples held in LDS
+constexpr int kPoolHalves = 4096;   // 32-span halves of the new mask held in LDS
+
+// Block-wide inclusive scan over kPoolThreads threads; total = block sum.
+__device__ int block_scan_pool(int v, int* s_tmp, int& total) {
+  constexpr int NWV = kPoolThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) s_tmp[wave] = v;
+  __syncthreads();
+  int add = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    const int x = s_tmp[w];
+    add += (w < wave) ? x : 0;
+    tot += x;
+  }
+  total = tot;
+  __syncthreads();
+  return v + add;
+}
+
+// The bin of the k-th largest key in s_hist (nbins bins, descending): thread
+// i holds bins nbins-1-2i and nbins-2-2i; one thread writes (bin, rank of
+// the key within its bin) to s_sel.
+__device__ void pool_pick_bin(const uint32_t* s_hist, int nbins, int k, int* s_tmp, int* s_sel) {
+  const int hi = nbins - 1 - 2 * (int)threadIdx.x, lo = hi - 1;
+  const int chi = (hi >= 0) ? (int)s_hist[hi] : 0;
+  const int clo = (lo >= 0) ? (int)s_hist[lo] : 0;
+  int tot;
+  const int incl = block_scan_pool(chi + clo, s_tmp, tot);
+  const int exc = incl - chi - clo;
+  if (exc < k && k <= incl) {
+    if (exc + chi >= k) {
+      s_sel[0] = hi;
+      s_sel[1] = k - exc;
+    } else {
+      s_sel[0] = lo;
+      s_sel[1] = k - exc - chi;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArgs a) {
+  __shared__ uint32_t s_hist[kPoolBins];
+  __shared__ uint32_t s_key[kPoolList];
+  __shared__ int32_t s_pos[kPoolList];
+  __shared__ uint32_t s_new[kPoolHalves];
+  __shared__ int s_tmp[kPoolThreads / 64];
+  __shared__ int s_sel[2];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t rows = (int64_t)a.layer_count * a.Hq;
+  const int64_t nh = rows * a.Wd * 2;                       // 32-span halves of b's words
+  uint32_t* mh = (uint32_t*)(a.mask + (int64_t)b * rows * a.Wd);
+  const float* ab = a.alpha + (int64_t)b * rows * a.Wd * 64;
+  int k = a.budget;
+  // ---- collect (flat order) + first histogram (top 11 bits)
+  for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
+  __syncthreads();
+  int total = 0;
+  for (int64_t base = 0; base < nh; base += kPoolThreads) {
+    const int64_t t = base + tid;
+    const int64_t tc = t < nh ? t : nh - 1;   // in range; a thread past the end counts nothing
+    const uint32_t bits = t < nh ? mh[tc] : 0u;
+    const float4* ap = (const float4*)(ab + 32 * tc);
+    float4 av[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) av[c] = ap[c];
+    const int cnt = __popc(bits);
+    int chunk;
+    int pos = total + block_scan_pool(cnt, s_tmp, chunk) - cnt;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((bits >> j) & 1u) {
+        const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+        atomicAdd(&s_hist[key >> 21], 1u);
+        if (pos < kPoolList) {
+          s_key[pos] = key;
+          s_pos[pos] = (int32_t)(32 * t + j);
+        }
+        ++pos;
+      }
+    }
+    total += chunk;
+  }
+  __syncthreads();
+  if (total <= k) return;   // uniform: b is within its budget
+  const bool in_lds = total <= kPoolList && nh <= kPoolHalves;
+  // ---- radix select: pass 0 from the collect histogram, then 11 and 10 bits
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 2 ? 1024 : 2048;
+    if (pass > 0) {
+      for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (int i = tid; i < total; i += kPoolThreads) {
+          const uint32_t key = s_key[i];
+          if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+        }
+      } else {
+        for (int64_t t = tid; t < nh; t += kPoolThreads) {
+          const uint32_t bits = mh[t];
+          if (bits == 0u) continue;
+          const float4* ap = (const float4*)(ab + 32 * t);
+          float4 av[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) av[c] = ap[c];
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+            if (((bits >> j) & 1u) && (key & pmask) == prefix)
+              atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    pool_pick_bin(s_hist, nbins, k, s_tmp, s_sel);
+    prefix |= (uint32_t)s_sel[0] << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    k = s_sel[1];
+    __syncthreads();
+  }
+  // prefix is the budget-th largest key; keep every larger key and the k
+  // lowest-position keys equal to it
+  const uint32_t vstar = prefix;
+  int carry = 0;
+  if (in_lds) {
+    for (int i = tid; i < (int)nh; i += kPoolThreads) s_new[i] = 0u;
+    __syncthreads();
+    for (int base = 0; base < total; base += kPoolThreads) {
+      const int i = base + tid;
+      const uint32_t key = i < total ? s_key[i] : 0u;
+      const int eq = (i < total && key == vstar) ? 1 : 0;
+      int chunk;
+      const int rank = carry + block_scan_pool(eq, s_tmp, chunk) - eq;
+      if (i < total && (key > vstar || (eq && rank < k))) {
+        const int p = s_pos[i];
+        atomicOr(&s_new[p >> 5], 1u << (p & 31));
+      }
+      carry += chunk;
+    }
+    __syncthreads();
+    for (int i = tid; i < (int)nh; i += kPoolThreads) mh[i] = s_new[i];
+    return;
+  }
+  for (int64_t base = 0; base < nh; base += kPoolThreads) {
+    const int64_t t = base + tid;
+    uint32_t bits = 0u, keep = 0u, eq = 0u;
+    if (t < nh) {
+      bits = mh[t];
+      if (bits != 0u) {
+        const float4* ap = (const float4*)(ab + 32 * t);
+        float4 av[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) av[c] = ap[c];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+          const bool on = (bits >> j) & 1u;
+          keep |= (uint32_t)(on && key > vstar) << j;
+          eq |= (uint32_t)(on && key == vstar) << j;
+        }
+      }
+    }
+    const int ne = __popc(eq);
+    int chunk;
+    int rank = carry + block_scan_pool(ne, s_tmp, chunk) - ne;
+    for (uint32_t x = eq; x; x &= x - 1) {
+      if (rank < k) keep |= 1u << __builtin_ctz(x);
+      ++rank;
+    }
+    if (t < nh && bits != 0u) mh[t] = keep;
+    carry += chunk;
+  }
+}
+
 // tau^(l,h): midpoint of the k-th and (k+1)-th largest alpha over every
 // (b, span), k = round(frac * N) clipped to [1, N - 1].
 __global__ __launch_bounds__(256) void calibrate_kernel(const CalibArgs a) {
@@ -509,6 +713,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
 
 hipError_t launch_route_cap(const RouteArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(route_cap_kernel, dim3(a.B, a.Hq, a.layer_count), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_pool(const RouteArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(route_pool_kernel, dim3(a.B), dim3(kPoolThreads), 0, st, a);
   return hipGetLastError();
 }
 

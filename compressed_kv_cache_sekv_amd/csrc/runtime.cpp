@@ -945,6 +945,37 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   return SEKV_OK;
 }
 
+extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc, const void* q,
+                                         const float* tau, int32_t budget, uint64_t* mask, float* alpha) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q || !tau || !mask) return fail(SEKV_EINVAL, "null q, tau or mask");
+  if (budget < 0) return fail(SEKV_EINVAL, "budget < 0");
+  if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
+  if ((st = set_device(c))) return st;
+  if ((st = ensure_route_scratch(x, lc))) return st;
+  RouteArgs ra{};
+  ra.q = (const bf16_t*)q;
+  ra.tau = tau;
+  ra.W = (const float*)x->d_W.p;
+  ra.s = (const float*)x->d_s.p;
+  ra.meta = (const BMeta*)x->d_meta.p;
+  ra.mask = mask;
+  ra.alpha = alpha ? alpha : (budget > 0 ? (float*)x->d_alpha.p : nullptr);
+  ra.layer_begin = lb; ra.layer_count = lc;
+  ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
+  ra.cap = 0;
+  ra.budget = budget;
+  size_t slot = 0;
+  if (c->timing) HIP_TRY(c->t_route.begin(c->stream, &slot));
+  HIP_TRY(launch_route(ra, c->stream));
+  if (budget > 0) HIP_TRY(launch_route_pool(ra, c->stream));
+  if (c->timing) HIP_TRY(c->t_route.end(c->stream, slot));
+  return SEKV_OK;
+}
+
 extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
                                           const void* q_cal, float frac, float* tau_out) {
   sekv_index* x = const_cast<sekv_index*>(xc);

@@ -29,7 +29,7 @@ STATUS = {0: "SEKV_OK", 1: "SEKV_EINVAL", 2: "SEKV_ENOMEM", 3: "SEKV_EHIP",
 EXPORTS = ("sekv_create", "sekv_destroy", "sekv_last_error", "sekv_max_spans",
            "sekv_validate_params", "sekv_rsvd_batched", "sekv_build_index", "sekv_index_import", "sekv_index_export",
            "sekv_index_get_info", "sekv_index_counts", "sekv_index_free",
-           "sekv_route", "sekv_calibrate_tau", "sekv_decode_attend",
+           "sekv_route", "sekv_route_pooled", "sekv_calibrate_tau", "sekv_decode_attend",
            "sekv_timing_enable", "sekv_timing_read")
 
 
@@ -95,6 +95,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.sekv_index_free.argtypes = [vp]
     lib.sekv_index_free.restype = None
     lib.sekv_route.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
+    lib.sekv_route_pooled.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
     lib.sekv_calibrate_tau.argtypes = [vp, vp, i32, i32, vp, f32, vp]
     lib.sekv_decode_attend.argtypes = [vp, vp, i32, i32, vp, vp, vp, C.POINTER(Stats)]
     lib.sekv_timing_enable.argtypes = [vp, i32]
@@ -229,6 +230,10 @@ class Index:
     def route(self, layer_begin, layer_count, q, tau, cap, mask, alpha=None):
         check(lib().sekv_route(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q), _ptr(tau),
                                int(cap), _ptr(mask), _ptr(alpha)))
+
+    def route_pooled(self, layer_begin, layer_count, q, tau, budget, mask, alpha=None):
+        check(lib().sekv_route_pooled(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q), _ptr(tau),
+                                      int(budget), _ptr(mask), _ptr(alpha)))
 
     def calibrate_tau(self, layer_begin, layer_count, q_cal, frac, tau_out):
         check(lib().sekv_calibrate_tau(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q_cal),

@@ -246,6 +246,20 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin
                        int32_t layer_count, const void* q, const float* tau,
                        int32_t cap, uint64_t* mask, float* alpha);
 
+/* Stage 1 routing as sekv_route with no per-head cap, then the budget rule
+ * ([Tech]: spans taken in descending alpha until the budget holds) applied to
+ * a pool: for each sequence b, over every (layer, head, span) triple of the
+ * call, keep the budget largest alpha among the routed triples, ties to the
+ * lower (layer, head, span) position (the flat order of the mask words).
+ * A call over one layer pools that layer's heads; a call over all layers
+ * pools the whole model.  budget 0 = no budget; budget < 0 is SEKV_EINVAL.
+ *   q, tau, mask, alpha  as for sekv_route (alpha NULL: library scratch)
+ * Calls that overlap on one context's scratch (alpha NULL) must be ordered on
+ * its stream, as every call on a context is. */
+sekv_status sekv_route_pooled(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
+                              int32_t layer_count, const void* q, const float* tau,
+                              int32_t budget, uint64_t* mask, float* alpha);
+
 /* Place tau per (l, h) from a calibration query so that k = round(frac * sum_b
  * N_S(b)) of the (b, span) pairs exceed it: the midpoint of the k-th and
  * (k+1)-th largest alpha, k clipped to [1, sum_b N_S(b) - 1].  The pages learn

@@ -86,6 +86,7 @@ def test_null_arguments_fail_before_any_hip_call(L):
     assert lib.sekv_build_index(None, C.byref(p), 1, 1, 1, 1, None, C.byref(out)) == 1
     assert lib.sekv_index_import(None, C.byref(p), None, C.byref(out)) == 1
     assert lib.sekv_route(None, None, 0, 1, 1, 1, 0, 1, None) == 1
+    assert lib.sekv_route_pooled(None, None, 0, 1, 1, 1, 5, 1, None) == 1
     assert lib.sekv_decode_attend(None, None, 0, 1, 1, 1, 1, None) == 1
     assert lib.sekv_calibrate_tau(None, None, 0, 1, 1, 0.1, 1) == 1
     assert lib.sekv_rsvd_batched(None, 1, 1, 1, 1, 8, 128, 16, 8, 2, 0, 1, 1, 1) == 1

@@ -242,6 +242,101 @@ def test_route_cap(ctx, sl):
     idx.free()
 
 
+def gpu_route_pooled(idx, c, q, tau, budget, lb=0, lc=None):
+    w = c.w
+    lc = w.L - lb if lc is None else lc
+    Wd = idx.mask_words
+    mask = torch.zeros(w.B, lc, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    alpha = torch.zeros(w.B, lc, w.Hq, Wd * 64, dtype=torch.float32, device="cuda")
+    idx.route_pooled(lb, lc, dev(q[:, lb:lb + lc]), dev(tau[lb:lb + lc], torch.float32), budget, mask, alpha)
+    torch.cuda.synchronize()
+    return mask.cpu().numpy().view(np.uint64), alpha.cpu().numpy()
+
+
+def pool_boundary(alpha, z_pre, budget, b):
+    """alpha of the budget-th largest routed triple of sequence b, or None."""
+    a = np.concatenate([alpha[k][z_pre[k]] for k in sorted(z_pre) if k[0] == b])
+    if budget <= 0 or len(a) <= budget:
+        return None
+    return float(np.sort(a)[::-1][budget - 1])
+
+
+def check_pooled(c, words, alpha_o, z_pre, budget, lb, label):
+    """Compare the GPU's pooled masks (layers lb..) with the oracle's pooled
+    budget over the same triples; returns the oracle masks."""
+    z_ref = O.pool_budget(alpha_o, z_pre, budget)
+    bad = excl = ties = 0
+    for b in range(c.w.B):
+        bnd = pool_boundary(alpha_o, z_pre, budget, b)
+        kept = 0
+        for key in sorted(k for k in z_ref if k[0] == b):
+            _, l, h = key
+            m, e, t = SC.compare_masks(words[b, l - lb, h], z_ref[key], alpha_o[key], c.tau[l, h], bnd)
+            bad += m
+            excl += e
+            ties += t
+            kept += int(SC.unpack_mask(words[b, l - lb, h], len(z_ref[key])).sum())
+        assert kept <= budget or budget == 0
+    print(f"[pool {label}] budget {budget}: mismatches {bad}, excluded (1e-6) {excl}, ties at 1e-4 {ties}")
+    assert bad == 0
+    return z_ref
+
+
+def test_route_pooled_budget(ctx, sl):
+    """The budget pooled over every (layer, head, span) of the call: over both
+    layers in one call, over each layer alone, and at the edge budgets."""
+    c = case("8b_l2_cap")
+    w = c.w
+    idx = imported(ctx, sl, c)
+    ns = c.idxs[0].n_spans
+    for step in range(2):
+        q = c.q(step)
+        alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+        total = sum(int(v.sum()) for v in z_pre.values())
+        # both layers pooled, 10% of all (layer, head, span) triples
+        budget = int(math.floor(0.10 * w.L * w.Hq * ns))
+        assert budget < total
+        words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
+        z_ref = check_pooled(c, words, alpha_o, z_pre, budget, 0, "2 layers")
+        # decode over the pooled masks
+        out_o = O.decode_step(c.idxs, q.double().numpy(), z_ref, w.Hkv)
+        out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_ref, w.B, w.L, w.Hq, idx.mask_words))
+        assert max(SC.rel_l2(out_g[k], v) for k, v in out_o.items()) <= SC.REL_L2
+        # each layer alone: that layer's heads form the pool
+        for l in range(w.L):
+            sub_a = {k: v for k, v in alpha_o.items() if k[1] == l}
+            sub_z = {k: v for k, v in z_pre.items() if k[1] == l}
+            bl = int(math.floor(0.10 * w.Hq * ns))
+            words_l, _ = gpu_route_pooled(idx, c, q, c.tau, bl, lb=l, lc=1)
+            check_pooled(c, words_l, sub_a, sub_z, bl, l, f"layer {l}")
+    # edge budgets: one triple; exactly the routed count; none (0) = plain routing
+    q = c.q(0)
+    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+    total = sum(int(v.sum()) for v in z_pre.values())
+    plain, _ = gpu_route(idx, c, q, c.tau, 0)
+    for budget in (1, total):
+        words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
+        check_pooled(c, words, alpha_o, z_pre, budget, 0, "edge")
+    words, _ = gpu_route_pooled(idx, c, q, c.tau, total + 1000)
+    assert np.array_equal(words, plain)
+    words, _ = gpu_route_pooled(idx, c, q, c.tau, 0)
+    assert np.array_equal(words, plain)
+    idx.free()
+
+
+def test_route_pooled_budget_per_sequence(ctx, sl):
+    """Two sequences: each keeps its own budget over its own triples."""
+    c = case("70b_b2")
+    w = c.w
+    idx = imported(ctx, sl, c)
+    q = c.q(0)
+    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+    budget = int(math.floor(0.10 * w.Hq * min(i.n_spans for i in c.idxs)))
+    words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
+    check_pooled(c, words, alpha_o, z_pre, budget, 0, "B=2")
+    idx.free()
+
+
 def test_pinned_tier_matches_hbm(ctx, sl):
     c = case("8b_l2_cap")
     w = c.w
