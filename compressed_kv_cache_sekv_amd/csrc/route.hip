@@ -473,18 +473,20 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
 // span) position (the flat order of the mask words).  The budget rule of the
 // Technical-details section of the SeKV article, read over the whole call
 // instead of one (layer, head).
-//  * Collect: threads take 32-span halves of the mask words in flat order,
-//    each with its 32 alpha as eight 16-byte loads, chunk by chunk; a block
-//    scan of the per-half counts places each routed triple (alpha bits, flat
-//    position) in an LDS list in flat order, and the same sweep builds the
-//    first histogram and counts the triples.  A sequence within its budget
-//    stops there.
-//  * Radix select of the budget-th largest alpha bits (alpha >= 0, so the bits
-//    order like the values): histogram passes of 11, 11 and 10 bits in LDS.
-//  * Keys equal to the selected one are kept lowest position first (a block
-//    scan over the list, or over the halves, in flat order).
-// When the routed triples or the halves do not fit in LDS, every pass sweeps
-// the mask words and alpha in global memory instead.
+//  * Collect: threads take 32-span halves of the mask words, two a round, each
+//    with its 32 alpha as eight 16-byte loads, all issued before use; every
+//    routed triple (alpha bits, flat position) goes to an LDS list at a slot
+//    from one LDS counter per wave (wave prefixes by bit-sliced ballots).  A
+//    sequence within its budget stops there.
+//  * Radix select of the budget-th largest key over the list, binned over the
+//    keys' own range (offsets key - min, at most 11 bits a pass from the top
+//    of max - min; alpha >= 0, so the bits order like the values).
+//  * Keep every larger key.  If the boundary key's equals are not all kept,
+//    their positions are ranked against each other and the lowest kept.
+// When the routed triples or the halves do not fit in LDS (or the boundary
+// has more equal keys than LDS ranks), the passes sweep the mask words and
+// alpha in global memory in flat order instead: fixed 11, 11, 10-bit passes,
+// then a block scan of the equal keys chunk by chunk.
 constexpr int kPoolThreads = 1024;
 constexpr int kPoolBins = 2048;
 constexpr int kPoolList = 12288;    // routed triples held in LDS
@@ -513,9 +515,23 @@ __device__ int block_scan_pool(int v, int* s_tmp, int& total) {
   return v + add;
 }
 
+// Exclusive wave prefix and wave total of per-lane counts below 128.
+__device__ __forceinline__ int wave_prefix_pool(int c, int lane, int& total) {
+  const uint64_t lt = (1ull << lane) - 1;
+  int s = 0, t = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const uint64_t bal = __ballot((c >> i) & 1);
+    s += (int)__popcll(bal & lt) << i;
+    t += (int)__popcll(bal) << i;
+  }
+  total = t;
+  return s;
+}
+
 // The bin of the k-th largest key in s_hist (nbins bins, descending): thread
 // i holds bins nbins-1-2i and nbins-2-2i; one thread writes (bin, rank of
-// the key within its bin) to s_sel.
+// the key within its bin, the bin's count) to s_sel.
 __device__ void pool_pick_bin(const uint32_t* s_hist, int nbins, int k, int* s_tmp, int* s_sel) {
   const int hi = nbins - 1 - 2 * (int)threadIdx.x, lo = hi - 1;
   const int chi = (hi >= 0) ? (int)s_hist[hi] : 0;
@@ -527,137 +543,200 @@ __device__ void pool_pick_bin(const uint32_t* s_hist, int nbins, int k, int* s_t
     if (exc + chi >= k) {
       s_sel[0] = hi;
       s_sel[1] = k - exc;
+      s_sel[2] = chi;
     } else {
       s_sel[0] = lo;
       s_sel[1] = k - exc - chi;
+      s_sel[2] = clo;
     }
   }
   __syncthreads();
 }
 
+__device__ __forceinline__ void load_half(const uint32_t* mh, const float* ab, int64_t t, int64_t nh, uint32_t& bits,
+                                          float4 (&av)[8]) {
+  const int64_t tc = t < nh ? t : nh - 1;   // in range; a half past the end has no bits
+  bits = t < nh ? mh[tc] : 0u;
+  const float4* ap = (const float4*)(ab + 32 * tc);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) av[c] = ap[c];
+}
+
 __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArgs a) {
+  constexpr int NWV = kPoolThreads / 64;
   __shared__ uint32_t s_hist[kPoolBins];
   __shared__ uint32_t s_key[kPoolList];
   __shared__ int32_t s_pos[kPoolList];
   __shared__ uint32_t s_new[kPoolHalves];
-  __shared__ int s_tmp[kPoolThreads / 64];
-  __shared__ int s_sel[2];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ int s_tmp[NWV];
+  __shared__ uint32_t s_lo[NWV], s_hi[NWV];
+  __shared__ int s_sel[3];
+  __shared__ int s_count;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t rows = (int64_t)a.layer_count * a.Hq;
   const int64_t nh = rows * a.Wd * 2;                       // 32-span halves of b's words
   uint32_t* mh = (uint32_t*)(a.mask + (int64_t)b * rows * a.Wd);
   const float* ab = a.alpha + (int64_t)b * rows * a.Wd * 64;
   int k = a.budget;
-  // ---- collect (flat order) + first histogram (top 11 bits)
-  for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
+  if (tid == 0) s_count = 0;
+  for (int i = tid; i < kPoolHalves; i += kPoolThreads) s_new[i] = 0u;
   __syncthreads();
-  int total = 0;
-  for (int64_t base = 0; base < nh; base += kPoolThreads) {
-    const int64_t t = base + tid;
-    const int64_t tc = t < nh ? t : nh - 1;   // in range; a thread past the end counts nothing
-    const uint32_t bits = t < nh ? mh[tc] : 0u;
-    const float4* ap = (const float4*)(ab + 32 * tc);
-    float4 av[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) av[c] = ap[c];
-    const int cnt = __popc(bits);
-    int chunk;
-    int pos = total + block_scan_pool(cnt, s_tmp, chunk) - cnt;
+  // ---- collect
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int64_t base = 0; base < nh; base += 2 * kPoolThreads) {
+    uint32_t bits0, bits1;
+    float4 av0[8], av1[8];
+    const int64_t t0 = base + tid, t1 = t0 + kPoolThreads;
+    load_half(mh, ab, t0, nh, bits0, av0);
+    load_half(mh, ab, t1, nh, bits1, av1);
+    int wt;
+    const int pre = wave_prefix_pool(__popc(bits0) + __popc(bits1), lane, wt);
+    int wb = 0;
+    if (lane == 0 && wt > 0) wb = atomicAdd(&s_count, wt);
+    int pos = __shfl(wb, 0) + pre;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      if ((bits >> j) & 1u) {
-        const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
-        atomicAdd(&s_hist[key >> 21], 1u);
+      if ((bits0 >> j) & 1u) {
+        const uint32_t key = __float_as_uint(f4_at(av0[j >> 2], j & 3));
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
         if (pos < kPoolList) {
           s_key[pos] = key;
-          s_pos[pos] = (int32_t)(32 * t + j);
+          s_pos[pos] = (int32_t)(32 * t0 + j);
         }
         ++pos;
       }
     }
-    total += chunk;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((bits1 >> j) & 1u) {
+        const uint32_t key = __float_as_uint(f4_at(av1[j >> 2], j & 3));
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+        if (pos < kPoolList) {
+          s_key[pos] = key;
+          s_pos[pos] = (int32_t)(32 * t1 + j);
+        }
+        ++pos;
+      }
+    }
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+  }
+  if (lane == 0) {
+    s_lo[wave] = kmin;
+    s_hi[wave] = kmax;
   }
   __syncthreads();
+  const int total = s_count;
   if (total <= k) return;   // uniform: b is within its budget
-  const bool in_lds = total <= kPoolList && nh <= kPoolHalves;
-  // ---- radix select: pass 0 from the collect histogram, then 11 and 10 bits
-  uint32_t prefix = 0, pmask = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    if (pass > 0) {
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    kmin = min(kmin, s_lo[w]);
+    kmax = max(kmax, s_hi[w]);
+  }
+  uint32_t vstar = 0u;
+  if (total <= kPoolList && nh <= kPoolHalves) {
+    // ---- radix select over the LDS list, binned over [kmin, kmax]
+    const uint32_t r = kmax - kmin;
+    const int nb = r ? 32 - __clz((int)r) : 0;
+    uint32_t prefix = 0, pmask = 0;
+    int ceq = total;   // keys equal to the selected one
+    for (int top = nb; top > 0; top -= 11) {
+      const int shift = max(top - 11, 0), nbins = 1 << (top - shift);
       for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
       __syncthreads();
-      if (in_lds) {
-        for (int i = tid; i < total; i += kPoolThreads) {
-          const uint32_t key = s_key[i];
-          if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
-        }
-      } else {
-        for (int64_t t = tid; t < nh; t += kPoolThreads) {
-          const uint32_t bits = mh[t];
-          if (bits == 0u) continue;
-          const float4* ap = (const float4*)(ab + 32 * t);
-          float4 av[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) av[c] = ap[c];
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
-            if (((bits >> j) & 1u) && (key & pmask) == prefix)
-              atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
-          }
-        }
+      for (int i = tid; i < total; i += kPoolThreads) {
+        const uint32_t o = s_key[i] - kmin;
+        if ((o & pmask) == prefix) atomicAdd(&s_hist[(o >> shift) & (uint32_t)(nbins - 1)], 1u);
       }
       __syncthreads();
+      pool_pick_bin(s_hist, nbins, k, s_tmp, s_sel);
+      prefix |= (uint32_t)s_sel[0] << shift;
+      pmask |= (uint32_t)(nbins - 1) << shift;
+      k = s_sel[1];
+      ceq = s_sel[2];
+      __syncthreads();
     }
-    pool_pick_bin(s_hist, nbins, k, s_tmp, s_sel);
-    prefix |= (uint32_t)s_sel[0] << shift;
-    pmask |= (uint32_t)(nbins - 1) << shift;
-    k = s_sel[1];
-    __syncthreads();
-  }
-  // prefix is the budget-th largest key; keep every larger key and the k
-  // lowest-position keys equal to it
-  const uint32_t vstar = prefix;
-  int carry = 0;
-  if (in_lds) {
-    for (int i = tid; i < (int)nh; i += kPoolThreads) s_new[i] = 0u;
-    __syncthreads();
-    for (int base = 0; base < total; base += kPoolThreads) {
-      const int i = base + tid;
-      const uint32_t key = i < total ? s_key[i] : 0u;
-      const int eq = (i < total && key == vstar) ? 1 : 0;
-      int chunk;
-      const int rank = carry + block_scan_pool(eq, s_tmp, chunk) - eq;
-      if (i < total && (key > vstar || (eq && rank < k))) {
+    vstar = kmin + prefix;
+    // ---- keep: every larger key, and the k lowest-position equal keys
+    bool done = false;
+    if (k == ceq) {
+      for (int i = tid; i < total; i += kPoolThreads)
+        if (s_key[i] >= vstar) {
+          const int p = s_pos[i];
+          atomicOr(&s_new[p >> 5], 1u << (p & 31));
+        }
+      done = true;
+    } else if (ceq <= kPoolBins) {
+      // the equal keys' positions (in s_hist), each ranked against the others
+      if (tid == 0) s_count = 0;
+      __syncthreads();
+      for (int i = tid; i < total; i += kPoolThreads) {
+        const uint32_t key = s_key[i];
         const int p = s_pos[i];
-        atomicOr(&s_new[p >> 5], 1u << (p & 31));
+        if (key > vstar) atomicOr(&s_new[p >> 5], 1u << (p & 31));
+        else if (key == vstar) s_hist[atomicAdd(&s_count, 1)] = (uint32_t)p;
       }
-      carry += chunk;
+      __syncthreads();
+      for (int e = tid; e < ceq; e += kPoolThreads) {
+        const uint32_t p = s_hist[e];
+        int rank = 0;
+        for (int f = 0; f < ceq; ++f) rank += s_hist[f] < p;
+        if (rank < k) atomicOr(&s_new[p >> 5], 1u << (p & 31));
+      }
+      done = true;
     }
-    __syncthreads();
-    for (int i = tid; i < (int)nh; i += kPoolThreads) mh[i] = s_new[i];
-    return;
-  }
-  for (int64_t base = 0; base < nh; base += kPoolThreads) {
-    const int64_t t = base + tid;
-    uint32_t bits = 0u, keep = 0u, eq = 0u;
-    if (t < nh) {
-      bits = mh[t];
-      if (bits != 0u) {
-        const float4* ap = (const float4*)(ab + 32 * t);
+    if (done) {   // uniform
+      __syncthreads();
+      for (int i = tid; i < (int)nh; i += kPoolThreads) mh[i] = s_new[i];
+      return;
+    }
+  } else {
+    // ---- radix select sweeping global memory: fixed 11, 11, 10-bit digits
+    uint32_t prefix = 0, pmask = 0;
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nbins = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
+      __syncthreads();
+      for (int64_t t = tid; t < nh; t += kPoolThreads) {
+        uint32_t bits;
         float4 av[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) av[c] = ap[c];
+        load_half(mh, ab, t, nh, bits, av);
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
           const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
-          const bool on = (bits >> j) & 1u;
-          keep |= (uint32_t)(on && key > vstar) << j;
-          eq |= (uint32_t)(on && key == vstar) << j;
+          if (((bits >> j) & 1u) && (key & pmask) == prefix)
+            atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
         }
       }
+      __syncthreads();
+      pool_pick_bin(s_hist, nbins, k, s_tmp, s_sel);
+      prefix |= (uint32_t)s_sel[0] << shift;
+      pmask |= (uint32_t)(nbins - 1) << shift;
+      k = s_sel[1];
+      __syncthreads();
+    }
+    vstar = prefix;
+  }
+  // ---- keep, sweeping global memory in flat order: every larger key, and
+  // the k lowest-position keys equal to vstar (block scan of their counts)
+  int carry = 0;
+  for (int64_t base = 0; base < nh; base += kPoolThreads) {
+    const int64_t t = base + tid;
+    uint32_t bits, keep = 0u, eq = 0u;
+    float4 av[8];
+    load_half(mh, ab, t, nh, bits, av);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+      const bool on = (bits >> j) & 1u;
+      keep |= (uint32_t)(on && key > vstar) << j;
+      eq |= (uint32_t)(on && key == vstar) << j;
     }
     const int ne = __popc(eq);
     int chunk;

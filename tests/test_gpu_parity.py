@@ -337,6 +337,70 @@ def test_route_pooled_budget_per_sequence(ctx, sl):
     idx.free()
 
 
+def _gpu_alpha_pool_ref(c, words_plain, alpha_g, budget):
+    """The oracle's pooled budget on the library's own fp32 alpha and
+    pre-budget masks (the selection decided in the kernel's precision)."""
+    w = c.w
+    a, z = {}, {}
+    for b in range(w.B):
+        n = c.idxs[b].n_spans
+        for l in range(words_plain.shape[1]):
+            for h in range(w.Hq):
+                a[b, l, h] = alpha_g[b, l, h, :n].astype(np.float64)
+                z[b, l, h] = SC.unpack_mask(words_plain[b, l, h], n)
+    return O.pool_budget(a, z, budget), sum(int(v.sum()) for v in z.values())
+
+
+def _check_pool_exact(c, idx, q, tau, budgets, label):
+    w = c.w
+    plain, alpha_p = gpu_route(idx, c, q, tau, 0)
+    total = None
+    for budget in budgets(plain):
+        words, alpha_g = gpu_route_pooled(idx, c, q, tau, budget)
+        assert np.array_equal(alpha_g, alpha_p)
+        ref, total = _gpu_alpha_pool_ref(c, plain, alpha_g, budget)
+        for (b, l, h), zz in ref.items():
+            got = SC.unpack_mask(words[b, l, h], len(zz))
+            assert np.array_equal(got, zz), (label, budget, b, l, h)
+            assert not SC.unpack_mask(words[b, l, h], idx.mask_words * 64)[len(zz):].any()
+        ties = 0
+        if 0 < budget < total:
+            keys = np.sort(np.concatenate([alpha_g[b, l, h, :c.idxs[b].n_spans][SC.unpack_mask(plain[b, l, h],
+                                                                                      c.idxs[b].n_spans)]
+                                           for b in range(w.B) for l in range(w.L) for h in range(w.Hq)]))[::-1]
+            ties = int((keys == keys[budget - 1]).sum())
+        print(f"[pool exact {label}] budget {budget} of {total}: bit-exact; keys equal to the boundary {ties}")
+    return total
+
+
+def test_route_pooled_selection_paths(ctx, sl):
+    """Every selection path of the pool kernel, bit-exact against the oracle's
+    pooled budget on the library's alpha: the LDS list (with ranked split
+    ties at saturated alpha), the global sweeps (more routed triples than the
+    LDS list holds), and the LDS list with more equal boundary keys than LDS
+    ranks (saturated routing scores)."""
+    c = case("8b_l2_cap")
+    w = c.w
+    ns = c.idxs[0].n_spans
+    idx = imported(ctx, sl, c)
+    q = c.q(0)
+    ten = int(math.floor(0.10 * w.L * w.Hq * ns))
+    # calibrated tau: the LDS list
+    _check_pool_exact(c, idx, q, c.tau, lambda p: (1, 7, ten, ten + 1), "lds")
+    # tau = -inf: every span routed, 2 x 32 x N_S triples > the LDS list
+    tinf = np.full_like(c.tau, -np.inf)
+    total = _check_pool_exact(c, idx, q, tinf, lambda p: (ten, 3 * ten), "global")
+    assert total > 12288
+    idx.free()
+    # saturated alpha (W scaled by 64): thousands of alpha == 1.0 at the boundary
+    arr = SC.import_arrays(c)
+    arr["W"] = (arr["W"] * 64.0).astype(np.float32)
+    sat = ctx.import_index(sl.build_params(c.w), arr)
+    tau5 = np.full_like(c.tau, 0.5)
+    _check_pool_exact(c, sat, q, tau5, lambda p: (ten, 5), "saturated")
+    sat.free()
+
+
 def test_pinned_tier_matches_hbm(ctx, sl):
     c = case("8b_l2_cap")
     w = c.w
