@@ -176,6 +176,24 @@ def prefill(args) -> int:
     flops = float(np.sum(2 * n * w.d * lw * (2 + 2 * w.power_iters)))
     t = float(np.median(rsvd_ms))
     tflops = flops / (t * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's exact truncated SVD (LAPACK, fp64) of the first span
+        # matrices of the same batch, one thread, ~10 s, scaled to all of them
+        from threadpoolctl import threadpool_limits
+        from oracle import sekv_oracle as O
+        Ah = A.cpu()
+        offs = row_off.cpu().numpy() // w.d
+        done, t0 = 0, time.time()
+        with threadpool_limits(1):
+            while done < cnt and time.time() - t0 < 10.0:
+                O.truncated_svd(Ah[offs[done]:offs[done] + int(n[done])].double().numpy(), w.R)
+                done += 1
+        el = time.time() - t0
+        cpu = {"value": round(el / done * cnt * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+               "sample": f"exact truncated SVD (numpy LAPACK, fp64) of the first {done} of the {cnt} span "
+                         f"matrices in {el:.1f} s, scaled to all {cnt}"}
+        log(f"[cpu] oracle SVD of {done} matrices in {el:.1f} s: {cpu['value']:.0f} ms for the layer")
     print(json.dumps({
         "metric": "prefill: randomized SVD of every span K/V of one 128K layer (R=32, oversampling 8, "
                   "2 power iterations)",
@@ -185,6 +203,7 @@ def prefill(args) -> int:
         "gemm_gflop": round(flops / 1e9, 2),
         "mfma": {"achieved": round(tflops, 3), "peak": 2500.0, "unit": "TFLOP/s",
                  "frac": round(tflops / 2500.0, 5)},
+        "cpu_baseline": cpu,
         "config": {"workload": w.name, "kv_heads": w.Hkv, "head_dim": w.d, "context": w.T, "R": w.R}}),
         flush=True)
     ctx.close()
