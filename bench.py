@@ -16,7 +16,8 @@ roofline    = the attention kernel's algorithmic bytes per launch (resident
               K/V rows, the factor blobs of the routed union, queries, masks)
               over its mean launch time from HIP events in the timed region,
               against MI355X's 8 TB/s HBM peak
-cpu_baseline= the fp64 CPU oracle, single-threaded, on a bounded sample of the
+cpu_baseline= the fp64 CPU oracle (BLAS on the process's cores; a one-thread
+              run beside it), on a bounded sample of the
               same workload (one layer x one KV head), scaled to a full step
 pcie        = the same decode with span factors in pinned host memory and the
               routed union gathered into an HBM ring (PCIe bytes and time per
@@ -86,38 +87,49 @@ def union_alg_bytes(masks, n_spans, span_len, G, R, d):
     return tot, nun
 
 
-def cpu_baseline(w, H, K, V, W, gates, tau, cap, q_steps, budget_s=12.0):
-    """Time the oracle (one thread) on one (layer 0, KV head 0) unit of the
-    workload: build that unit's index (untimed), then route + attend for the
-    G query heads for as many decode steps as fit in ~budget_s."""
+def cpu_baseline(w, H, K, V, W, gates, tau, cap, q_steps, budget_s=8.0):
+    """Time the oracle on one (layer 0, KV head 0) unit of the workload: build
+    that unit's index (untimed), then route + attend for the G query heads for
+    as many decode steps as fit in ~budget_s, scaled to the L Hkv B units of a
+    step.  Run with BLAS on the process's cores (the oracle as it stands; the
+    reported baseline) and again on one thread (`one_thread`)."""
     from threadpoolctl import threadpool_limits
     from oracle import sekv_oracle as O
     G = w.G
-    with threadpool_limits(1):
-        t0 = time.time()
-        gb = None if gates is None else gates[0][0:1, 0:1].double().numpy()
-        idx = O.build_index_b(H[0].numpy(), K[0][0:1, 0:1].double().numpy(),
-                              V[0][0:1, 0:1].double().numpy(), W[0:1, 0:G].double().numpy(), gb,
-                              R=w.R, alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=G)
-        log(f"[cpu] oracle index of one (layer, kv head) unit built in {time.time() - t0:.1f} s")
-        Wn = W[0, 0:G].double().numpy()
-        done, t0 = 0, time.time()
-        while True:
-            q = q_steps[done % len(q_steps)][0, 0, 0:G].double().numpy()   # [G, d]
-            for h in range(G):
-                _, z = O.route_head(Wn[h], q[h], idx.s[0, h], float(tau[0, h]), cap)
-                O.decode_head(q[h], idx, 0, 0, z)
-            done += 1
-            el = time.time() - t0
-            if el > budget_s or done >= 200:
-                break
-    per_unit = el / done
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.time()
+    gb = None if gates is None else gates[0][0:1, 0:1].double().numpy()
+    idx = O.build_index_b(H[0].numpy(), K[0][0:1, 0:1].double().numpy(),
+                          V[0][0:1, 0:1].double().numpy(), W[0:1, 0:G].double().numpy(), gb,
+                          R=w.R, alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=G)
+    log(f"[cpu] oracle index of one (layer, kv head) unit built in {time.time() - t0:.1f} s")
+    Wn = W[0, 0:G].double().numpy()
     units = w.L * w.Hkv * w.B
-    step_s = per_unit * units
-    return {"value": w.B / step_s, "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+
+    def run(threads):
+        with threadpool_limits(threads):
+            done, t0 = 0, time.time()
+            while True:
+                q = q_steps[done % len(q_steps)][0, 0, 0:G].double().numpy()   # [G, d]
+                for h in range(G):
+                    _, z = O.route_head(Wn[h], q[h], idx.s[0, h], float(tau[0, h]), cap)
+                    O.decode_head(q[h], idx, 0, 0, z)
+                done += 1
+                el = time.time() - t0
+                if el > budget_s or done >= 200:
+                    break
+        per_unit = el / done
+        return done, per_unit, w.B / (per_unit * units)
+
+    done, per_unit, value = run(cores)
+    done1, per_unit1, value1 = run(1)
+    return {"value": value, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
             "sample": (f"{done} decode steps of one (layer 0, KV head 0) unit (route + attend for its {G} "
                        f"query heads over the oracle-built index of that unit at T={w.T}), "
-                       f"{per_unit * 1e3:.1f} ms per unit, scaled by {units} units per step")}
+                       f"{per_unit * 1e3:.1f} ms per unit with BLAS on {cores} threads, scaled by {units} "
+                       f"units per step"),
+            "one_thread": {"value": value1, "cores": 1, "ms_per_unit": round(per_unit1 * 1e3, 2),
+                           "steps": done1}}
 
 
 def prefill(args) -> int:
