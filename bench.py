@@ -442,6 +442,8 @@ def main(argv=None):
         pb = pc = 0
         pms = 0.0
         torch.cuda.synchronize()
+        ctx.timing(True)
+        ctx.timing_read()
         t0 = time.time()
         for s in range(args.warmup, args.warmup + psteps):
             for l in range(L):
@@ -452,8 +454,12 @@ def main(argv=None):
                 pms += st.pcie_ms
         torch.cuda.synchronize()
         wall = time.time() - t0
+        p_route_ms, p_route_n, p_attend_ms, p_attend_n = ctx.timing_read()
+        ctx.timing(False)
         result["pcie"] = {"build_s": round(pbuild_s, 3), "steps": psteps, "bytes_per_step": int(pb / psteps),
                           "copies_per_step": int(pc / psteps), "copy_ms_per_step": round(pms / psteps, 3),
+                          "attend_us_per_launch_ring": round(p_attend_ms / max(p_attend_n, 1) * 1e3, 2),
+                          "route_us_per_launch": round(p_route_ms / max(p_route_n, 1) * 1e3, 2),
                           "GB_per_s": round(pb / (pms / 1e3) / 1e9, 2) if pms > 0 else None,
                           "query_tokens_per_s_incl_pcie": round(B * psteps / wall, 3)}
         log(f"[bench] pinned tier: {pb / psteps / 1e9:.3f} GB and {pc / psteps:.0f} copies per step, "
