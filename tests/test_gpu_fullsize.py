@@ -6,6 +6,9 @@ times (one layer per call, the 8B-shaped 128K layer of the 32-layer stack).
   (masks bit-exact, ties at the threshold and at the cap boundary excluded)
   and decoded (5e-3 relative L2).  The library's own index from the same
   inputs: span table and raw positions bit-exact.
+* The same layer with the budget pooled over its 32 heads (three quarters of
+  the routed triples): masks against the oracle's pooled budget, and bit for bit
+  on the library's own alpha; decode over the pooled masks.
 * 70B-shaped layer, 32 sequences of 65536 tokens (64 query / 8 KV heads,
   R = 64): the library builds the whole index on the GPU from inputs drawn on
   the GPU; the span table of every sequence is checked against the oracle's
@@ -23,7 +26,8 @@ import torch
 from compressed_kv_cache_sekv_amd import synth
 from oracle import sekv_oracle as O
 from tests import sekv_cases as SC
-from tests.test_gpu_parity import dev, gpu_decode, gpu_route, imported, oracle_route_all
+from tests.test_gpu_parity import (_check_pool_exact, check_pooled, dev, gpu_decode, gpu_route, gpu_route_pooled,
+                                   imported, oracle_route_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +54,30 @@ def case_128k():
     w = synth.WORKLOADS["llama8b_l32_128k"].scaled(L=1, tier="hbm")
     print(f"[case] building the oracle index of one 128K layer", flush=True)
     return SC.make_case(w)
+
+
+def test_128k_layer_pooled_budget(ctx, sl, case_128k):
+    """The budget pooled over the 32 heads of the 128K layer, the size
+    bench.py --pooled times: against the oracle's pooled budget on its fp64
+    alpha (near ties excluded), then bit for bit on the library's own alpha,
+    with decode over the pooled masks."""
+    c = case_128k
+    w = c.w
+    idx = imported(ctx, sl, c)
+    q = c.q(0)
+    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+    # three quarters of the routed triples: the selection runs (the cap-sized
+    # budget, cap x 32, can exceed what one query routes)
+    budget = (3 * sum(int(v.sum()) for v in z_pre.values())) // 4
+    words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
+    z_ref = check_pooled(c, words, alpha_o, z_pre, budget, 0, "128k")
+    _check_pool_exact(c, idx, q, c.tau, lambda p: (budget,), "128k")
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_ref, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_ref, w.B, w.L, w.Hq, idx.mask_words))
+    worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+    print(f"[128k pool] decode over {len(out_o)} heads: worst rel-L2 {worst:.3e}", flush=True)
+    assert worst <= SC.REL_L2
+    idx.free()
 
 
 def test_128k_layer_identical_index(ctx, sl, case_128k):
