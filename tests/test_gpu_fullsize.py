@@ -9,6 +9,8 @@ times (one layer per call, the 8B-shaped 128K layer of the 32-layer stack).
 * The same layer with the budget pooled over its 32 heads (three quarters of
   the routed triples): masks against the oracle's pooled budget, and bit for bit
   on the library's own alpha; decode over the pooled masks.
+* The largest span count the mask layout holds (65535 spans of 8 tokens):
+  masks without and with a cap, decode, and the library's own split.
 * 70B-shaped layer, 32 sequences of 65536 tokens (64 query / 8 KV heads,
   R = 64): the library builds the whole index on the GPU from inputs drawn on
   the GPU; the span table of every sequence is checked against the oracle's
@@ -78,6 +80,60 @@ def test_128k_layer_pooled_budget(ctx, sl, case_128k):
     print(f"[128k pool] decode over {len(out_o)} heads: worst rel-L2 {worst:.3e}", flush=True)
     assert worst <= SC.REL_L2
     idx.free()
+
+
+def test_max_span_count(ctx, sl):
+    """The largest span count the mask layout holds (1024 words, 65535 spans):
+    an anchor every 9th token makes every run exactly l_min = 8 tokens long.
+    The attention kernel's union words then need its larger dynamic-LDS launch
+    and the plan runs more items than one wave of workgroups.  Identical
+    index: masks bit-exact without and with a 10% cap (more candidates than
+    the cap kernel's LDS list), decode within 5e-3; the library's own split
+    of the same inputs is bit-exact."""
+    T = 9 * 65535
+    w = synth.WORKLOADS["tiny_2k"].scaled(T=T)      # 4 / 1 heads, d 64, R 16, d' 32, tau 0.5
+    H = torch.where(torch.arange(T) % 9 == 8, torch.tensor(10.0), torch.tensor(0.5)).float()[None]
+    K = synth.kv_rows(w, H[0], 0, 0, 0, "K")[None, None, None]
+    V = synth.kv_rows(w, H[0], 0, 0, 0, "V")[None, None, None]
+    W = synth.routing_w(w, 0)[None]
+    print("[max] building the oracle index of 65535 spans", flush=True)
+    idxs = [O.build_index_b(H[0].numpy(), K[0].double().numpy(), V[0].double().numpy(), W.double().numpy(), None,
+                            R=w.R, alpha_sp=w.alpha_sp, l_min=w.l_min, Hq=w.Hq)]
+    assert idxs[0].n_spans == 65535 == synth.max_spans(T, w.l_min)
+    tau = np.full((w.L, w.Hq), 0.5)
+    c = SC.Case(w, H, K, V, W, None, idxs, tau)
+    idx = imported(ctx, sl, c)
+    assert idx.mask_words == 1024
+    q = c.q(0)
+    alpha_o, z_o = oracle_route_all(c, q, tau)
+    words, _ = gpu_route(idx, c, q, tau)
+    bad = excl = 0
+    for (b, l, h), z in z_o.items():
+        m, e, _ = SC.compare_masks(words[b, l, h], z, alpha_o[b, l, h], tau[l, h])
+        bad += m
+        excl += e
+    cap = 6553
+    _, z_cap = oracle_route_all(c, q, tau, cap)
+    words_c, _ = gpu_route(idx, c, q, tau, cap)
+    for (b, l, h), z in z_cap.items():
+        bnd = SC.cap_boundary(alpha_o[b, l, h], z_o[b, l, h], cap)
+        m, e, _ = SC.compare_masks(words_c[b, l, h], z, alpha_o[b, l, h], tau[l, h], bnd)
+        bad += m
+        excl += e
+    print(f"[max] routed {[int(z.sum()) for z in z_o.values()]}, cap {cap}: mismatches {bad}, excluded {excl}",
+          flush=True)
+    assert bad == 0
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, words)
+    worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
+    print(f"[max] decode over {len(out_o)} heads: worst rel-L2 {worst:.3e}", flush=True)
+    assert worst <= SC.REL_L2
+    idx.free()
+    lib_idx = ctx.build_index(sl.build_params(w), K.cuda(), V.cuda(), H.cuda(), W.cuda())
+    start, length, raw = lib_idx.spans()
+    assert np.array_equal(start, idxs[0].split.spans[:, 0]) and np.array_equal(length, idxs[0].split.spans[:, 1])
+    assert np.array_equal(raw, idxs[0].split.raw)
+    lib_idx.free()
 
 
 def test_128k_layer_identical_index(ctx, sl, case_128k):
