@@ -102,8 +102,14 @@ __device__ __forceinline__ void tri_decode(int e, int& r, int& c) {
   c = e - r * (r + 1) / 2;
 }
 
-constexpr int kNC = 32;          // rows of A staged per chunk
-constexpr int kNRT = kNC / 16;   // 16-row tiles per chunk
+// Rows of A staged per chunk: 32, or 16 when the sketch is at most 32 wide
+// (the smaller staging area then lets four workgroups share a CU instead of
+// three; for wider sketches 16 rows save too little LDS to add one).
+template <int LP>
+struct Chunk {
+  static constexpr int NC = LP <= 32 ? 16 : 32;
+  static constexpr int NRT = NC / 16;   // 16-row tiles per chunk
+};
 
 // LDS layout (bytes).
 //   ZT  float [LP][D + 4]   basis columns as rows (Z^T), later V^T
@@ -116,6 +122,7 @@ constexpr int kNRT = kNC / 16;   // 16-row tiles per chunk
 //       or T float [LP][LP + 1] and E^T float [LP][LP + 4] (Jacobi)
 template <int D, int LP>
 struct Lay {
+  static constexpr int kNC = Chunk<LP>::NC;
   static constexpr int ZP = D + 4;
   static constexpr int ARP = D + 8;
   static constexpr int CTP = kNC + 4;
@@ -138,8 +145,9 @@ struct Lay {
 
 // Stage rows [c0, c0 + kNC) of A (rows >= n read as zero) into Ar and, for
 // the range finder, into the transposed operand tiles At.
-template <int D, bool WITH_AT>
+template <int D, int kNC, bool WITH_AT>
 __device__ void stage(const bf16_t* __restrict__ A, int n, int c0, bf16_t* Ar, bf16_t* At) {
+  constexpr int kNRT = kNC / 16;
   constexpr int CPR = D / 8;
   constexpr int ARP = D + 8;
   for (int u = threadIdx.x; u < kNC * CPR; u += 256) {
@@ -195,6 +203,7 @@ __device__ __forceinline__ f32x4 az_tile(const bf16_t* Ar, const float* ZT, int 
 // ZT <- rows of A^T (A Z) (all columns of Z; unused columns of Z are zero).
 template <int D, int LP>
 __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
+  constexpr int kNC = Chunk<LP>::NC, kNRT = Chunk<LP>::NRT;
   using Y = Lay<D, LP>;
   constexpr int NJT = LP / 16, NDT = D / 16, DTW = (NDT + 3) / 4;
   float* ZT = (float*)(lds + Y::zt);
@@ -209,7 +218,7 @@ __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
 #pragma unroll
     for (int j = 0; j < NJT; ++j) w[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < n; c0 += kNC) {
-    stage<D, true>(A, n, c0, Ar, At);
+    stage<D, kNC, true>(A, n, c0, Ar, At);
     __syncthreads();
     for (int t = wave; t < kNRT * NJT; t += 4) {
       const int rt = t / NJT, jt = t - rt * NJT;
@@ -426,6 +435,7 @@ __device__ void jacobi(float* T, float* ET, int l, f32x4* rot, int* flag) {
 
 template <int D, int LP, bool BATCHED>
 __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
+  constexpr int kNC = Chunk<LP>::NC, kNRT = Chunk<LP>::NRT;
   using Y = Lay<D, LP>;
   constexpr int NJT = LP / 16;
   constexpr int MAXB = ((LP / 2) * (LP / 2 + 1) / 2 + 255) / 256;  // Gram blocks per thread
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
 #pragma unroll
     for (int i = 0; i < MAXB; ++i) acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.0;
     for (int c0 = 0; c0 < n; c0 += kNC) {
-      stage<D, false>(A, n, c0, Ar, nullptr);
+      stage<D, kNC, false>(A, n, c0, Ar, nullptr);
       __syncthreads();
       for (int t = wave; t < kNRT * NJT; t += 4) {
         const int rt = t / NJT, jt = t - rt * NJT;
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   // ---- U = orth(A V Sigma^-1): Gram of U' (fp64), Cholesky, L^-1, U = U' L^-T
   const int nbu = (re + 1) >> 1, nblku = nbu * (nbu + 1) / 2;
   auto u_chunk = [&](int c0) {
-    stage<D, false>(A, n, c0, Ar, nullptr);
+    stage<D, kNC, false>(A, n, c0, Ar, nullptr);
     __syncthreads();
     for (int t = wave; t < kNRT * NJT; t += 4) {
       const int rt = t / NJT, jt = t - rt * NJT;
