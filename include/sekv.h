@@ -252,7 +252,9 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin
  * call, keep the budget largest alpha among the routed triples, ties to the
  * lower (layer, head, span) position (the flat order of the mask words).
  * A call over one layer pools that layer's heads; a call over all layers
- * pools the whole model.  budget 0 = no budget; budget < 0 is SEKV_EINVAL.
+ * pools the whole model (which needs every layer's query at once: a decode
+ * loop whose layer l + 1 query depends on layer l pools per layer).
+ * budget 0 = no budget; budget < 0 is SEKV_EINVAL.
  *   q, tau, mask, alpha  as for sekv_route (alpha NULL: library scratch)
  * Calls that overlap on one context's scratch (alpha NULL) must be ordered on
  * its stream, as every call on a context is. */
