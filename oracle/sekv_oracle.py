@@ -22,7 +22,8 @@ reordering beyond the stated definitions.
 Parity pins (tests/test_oracle_pins.py): full-rank + tau=-inf equals full
 attention; tau=+inf equals full attention over span-mean-replaced rows; brute
 force span split on tiny inputs; SVD against an eigen-decomposition of A^T A;
-routing against the (W^T W) identity and a sign test at tau=0.5; the cap rule
+routing against the (W^T W) identity and a sign test at tau=0.5; the
+summary keys of a built index against numpy's weighted average; the cap rule
 against brute force; the pooled budget against brute force and against the
 per-head cap on a one-head pool; calibration by counting.  Unpinned: absolute decode
 outputs at generic tau (no worked example is printed on the pages); they stand
@@ -264,38 +265,63 @@ def build_index_b(H_b, K_b, V_b, W, gates_b, *, R: int, alpha_sp: float,
 # budget holds.
 # ----------------------------------------------------------------------------
 
+def logit_threshold(tau: float) -> float:
+    """The routing-score threshold equivalent to alpha > tau (R27).  alpha =
+    sigmoid(a) is strictly increasing and lies in (0, 1), so alpha > tau
+    exactly when a > log(tau / (1 - tau)) for 0 < tau < 1; every score passes
+    a tau <= 0 and none passes a tau >= 1.  A NaN tau passes nothing."""
+    tau = float(tau)
+    if tau != tau:
+        return math.nan
+    if tau <= 0.0:
+        return -math.inf
+    if tau >= 1.0:
+        return math.inf
+    return math.log(tau) - math.log1p(-tau)
+
+
+def routing_score(W_h, q_h, s_h) -> np.ndarray:
+    """a_S = (W^(l,h) q) . s_S for every span: the argument of the sigmoid."""
+    u = np.asarray(W_h, f64) @ np.asarray(q_h, f64)
+    return u @ np.asarray(s_h, f64)
+
+
 def route_head(W_h, q_h, s_h, tau: float, cap: int = 0):
     """One (layer, query head).  W_h [d', d], q_h [d], s_h [d', N_S].
-    Returns (alpha [N_S] fp64, z bool [N_S]).  Per query head (R8); alpha~ of
-    the budget rule read as alpha (R10); the cap is per (layer, head), ties
-    broken toward the lower span index (R11)."""
-    u = np.asarray(W_h, f64) @ np.asarray(q_h, f64)
-    a = u @ np.asarray(s_h, f64)
-    alpha = 1.0 / (1.0 + np.exp(-a))
-    z = alpha > tau
+    Returns (alpha [N_S] fp64, z bool [N_S]).  Per query head (R8).  z_S =
+    [alpha_S > tau] is decided on the score a_S against logit(tau) and the
+    budget cap keeps the cap largest a_S (R27: the same decisions as alpha in
+    exact arithmetic, and still ordered where alpha rounds to 1); alpha~ of the
+    budget rule read as alpha (R10); the cap is per (layer, head), ties broken
+    toward the lower span index (R11)."""
+    a = routing_score(W_h, q_h, s_h)
+    with np.errstate(over="ignore"):
+        alpha = 1.0 / (1.0 + np.exp(-a))
+    z = a > logit_threshold(tau)
     if cap > 0 and int(z.sum()) > cap:
         cand = np.nonzero(z)[0]
-        order = sorted(cand, key=lambda j: (-alpha[j], j))
+        order = sorted(cand, key=lambda j: (-a[j], j))
         keep = np.zeros_like(z)
         keep[order[:cap]] = True
         z = keep
     return alpha, z
 
 
-def pool_budget(alpha, z, budget: int):
+def pool_budget(score, z, budget: int):
     """The budget rule of [Tech] (expand in descending alpha until the budget
     holds) read over a pool instead of one (layer, head): every (layer, head,
-    span) triple of one sequence that a routing call covers.  alpha, z: dicts
-    keyed (b, l, h) -> [N_S(b)] arrays, the pre-budget routing.  For each b,
-    keep the `budget` largest alpha among the routed triples, ties broken
-    toward the lower (l, h, span) position (R26); budget 0 = no budget.
-    Returns the new z dict."""
+    span) triple of one sequence that a routing call covers.  score, z: dicts
+    keyed (b, l, h) -> [N_S(b)] arrays: the routing scores a_S (ordered as
+    alpha, R27) and the pre-budget routing.  For each b, keep the `budget`
+    largest scores among the routed triples, ties broken toward the lower
+    (l, h, span) position (R26); budget 0 = no budget.  Returns the new z
+    dict."""
     out = {k: np.array(v, bool) for k, v in z.items()}
     if budget <= 0:
         return out
     for b in sorted({k[0] for k in z}):
         keys = sorted(k for k in z if k[0] == b)
-        cand = [(-float(alpha[k][S]), k[1], k[2], int(S)) for k in keys for S in np.nonzero(z[k])[0]]
+        cand = [(-float(score[k][S]), k[1], k[2], int(S)) for k in keys for S in np.nonzero(z[k])[0]]
         if len(cand) <= budget:
             continue
         cand.sort()
@@ -379,6 +405,16 @@ def route_step(idxs: List[BatchIndex], W, q, tau, cap: int = 0, layers=None, hea
             for h in (range(Hq) if heads is None else heads):
                 alpha[b, l, h], z[b, l, h] = route_head(W[l, h], q[b, l, h], idxs[b].s[l, h], tau[l, h], cap)
     return alpha, z
+
+
+def score_step(idxs: List[BatchIndex], W, q, layers=None, heads=None):
+    """Routing scores a_S per (b, l, h): dict keyed by (b, l, h)."""
+    W = np.asarray(W, f64)
+    q = np.asarray(q, f64)
+    L, Hq = W.shape[0], W.shape[1]
+    return {(b, l, h): routing_score(W[l, h], q[b, l, h], idxs[b].s[l, h])
+            for b in range(len(idxs)) for l in (range(L) if layers is None else layers)
+            for h in (range(Hq) if heads is None else heads)}
 
 
 def decode_step(idxs: List[BatchIndex], q, z, Hkv: int, keys=None):

@@ -215,15 +215,49 @@ def test_route_infinite_thresholds():
     W, q, s = rng.standard_normal((4, 8)), rng.standard_normal(8), rng.standard_normal((4, 30))
     assert O.route_head(W, q, s, -math.inf)[1].all()
     assert not O.route_head(W, q, s, math.inf)[1].any()
+    # thresholds outside (0, 1): alpha lies strictly between 0 and 1
+    assert O.route_head(W, q, s, 0.0)[1].all() and O.route_head(W, q, s, -3.0)[1].all()
+    assert not O.route_head(W, q, s, 1.0)[1].any() and not O.route_head(W, q, s, 2.0)[1].any()
+    assert not O.route_head(W, q, s, math.nan)[1].any()
 
 
-def _brute_cap(alpha, z, cap):
+def test_logit_threshold_matches_alpha_comparison():
+    """R27: deciding a > logit(tau) is deciding sigmoid(a) > tau.  Checked
+    against the sigmoid computed by scipy's expit where it is not saturated, on
+    scores placed a few ulps either side of the threshold."""
+    from scipy.special import expit
+    rng = np.random.default_rng(21)
+    for tau in (0.5, 0.1, 0.9, 0.99, 0.9999, 1e-6, 0.37):
+        thr = O.logit_threshold(tau)
+        assert abs(expit(thr) - tau) <= 4e-16 * max(1.0, 1.0 / (1.0 - tau))
+        a = np.concatenate([rng.normal(thr, 3.0, 200), np.nextafter(thr, [np.inf, -np.inf])])
+        z = a > thr
+        keep = np.abs(a - thr) > 1e-9 * max(1.0, abs(thr))      # away from the rounding of expit
+        assert np.array_equal(z[keep], (expit(a) > tau)[keep])
+        assert z[-2] and not z[-1]
+    assert O.logit_threshold(0.5) == 0.0
+
+
+def test_cap_orders_scores_where_alpha_saturates():
+    """R27: with scores above ~37 alpha rounds to 1.0 in fp64 and every such
+    span would tie; the cap keeps the largest scores, which the exact rule
+    (descending alpha) also keeps, not merely the lowest span indices."""
+    W = np.eye(2)
+    q = np.array([1.0, 0.0])
+    a = np.array([40.0, 45.0, 50.0, 41.0, 60.0, 39.0])
+    s = np.stack([a, np.zeros_like(a)])
+    alpha, z = O.route_head(W, q, s, 0.5, cap=2)
+    assert np.all(alpha == 1.0)                            # saturated in fp64
+    assert np.nonzero(z)[0].tolist() == [2, 4]
+
+
+def _brute_cap(score, z, cap):
     cand = [j for j in range(len(z)) if z[j]]
     if len(cand) <= cap:
         return np.array(z)
     best = None
     for keep in itertools.combinations(cand, cap):
-        key = (sorted((-alpha[j] for j in keep)), sorted(keep))
+        key = (sorted((-score[j] for j in keep)), sorted(keep))
         if best is None or key < best[0]:
             best = (key, keep)
     out = np.zeros(len(z), bool)
@@ -238,21 +272,22 @@ def test_route_cap_brute_force_with_ties(seed):
     W = rng.standard_normal((dp, d))
     q = rng.standard_normal(d)
     s = rng.standard_normal((dp, N))
-    s[:, 1::3] = s[:, 0:1]          # repeated columns -> exactly equal alphas
+    s[:, 1::3] = s[:, 0:1]          # repeated columns -> exactly equal scores
+    a = np.einsum("i,ij,jn->n", q, W.T, s)                 # (W q) . s, an independent contraction
     for cap in (1, 2, 3, 5):
-        alpha, z0 = O.route_head(W, q, s, 0.3)
+        _, z0 = O.route_head(W, q, s, 0.3)
         _, z = O.route_head(W, q, s, 0.3, cap)
-        assert np.array_equal(z, _brute_cap(alpha, z0, cap))
+        assert np.array_equal(z, _brute_cap(a, z0, cap))
         assert z.sum() == min(cap, z0.sum()) and not (z & ~z0).any()
 
 
-def _brute_pool(alpha, z, budget):
+def _brute_pool(score, z, budget):
     """Every budget-subset of the routed triples of one sequence; the kept set
-    is the one subset that beats every triple it leaves out, comparing alpha
-    first and the lower (l, h, span) position second.  Returns it, checking
-    that exactly one subset has that property."""
+    is the one subset that beats every triple it leaves out, comparing the
+    score first and the lower (l, h, span) position second.  Returns it,
+    checking that exactly one subset has that property."""
     cand = [(k[1], k[2], int(S)) for k in sorted(z) for S in np.nonzero(z[k])[0]]
-    a = {(k[1], k[2], int(S)): float(alpha[k][S]) for k in z for S in np.nonzero(z[k])[0]}
+    a = {(k[1], k[2], int(S)): float(score[k][S]) for k in z for S in np.nonzero(z[k])[0]}
 
     def beats(x, y):   # x kept ahead of y
         return a[x] > a[y] or (a[x] == a[y] and x < y)
@@ -273,19 +308,20 @@ def test_pool_budget_brute_force_with_ties(seed):
     W = rng.standard_normal((L, Hq, dp, d))
     q = rng.standard_normal((L, Hq, d))
     s = rng.standard_normal((L, Hq, dp, N))
-    s[1, 0] = s[0, 1]                      # one head repeats another: equal alphas across heads
+    s[1, 0] = s[0, 1]                      # one head repeats another: equal scores across heads
     s[0, 0, :, 3] = s[0, 0, :, 1]          # and within a head
     q[1, 0] = q[0, 1]
     W[1, 0] = W[0, 1]
-    alpha, z = {}, {}
+    score, z = {}, {}
     for l in range(L):
         for h in range(Hq):
-            alpha[0, l, h], z[0, l, h] = O.route_head(W[l, h], q[l, h], s[l, h], 0.2)
+            score[0, l, h] = O.routing_score(W[l, h], q[l, h], s[l, h])
+            _, z[0, l, h] = O.route_head(W[l, h], q[l, h], s[l, h], 0.2)
     total = sum(int(v.sum()) for v in z.values())
     for budget in range(1, total + 2):
-        zp = O.pool_budget(alpha, z, budget)
+        zp = O.pool_budget(score, z, budget)
         kept = {(k[1], k[2], int(S)) for k in zp for S in np.nonzero(zp[k])[0]}
-        assert kept == _brute_pool(alpha, z, budget)
+        assert kept == _brute_pool(score, z, budget)
         assert len(kept) == min(budget, total)
         assert all(not (zp[k] & ~z[k]).any() for k in z)
 
@@ -296,33 +332,87 @@ def test_pool_budget_one_head_is_the_cap():
     W = rng.standard_normal((dp, d))
     q = rng.standard_normal(d)
     s = rng.standard_normal((dp, N))
-    alpha, z = O.route_head(W, q, s, 0.4)
+    a = O.routing_score(W, q, s)
+    _, z = O.route_head(W, q, s, 0.4)
     for cap in (1, 3, 7, int(z.sum()) - 1):
         _, zc = O.route_head(W, q, s, 0.4, cap)
-        zp = O.pool_budget({(0, 0, 0): alpha}, {(0, 0, 0): z}, cap)
+        zp = O.pool_budget({(0, 0, 0): a}, {(0, 0, 0): z}, cap)
         assert np.array_equal(zp[0, 0, 0], zc)
 
 
 def test_pool_budget_sequences_are_separate_and_monotone():
     rng = np.random.default_rng(9)
     B, L, Hq, N = 2, 2, 3, 30
-    alpha = {(b, l, h): rng.random(N) for b in range(B) for l in range(L) for h in range(Hq)}
-    z = {k: v > 0.5 for k, v in alpha.items()}
+    score = {(b, l, h): rng.standard_normal(N) for b in range(B) for l in range(L) for h in range(Hq)}
+    z = {k: v > 0.0 for k, v in score.items()}
     per_b = {b: sum(int(z[k].sum()) for k in z if k[0] == b) for b in range(B)}
     prev = None
     for budget in (0, 1, 5, 12, 20, max(per_b.values()), max(per_b.values()) + 3):
-        zp = O.pool_budget(alpha, z, budget)
+        zp = O.pool_budget(score, z, budget)
         for b in range(B):
             n = sum(int(zp[k].sum()) for k in zp if k[0] == b)
             assert n == (per_b[b] if budget == 0 else min(budget, per_b[b]))
-            # every kept alpha of b is at least every dropped one
-            kept = [alpha[k][S] for k in zp if k[0] == b for S in np.nonzero(zp[k])[0]]
-            drop = [alpha[k][S] for k in zp if k[0] == b for S in np.nonzero(z[k] & ~zp[k])[0]]
+            # every kept score of b is at least every dropped one
+            kept = [score[k][S] for k in zp if k[0] == b for S in np.nonzero(zp[k])[0]]
+            drop = [score[k][S] for k in zp if k[0] == b for S in np.nonzero(z[k] & ~zp[k])[0]]
             if kept and drop:
                 assert min(kept) >= max(drop)
         if prev is not None and budget > 0 and prev[0] > 0:
             assert all(not (prev[1][k] & ~zp[k]).any() for k in z)   # a larger budget keeps a superset
         prev = (budget, zp)
+
+
+def test_summary_keys_of_a_built_index():
+    """The summary key of query head h and span j of a built index is W^(l,h)
+    applied to the surprisal-weighted mean key of KV head h // G (np.average),
+    with distinct W per query head and distinct keys per KV head, so that
+    taking W of another head, or the keys of another KV head, fails."""
+    w = synth.WORKLOADS["tiny_2k"].scaled(T=700, L=2, Hq=6, Hkv=2, d=16, R=4, dprime=5, rank=3)
+    H, K, V = synth.kv_cache(w)
+    W = torch.stack([synth.routing_w(w, l) for l in range(w.L)]).double().numpy()
+    Hn, Kn = H[0].double().numpy(), K[0].double().numpy()
+    idx = O.build_index_b(Hn, Kn, V[0].double().numpy(), W, None, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False)
+    assert idx.n_spans >= 4
+    G = w.Hq // w.Hkv
+    for l in range(w.L):
+        for h in range(w.Hq):
+            for j, (a, n) in enumerate(idx.split.spans):
+                kbar = np.average(Kn[l, h // G, a:a + n], axis=0, weights=Hn[a:a + n])
+                ref = W[l, h] @ kbar
+                assert np.allclose(idx.s[l, h, :, j], ref, rtol=1e-12, atol=1e-12)
+                # another query head's W, or another KV head's keys, differ
+                other = W[l, (h + 1) % w.Hq] @ kbar
+                kb2 = np.average(Kn[l, (h // G + 1) % w.Hkv, a:a + n], axis=0, weights=Hn[a:a + n])
+                assert not np.allclose(idx.s[l, h, :, j], other)
+                assert not np.allclose(idx.s[l, h, :, j], W[l, h] @ kb2)
+
+
+def test_route_on_a_built_index_at_finite_tau():
+    """Routing of a built index at a finite tau against the Gram identity
+    (W q) . (W kbar) = q^T (W^T W) kbar, computed from the raw keys with
+    np.average, per query head and span."""
+    w = synth.WORKLOADS["tiny_2k"].scaled(T=900, L=2, Hq=4, Hkv=2, d=16, R=4, dprime=6, rank=3)
+    H, K, V = synth.kv_cache(w)
+    W = torch.stack([synth.routing_w(w, l) for l in range(w.L)]).double().numpy()
+    q = synth.query(w, 0).double().numpy()
+    Hn, Kn = H[0].double().numpy(), K[0].double().numpy()
+    idx = O.build_index_b(Hn, Kn, V[0].double().numpy(), W, None, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False)
+    G = w.Hq // w.Hkv
+    tau = 0.73
+    routed = 0
+    for l in range(w.L):
+        for h in range(w.Hq):
+            kb = np.stack([np.average(Kn[l, h // G, a:a + n], axis=0, weights=Hn[a:a + n])
+                           for a, n in idx.split.spans])
+            gram = np.einsum("i,ik,jk->j", q[0, l, h], W[l, h].T @ W[l, h], kb)
+            alpha, z = O.route_head(W[l, h], q[0, l, h], idx.s[l, h], tau)
+            assert np.allclose(alpha, 1.0 / (1.0 + np.exp(-gram)), rtol=1e-12)
+            far = np.abs(gram - math.log(tau / (1 - tau))) > 1e-9
+            assert np.array_equal(z[far], (1.0 / (1.0 + np.exp(-gram)) > tau)[far])
+            routed += int(z.sum())
+    assert 0 < routed < w.L * w.Hq * idx.n_spans
 
 
 def test_calibrate_tau_counts():
