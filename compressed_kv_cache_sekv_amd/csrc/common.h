@@ -157,7 +157,9 @@ struct RouteArgs {
   const float* s;
   const BMeta* meta;
   uint64_t* mask;           // [B][Lc][Hq][Wd]
-  float* alpha;             // [B][Lc][Hq][Wd*64] (scratch or caller)
+  float* alpha;             // [B][Lc][Hq][Wd*64] sigmoid of the score, or NULL
+  float* score;             // [B][Lc][Hq][Wd*64] score a = u . s (library
+                            // scratch the budget kernels rank), or NULL
   int32_t layer_begin, layer_count;
   int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
   int32_t budget;           // pooled budget per sequence (route_pool_kernel)

@@ -8,6 +8,12 @@
 // descending alpha until the GPU budget holds (here a per-(layer, head) cap,
 // ties to the lower span index).
 //
+// The sigmoid is strictly increasing, so z_S = [alpha_S > tau] is decided as
+// a_S > logit(tau) on the score a_S = u . s_S (fp32), with logit(tau) taken in
+// fp64 from the fp32 tau, and the budget ranks spans by a_S: the same
+// decisions as alpha in exact arithmetic, and still ordered where alpha
+// rounds to 1.0f (a_S above ~17).  alpha itself is an optional output.
+//
 // One workgroup per (b, 512-span chunk, head, layer); each wave scores 64
 // spans, one per lane, and writes one mask word with a ballot.  The budget cap
 // runs as a second small kernel (route_cap_kernel) on the finished masks.
@@ -16,6 +22,23 @@
 namespace sekv {
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Order-preserving 32-bit key of an fp32 score: unsigned comparison of keys
+// is the comparison of the scores (-0 is taken as +0).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// logit(tau) = ln(tau / (1 - tau)) in fp64: alpha > tau exactly when the
+// score exceeds it; -inf for tau <= 0, +inf for tau >= 1, NaN for a NaN tau
+// (which then routes nothing).
+__device__ __forceinline__ double logit_threshold(float tau) {
+  if (tau <= 0.f) return -HUGE_VAL;
+  if (tau >= 1.f) return HUGE_VAL;
+  const double t = (double)tau;
+  return log(t) - log1p(-t);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -142,8 +165,9 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   if (wi >= a.Wd) return;
   uint64_t* mrow = a.mask + row * a.Wd;
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
-  const float tau = a.tau[lc * a.Hq + h];
-  float alpha = 0.f;
+  float* srow = a.score ? a.score + row * (int64_t)a.Wd * 64 : nullptr;
+  const double thr = logit_threshold(a.tau[lc * a.Hq + h]);
+  float alpha = 0.f, dot = 0.f;
   bool z = false;
   if (live) {
     float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
@@ -154,31 +178,33 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
       d2 += s_u[4 * k + 2] * v4[k].z;
       d3 += s_u[4 * k + 3] * v4[k].w;
     }
-    const float dot = (d0 + d1) + (d2 + d3);
-    alpha = 1.f / (1.f + expf(-dot));
-    z = alpha > tau;
+    dot = (d0 + d1) + (d2 + d3);
+    z = (double)dot > thr;
+    if (arow) alpha = 1.f / (1.f + expf(-dot));
   }
   const uint64_t word = __ballot(z);
   if (lane == 0) mrow[wi] = word;
   if (arow) arow[S] = alpha;
+  if (srow) srow[S] = dot;
 }
 
 // Budget cap, one workgroup per (b, h, lc), after route_kernel: when more than
-// cap spans are expanded keep the cap largest alpha, ties to the lower span
-// index.  Each candidate is keyed (alpha bits, complemented span index): the
-// key order is alpha descending then index ascending, and keys are distinct,
-// so the kept set is exactly the keys at or above the cap-th largest key K*.
+// cap spans are expanded keep the cap largest scores (the order of alpha),
+// ties to the lower span index.  Each candidate is keyed (order key of the
+// score, complemented span index): the key order is score descending then
+// index ascending, and keys are distinct, so the kept set is exactly the keys
+// at or above the cap-th largest key K*.
 //  * Collect: thread t takes spans 32t .. 32t+31 (half a mask word and eight
 //    16-byte alpha loads, all issued together); a block scan of the per-thread
 //    counts places the candidates in LDS in span order.
-//  * Select: one histogram of the alpha bits over the candidates' own range
-//    (1024 bins by a shift of (bits - min); alpha >= 0, so the bits order like
-//    the values and the binning is monotone) finds the bin holding K* and how
-//    many of its keys are kept; only that bin's keys are then ranked against
-//    each other.  A boundary bin of more than kCapRank keys (alpha saturated
-//    at one value) falls back to an 8-pass radix select of the composite keys.
-//  * Candidate sets above kCapList fall back to a 4-pass radix select on alpha
-//    over global memory.
+//  * Select: one histogram of the score keys over the candidates' own range
+//    (1024 bins by a shift of (key - min); the keys order like the scores, so
+//    the binning is monotone) finds the bin holding K* and how many of its
+//    keys are kept; only that bin's keys are then ranked against each other.
+//    A boundary bin of more than kCapRank keys (many equal scores) falls back
+//    to an 8-pass radix select of the composite keys.
+//  * Candidate sets above kCapList fall back to a 4-pass radix select on the
+//    score keys over global memory.
 constexpr int kCapList = 2048;
 constexpr int kCapBins = 1024;
 constexpr int kCapRank = 256;
@@ -313,7 +339,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   const BMeta bm = a.meta[b];
   const int64_t row = ((int64_t)b * a.layer_count + lc) * a.Hq + h;
   uint64_t* mrow = a.mask + row * a.Wd;
-  const float* arow = a.alpha + row * (int64_t)a.Wd * 64;
+  const float* arow = a.score + row * (int64_t)a.Wd * 64;
   for (int w = tid; w < a.Wd; w += 256) s_new[w] = 0ull;
   if (tid == 0) s_nb = 0;
   // collect (mask bits at or past N_S are 0, so their alpha is never used)
@@ -336,7 +362,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if ((bits >> j) & 1u) {
-        const uint32_t ab = __float_as_uint(f4_at(av[j >> 2], j & 3));
+        const uint32_t ab = order_key(f4_at(av[j >> 2], j & 3));
         if (pos < kCapList) s_cand[pos] = ((uint64_t)ab << 32) | (uint64_t)(~(uint32_t)(32 * t + j));
         ++pos;
         lo = min(lo, ab);
@@ -425,16 +451,16 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
     for (int w = tid; w < a.Wd; w += 256) mrow[w] = s_new[w];
     return;
   }
-  // large candidate sets: radix select on alpha, ties by span index
+  // large candidate sets: radix select on the score keys, ties by span index
   int k = a.cap;
   auto cand = [&](int S, uint32_t& key) -> bool {
     const uint64_t word = mrow[S >> 6];
     if (!((word >> (S & 63)) & 1ull)) return false;
-    key = __float_as_uint(arow[S]);
+    key = order_key(arow[S]);
     return true;
   };
   const uint32_t vstar = radix_select(bm.n_spans, k, cand, s_hist, s_sel);
-  // k = number of spans with alpha == vstar to keep, lowest span index first
+  // k = number of spans with key == vstar to keep, lowest span index first
   for (int w = tid; w < a.Wd; w += 256) s_new[w] = mrow[w];
   __syncthreads();
   int carry = 0;
@@ -445,7 +471,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
     if (ww < a.Wd) {
       zz = s_new[ww];
       for (uint64_t bits = zz; bits; bits &= bits - 1)
-        tw += (__float_as_uint(arow[64 * ww + __builtin_ctzll(bits)]) == vstar);
+        tw += (order_key(arow[64 * ww + __builtin_ctzll(bits)]) == vstar);
     }
     int total;
     const int incl = block_scan256_total(tw, s_tmp, total);
@@ -454,7 +480,7 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
       uint64_t keep = 0;
       for (uint64_t bits = zz; bits; bits &= bits - 1) {
         const int bit = __builtin_ctzll(bits);
-        const uint32_t key = __float_as_uint(arow[64 * ww + bit]);
+        const uint32_t key = order_key(arow[64 * ww + bit]);
         if (key > vstar) keep |= 1ull << bit;
         else if (key == vstar) {
           if (rank < k) keep |= 1ull << bit;
@@ -469,23 +495,23 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
 
 // Budget pooled over a routing call, one 1024-thread workgroup per sequence b,
 // after route_kernel: among the routed (layer, head, span) triples of b in the
-// call, keep the `budget` largest alpha, ties to the lower (layer, head,
-// span) position (the flat order of the mask words).  The budget rule of the
+// call, keep the `budget` largest scores (the order of alpha), ties to the
+// lower (layer, head, span) position (the flat order of the mask words).  The budget rule of the
 // Technical-details section of the SeKV article, read over the whole call
 // instead of one (layer, head).
 //  * Collect: threads take 32-span halves of the mask words, two a round, each
-//    with its 32 alpha as eight 16-byte loads, all issued before use; every
-//    routed triple (alpha bits, flat position) goes to an LDS list at a slot
+//    with its 32 scores as eight 16-byte loads, all issued before use; every
+//    routed triple (score key, flat position) goes to an LDS list at a slot
 //    from one LDS counter per wave (wave prefixes by bit-sliced ballots).  A
 //    sequence within its budget stops there.
 //  * Radix select of the budget-th largest key over the list, binned over the
 //    keys' own range (offsets key - min, at most 11 bits a pass from the top
-//    of max - min; alpha >= 0, so the bits order like the values).
+//    of max - min; the keys order like the scores).
 //  * Keep every larger key.  If the boundary key's equals are not all kept,
 //    their positions are ranked against each other and the lowest kept.
 // When the routed triples or the halves do not fit in LDS (or the boundary
 // has more equal keys than LDS ranks), the passes sweep the mask words and
-// alpha in global memory in flat order instead: fixed 11, 11, 10-bit passes,
+// scores in global memory in flat order instead: fixed 11, 11, 10-bit passes,
 // then a block scan of the equal keys chunk by chunk.
 constexpr int kPoolThreads = 1024;
 constexpr int kPoolBins = 2048;
@@ -576,7 +602,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
   const int64_t rows = (int64_t)a.layer_count * a.Hq;
   const int64_t nh = rows * a.Wd * 2;                       // 32-span halves of b's words
   uint32_t* mh = (uint32_t*)(a.mask + (int64_t)b * rows * a.Wd);
-  const float* ab = a.alpha + (int64_t)b * rows * a.Wd * 64;
+  const float* ab = a.score + (int64_t)b * rows * a.Wd * 64;
   int k = a.budget;
   if (tid == 0) s_count = 0;
   for (int i = tid; i < kPoolHalves; i += kPoolThreads) s_new[i] = 0u;
@@ -597,7 +623,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if ((bits0 >> j) & 1u) {
-        const uint32_t key = __float_as_uint(f4_at(av0[j >> 2], j & 3));
+        const uint32_t key = order_key(f4_at(av0[j >> 2], j & 3));
         kmin = min(kmin, key);
         kmax = max(kmax, key);
         if (pos < kPoolList) {
@@ -610,7 +636,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       if ((bits1 >> j) & 1u) {
-        const uint32_t key = __float_as_uint(f4_at(av1[j >> 2], j & 3));
+        const uint32_t key = order_key(f4_at(av1[j >> 2], j & 3));
         kmin = min(kmin, key);
         kmax = max(kmax, key);
         if (pos < kPoolList) {
@@ -709,7 +735,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
         load_half(mh, ab, t, nh, bits, av);
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-          const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+          const uint32_t key = order_key(f4_at(av[j >> 2], j & 3));
           if (((bits >> j) & 1u) && (key & pmask) == prefix)
             atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nbins - 1)], 1u);
         }
@@ -733,7 +759,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
     load_half(mh, ab, t, nh, bits, av);
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const uint32_t key = __float_as_uint(f4_at(av[j >> 2], j & 3));
+      const uint32_t key = order_key(f4_at(av[j >> 2], j & 3));
       const bool on = (bits >> j) & 1u;
       keep |= (uint32_t)(on && key > vstar) << j;
       eq |= (uint32_t)(on && key == vstar) << j;

@@ -52,24 +52,17 @@ constexpr uint32_t CTX_MAGIC = 0x53454b43u;   // "SEKC"
 constexpr uint32_t IDX_MAGIC = 0x53454b49u;   // "SEKI"
 constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
 
-// Work decomposition of the decode kernel: at most this many resident 32-row
-// steps (default 8, two per wave) and compressed spans of the sequence
-// (default 48: where the items run in many waves of workgroups, larger items
-// amortise each one's start-up chain; 32 and 64 measured slower on the batch of
-// 32 sequences) per workgroup; the larger count sets the items of a KV head,
-// raised (SEKV_FILL_SLOTS, default on) until the items fill the attention
-// kernel's resident workgroup slots, keeping at least kMinFillSpans spans of
-// the sequence per item.  SEKV_STEPS_PER_ITEM / SEKV_SPANS_PER_ITEM /
-// SEKV_FILL_SLOTS override them when an index is created (tuning).
-int env_int(const char* name, int dflt, int lo, int hi) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  const int x = atoi(v);
-  return (x >= lo && x <= hi) ? x : dflt;
-}
-int steps_per_item() { return env_int("SEKV_STEPS_PER_ITEM", 8, 1, 1 << 20); }
-int spans_per_item() { return env_int("SEKV_SPANS_PER_ITEM", 48, 1, kMaxSpanList); }
-bool fill_slots() { return env_int("SEKV_FILL_SLOTS", 1, 0, 1) != 0; }
+// Work decomposition of the decode kernel: at most kStepsPerItem resident
+// 32-row steps (two per wave) and kSpansPerItem compressed spans of the
+// sequence per workgroup (where the items run in many waves of workgroups,
+// larger items amortise each one's start-up chain; 32 and 64 measured slower
+// on the batch of 32 sequences); the larger count sets the items of a KV
+// head, raised until the items fill the attention kernel's resident
+// workgroup slots, keeping at least kMinFillSpans spans of the sequence per
+// item.
+constexpr int kStepsPerItem = 8;
+constexpr int kSpansPerItem = 48;
+static_assert(kSpansPerItem <= kMaxSpanList, "items hold at most one span per lane");
 constexpr int kMinFillSpans = 16;
 
 // Device buffer owned by the library.
@@ -189,8 +182,8 @@ struct sekv_index {
   std::vector<WorkItem> items;
   std::vector<int32_t> bg_first;
   DBuf d_items, d_bg_first, d_part;
-  // routing scratch
-  DBuf d_alpha, d_tau_inf;
+  // routing scratch: scores ranked by the budget kernels; alpha for calibration
+  DBuf d_score, d_alpha, d_tau_inf;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
 
@@ -238,6 +231,10 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
 // n_spans, n_raw: per b; lens: concatenated span lengths.
 sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::vector<int32_t>& n_spans,
                  const std::vector<int32_t>& n_raw, const std::vector<int32_t>& lens) {
+  for (int b = 0; b < p->B; ++b)
+    if (n_spans[b] > 64 * kMaxWords)
+      return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d: the routing masks hold at most %d per sequence",
+                  n_spans[b], b, 64 * kMaxWords);
   x->B = p->B; x->L = p->L; x->Hq = p->Hq; x->Hkv = p->Hkv; x->D = p->d; x->R = p->R;
   x->dp = p->dprime; x->G = p->Hq / p->Hkv; x->tier = p->tier;
   x->meta.assign(x->B, BMeta{});
@@ -283,16 +280,16 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   x->Wd = std::max(1, (x->max_spans + 63) / 64);
   // decode work items: nj per (b, g), each with an equal slice of the
   // resident steps and an equal share of the routed union; nj covers the
-  // larger of the two (at most spans_per_item union spans and
-  // steps_per_item steps an item)
-  const int spi = spans_per_item(), spw = steps_per_item();
+  // larger of the two (at most kSpansPerItem union spans and kStepsPerItem
+  // steps an item)
+  const int spi = kSpansPerItem, spw = kStepsPerItem;
   // workgroups of the attention kernel resident at once on this device: the
   // items of one launch (one layer) share them out per (b, g).  One wave of
   // workgroups that fills them measured fastest (items of fewer routed spans
   // shorten each wave's chain of blob round trips; a second wave of
   // workgroups costs more than it saves).
   int fill = 0;
-  if (fill_slots() && attend_supported(x->D, x->G, x->R)) {
+  if (attend_supported(x->D, x->G, x->R)) {
     int slots = 0;
     HIP_TRY(attend_slots(x->D, x->G, x->R, x->Wd, x->ctx->device, &slots));
     fill = slots / std::max(1, x->B * x->Hkv);
@@ -372,7 +369,7 @@ void free_index(sekv_index* x) {
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
                   &x->d_ring, &x->d_ring_off, &x->d_usize, &x->d_ubase, &x->d_items, &x->d_bg_first,
-                  &x->d_part, &x->d_alpha, &x->d_tau_inf};
+                  &x->d_part, &x->d_score, &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
   if (x->h_usize) (void)hipHostFree(x->h_usize);
@@ -393,9 +390,11 @@ sekv_status set_device(sekv_ctx* c) {
   return SEKV_OK;
 }
 
-sekv_status ensure_route_scratch(sekv_index* x, int lc) {
+// Per-span routing scratch of lc layers: the scores (budget kernels) or alpha
+// (calibration).
+sekv_status ensure_route_scratch(sekv_index* x, int lc, DBuf& buf) {
   const size_t rows = (size_t)x->B * lc * x->Hq;
-  HIP_TRY(dgrow(x->d_alpha, rows * x->Wd * 64 * sizeof(float)));
+  HIP_TRY(dgrow(buf, rows * x->Wd * 64 * sizeof(float)));
   return SEKV_OK;
 }
 
@@ -694,6 +693,9 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
   int64_t tot_sp = 0, tot_raw = 0;
   for (int b = 0; b < B; ++b) {
     if (n_spans[b] < 0 || n_raw[b] < 0) return fail(SEKV_EINVAL, "negative count at b=%d", b);
+    if (n_spans[b] > 64 * kMaxWords)
+      return fail(SEKV_EUNSUPPORTED, "%d spans in sequence %d: the routing masks hold at most %d per sequence",
+                  n_spans[b], b, 64 * kMaxWords);
     tot_sp += n_spans[b];
     tot_raw += n_raw[b];
   }
@@ -821,46 +823,74 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
   return SEKV_OK;
 }
 
-extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const sekv_host_index_out* h) {
+namespace {
+
+// Export of sequences [bb, bb + bc) and layers [lb, lb + lc): the logical
+// layout with bc sequences and lc in place of L.
+sekv_status export_part(sekv_ctx* c, const sekv_index* x, int bb, int bc, int lb, int lc,
+                        const sekv_host_index_out* h) {
   sekv_status st = check_idx(c, x);
   if (st) return st;
   if (!h) return fail(SEKV_EINVAL, "null host index");
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (bb < 0 || bc < 1 || bb + bc > x->B)
+    return fail(SEKV_EINVAL, "sequence range [%d, %d) outside [0, %d)", bb, bb + bc, x->B);
   if ((st = set_device(c))) return st;
   hipStream_t stream = c->stream;
-  const int B = x->B, D = x->D, R = x->R, L = x->L, Hkv = x->Hkv, Hq = x->Hq, dp = x->dp;
+  const int D = x->D, R = x->R, L = lc, Hkv = x->Hkv, Hq = x->Hq, dp = x->dp;
   const bool want_res = h->k_res || h->v_res;
   const bool want_fac = h->uk || h->uv || h->vkt || h->vvt || h->smk || h->smv;
-  std::vector<bf16_t> kres(want_res ? (size_t)x->kres_elems : 0), vres(want_res ? (size_t)x->kres_elems : 0);
-  std::vector<float> s(h->s ? (size_t)x->s_elems : 0);
-  std::vector<int32_t> sst((size_t)std::max<int64_t>(x->total_spans, 1)), rp((size_t)std::max<int64_t>(x->total_raw, 1));
+  const BMeta& m0 = x->meta[bb];
+  const BMeta& m1 = x->meta[bb + bc - 1];
+  // device ranges of the sequences: resident rows, summary keys, span tables,
+  // and each layer's factor region
+  const int64_t res0 = m0.res_base, res1 = m1.res_base + (int64_t)x->L * Hkv * m1.n_res_pad * D;
+  const int64_t s0 = m0.s_base, s1 = m1.s_base + (int64_t)x->L * Hq * dp_pad4(dp) * m1.s_pad;
+  const int64_t sp0 = m0.span_base, sp1 = m1.span_base + m1.n_spans;
+  const int64_t rw0 = m0.raw_base, rw1 = m1.raw_base + m1.n_raw;
+  const int64_t pb0 = m0.pool_base, pb1 = m1.pool_base + (int64_t)Hkv * m1.pool_lg;
+  std::vector<bf16_t> kres(want_res ? (size_t)(res1 - res0) : 0), vres(want_res ? (size_t)(res1 - res0) : 0);
+  std::vector<float> s(h->s ? (size_t)(s1 - s0) : 0);
+  std::vector<int32_t> sst((size_t)std::max<int64_t>(sp1 - sp0, 1)), rp((size_t)std::max<int64_t>(rw1 - rw0, 1));
   std::vector<uint8_t> pool;
-  const uint8_t* pool_src = x->h_pool;
-  if (x->tier == SEKV_TIER_HBM && want_fac) {
-    pool.resize((size_t)x->pool_bytes);
-    HIP_TRY(hipMemcpyAsync(pool.data(), x->d_pool.p, pool.size(), hipMemcpyDeviceToHost, stream));
-    pool_src = pool.data();
+  const int64_t preg = pb1 - pb0;   // bytes of the sequences' region in one layer
+  if (want_fac) {
+    pool.resize((size_t)std::max<int64_t>(lc * preg, 1));
+    for (int l = 0; l < lc && preg > 0; ++l) {
+      const size_t src = (size_t)(lb + l) * x->layer_bytes + pb0;
+      if (x->tier == SEKV_TIER_HBM)
+        HIP_TRY(hipMemcpyAsync(pool.data() + (size_t)l * preg, (const uint8_t*)x->d_pool.p + src, (size_t)preg,
+                               hipMemcpyDeviceToHost, stream));
+      else
+        memcpy(pool.data() + (size_t)l * preg, x->h_pool + src, (size_t)preg);
+    }
   }
   if (want_res) {
-    HIP_TRY(hipMemcpyAsync(kres.data(), x->d_kres.p, 2 * kres.size(), hipMemcpyDeviceToHost, stream));
-    HIP_TRY(hipMemcpyAsync(vres.data(), x->d_vres.p, 2 * vres.size(), hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipMemcpyAsync(kres.data(), (const bf16_t*)x->d_kres.p + res0, 2 * kres.size(), hipMemcpyDeviceToHost,
+                           stream));
+    HIP_TRY(hipMemcpyAsync(vres.data(), (const bf16_t*)x->d_vres.p + res0, 2 * vres.size(), hipMemcpyDeviceToHost,
+                           stream));
   }
-  if (h->s) HIP_TRY(hipMemcpyAsync(s.data(), x->d_s.p, 4 * s.size(), hipMemcpyDeviceToHost, stream));
-  if (x->total_spans)
-    HIP_TRY(hipMemcpyAsync(sst.data(), x->d_span_start.p, 4 * (size_t)x->total_spans, hipMemcpyDeviceToHost, stream));
-  if (x->total_raw)
-    HIP_TRY(hipMemcpyAsync(rp.data(), x->d_raw_pos.p, 4 * (size_t)x->total_raw, hipMemcpyDeviceToHost, stream));
+  if (h->s)
+    HIP_TRY(hipMemcpyAsync(s.data(), (const float*)x->d_s.p + s0, 4 * s.size(), hipMemcpyDeviceToHost, stream));
+  if (sp1 > sp0)
+    HIP_TRY(hipMemcpyAsync(sst.data(), (const int32_t*)x->d_span_start.p + sp0, 4 * (size_t)(sp1 - sp0),
+                           hipMemcpyDeviceToHost, stream));
+  if (rw1 > rw0)
+    HIP_TRY(hipMemcpyAsync(rp.data(), (const int32_t*)x->d_raw_pos.p + rw0, 4 * (size_t)(rw1 - rw0),
+                           hipMemcpyDeviceToHost, stream));
   HIP_TRY(hipStreamSynchronize(stream));
-  if (h->span_start) std::copy(sst.begin(), sst.begin() + x->total_spans, h->span_start);
-  if (h->span_len) std::copy(x->h_span_len.begin(), x->h_span_len.end(), h->span_len);
-  if (h->raw_pos) std::copy(rp.begin(), rp.begin() + x->total_raw, h->raw_pos);
+  if (h->span_start) std::copy(sst.begin(), sst.begin() + (sp1 - sp0), h->span_start);
+  if (h->span_len) std::copy(x->h_span_len.begin() + sp0, x->h_span_len.begin() + sp1, h->span_len);
+  if (h->raw_pos) std::copy(rp.begin(), rp.begin() + (rw1 - rw0), h->raw_pos);
   int64_t kro = 0, so = 0, tko = 0, spo = 0;
-  for (int b = 0; b < B; ++b) {
+  for (int b = bb; b < bb + bc; ++b) {
     const BMeta& m = x->meta[b];
     const int NS = m.n_spans, NR = m.n_res;
     int64_t ntok = 0;
     for (int S = 0; S < NS; ++S) ntok += x->h_span_len[m.span_base + S];
     for (int lg = 0; want_res && lg < L * Hkv; ++lg) {
-      const int64_t src = m.res_base + (int64_t)lg * m.n_res_pad * D;
+      const int64_t src = m.res_base - res0 + ((int64_t)lb * Hkv + lg) * m.n_res_pad * D;
       for (int r = 0; r < NR; ++r)
         for (int d = 0; d < D; ++d) {
           const int64_t dst = kro + ((int64_t)lg * NR + r) * D + d;
@@ -874,7 +904,7 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
         for (int j = 0; j < dp; ++j)
           for (int S = 0; S < NS; ++S)
             h->s[so + ((int64_t)lh * dp + j) * NS + S] =
-                s[m.s_base + (int64_t)lh * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))];
+                s[m.s_base - s0 + ((int64_t)lb * Hq + lh) * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))];
     so += (int64_t)L * Hq * dp * NS;
     for (int l = 0; want_fac && l < L; ++l)
       for (int g = 0; g < Hkv; ++g) {
@@ -882,7 +912,7 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
         int64_t toff = 0;
         for (int S = 0; S < NS; ++S) {
           const int n = x->h_span_len[m.span_base + S], np = Blob::npad(n);
-          const uint8_t* blob = pool_src + (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg +
+          const uint8_t* blob = pool.data() + (int64_t)l * preg + (m.pool_base - pb0) + (int64_t)g * m.pool_lg +
                                 x->h_span_off[m.span_base + S];
           const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt(R, D));
           const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(R, D));
@@ -915,6 +945,20 @@ extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const
   return SEKV_OK;
 }
 
+}  // namespace
+
+extern "C" sekv_status sekv_index_export(sekv_ctx* c, const sekv_index* x, const sekv_host_index_out* h) {
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  return export_part(c, x, 0, x->B, 0, x->L, h);
+}
+
+extern "C" sekv_status sekv_index_export_part(sekv_ctx* c, const sekv_index* x, int32_t seq_begin,
+                                              int32_t seq_count, int32_t layer_begin, int32_t layer_count,
+                                              const sekv_host_index_out* h) {
+  return export_part(c, x, seq_begin, seq_count, layer_begin, layer_count, h);
+}
+
 // ================================================================= decode ===
 
 extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc, const void* q,
@@ -927,7 +971,7 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   if (cap < 0) return fail(SEKV_EINVAL, "cap < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
-  if ((st = ensure_route_scratch(x, lc))) return st;
+  if (cap > 0 && (st = ensure_route_scratch(x, lc, x->d_score))) return st;
   RouteArgs ra{};
   ra.q = (const bf16_t*)q;
   ra.tau = tau;
@@ -935,7 +979,8 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   ra.s = (const float*)x->d_s.p;
   ra.meta = (const BMeta*)x->d_meta.p;
   ra.mask = mask;
-  ra.alpha = alpha ? alpha : (cap > 0 ? (float*)x->d_alpha.p : nullptr);
+  ra.alpha = alpha;
+  ra.score = cap > 0 ? (float*)x->d_score.p : nullptr;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = cap;
@@ -957,7 +1002,7 @@ extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int3
   if (budget < 0) return fail(SEKV_EINVAL, "budget < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
-  if ((st = ensure_route_scratch(x, lc))) return st;
+  if (budget > 0 && (st = ensure_route_scratch(x, lc, x->d_score))) return st;
   RouteArgs ra{};
   ra.q = (const bf16_t*)q;
   ra.tau = tau;
@@ -965,7 +1010,8 @@ extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int3
   ra.s = (const float*)x->d_s.p;
   ra.meta = (const BMeta*)x->d_meta.p;
   ra.mask = mask;
-  ra.alpha = alpha ? alpha : (budget > 0 ? (float*)x->d_alpha.p : nullptr);
+  ra.alpha = alpha;
+  ra.score = budget > 0 ? (float*)x->d_score.p : nullptr;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = 0;
@@ -988,7 +1034,7 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
   if (!(frac >= 0.f && frac <= 1.f)) return fail(SEKV_EINVAL, "frac must be in [0, 1]");
   if (x->total_spans < 2) return fail(SEKV_EINVAL, "calibration needs at least 2 spans");
   if ((st = set_device(c))) return st;
-  if ((st = ensure_route_scratch(x, lc))) return st;
+  if ((st = ensure_route_scratch(x, lc, x->d_alpha))) return st;
   const size_t ntau = (size_t)lc * x->Hq;
   if (!x->d_tau_inf.p || x->d_tau_inf.n < 4 * ntau) {
     HIP_TRY(dalloc(x->d_tau_inf, 4 * ntau));
@@ -1007,6 +1053,7 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
   ra.meta = (const BMeta*)x->d_meta.p;
   ra.mask = (uint64_t*)mk.p;
   ra.alpha = (float*)x->d_alpha.p;
+  ra.score = nullptr;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = 0;

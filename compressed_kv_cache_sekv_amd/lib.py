@@ -28,6 +28,7 @@ STATUS = {0: "SEKV_OK", 1: "SEKV_EINVAL", 2: "SEKV_ENOMEM", 3: "SEKV_EHIP",
 # Every entry point declared in include/sekv.h.
 EXPORTS = ("sekv_create", "sekv_destroy", "sekv_last_error", "sekv_max_spans",
            "sekv_validate_params", "sekv_rsvd_batched", "sekv_build_index", "sekv_index_import", "sekv_index_export",
+           "sekv_index_export_part",
            "sekv_index_get_info", "sekv_index_counts", "sekv_index_free",
            "sekv_route", "sekv_route_pooled", "sekv_calibrate_tau", "sekv_decode_attend",
            "sekv_timing_enable", "sekv_timing_read")
@@ -90,6 +91,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.sekv_build_index.argtypes = [vp, C.POINTER(BuildParams), vp, vp, vp, vp, vp, C.POINTER(vp)]
     lib.sekv_index_import.argtypes = [vp, C.POINTER(BuildParams), C.POINTER(HostIndex), C.POINTER(vp)]
     lib.sekv_index_export.argtypes = [vp, vp, C.POINTER(HostIndexOut)]
+    lib.sekv_index_export_part.argtypes = [vp, vp, i32, i32, i32, i32, C.POINTER(HostIndexOut)]
     lib.sekv_index_get_info.argtypes = [vp, C.POINTER(IndexInfo)]
     lib.sekv_index_counts.argtypes = [vp, vp, vp]
     lib.sekv_index_free.argtypes = [vp]
@@ -255,20 +257,35 @@ class Index:
         check(lib().sekv_index_export(self.ctx.h, self.h, C.byref(ho)))
         return out["span_start"], out["span_len"], out["raw_pos"]
 
-    def export(self) -> dict:
-        """Logical-layout numpy arrays of the whole index."""
+    def export(self, layer_begin: int = 0, layer_count: Optional[int] = None, fields=None,
+               seq_begin: int = 0, seq_count: Optional[int] = None) -> dict:
+        """Logical-layout numpy arrays of layers [layer_begin, layer_begin +
+        layer_count) of sequences [seq_begin, seq_begin + seq_count) (default:
+        everything); `fields` limits which arrays are copied back."""
         i = self.info
-        L, Hkv, Hq, d, R, dp = i.L, i.Hkv, i.Hq, i.d, i.R, i.dprime
-        NS, NR, NT = int(i.total_spans), int(i.total_raw), int(i.total_span_tokens)
-        nres = int(self.n_spans.sum() + self.n_raw.sum())
+        lc = i.L - layer_begin if layer_count is None else layer_count
+        bc = i.B - seq_begin if seq_count is None else seq_count
+        Hkv, Hq, d, R, dp = i.Hkv, i.Hq, i.d, i.R, i.dprime
+        sl = slice(seq_begin, seq_begin + bc)
+        NS, NR = int(self.n_spans[sl].sum()), int(self.n_raw[sl].sum())
+        lens = self.span_lengths()[int(self.n_spans[:seq_begin].sum()):][:NS]
+        NT = int(lens.sum())
+        nres = NS + NR
         u16 = np.uint16
-        out = dict(span_start=np.zeros(NS, np.int32), span_len=np.zeros(NS, np.int32),
-                   raw_pos=np.zeros(NR, np.int32),
-                   k_res=np.zeros(L * Hkv * nres * d, u16), v_res=np.zeros(L * Hkv * nres * d, u16),
-                   s=np.zeros(L * Hq * dp * NS, np.float32),
-                   uk=np.zeros(L * Hkv * NT * R, u16), uv=np.zeros(L * Hkv * NT * R, u16),
-                   vkt=np.zeros(L * Hkv * NS * R * d, u16), vvt=np.zeros(L * Hkv * NS * R * d, u16),
-                   smk=np.zeros(L * Hkv * NS * R, np.float32), smv=np.zeros(L * Hkv * NS * R, np.float32))
+        shapes = dict(span_start=(NS, np.int32), span_len=(NS, np.int32), raw_pos=(NR, np.int32),
+                      k_res=(lc * Hkv * nres * d, u16), v_res=(lc * Hkv * nres * d, u16),
+                      s=(lc * Hq * dp * NS, np.float32),
+                      uk=(lc * Hkv * NT * R, u16), uv=(lc * Hkv * NT * R, u16),
+                      vkt=(lc * Hkv * NS * R * d, u16), vvt=(lc * Hkv * NS * R * d, u16),
+                      smk=(lc * Hkv * NS * R, np.float32), smv=(lc * Hkv * NS * R, np.float32))
+        out = {k: np.zeros(n, t) for k, (n, t) in shapes.items() if fields is None or k in fields}
         ho = HostIndexOut(**{k: (v.ctypes.data if v.size else None) for k, v in out.items()})
-        check(lib().sekv_index_export(self.ctx.h, self.h, C.byref(ho)))
+        check(lib().sekv_index_export_part(self.ctx.h, self.h, int(seq_begin), int(bc), int(layer_begin), int(lc),
+                                           C.byref(ho)))
         return out
+
+    def span_lengths(self) -> np.ndarray:
+        """Span lengths of every sequence, concatenated over b (cached)."""
+        if getattr(self, "_lens", None) is None:
+            self._lens = self.spans()[1]
+        return self._lens

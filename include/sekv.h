@@ -220,6 +220,15 @@ sekv_status sekv_index_import(sekv_ctx* ctx, const sekv_build_params* p,
 sekv_status sekv_index_export(sekv_ctx* ctx, const sekv_index* idx,
                               const sekv_host_index_out* h);
 
+/* As sekv_index_export for sequences [seq_begin, seq_begin + seq_count) and
+ * layers [layer_begin, layer_begin + layer_count) only: the logical layout
+ * of those sequences (concatenated in order), with layer_count in place of L
+ * (layer layer_begin first).  SEKV_EINVAL for a range outside [0, B) or
+ * [0, L).  Synchronises the stream. */
+sekv_status sekv_index_export_part(sekv_ctx* ctx, const sekv_index* idx, int32_t seq_begin,
+                                   int32_t seq_count, int32_t layer_begin, int32_t layer_count,
+                                   const sekv_host_index_out* h);
+
 sekv_status sekv_index_get_info(const sekv_index* idx, sekv_index_info* info);
 
 /* Per-sequence counts: n_spans[b] = N_S(b), n_raw[b] = N_raw(b) (host [B]). */
@@ -231,17 +240,24 @@ void sekv_index_free(sekv_index* idx);
 /* ------------------------------------------------------------------- decode */
 
 /* Stage 1 routing ([Method]; [Tech]) for layers [layer_begin, layer_begin +
- * layer_count): u = W^(l,h) q^(l,h); alpha_S = sigmoid(u . s_S);
- * z_S = [alpha_S > tau^(l,h)].  With cap > 0, a (b, l, h) with more than cap
- * expansions keeps the cap largest alpha, ties to the lower span index
- * ([Tech]: spans taken in descending alpha until the budget holds).
+ * layer_count): u = W^(l,h) q^(l,h); score a_S = u . s_S (fp32);
+ * alpha_S = sigmoid(a_S); z_S = [alpha_S > tau^(l,h)].  The sigmoid is
+ * strictly increasing, so z_S is decided as a_S > logit(tau) = ln(tau / (1 -
+ * tau)), taken in fp64 from the fp32 tau (every span for tau <= 0, none for
+ * tau >= 1 or NaN): the same decision in exact arithmetic, and exact where
+ * alpha rounds to 1 in fp32.  With cap > 0, a (b, l, h) with more than cap
+ * expansions keeps the cap largest a_S (the order of alpha), ties to the
+ * lower span index ([Tech]: spans taken in descending alpha until the budget
+ * holds).
  *   q      device bf16 [B][layer_count][Hq][d]
  *   tau    device fp32 [layer_count][Hq]  (+-inf allowed)
  *   mask   device uint64 [B][layer_count][Hq][mask_words]; bit j of word w is
  *          z of span 64w + j; bits at or past N_S(b) are 0
  *   alpha  device fp32 [B][layer_count][Hq][mask_words * 64], 16-byte
- *          aligned (SEKV_EINVAL otherwise), or NULL; entries at or past N_S(b)
- *          are unspecified */
+ *          aligned (SEKV_EINVAL otherwise), or NULL: sigmoid(a_S) in fp32,
+ *          for inspection; entries at or past N_S(b) are unspecified
+ * With cap > 0 the call uses index-owned scratch for the scores (grown on
+ * first use); calls on one context are ordered on its stream. */
 sekv_status sekv_route(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                        int32_t layer_count, const void* q, const float* tau,
                        int32_t cap, uint64_t* mask, float* alpha);
@@ -249,15 +265,16 @@ sekv_status sekv_route(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin
 /* Stage 1 routing as sekv_route with no per-head cap, then the budget rule
  * ([Tech]: spans taken in descending alpha until the budget holds) applied to
  * a pool: for each sequence b, over every (layer, head, span) triple of the
- * call, keep the budget largest alpha among the routed triples, ties to the
- * lower (layer, head, span) position (the flat order of the mask words).
+ * call, keep the budget largest scores a_S (the order of alpha) among the
+ * routed triples, ties to the lower (layer, head, span) position (the flat
+ * order of the mask words).
  * A call over one layer pools that layer's heads; a call over all layers
  * pools the whole model (which needs every layer's query at once: a decode
  * loop whose layer l + 1 query depends on layer l pools per layer).
  * budget 0 = no budget; budget < 0 is SEKV_EINVAL.
- *   q, tau, mask, alpha  as for sekv_route (alpha NULL: library scratch)
- * Calls that overlap on one context's scratch (alpha NULL) must be ordered on
- * its stream, as every call on a context is. */
+ *   q, tau, mask, alpha  as for sekv_route
+ * With budget > 0 the call uses index-owned score scratch, as sekv_route with
+ * a cap does. */
 sekv_status sekv_route_pooled(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                               int32_t layer_count, const void* q, const float* tau,
                               int32_t budget, uint64_t* mask, float* alpha);

@@ -73,26 +73,26 @@ def dev(x, dtype=None):
     return t.contiguous().cuda()
 
 
-def oracle_route_all(c, q, tau, cap=0):
+def gpu_route(idx, c, q, tau, cap=0, lb=0, lc=None, alpha=False):
+    """The library's routing of layers [lb, lb + lc): mask words [B, lc, Hq, Wd]
+    (and alpha when asked)."""
     w = c.w
-    return O.route_step(c.idxs, c.W.double().numpy(), q.double().numpy(), tau, cap)
-
-
-def gpu_route(idx, c, q, tau, cap=0):
-    w = c.w
+    lc = w.L - lb if lc is None else lc
     Wd = idx.mask_words
-    mask = torch.zeros(w.B, w.L, w.Hq, Wd, dtype=torch.int64, device="cuda")
-    alpha = torch.zeros(w.B, w.L, w.Hq, Wd * 64, dtype=torch.float32, device="cuda")
-    idx.route(0, w.L, dev(q), dev(tau, torch.float32), cap, mask, alpha)
+    mask = torch.zeros(w.B, lc, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    al = torch.zeros(w.B, lc, w.Hq, Wd * 64, dtype=torch.float32, device="cuda") if alpha else None
+    idx.route(lb, lc, dev(q[:, lb:lb + lc]), dev(np.asarray(tau)[lb:lb + lc], torch.float32), cap, mask, al)
     torch.cuda.synchronize()
-    return mask.cpu().numpy().view(np.uint64), alpha.cpu().numpy()
+    words = mask.cpu().numpy().view(np.uint64)
+    return (words, al.cpu().numpy()) if alpha else words
 
 
-def gpu_decode(idx, c, q, mask_np, stats=False):
+def gpu_decode(idx, c, q, mask_np, stats=False, lb=0, lc=None):
     w = c.w
-    out = torch.zeros(w.B, w.L, w.Hq, w.d, dtype=torch.float32, device="cuda")
+    lc = w.L - lb if lc is None else lc
+    out = torch.zeros(w.B, lc, w.Hq, w.d, dtype=torch.float32, device="cuda")
     m = torch.from_numpy(np.ascontiguousarray(mask_np).view(np.int64)).cuda()
-    st = idx.decode_attend(0, w.L, dev(q), m, out, stats=stats)
+    st = idx.decode_attend(lb, lc, dev(q[:, lb:lb + lc]), m, out, stats=stats)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), st
 
@@ -100,12 +100,27 @@ def gpu_decode(idx, c, q, mask_np, stats=False):
 # ----------------------------------------------------------- identical index
 
 def test_import_export_roundtrip(ctx, sl):
-    c = case("tiny")
+    c = case("8b_l2_cap")
     arrays = SC.import_arrays(c)
     idx = ctx.import_index(sl.build_params(c.w), arrays)
     ex = idx.export()
     for k, v in ex.items():
         assert np.array_equal(v, arrays[k].ravel()), k
+    # one layer at a time: the slices of the whole export
+    w, i = c.w, c.idxs[0]
+    per_l = {"k_res": w.Hkv * (i.n_raw + i.n_spans) * w.d, "v_res": w.Hkv * (i.n_raw + i.n_spans) * w.d,
+             "s": w.Hq * w.dprime * i.n_spans, "uk": w.Hkv * int(i.split.spans[:, 1].sum()) * w.R,
+             "uv": w.Hkv * int(i.split.spans[:, 1].sum()) * w.R, "vkt": w.Hkv * i.n_spans * w.R * w.d,
+             "vvt": w.Hkv * i.n_spans * w.R * w.d, "smk": w.Hkv * i.n_spans * w.R, "smv": w.Hkv * i.n_spans * w.R}
+    for l in range(w.L):
+        ex1 = idx.export(l, 1)
+        for k, n in per_l.items():
+            assert np.array_equal(ex1[k], ex[k][l * n:(l + 1) * n]), (k, l)
+        for k in ("span_start", "span_len", "raw_pos"):
+            assert np.array_equal(ex1[k], ex[k])
+    with pytest.raises(sl.SekvError) as e:
+        idx.export(1, 2)
+    assert e.value.status == 1
     idx.free()
 
 
@@ -115,20 +130,11 @@ def test_route_identical_index(ctx, sl, name):
     idx = imported(ctx, sl, c)
     for step in range(2):
         q = c.q(step)
-        alpha_o, z_o = oracle_route_all(c, q, c.tau)
-        words, alpha_g = gpu_route(idx, c, q, c.tau)
-        bad = excl = ties = npairs = 0
-        for (b, l, h), z in z_o.items():
-            n = len(z)
-            assert np.max(np.abs(alpha_g[b, l, h, :n] - alpha_o[b, l, h])) < 2e-5
-            m, e, t = SC.compare_masks(words[b, l, h], z, alpha_o[b, l, h], c.tau[l, h])
-            bad += m
-            excl += e
-            ties += t
-            npairs += n
-        print(f"[route] {name} step {step}: {npairs} pairs, mismatches {bad}, excluded (|a-tau|<1e-6) {excl}, "
-              f"ties at 1e-4 {ties}")
-        assert bad == 0
+        ref = SC.route_ref(c.idxs, c.W, q, c.tau)
+        words, alpha_g = gpu_route(idx, c, q, c.tau, alpha=True)
+        for (b, l, h), al in ref.alpha.items():
+            assert np.max(np.abs(alpha_g[b, l, h, :len(al)] - al)) < 2e-5
+        SC.check_masks(lambda k: words[k], ref, f"{name} step {step}")
     idx.free()
 
 
@@ -140,7 +146,7 @@ def test_decode_identical_index(ctx, sl, name):
     worst = 0.0
     for step in range(2):
         q = c.q(step)
-        _, z_o = oracle_route_all(c, q, c.tau)
+        _, z_o = O.route_step(c.idxs, c.W.double().numpy(), q.double().numpy(), c.tau)
         out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
         mask = SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words)
         out_g, _ = gpu_decode(idx, c, q, mask)
@@ -176,16 +182,12 @@ def test_decode_sequence_without_spans(ctx, sl):
     built.free()
     idx = imported(ctx, sl, c)
     q = c.q(0)
-    alpha_o, z_o = oracle_route_all(c, q, c.tau)
-    words, _ = gpu_route(idx, c, q, c.tau)
-    bad = 0
-    for (b, l, h), z in z_o.items():
-        m, _, _ = SC.compare_masks(words[b, l, h], z, alpha_o[(b, l, h)], c.tau[l, h])
-        bad += m
-    assert bad == 0
+    ref = SC.route_ref(c.idxs, c.W, q, c.tau)
+    words = gpu_route(idx, c, q, c.tau)
+    SC.check_masks(lambda k: words[k], ref, "no-span sequence")
     assert not words[1].any()
-    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
-    out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words))
+    out_o = O.decode_step(c.idxs, q.double().numpy(), ref.z, w.Hkv)
+    out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(ref.z, w.B, w.L, w.Hq, idx.mask_words))
     worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
     print(f"[no-span sequence] N_S {[i.n_spans for i in c.idxs]}, worst rel-L2 {worst:.3e}")
     assert worst <= SC.REL_L2
@@ -199,8 +201,8 @@ def test_decode_all_or_nothing(ctx, sl, tau_val):
     idx = imported(ctx, sl, c)
     tau = np.full((w.L, w.Hq), tau_val)
     q = c.q(0)
-    _, z_o = oracle_route_all(c, q, tau)
-    words, _ = gpu_route(idx, c, q, tau)
+    _, z_o = O.route_step(c.idxs, c.W.double().numpy(), q.double().numpy(), tau)
+    words = gpu_route(idx, c, q, tau)
     for (b, l, h), z in z_o.items():
         assert np.array_equal(SC.unpack_mask(words[b, l, h], len(z)), z)
     out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
@@ -218,25 +220,15 @@ def test_route_cap(ctx, sl):
     cap = int(math.floor(w.cap_frac * c.idxs[0].n_spans))
     for step in range(2):
         q = c.q(step)
-        alpha_o, z_pre = oracle_route_all(c, q, c.tau)
-        _, z_o = oracle_route_all(c, q, c.tau, cap)
-        words, _ = gpu_route(idx, c, q, c.tau, cap)
-        bad = excl = ties = over = 0
-        for key, z in z_o.items():
-            b, l, h = key
-            bnd = SC.cap_boundary(alpha_o[key], z_pre[key], cap)
-            over += bnd is not None
-            m, e, t = SC.compare_masks(words[b, l, h], z, alpha_o[key], c.tau[l, h], bnd)
-            bad += m
-            excl += e
-            ties += t
+        ref = SC.route_ref(c.idxs, c.W, q, c.tau, cap)
+        words = gpu_route(idx, c, q, c.tau, cap)
+        over = sum(v is not None for v in ref.bnd.values())
+        SC.check_masks(lambda k: words[k], ref, f"cap {cap} step {step} ({over} heads over budget)")
+        for (b, l, h), z in ref.z.items():
             assert SC.unpack_mask(words[b, l, h], len(z)).sum() <= cap
-        print(f"[cap] step {step}: cap {cap}, heads over budget {over}, mismatches {bad}, "
-              f"excluded (1e-6) {excl}, ties at 1e-4 {ties}")
-        assert bad == 0
         # decode over the capped masks
-        out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
-        out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_o, w.B, w.L, w.Hq, idx.mask_words))
+        out_o = O.decode_step(c.idxs, q.double().numpy(), ref.z, w.Hkv)
+        out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(ref.z, w.B, w.L, w.Hq, idx.mask_words))
         worst = max(SC.rel_l2(out_g[k], v) for k, v in out_o.items())
         assert worst <= SC.REL_L2
     idx.free()
@@ -247,38 +239,35 @@ def gpu_route_pooled(idx, c, q, tau, budget, lb=0, lc=None):
     lc = w.L - lb if lc is None else lc
     Wd = idx.mask_words
     mask = torch.zeros(w.B, lc, w.Hq, Wd, dtype=torch.int64, device="cuda")
-    alpha = torch.zeros(w.B, lc, w.Hq, Wd * 64, dtype=torch.float32, device="cuda")
-    idx.route_pooled(lb, lc, dev(q[:, lb:lb + lc]), dev(tau[lb:lb + lc], torch.float32), budget, mask, alpha)
+    idx.route_pooled(lb, lc, dev(q[:, lb:lb + lc]), dev(np.asarray(tau)[lb:lb + lc], torch.float32), budget, mask,
+                     None)
     torch.cuda.synchronize()
-    return mask.cpu().numpy().view(np.uint64), alpha.cpu().numpy()
+    return mask.cpu().numpy().view(np.uint64)
 
 
-def pool_boundary(alpha, z_pre, budget, b):
-    """alpha of the budget-th largest routed triple of sequence b, or None."""
-    a = np.concatenate([alpha[k][z_pre[k]] for k in sorted(z_pre) if k[0] == b])
-    if budget <= 0 or len(a) <= budget:
-        return None
-    return float(np.sort(a)[::-1][budget - 1])
-
-
-def check_pooled(c, words, alpha_o, z_pre, budget, lb, label):
+def check_pooled(c, words, ref, budget, lb, label, boundary_windows=True):
     """Compare the GPU's pooled masks (layers lb..) with the oracle's pooled
-    budget over the same triples; returns the oracle masks."""
-    z_ref = O.pool_budget(alpha_o, z_pre, budget)
-    bad = excl = ties = 0
+    budget over the same triples (pairs within the score window of tau, or
+    of a sequence's budget boundary, excluded); returns the oracle masks."""
+    z_ref, bnd = SC.pool_ref(ref, budget)
+    bad = excl = pairs = 0
     for b in range(c.w.B):
-        bnd = pool_boundary(alpha_o, z_pre, budget, b)
         kept = 0
-        for key in sorted(k for k in z_ref if k[0] == b):
-            _, l, h = key
-            m, e, t = SC.compare_masks(words[b, l - lb, h], z_ref[key], alpha_o[key], c.tau[l, h], bnd)
+        for k in sorted(x for x in z_ref if x[0] == b):
+            _, l, h = k
+            extra = None
+            if boundary_windows and b in bnd:
+                extra = SC.boundary_uncertain(ref.score[k], ref.win[k], ref.z_pre[k], z_ref[k], bnd[b])
+            m, e, _ = SC.compare_masks(words[b, l - lb, h], ref, k, z_ref[k], extra)
             bad += m
             excl += e
-            ties += t
-            kept += int(SC.unpack_mask(words[b, l - lb, h], len(z_ref[key])).sum())
+            pairs += len(z_ref[k])
+            kept += int(SC.unpack_mask(words[b, l - lb, h], len(z_ref[k])).sum())
         assert kept <= budget or budget == 0
-    print(f"[pool {label}] budget {budget}: mismatches {bad}, excluded (1e-6) {excl}, ties at 1e-4 {ties}")
+    print(f"[pool {label}] budget {budget}: {pairs} pairs, mismatches {bad}, excluded (score windows) {excl}",
+          flush=True)
     assert bad == 0
+    assert SC.excluded_ok(excl, pairs), (label, excl, pairs)
     return z_ref
 
 
@@ -291,35 +280,34 @@ def test_route_pooled_budget(ctx, sl):
     ns = c.idxs[0].n_spans
     for step in range(2):
         q = c.q(step)
-        alpha_o, z_pre = oracle_route_all(c, q, c.tau)
-        total = sum(int(v.sum()) for v in z_pre.values())
+        ref = SC.route_ref(c.idxs, c.W, q, c.tau)
+        total = sum(int(v.sum()) for v in ref.z_pre.values())
         # both layers pooled, 10% of all (layer, head, span) triples
         budget = int(math.floor(0.10 * w.L * w.Hq * ns))
         assert budget < total
-        words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
-        z_ref = check_pooled(c, words, alpha_o, z_pre, budget, 0, "2 layers")
+        words = gpu_route_pooled(idx, c, q, c.tau, budget)
+        z_ref = check_pooled(c, words, ref, budget, 0, "2 layers")
         # decode over the pooled masks
         out_o = O.decode_step(c.idxs, q.double().numpy(), z_ref, w.Hkv)
         out_g, _ = gpu_decode(idx, c, q, SC.pack_mask(z_ref, w.B, w.L, w.Hq, idx.mask_words))
         assert max(SC.rel_l2(out_g[k], v) for k, v in out_o.items()) <= SC.REL_L2
         # each layer alone: that layer's heads form the pool
         for l in range(w.L):
-            sub_a = {k: v for k, v in alpha_o.items() if k[1] == l}
-            sub_z = {k: v for k, v in z_pre.items() if k[1] == l}
+            sub = SC.route_ref(c.idxs, c.W, q, c.tau, keys=[k for k in ref.z if k[1] == l])
             bl = int(math.floor(0.10 * w.Hq * ns))
-            words_l, _ = gpu_route_pooled(idx, c, q, c.tau, bl, lb=l, lc=1)
-            check_pooled(c, words_l, sub_a, sub_z, bl, l, f"layer {l}")
+            words_l = gpu_route_pooled(idx, c, q, c.tau, bl, lb=l, lc=1)
+            check_pooled(c, words_l, sub, bl, l, f"layer {l}")
     # edge budgets: one triple; exactly the routed count; none (0) = plain routing
     q = c.q(0)
-    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
-    total = sum(int(v.sum()) for v in z_pre.values())
-    plain, _ = gpu_route(idx, c, q, c.tau, 0)
+    ref = SC.route_ref(c.idxs, c.W, q, c.tau)
+    total = sum(int(v.sum()) for v in ref.z_pre.values())
+    plain = gpu_route(idx, c, q, c.tau, 0)
     for budget in (1, total):
-        words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
-        check_pooled(c, words, alpha_o, z_pre, budget, 0, "edge")
-    words, _ = gpu_route_pooled(idx, c, q, c.tau, total + 1000)
+        words = gpu_route_pooled(idx, c, q, c.tau, budget)
+        check_pooled(c, words, ref, budget, 0, "edge")
+    words = gpu_route_pooled(idx, c, q, c.tau, total + 1000)
     assert np.array_equal(words, plain)
-    words, _ = gpu_route_pooled(idx, c, q, c.tau, 0)
+    words = gpu_route_pooled(idx, c, q, c.tau, 0)
     assert np.array_equal(words, plain)
     idx.free()
 
@@ -330,102 +318,190 @@ def test_route_pooled_budget_per_sequence(ctx, sl):
     w = c.w
     idx = imported(ctx, sl, c)
     q = c.q(0)
-    alpha_o, z_pre = oracle_route_all(c, q, c.tau)
+    ref = SC.route_ref(c.idxs, c.W, q, c.tau)
     budget = int(math.floor(0.10 * w.Hq * min(i.n_spans for i in c.idxs)))
-    words, _ = gpu_route_pooled(idx, c, q, c.tau, budget)
-    check_pooled(c, words, alpha_o, z_pre, budget, 0, "B=2")
+    words = gpu_route_pooled(idx, c, q, c.tau, budget)
+    check_pooled(c, words, ref, budget, 0, "B=2")
     idx.free()
 
 
-def _gpu_alpha_pool_ref(c, words_plain, alpha_g, budget):
-    """The oracle's pooled budget on the library's own fp32 alpha and
-    pre-budget masks (the selection decided in the kernel's precision)."""
+def tie_group_case(c, q, group, lift=8.0):
+    """An import of case c whose query heads all share layer 0's head-0
+    projection and query, and whose spans `group` (per (l, h): span indices)
+    share one summary key placed `lift` above every other score of that
+    head: their scores are then exactly equal in the library's fp32 and the
+    oracle's fp64, in every head and layer, and isolated from the rest.
+    Returns (import arrays, oracle indexes, query)."""
     w = c.w
-    a, z = {}, {}
-    for b in range(w.B):
-        n = c.idxs[b].n_spans
-        for l in range(words_plain.shape[1]):
-            for h in range(w.Hq):
-                a[b, l, h] = alpha_g[b, l, h, :n].astype(np.float64)
-                z[b, l, h] = SC.unpack_mask(words_plain[b, l, h], n)
-    return O.pool_budget(a, z, budget), sum(int(v.sum()) for v in z.values())
-
-
-def _check_pool_exact(c, idx, q, tau, budgets, label):
-    w = c.w
-    plain, alpha_p = gpu_route(idx, c, q, tau, 0)
-    total = None
-    for budget in budgets(plain):
-        words, alpha_g = gpu_route_pooled(idx, c, q, tau, budget)
-        assert np.array_equal(alpha_g, alpha_p)
-        ref, total = _gpu_alpha_pool_ref(c, plain, alpha_g, budget)
-        for (b, l, h), zz in ref.items():
-            got = SC.unpack_mask(words[b, l, h], len(zz))
-            assert np.array_equal(got, zz), (label, budget, b, l, h)
-            assert not SC.unpack_mask(words[b, l, h], idx.mask_words * 64)[len(zz):].any()
-        ties = 0
-        if 0 < budget < total:
-            keys = np.sort(np.concatenate([alpha_g[b, l, h, :c.idxs[b].n_spans][SC.unpack_mask(plain[b, l, h],
-                                                                                      c.idxs[b].n_spans)]
-                                           for b in range(w.B) for l in range(w.L) for h in range(w.Hq)]))[::-1]
-            ties = int((keys == keys[budget - 1]).sum())
-        print(f"[pool exact {label}] budget {budget} of {total}: bit-exact; keys equal to the boundary {ties}")
-    return total
+    arr = SC.import_arrays(c)
+    W = arr["W"].reshape(w.L, w.Hq, w.dprime, w.d).copy()
+    W[:] = W[0, 0]
+    arr["W"] = W.reshape(-1).copy()
+    qq = q.clone()
+    qq[:] = qq[0, 0, 0]
+    u = W[0, 0].astype(np.float64) @ qq[0, 0, 0].double().numpy()
+    idxs = []
+    for i in c.idxs:
+        j = O.BatchIndex(i.split, i.kres, i.vres, i.s.copy(), i.uk, i.uv, i.vkt, i.vvt, i.smk, i.smv,
+                         i.sig_k, i.sig_v)
+        top = max(float(np.max(u @ j.s[l, h])) for l in range(w.L) for h in range(w.Hq))
+        v = (u * (top + lift) / float(u @ u)).astype(np.float32).astype(np.float64)
+        for (l, h), spans in group.items():
+            j.s[l, h][:, spans] = v[:, None]
+        idxs.append(j)
+    arr["s"] = np.concatenate([j.s.ravel() for j in idxs]).astype(np.float32)
+    return arr, idxs, qq
 
 
 def test_route_pooled_selection_paths(ctx, sl):
-    """Every selection path of the pool kernel, bit-exact against the oracle's
-    pooled budget on the library's alpha: the LDS list (with ranked split
-    ties at saturated alpha), the global sweeps (more routed triples than the
-    LDS list holds), and the LDS list with more equal boundary keys than LDS
-    ranks (saturated routing scores)."""
+    """Every selection path of the pool kernel against the oracle's pooled
+    budget: the LDS list (natural scores, and a group of equal scores split
+    by the budget, ranked by position), the global sweeps (more routed
+    triples than the LDS list holds), and more equal boundary keys than the
+    LDS ranks (the global keep pass)."""
     c = case("8b_l2_cap")
     w = c.w
     ns = c.idxs[0].n_spans
     idx = imported(ctx, sl, c)
     q = c.q(0)
     ten = int(math.floor(0.10 * w.L * w.Hq * ns))
-    # calibrated tau: the LDS list
-    _check_pool_exact(c, idx, q, c.tau, lambda p: (1, 7, ten, ten + 1), "lds")
+    ref = SC.route_ref(c.idxs, c.W, q, c.tau)
+    for budget in (1, 7, ten, ten + 1):
+        check_pooled(c, gpu_route_pooled(idx, c, q, c.tau, budget), ref, budget, 0, "lds")
     # tau = -inf: every span routed, 2 x 32 x N_S triples > the LDS list
     tinf = np.full_like(c.tau, -np.inf)
-    total = _check_pool_exact(c, idx, q, tinf, lambda p: (ten, 3 * ten), "global")
+    ref_inf = SC.route_ref(c.idxs, c.W, q, tinf)
+    total = sum(int(v.sum()) for v in ref_inf.z_pre.values())
     assert total > 12288
+    for budget in (ten, 3 * ten):
+        check_pooled(c, gpu_route_pooled(idx, c, q, tinf, budget), ref_inf, budget, 0, "global")
     idx.free()
-    # saturated alpha (W scaled by 64): thousands of alpha == 1.0 at the boundary
-    arr = SC.import_arrays(c)
-    arr["W"] = (arr["W"] * 64.0).astype(np.float32)
-    sat = ctx.import_index(sl.build_params(c.w), arr)
-    tau5 = np.full_like(c.tau, 0.5)
-    _check_pool_exact(c, sat, q, tau5, lambda p: (ten, 5), "saturated")
-    sat.free()
+    # equal scores at the boundary: 6 spans of every head in both layers
+    # (384 triples) and 50 of every head (3200 > 2048 LDS ranks), with tau
+    # placed so that the routed triples fit the LDS list
+    for per_head, budget in ((6, 250), (50, 1500)):
+        group = {(l, h): list(range(3, 3 + 3 * per_head, 3)) for l in range(w.L) for h in range(w.Hq)}
+        arr, idxs, qq = tie_group_case(c, q, group)
+        tie = ctx.import_index(sl.build_params(w), arr)
+        Wt = torch.from_numpy(arr["W"].reshape(w.L, w.Hq, w.dprime, w.d))
+        tc = SC.Case(w, c.H, c.K, c.V, Wt, None, idxs, c.tau)
+        nat = np.concatenate([np.delete(O.routing_score(Wt[l, h].double().numpy(), qq[0, l, h].double().numpy(),
+                                                        idxs[0].s[l, h]), group[l, h])
+                              for l in range(w.L) for h in range(w.Hq)])
+        t = min(float(np.quantile(nat, 0.75)), 10.0)
+        tau_t = np.full_like(c.tau, float(np.float32(1.0 / (1.0 + math.exp(-t)))))
+        ref_t = SC.route_ref(idxs, Wt, qq, tau_t)
+        total = sum(int(v.sum()) for v in ref_t.z_pre.values())
+        assert budget < per_head * w.L * w.Hq <= total <= 12288
+        words = gpu_route_pooled(tie, tc, qq, tau_t, budget)
+        # the group is isolated: no other score near the tie, so no boundary window is needed
+        gv = {ref_t.score[k][group[k[1], k[2]][0]] for k in ref_t.score}
+        assert len(gv) == 1
+        for k in ref_t.score:
+            others = np.delete(ref_t.score[k], group[k[1], k[2]])
+            assert np.all(np.abs(others - next(iter(gv))) > 1.0)
+        check_pooled(tc, words, ref_t, budget, 0, f"{per_head * w.L * w.Hq} tied of {total}",
+                     boundary_windows=False)
+        tie.free()
 
 
-def test_pinned_tier_matches_hbm(ctx, sl):
+def test_pinned_tier_against_oracle(ctx, sl):
+    """The pinned-host tier (the routed union gathered over PCIe into the HBM
+    ring) against the oracle on the same index, one layer per call as the
+    decode loop makes them (layer_begin 1 included), and bit-identical to the
+    HBM tier."""
     c = case("8b_l2_cap")
     w = c.w
     hbm = imported(ctx, sl, c, tier=0)
     pin = imported(ctx, sl, c, tier=1)
     q = c.q(0)
-    _, z_o = oracle_route_all(c, q, c.tau)
+    _, z_o = O.route_step(c.idxs, c.W.double().numpy(), q.double().numpy(), c.tau)
+    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
     mask = SC.pack_mask(z_o, w.B, w.L, w.Hq, hbm.mask_words)
-    out_h, _ = gpu_decode(hbm, c, q, mask)
-    out_p, st = gpu_decode(pin, c, q, mask, stats=True)
-    assert np.array_equal(out_h, out_p)
-    # bytes gathered = padded blobs of the union of every (b, l, g)
-    G = w.G
-    nu = 0
+    worst = 0.0
     for l in range(w.L):
+        out_h, _ = gpu_decode(hbm, c, q, mask[:, l:l + 1], lb=l, lc=1)
+        out_p, st = gpu_decode(pin, c, q, mask[:, l:l + 1], stats=True, lb=l, lc=1)
+        assert np.array_equal(out_h, out_p)
+        for h in range(w.Hq):
+            worst = max(worst, SC.rel_l2(out_p[0, 0, h], out_o[0, l, h]))
+        # bytes gathered = padded blobs of the union of every (b, l, g)
+        nu = 0
         for g in range(w.Hkv):
             u = np.zeros(c.idxs[0].n_spans, bool)
-            for h in range(g * G, (g + 1) * G):
+            for h in range(g * w.G, (g + 1) * w.G):
                 u |= z_o[0, l, h]
             nu += int(u.sum())
-    print(f"[pinned] union spans {st.union_spans}, PCIe bytes {st.pcie_bytes}, copies {st.pcie_copies}, "
-          f"{st.pcie_ms:.3f} ms")
-    assert st.union_spans == nu and st.pcie_bytes > 0 and st.pcie_copies >= 1
+        print(f"[pinned] layer {l}: union spans {st.union_spans}, PCIe bytes {st.pcie_bytes}, "
+              f"{st.pcie_ms:.3f} ms")
+        assert st.union_spans == nu and st.pcie_bytes > 0 and st.pcie_copies >= 1
+    print(f"[pinned] worst rel-L2 against the oracle {worst:.3e}")
+    assert worst <= SC.REL_L2
     hbm.free()
     pin.free()
+
+
+def _bench_loop(idx, w, q, tau, cap):
+    """bench.py's decode loop: for each layer l, sekv_route(l, 1, ..., cap) then
+    sekv_decode_attend(l, 1, ...).  Returns masks [B, L, Hq, Wd] and outputs
+    [B, L, Hq, d]."""
+    Wd = idx.mask_words
+    masks = [torch.zeros(w.B, 1, w.Hq, Wd, dtype=torch.int64, device="cuda") for _ in range(w.L)]
+    outs = [torch.zeros(w.B, 1, w.Hq, w.d, device="cuda") for _ in range(w.L)]
+    tau_d = torch.as_tensor(np.asarray(tau), dtype=torch.float32).cuda()
+    for l in range(w.L):
+        ql = q[:, l:l + 1].contiguous().cuda()
+        idx.route(l, 1, ql, tau_d[l:l + 1].contiguous(), cap, masks[l], None)
+        idx.decode_attend(l, 1, ql, masks[l], outs[l])
+    torch.cuda.synchronize()
+    words = torch.cat(masks, 1).cpu().numpy().view(np.uint64)
+    return words, torch.cat(outs, 1).cpu().double().numpy()
+
+
+def check_layers_against_export(idx, w, W, q, tau, cap, words, out, layers, label):
+    """Each layer of a library-built index against the oracle routing and
+    decoding the library's own exported index of that layer: masks bit-exact
+    outside the score windows, decode within 5e-3 over the library's masks.
+    W: the routing projection the index was built with [L, Hq, d', d]."""
+    worst = 0.0
+    pairs = excl = 0
+    Wn = W.cpu().double().numpy() if isinstance(W, torch.Tensor) else np.asarray(W, np.float64)
+    for l in layers:
+        ex = idx.export(l, 1)
+        ix = SC.index_from_export(ex, idx.n_spans, idx.n_raw, 1, w.Hq, w.Hkv, w.d, w.R, w.dprime)
+        ref = SC.route_ref(ix, Wn[l:l + 1], q[:, l:l + 1], np.asarray(tau)[l:l + 1], cap)
+        p, e = SC.check_masks(lambda k: words[k[0], l, k[2]], ref, f"{label} layer {l}")
+        pairs += p
+        excl += e
+        for b in range(w.B):
+            for h in range(w.Hq):
+                zg = SC.unpack_mask(words[b, l, h], ix[b].n_spans)
+                o = O.decode_head(q[b, l, h].double().numpy(), ix[b], 0, h // w.G, zg)
+                worst = max(worst, SC.rel_l2(out[b, l, h], o))
+    print(f"[{label}] layers {list(layers)}: {pairs} routing pairs, {excl} excluded; decode worst rel-L2 "
+          f"{worst:.3e}", flush=True)
+    assert worst <= SC.REL_L2
+    return worst
+
+
+@pytest.mark.parametrize("tier", ["hbm", "pinned"])
+def test_benchmarked_path_three_layers(ctx, sl, tier):
+    """bench.py's path on a library-built 3-layer index (config-3 shape at
+    16K tokens, 10% cap): per-layer routing and decoding (layer_begin 0, 1,
+    2) against the oracle on the library's own exported index, both tiers."""
+    w = W8["llama8b_l32_128k"].scaled(L=3, T=16384)
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, l, "cuda") for l in range(w.L)])
+    p = sl.build_params(w, tier=sl.TIER_HBM if tier == "hbm" else sl.TIER_PINNED_HOST)
+    idx = ctx.build_index(p, K, V, H, W, None)
+    tau = torch.zeros(w.L, w.Hq, device="cuda")
+    idx.calibrate_tau(0, w.L, synth.calibration_query(w, "cuda"), w.frac, tau)
+    cap = int(math.floor(w.cap_frac * int(idx.n_spans.min())))
+    q = synth.query(w, 5)
+    words, out = _bench_loop(idx, w, q, tau.cpu().numpy(), cap)
+    check_layers_against_export(idx, w, W, q, tau.cpu().numpy(), cap, words, out, range(w.L),
+                                f"bench path {tier}")
+    idx.free()
 
 
 def test_pinned_build_matches_hbm(ctx, sl):
@@ -577,30 +653,42 @@ def test_rsvd_batched_quality(ctx, sl):
 CASE_SPECS["tiny_fullrank"] = _wl("tiny_2k", R=64)
 
 
-@pytest.mark.parametrize("name,bar", [("tiny_fullrank", SC.REL_L2), ("tiny", 2e-2), ("8b_4k", 2e-2)])
-def test_end_to_end_decode(ctx, sl, name, bar):
-    """Library-built index and library routing against the oracle-built index
-    and oracle routing.  With R = d the truncated SVD reconstructs each span
-    exactly on both sides, so the outputs are held to the decode bar; with R
-    below the span rank the two sides keep different, equally valid rank-R
-    factors (randomized vs exact SVD pick different directions within the flat
-    noise spectrum), so the gap is reported under a looser bound."""
+@pytest.mark.parametrize("name", ["tiny_fullrank", "tiny", "8b_4k"])
+def test_end_to_end_decode(ctx, sl, name):
+    """Library-built index, library routing and decoding from the same inputs
+    as the oracle-built index, in two parts:
+      * contract: the oracle routing and decoding the library's own exported
+        index (masks bit-exact outside the score windows, outputs within
+        5e-3);
+      * end to end: the library's masks against the oracle's routing of its
+        own index (same windows), and the SVD-choice gap, the oracle's decode
+        of the library's factors against its decode of its exact factors
+        under the same masks.  With R = d both factorisations reconstruct
+        every span exactly and the gap is held to 5e-3; below full rank the
+        randomized and exact SVDs keep different, equally valid rank-R
+        subspaces of the flat noise spectrum, so the gap is reported against
+        a looser sanity bound."""
     c = case(name)
     w = c.w
     idx = _gpu_build(ctx, sl, c)
-    worst = 0.0
     q = c.q(0)
-    words, _ = gpu_route(idx, c, q, c.tau)
-    alpha_o, z_o = oracle_route_all(c, q, c.tau)
-    out_o = O.decode_step(c.idxs, q.double().numpy(), z_o, w.Hkv)
+    words = gpu_route(idx, c, q, c.tau)
     out_g, _ = gpu_decode(idx, c, q, words)
-    flips = 0
-    for (b, l, h), ref in out_o.items():
-        zg = SC.unpack_mask(words[b, l, h], len(z_o[b, l, h]))
-        if not np.array_equal(zg, z_o[b, l, h]):
-            flips += 1
-            continue
-        worst = max(worst, SC.rel_l2(out_g[b, l, h], ref))
-    print(f"[end-to-end] {name}: worst rel-L2 {worst:.3e}; heads with routing ties skipped {flips}")
-    assert worst <= bar
+    lib_ix = SC.index_from_export(idx.export(), idx.n_spans, idx.n_raw, w.L, w.Hq, w.Hkv, w.d, w.R, w.dprime)
+    ref_lib = SC.route_ref(lib_ix, c.W, q, c.tau)
+    SC.check_masks(lambda k: words[k], ref_lib, f"{name} library index")
+    ref_own = SC.route_ref(c.idxs, c.W, q, c.tau)
+    SC.check_masks(lambda k: words[k], ref_own, f"{name} oracle-built index")
+    contract = gap = 0.0
+    for (b, l, h) in ref_lib.z:
+        zg = SC.unpack_mask(words[b, l, h], lib_ix[b].n_spans)
+        o_lib = O.decode_head(q[b, l, h].double().numpy(), lib_ix[b], l, h // w.G, zg)
+        o_own = O.decode_head(q[b, l, h].double().numpy(), c.idxs[b], l, h // w.G, zg)
+        contract = max(contract, SC.rel_l2(out_g[b, l, h], o_lib))
+        gap = max(gap, SC.rel_l2(o_lib, o_own))
+    bound = SC.REL_L2 if w.R >= w.d else 2e-2
+    print(f"[end-to-end] {name}: library vs oracle on the library's index {contract:.3e}; SVD-choice gap "
+          f"(library factors vs exact factors, same masks) {gap:.3e} (bound {bound:g})")
+    assert contract <= SC.REL_L2
+    assert gap <= bound
     idx.free()
