@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -93,6 +94,17 @@ hipError_t dgrow(DBuf& b, size_t bytes) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
+
+// Scratch of sekv_decode_attend_noalloc: the softmax partials of the attention
+// items live in this file-scope device array (one copy per GPU, held until the
+// process ends) instead of index-owned memory.  Host code never uses the
+// array's name as an address: sekv_create takes the device address of each
+// GPU's copy once, with that GPU current, and keeps it in g_scratch.
+constexpr size_t kScratchBytes = size_t(40) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxScratchDevices];
 
 // Event pairs bracketing kernel launches (instrumentation).
 struct Timer {
@@ -415,6 +427,14 @@ extern "C" sekv_status sekv_create(int32_t device, void* stream, sekv_ctx** out)
   HIP_TRY(hipGetDeviceCount(&n));
   if (device < 0 || device >= n) return fail(SEKV_EINVAL, "device %d not in [0, %d)", device, n);
   HIP_TRY(hipSetDevice(device));
+  if (device < kMaxScratchDevices) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[device]) {
+      void* ptr = nullptr;
+      HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+      g_scratch[device] = ptr;
+    }
+  }
   sekv_ctx* c = new sekv_ctx();
   c->device = device;
   c->stream = (hipStream_t)stream;
@@ -1136,17 +1156,20 @@ sekv_status gather(sekv_index* x, int lb, int lc, const uint64_t* mask, sekv_sta
 
 }  // namespace
 
-extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
-                                          const void* q, const uint64_t* mask, float* out, sekv_stats* stats) {
-  sekv_index* x = const_cast<sekv_index*>(xc);
-  sekv_status st = check_idx(c, x);
-  if (st) return st;
-  if ((st = check_layers(x, lb, lc))) return st;
-  if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
-  if ((st = set_device(c))) return st;
+namespace {
+
+// Softmax-partial bytes of one decode call over lc layers.
+size_t part_bytes(const sekv_index* x, int lc) {
+  return sizeof(float) * (size_t)lc * std::max<size_t>(x->items.size(), 1) * x->G * (x->D + 2);
+}
+
+// The decode call after its checks: gather (pinned tier), attention items
+// writing their partials to `part`, merge into out.
+sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q, const uint64_t* mask, float* out,
+                       sekv_stats* stats, float* part, bool timed) {
+  sekv_status st;
   if (stats) memset(stats, 0, sizeof *stats);
   const int n_items = (int)x->items.size();
-  HIP_TRY(dgrow(x->d_part, sizeof(float) * (size_t)lc * std::max(n_items, 1) * x->G * (x->D + 2)));
   AttendArgs aa{};
   aa.q = (const bf16_t*)q;
   aa.mask = mask;
@@ -1165,7 +1188,7 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     aa.pool = (const uint8_t*)x->d_ring.p;
     aa.ring_off = (const int64_t*)x->d_ring_off.p;
   }
-  aa.part = (float*)x->d_part.p;
+  aa.part = part;
   aa.layer_bytes = x->layer_bytes;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
@@ -1173,7 +1196,7 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   aa.scale = 1.0f / sqrtf((float)x->D);
   if (n_items > 0) {
     size_t slot = 0;
-    if (c->timing) {
+    if (timed) {
       HIP_TRY(c->t_attend.reserve(&slot));
       HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream, c->t_attend.ev[slot], c->t_attend.ev[slot + 1]));
     } else {
@@ -1181,11 +1204,46 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
     }
   }
   MergeArgs mg{};
-  mg.part = (const float*)x->d_part.p;
+  mg.part = part;
   mg.items = (const WorkItem*)x->d_items.p;
   mg.bg_first = (const int32_t*)x->d_bg_first.p;
   mg.out = out;
   mg.layer_count = lc; mg.n_items = n_items; mg.B = x->B; mg.Hq = x->Hq; mg.Hkv = x->Hkv;
   HIP_TRY(launch_merge(mg, x->D, x->G, c->stream));
   return SEKV_OK;
+}
+
+}  // namespace
+
+extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
+                                          const void* q, const uint64_t* mask, float* out, sekv_stats* stats) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if ((st = set_device(c))) return st;
+  HIP_TRY(dgrow(x->d_part, part_bytes(x, lc)));
+  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)x->d_part.p, c->timing);
+}
+
+extern "C" sekv_status sekv_decode_attend_noalloc(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
+                                                  const void* q, const uint64_t* mask, float* out,
+                                                  sekv_stats* stats) {
+  sekv_index* x = const_cast<sekv_index*>(xc);
+  sekv_status st = check_idx(c, x);
+  if (st) return st;
+  if ((st = check_layers(x, lb, lc))) return st;
+  if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if (x->tier != SEKV_TIER_HBM)
+    return fail(SEKV_EUNSUPPORTED, "the no-allocation decode serves the HBM tier only (the pinned-tier gather "
+                                   "allocates its bookkeeping)");
+  const size_t need = part_bytes(x, lc);
+  if (need > kScratchBytes)
+    return fail(SEKV_ECAPACITY, "this call needs %zu bytes of partials; the no-allocation scratch holds %zu "
+                                "(call fewer layers at once)", need, kScratchBytes);
+  if (c->device >= kMaxScratchDevices || !g_scratch[c->device])
+    return fail(SEKV_ESTATE, "no scratch address for device %d", c->device);
+  if ((st = set_device(c))) return st;
+  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)g_scratch[c->device], false);
 }

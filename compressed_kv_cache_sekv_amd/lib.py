@@ -31,6 +31,7 @@ EXPORTS = ("sekv_create", "sekv_destroy", "sekv_last_error", "sekv_max_spans",
            "sekv_index_export_part",
            "sekv_index_get_info", "sekv_index_counts", "sekv_index_free",
            "sekv_route", "sekv_route_pooled", "sekv_calibrate_tau", "sekv_decode_attend",
+           "sekv_decode_attend_noalloc",
            "sekv_timing_enable", "sekv_timing_read")
 
 
@@ -100,6 +101,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.sekv_route_pooled.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp]
     lib.sekv_calibrate_tau.argtypes = [vp, vp, i32, i32, vp, f32, vp]
     lib.sekv_decode_attend.argtypes = [vp, vp, i32, i32, vp, vp, vp, C.POINTER(Stats)]
+    lib.sekv_decode_attend_noalloc.argtypes = [vp, vp, i32, i32, vp, vp, vp, C.POINTER(Stats)]
     lib.sekv_timing_enable.argtypes = [vp, i32]
     lib.sekv_timing_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i64),
                                      C.POINTER(C.c_double), C.POINTER(i64)]
@@ -246,6 +248,10 @@ class Index:
         check(lib().sekv_decode_attend(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q),
                                        _ptr(mask), _ptr(out), C.byref(st) if st is not None else None))
         return st
+
+    def decode_attend_noalloc(self, layer_begin, layer_count, q, mask, out):
+        check(lib().sekv_decode_attend_noalloc(self.ctx.h, self.h, layer_begin, layer_count, _ptr(q),
+                                               _ptr(mask), _ptr(out), None))
 
     def spans(self):
         """(span_start, span_len, raw_pos) of every sequence, concatenated over b."""

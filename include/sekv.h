@@ -46,7 +46,9 @@ typedef enum {
   SEKV_EINVAL = 1,       /* bad argument (null, shape, range)                 */
   SEKV_ENOMEM = 2,       /* device or pinned host allocation failed           */
   SEKV_EHIP = 3,         /* a HIP runtime call failed (message has the text)  */
-  SEKV_ECAPACITY = 4,    /* staging ring too small for this call's union      */
+  SEKV_ECAPACITY = 4,    /* a fixed-size buffer too small for this call: the
+                            staging ring for its union, or the no-allocation
+                            decode's scratch                                  */
   SEKV_ESTATE = 5,       /* object used after free or on the wrong context    */
   SEKV_EUNSUPPORTED = 6  /* shape not compiled (d, G or R outside the set)    */
 } sekv_status;
@@ -307,6 +309,27 @@ sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
 sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                                int32_t layer_count, const void* q, const uint64_t* mask,
                                float* out, sekv_stats* stats);
+
+/* sekv_decode_attend for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and arguments, with the attention items' softmax partials
+ * in a static device scratch array that the library holds for each GPU until
+ * the process ends (its address is taken once per device in sekv_create), so
+ * the call itself calls no hipMalloc, hipFree or other allocating routine.
+ * Limits and conditions:
+ *  - the partials of one call, 4 * layer_count * items * G * (d + 2) bytes,
+ *    must fit the 40 MiB scratch, else SEKV_ECAPACITY with nothing written
+ *    (a 32-query-head, 8-KV-head 128K layer needs 1.6 MB per layer);
+ *  - HBM tier only (SEKV_EUNSUPPORTED for the pinned tier, whose gather
+ *    allocates its bookkeeping);
+ *  - every call on one GPU shares that GPU's scratch: calls that overlap in
+ *    time on one GPU (other streams or contexts) race and must be ordered by
+ *    the caller;
+ *  - the attention kernel is not timed (sekv_timing_enable does not apply);
+ *    stats is zero-filled or NULL. */
+sekv_status sekv_decode_attend_noalloc(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
+                                       int32_t layer_count, const void* q, const uint64_t* mask,
+                                       float* out, sekv_stats* stats);
 
 /* --------------------------------------------------------- instrumentation */
 
