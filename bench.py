@@ -4,9 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one decode token through every layer of the workload: per layer,
-routing (sekv_route) then attention over anchors, pseudo-tokens and the
-factored spans (sekv_decode_attend), launched layer by layer as a model's
-decode loop would.  Inputs (cache, index, queries, thresholds) are resident in
+routing with the budget cap (sekv_route) then attention over anchors,
+pseudo-tokens and the factored spans (sekv_decode_attend), launched layer by
+layer as a model's decode loop would.  Inputs (cache, index, queries, thresholds) are resident in
 HBM before the timed region.  Prints one JSON line on stdout.
 
 value       = decode query-tokens/s = B * K / (timed wall time of K steps)
@@ -417,16 +417,17 @@ def main(argv=None):
                    "batch": B, "context": w.T, "R": w.R, "dprime": w.dprime,
                    "expand_frac_target": w.frac if w.tau is None else None, "tau": w.tau,
                    "cap": 0 if args.pooled else cap, "pooled_budget_per_layer": budget or None,
-                   "factor_tier": "hbm", "launch": "per layer: route + decode_attend"},
+                   "factor_tier": "hbm",
+                   "launch": "per layer: " + ("route_pooled" if args.pooled else "route") + " + decode_attend"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attend_kernel", "alg_bytes_per_launch": int(per_launch),
                      "mean_launch_us": round(attend_ms / attend_n * 1e3, 2)},
         "route_call": {"achieved": round(route_gbs, 1), "unit": "GB/s",
                        "mean_call_us": round(route_ms / route_n * 1e3, 2),
-                       "covers": "the sekv_route call by events around it: route kernel, then the cap kernel "
-                                 "when cap > 0 (or the pool kernel), with the dispatch between them; bytes are "
-                                 "the summary keys and W"},
+                       "covers": ("the sekv_route call by events around it: route kernel, then the cap kernel "
+                                  "when cap > 0 (or the pool kernel), with the dispatch between them"),
+                       "bytes": "the summary keys and W"},
         "index": {"build_s": round(build_s, 3), "spans": [int(x) for x in idx.n_spans[:4]],
                   "raw": [int(x) for x in idx.n_raw[:4]], "union_spans_per_launch": round(unions / launches, 1),
                   "resident_gb": round(info.resident_bytes / 1e9, 3),

@@ -559,11 +559,8 @@ void attend_kernel(const AttendArgs a) {
   const int ek = (nsh > 0) ? s_ln[wave][min(lane, nsh - 1)] : 0;
   const int Sk = spans ? bm.span_base + (ek & 0xffffff) : 0;
   const int nk = a.span_len[Sk];
-  const bool ring = a.ring_off != nullptr;
-  const int64_t* okp = ring
-      ? a.ring_off + ((((int64_t)lc * a.B + b) * a.Hkv + g) * a.max_spans + b0 + min(lane, max(nsh - 1, 0)))
-      : a.span_off + Sk;
-  const int64_t ok = *okp + (ring ? 0 : (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg);
+  const int64_t ok = a.span_off[Sk] + (int64_t)(l - a.pool_layer0) * a.layer_bytes + bm.pool_base +
+                     (int64_t)g * bm.pool_lg;
 
   // resident slice: fold (the span metadata loads are in flight)
   if (t < it.step_end) {

@@ -132,11 +132,11 @@ struct AttendArgs {
   const float* logn;        // [span] ln n_S
   const int32_t* span_len;  // [span]
   const int64_t* span_off;  // [span] byte offset of the blob in its (b, l, g) region
-  const uint8_t* pool;      // factor pool (HBM tier) or staging ring
-  const int64_t* ring_off;  // ring tier: [Lc][B][Hkv][max_spans] offset of the
-                            // k-th union span's blob in the ring, else NULL
+  const uint8_t* pool;      // factor pool (HBM tier) or staging ring (pinned
+                            // tier: the call's layers, blobs at their pool offsets)
   float* part;              // [Lc][n_items][G][D + 2] softmax partials
   int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
+  int32_t pool_layer0;      // layer at the start of `pool` (0; the ring: layer_begin)
   int32_t layer_begin, layer_count, n_items;
   int32_t B, L, Hq, Hkv, W, max_spans;
   float scale;              // 1/sqrt(d)
@@ -173,19 +173,18 @@ struct CalibArgs {
   float frac;
 };
 
-// Pinned-tier gather (see gather.hip).
+// Pinned-tier gather (see gather.hip): the union's blobs copied from the
+// mapped pinned pool to the same layer-relative offsets of the HBM ring.
 struct GatherArgs {
   const uint64_t* mask;      // [B][Lc][Hq][W]
   const BMeta* meta;
   const int32_t* span_len;
   const int64_t* span_off;
   const uint8_t* host_pool;  // device address of the mapped pinned factor pool
-  uint8_t* ring;             // HBM staging ring
-  int64_t* usize;            // [Lc][B][Hkv][2]: union spans, union blob bytes
-  const int64_t* ubase;      // [Lc][B][Hkv]: ring offset of each (l, b, g) region
-  int64_t* ring_off;         // [Lc][B][Hkv][max_spans]: ring offset of the k-th union blob
+  uint8_t* ring;             // HBM staging ring: layer layer_begin + li at li * layer_bytes
+  int2* stat;                // [Lc][B][Hkv]: union spans, union blob bytes / 256 (or NULL)
   int64_t layer_bytes;
-  int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, R, D, max_spans, nsplit;
+  int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, R, D, nsplit;
 };
 
 // ------------------------------------------------------------ launchers ---
@@ -250,7 +249,6 @@ hipError_t launch_pack_raw(const PackArgs& a, hipStream_t st);
 hipError_t launch_summaries(const PackArgs& a, hipStream_t st);
 hipError_t launch_rsvd(const PackArgs& a, hipStream_t st);
 hipError_t launch_rsvd_batched(const PackArgs& a, hipStream_t st);
-hipError_t launch_union_size(const GatherArgs& a, hipStream_t st);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
 int gather_share();   // union spans per gather workgroup
 

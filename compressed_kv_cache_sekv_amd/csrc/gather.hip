@@ -8,13 +8,13 @@
 // cost.
 //
 // The pinned pool is mapped into the device address space and read by the
-// kernel over PCIe.  Two passes per call:
-//   union_size_kernel  per (layer, b, KV head): number and bytes of the blobs
-//                      of the union over the G heads' masks (the host turns
-//                      these into ring offsets and checks the ring capacity);
-//   gather_kernel      per (layer, b, KV head, share): copies its share of
-//                      the union, in union order, to consecutive ring
-//                      addresses and records each blob's ring offset.
+// kernel over PCIe.  The HBM ring mirrors the pool's layout for the layers of
+// the call: a blob of layer layer_begin + li lands at its own layer-relative
+// offset in ring layer li, so no placement is computed on the host and the
+// call does not synchronise.  gather_kernel, per (layer, b, KV head, share):
+// forms the union over the G heads' masks and its rank and byte prefix per
+// mask word, and copies its share of the union's blobs; share 0 records the
+// union's size for the call's statistics.
 #include "common.h"
 
 namespace sekv {
@@ -27,49 +27,13 @@ __device__ __forceinline__ uint64_t valid_bits(int n_spans, int w) {
   return left >= 64 ? ~0ull : (left > 0 ? (1ull << left) - 1 : 0ull);
 }
 
-__global__ __launch_bounds__(256) void union_size_kernel(const GatherArgs a) {
-  __shared__ int64_t s_red[2][4];
-  const int bg = blockIdx.x, li = blockIdx.y;
-  const int b = bg / a.Hkv, g = bg - b * a.Hkv;
-  const BMeta bm = a.meta[b];
-  const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + li) * a.Hq + (int64_t)g * a.G) * a.W;
-  int64_t cnt = 0, bytes = 0;
-  for (int w = threadIdx.x; w < a.W; w += 256) {
-    uint64_t u = 0;
-    for (int h = 0; h < a.G; ++h) u |= mrow[(int64_t)h * a.W + w];
-    u &= valid_bits(bm.n_spans, w);
-    cnt += __popcll(u);
-    for (; u; u &= u - 1) {
-      const int S = 64 * w + __builtin_ctzll(u);
-      bytes += Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    cnt += __shfl_xor(cnt, o);
-    bytes += __shfl_xor(bytes, o);
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s_red[0][wave] = cnt;
-    s_red[1][wave] = bytes;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t* o = a.usize + 2 * (((int64_t)li * a.B + b) * a.Hkv + g);
-    o[0] = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-    o[1] = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-  }
-}
-
 constexpr int kShare = 128;   // union spans one gather workgroup copies
 
 __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   __shared__ uint64_t s_uw[kMaxWords];
   __shared__ int32_t s_pre[kMaxWords + 1];      // union spans before word w
   __shared__ int64_t s_bpre[kMaxWords + 1];     // union bytes before word w
-  __shared__ int64_t s_src[kShare];
-  __shared__ int64_t s_dst[kShare];
+  __shared__ int64_t s_src[kShare];             // blob offset within the layer
   __shared__ int32_t s_len[kShare];             // 16-byte chunks
   const int li = blockIdx.y, l = a.layer_begin + li;
   const int j = blockIdx.x % a.nsplit, bg = blockIdx.x / a.nsplit;
@@ -120,34 +84,31 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   }
   __syncthreads();
   const int U = s_pre[a.W];
+  const int64_t region = (int64_t)bm.pool_base + (int64_t)g * bm.pool_lg;   // (b, g) blobs within a layer
+  if (j == 0 && threadIdx.x == 0 && a.stat) a.stat[rid] = make_int2(U, (int)(s_bpre[a.W] >> 8));
   const int beg = (int)((int64_t)j * U / a.nsplit), end = (int)((int64_t)(j + 1) * U / a.nsplit);
   const int cnt = min(end - beg, kShare);   // the host keeps shares <= kShare
-  const int64_t base = a.ubase[rid];
-  const int64_t region = (int64_t)l * a.layer_bytes + bm.pool_base + (int64_t)g * bm.pool_lg;
-  int64_t* roff = a.ring_off + rid * a.max_spans;
-  // this share's blobs: source in the pinned pool, ring destination
+  // this share's blobs: offset within the layer and 16-byte chunks
   for (int w = threadIdx.x; w < a.W; w += 256) {
     int k = s_pre[w];
     if (k >= beg + cnt || s_pre[w + 1] <= beg) continue;
-    int64_t off = s_bpre[w];
     for (uint64_t u = s_uw[w]; u && k < beg + cnt; u &= u - 1) {
       const int S = 64 * w + __builtin_ctzll(u);
-      const int64_t by = Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]);
       if (k >= beg) {
         s_src[k - beg] = region + a.span_off[bm.span_base + S];
-        s_dst[k - beg] = base + off;
-        s_len[k - beg] = (int32_t)(by >> 4);
-        roff[k] = base + off;
+        s_len[k - beg] = (int32_t)(Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]) >> 4);
       }
-      off += by;
       ++k;
     }
   }
   __syncthreads();
-  // copy, 16 bytes per lane, four loads in flight per lane
+  // copy to the same offset of ring layer li, 16 bytes per lane, four loads
+  // in flight per lane
+  const uint8_t* src_l = a.host_pool + (int64_t)l * a.layer_bytes;
+  uint8_t* dst_l = a.ring + (int64_t)li * a.layer_bytes;
   for (int e = 0; e < cnt; ++e) {
-    const u32x4* src = (const u32x4*)(a.host_pool + s_src[e]);
-    u32x4* dst = (u32x4*)(a.ring + s_dst[e]);
+    const u32x4* src = (const u32x4*)(src_l + s_src[e]);
+    u32x4* dst = (u32x4*)(dst_l + s_src[e]);
     const int nch = s_len[e];
     for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
       u32x4 v[4];
@@ -161,11 +122,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_union_size(const GatherArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(union_size_kernel, dim3(a.B * a.Hkv, a.layer_count), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(gather_kernel, dim3(a.B * a.Hkv * a.nsplit, a.layer_count), dim3(256), 0, st, a);

@@ -103,6 +103,7 @@ constexpr int kMaxDp = 64;
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[kMaxDp];
+  __shared__ double s_thr;
   // workgroup id -> (b, chunk, h) so that every chunk of one (b, h) lands on
   // the same XCD (consecutive ids go round-robin over the 8 XCDs): W^(l,h)
   // and q are then fetched once into that XCD's L2
@@ -124,6 +125,7 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   // The thread's W row slice and q slice (16-byte loads) are issued first,
   // then the summary keys of this lane's span: u is reduced while the keys
   // are still in flight.
+  const float tau_h = a.tau[lc * a.Hq + h];   // first: its logit is taken while the loads below fly
   const float* Wl = a.W + ((int64_t)l * a.Hq + h) * dp * D;
   const bf16_t* qp = a.q + (((int64_t)b * a.layer_count + lc) * a.Hq + h) * D;
   constexpr int QD = D / NW;          // dims per thread
@@ -147,6 +149,8 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxDp / 4; ++k) v4[k] = *(const float4*)(sp + skey_index(Sc, 4 * min(k, (d4 >> 2) - 1), d4));
   }
+  // logit(tau) once per workgroup, by one lane, while the loads are in flight
+  if (threadIdx.x == 0) s_thr = logit_threshold(tau_h);
   __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
   {
     float acc = 0.f;
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   uint64_t* mrow = a.mask + row * a.Wd;
   float* arow = a.alpha ? a.alpha + row * (int64_t)a.Wd * 64 : nullptr;
   float* srow = a.score ? a.score + row * (int64_t)a.Wd * 64 : nullptr;
-  const double thr = logit_threshold(a.tau[lc * a.Hq + h]);
+  const double thr = s_thr;
   float alpha = 0.f, dot = 0.f;
   bool z = false;
   if (live) {

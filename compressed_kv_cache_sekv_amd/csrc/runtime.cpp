@@ -185,11 +185,10 @@ struct sekv_index {
   DBuf d_pool;                 // HBM tier
   uint8_t* h_pool = nullptr;   // pinned tier (host address)
   const uint8_t* d_host_pool = nullptr;   // the same pool's device address
-  DBuf d_ring, d_ring_off, d_usize, d_ubase;
+  DBuf d_ring;                 // pinned tier: the call's layers, blobs at their pool offsets
+  DBuf d_gstat;                // pinned tier: per (l, b, g) union spans and bytes (sekv_stats)
   int64_t ring_bytes = 0;
-  int64_t* h_usize = nullptr;  // pinned [Lc][B][Hkv][2]
-  int64_t* h_ubase = nullptr;  // pinned [Lc][B][Hkv]
-  size_t h_gather_cap = 0;     // (l, b, g) regions the two buffers hold
+  std::vector<int2> h_gstat;
   // decode work
   std::vector<WorkItem> items;
   std::vector<int32_t> bg_first;
@@ -380,12 +379,10 @@ void free_index(sekv_index* x) {
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
-                  &x->d_ring, &x->d_ring_off, &x->d_usize, &x->d_ubase, &x->d_items, &x->d_bg_first,
-                  &x->d_part, &x->d_score, &x->d_alpha, &x->d_tau_inf};
+                  &x->d_ring, &x->d_gstat, &x->d_items, &x->d_bg_first, &x->d_part,
+                  &x->d_score, &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
-  if (x->h_usize) (void)hipHostFree(x->h_usize);
-  if (x->h_ubase) (void)hipHostFree(x->h_ubase);
   if (x->ev0) (void)hipEventDestroy(x->ev0);
   if (x->ev1) (void)hipEventDestroy(x->ev1);
   x->magic = DEAD_MAGIC;
@@ -1090,86 +1087,46 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
 
 namespace {
 
-// Pinned tier: size the union of every (l, b, g) on the device, read the
-// sizes back (one synchronisation), place the regions in the ring (capacity
-// check), then gather the blobs with one kernel that reads the mapped pinned
-// pool and records each union rank's ring offset.
-sekv_status gather(sekv_index* x, int lb, int lc, const uint64_t* mask, sekv_stats* stats) {
-  hipStream_t st = x->ctx->stream;
-  const size_t nreg = (size_t)lc * x->B * x->Hkv;
-  if (x->h_gather_cap < nreg) {
-    if (x->h_usize) (void)hipHostFree(x->h_usize);
-    if (x->h_ubase) (void)hipHostFree(x->h_ubase);
-    x->h_usize = nullptr;
-    x->h_ubase = nullptr;
-    x->h_gather_cap = 0;
-    HIP_TRY(hipHostMalloc((void**)&x->h_usize, 16 * nreg, hipHostMallocDefault));
-    HIP_TRY(hipHostMalloc((void**)&x->h_ubase, 8 * nreg, hipHostMallocDefault));
-    x->h_gather_cap = nreg;
-  }
-  HIP_TRY(dgrow(x->d_usize, 16 * nreg));
-  HIP_TRY(dgrow(x->d_ubase, 8 * nreg));
-  HIP_TRY(dgrow(x->d_ring_off, 8 * nreg * std::max(x->max_spans, 1)));
-  GatherArgs ga{};
-  ga.mask = mask;
-  ga.meta = (const BMeta*)x->d_meta.p;
-  ga.span_len = (const int32_t*)x->d_span_len.p;
-  ga.span_off = (const int64_t*)x->d_span_off.p;
-  ga.host_pool = x->d_host_pool;
-  ga.ring = (uint8_t*)x->d_ring.p;
-  ga.usize = (int64_t*)x->d_usize.p;
-  ga.ubase = (const int64_t*)x->d_ubase.p;
-  ga.ring_off = (int64_t*)x->d_ring_off.p;
-  ga.layer_bytes = x->layer_bytes;
-  ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
-  ga.W = x->Wd; ga.G = x->G; ga.R = x->R; ga.D = x->D;
-  ga.max_spans = std::max(x->max_spans, 1);
-  ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
-  HIP_TRY(launch_union_size(ga, st));
-  HIP_TRY(hipMemcpyAsync(x->h_usize, x->d_usize.p, 16 * nreg, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipStreamSynchronize(st));
-  int64_t used = 0;
-  uint64_t unions = 0;
-  for (size_t r = 0; r < nreg; ++r) {
-    x->h_ubase[r] = used;
-    unions += (uint64_t)x->h_usize[2 * r];
-    used += x->h_usize[2 * r + 1];
-  }
-  if (used > x->ring_bytes)
-    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes too small for the routed union (%lld bytes)",
-                (long long)x->ring_bytes, (long long)used);
-  HIP_TRY(hipMemcpyAsync(x->d_ubase.p, x->h_ubase, 8 * nreg, hipMemcpyHostToDevice, st));
-  HIP_TRY(hipEventRecord(x->ev0, st));
-  HIP_TRY(launch_gather(ga, st));
-  HIP_TRY(hipEventRecord(x->ev1, st));
-  if (stats) {
-    stats->union_spans = unions;
-    stats->pcie_bytes = (uint64_t)used;
-    stats->pcie_copies = 1;
-    HIP_TRY(hipEventSynchronize(x->ev1));
-    float ms = 0.f;
-    HIP_TRY(hipEventElapsedTime(&ms, x->ev0, x->ev1));
-    stats->pcie_ms = ms;
-  }
-  return SEKV_OK;
-}
-
-}  // namespace
-
-namespace {
-
 // Softmax-partial bytes of one decode call over lc layers.
 size_t part_bytes(const sekv_index* x, int lc) {
   return sizeof(float) * (size_t)lc * std::max<size_t>(x->items.size(), 1) * x->G * (x->D + 2);
 }
 
-// The decode call after its checks: gather (pinned tier), attention items
-// writing their partials to `part`, merge into out.
+// The ring of the pinned tier mirrors the pool: a call over lc layers needs
+// lc whole layers of it.
+sekv_status check_ring(const sekv_index* x, int lc) {
+  if (x->tier == SEKV_TIER_PINNED_HOST && (int64_t)lc * x->layer_bytes > x->ring_bytes)
+    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes holds fewer than the %d layers of this call "
+                "(%lld bytes each)", (long long)x->ring_bytes, lc, (long long)x->layer_bytes);
+  return SEKV_OK;
+}
+
+// Gather (pinned tier), attention items writing their partials to `part`,
+// merge into out.  Asynchronous unless stats are asked for on the pinned tier
+// (then the union sizes and the gather time are read back).
 sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q, const uint64_t* mask, float* out,
-                       sekv_stats* stats, float* part, bool timed) {
-  sekv_status st;
+                       sekv_stats* stats, float* part, int2* gstat, bool timed) {
   if (stats) memset(stats, 0, sizeof *stats);
   const int n_items = (int)x->items.size();
+  hipStream_t st = c->stream;
+  const bool pinned = x->tier == SEKV_TIER_PINNED_HOST;
+  if (pinned) {
+    GatherArgs ga{};
+    ga.mask = mask;
+    ga.meta = (const BMeta*)x->d_meta.p;
+    ga.span_len = (const int32_t*)x->d_span_len.p;
+    ga.span_off = (const int64_t*)x->d_span_off.p;
+    ga.host_pool = x->d_host_pool;
+    ga.ring = (uint8_t*)x->d_ring.p;
+    ga.stat = gstat;
+    ga.layer_bytes = x->layer_bytes;
+    ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
+    ga.W = x->Wd; ga.G = x->G; ga.R = x->R; ga.D = x->D;
+    ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
+    if (stats) HIP_TRY(hipEventRecord(x->ev0, st));
+    HIP_TRY(launch_gather(ga, st));
+    if (stats) HIP_TRY(hipEventRecord(x->ev1, st));
+  }
   AttendArgs aa{};
   aa.q = (const bf16_t*)q;
   aa.mask = mask;
@@ -1180,14 +1137,8 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
   aa.logn = (const float*)x->d_logn.p;
   aa.span_len = (const int32_t*)x->d_span_len.p;
   aa.span_off = (const int64_t*)x->d_span_off.p;
-  if (x->tier == SEKV_TIER_HBM) {
-    aa.pool = (const uint8_t*)x->d_pool.p;
-    aa.ring_off = nullptr;
-  } else {
-    if ((st = gather(x, lb, lc, mask, stats))) return st;
-    aa.pool = (const uint8_t*)x->d_ring.p;
-    aa.ring_off = (const int64_t*)x->d_ring_off.p;
-  }
+  aa.pool = pinned ? (const uint8_t*)x->d_ring.p : (const uint8_t*)x->d_pool.p;
+  aa.pool_layer0 = pinned ? lb : 0;
   aa.part = part;
   aa.layer_bytes = x->layer_bytes;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
@@ -1198,9 +1149,9 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
     size_t slot = 0;
     if (timed) {
       HIP_TRY(c->t_attend.reserve(&slot));
-      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream, c->t_attend.ev[slot], c->t_attend.ev[slot + 1]));
+      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, st, c->t_attend.ev[slot], c->t_attend.ev[slot + 1]));
     } else {
-      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, c->stream));
+      HIP_TRY(launch_attend(aa, x->D, x->G, x->R, st));
     }
   }
   MergeArgs mg{};
@@ -1209,7 +1160,24 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
   mg.bg_first = (const int32_t*)x->d_bg_first.p;
   mg.out = out;
   mg.layer_count = lc; mg.n_items = n_items; mg.B = x->B; mg.Hq = x->Hq; mg.Hkv = x->Hkv;
-  HIP_TRY(launch_merge(mg, x->D, x->G, c->stream));
+  HIP_TRY(launch_merge(mg, x->D, x->G, st));
+  if (pinned && stats && gstat) {
+    const size_t nreg = (size_t)lc * x->B * x->Hkv;
+    x->h_gstat.resize(nreg);
+    HIP_TRY(hipMemcpyAsync(x->h_gstat.data(), gstat, sizeof(int2) * nreg, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    uint64_t un = 0, by = 0;
+    for (const int2& v : x->h_gstat) {
+      un += (uint64_t)v.x;
+      by += (uint64_t)v.y << 8;
+    }
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, x->ev0, x->ev1));
+    stats->union_spans = un;
+    stats->pcie_bytes = by;
+    stats->pcie_copies = 1;
+    stats->pcie_ms = ms;
+  }
   return SEKV_OK;
 }
 
@@ -1222,9 +1190,15 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if ((st = check_ring(x, lc))) return st;
   if ((st = set_device(c))) return st;
   HIP_TRY(dgrow(x->d_part, part_bytes(x, lc)));
-  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)x->d_part.p, c->timing);
+  int2* gstat = nullptr;
+  if (stats && x->tier == SEKV_TIER_PINNED_HOST) {
+    HIP_TRY(dgrow(x->d_gstat, sizeof(int2) * (size_t)lc * x->B * x->Hkv));
+    gstat = (int2*)x->d_gstat.p;
+  }
+  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)x->d_part.p, gstat, c->timing);
 }
 
 extern "C" sekv_status sekv_decode_attend_noalloc(sekv_ctx* c, const sekv_index* xc, int32_t lb, int32_t lc,
@@ -1236,8 +1210,7 @@ extern "C" sekv_status sekv_decode_attend_noalloc(sekv_ctx* c, const sekv_index*
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
   if (x->tier != SEKV_TIER_HBM)
-    return fail(SEKV_EUNSUPPORTED, "the no-allocation decode serves the HBM tier only (the pinned-tier gather "
-                                   "allocates its bookkeeping)");
+    return fail(SEKV_EUNSUPPORTED, "the no-allocation decode serves the HBM tier only");
   const size_t need = part_bytes(x, lc);
   if (need > kScratchBytes)
     return fail(SEKV_ECAPACITY, "this call needs %zu bytes of partials; the no-allocation scratch holds %zu "
@@ -1245,5 +1218,5 @@ extern "C" sekv_status sekv_decode_attend_noalloc(sekv_ctx* c, const sekv_index*
   if (c->device >= kMaxScratchDevices || !g_scratch[c->device])
     return fail(SEKV_ESTATE, "no scratch address for device %d", c->device);
   if ((st = set_device(c))) return st;
-  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)g_scratch[c->device], false);
+  return decode_run(c, x, lb, lc, q, mask, out, stats, (float*)g_scratch[c->device], nullptr, false);
 }

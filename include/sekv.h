@@ -75,7 +75,8 @@ typedef struct {
   uint64_t seed;        /* Gaussian test matrices: Philox4x32-10 keyed by seed   */
   int32_t tier;         /* sekv_tier                                             */
   int64_t ring_bytes;   /* pinned tier: HBM staging ring size, 0 = one layer's
-                           whole factor set (the largest possible union)          */
+                           whole factor set; a decode call over n layers needs
+                           n layers' worth (the ring mirrors the pool layout)     */
 } sekv_build_params;
 
 /* Index summary. */
@@ -301,11 +302,19 @@ sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
  *          the caller)
  *   out    device fp32 [B][layer_count][Hq][d]
  *   stats  host, or NULL
- * Pinned tier: sizes the union of the routed spans of every (b, l, KV head)
- * on the device, reads those sizes back (synchronising the stream once),
- * places the unions in the HBM ring (SEKV_ECAPACITY if they do not fit) and
- * gathers the factor blobs with a kernel that reads the mapped pinned pool
- * over PCIe, before the attention kernels. */
+ * Work: the attention kernel's workgroups each take a slice of the resident
+ * rows and an equal share of the union of the G heads' routed spans of their
+ * (b, l, KV head); a merge kernel combines their softmax partials.
+ * Pinned tier: the routed union's factor blobs are first gathered from the
+ * mapped pinned pool into the HBM staging ring by a kernel reading them over
+ * PCIe ([Method] Stage 2: the factors are fetched from the CPU
+ * asynchronously).  The ring mirrors the pool layout of the call's layers (a
+ * blob sits at its own pool offset), so it must hold layer_count whole layers
+ * of factors (SEKV_ECAPACITY otherwise, before any device work), nothing is
+ * placed on the host and the call does not synchronise, except when stats is
+ * non-NULL on the pinned tier (to read back the union sizes and the gather
+ * time).  The index owns the partials buffer (grown on first use): calls on
+ * one context are ordered on its stream. */
 sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                                int32_t layer_count, const void* q, const uint64_t* mask,
                                float* out, sekv_stats* stats);
