@@ -25,7 +25,10 @@ force span split on tiny inputs; SVD against an eigen-decomposition of A^T A;
 routing against the (W^T W) identity and a sign test at tau=0.5; the
 summary keys of a built index against numpy's weighted average; the cap rule
 against brute force; the pooled budget against brute force and against the
-per-head cap on a one-head pool; calibration by counting.  Unpinned: absolute decode
+per-head cap on a one-head pool; calibration by counting; dropped components
+(gate below eps) against the Eckart-Young error of the kept set, against a
+reconstruction that leaves them out, and, all dropped, against the closed
+form of attention over zero rows.  Unpinned: absolute decode
 outputs at generic tau (no worked example is printed on the pages); they stand
 on the pinned pieces.
 """
@@ -155,6 +158,22 @@ def svd_optimum_error(A, R: int) -> float:
     return float(math.sqrt(math.fsum(float(x) ** 2 for x in s_[r:])))
 
 
+def kept_components(m, n: int, R: int, eps: Optional[float]) -> np.ndarray:
+    """Which of a span's R stored components survive (R28).  [Contrib] (the
+    dual-resolution item) and [Tech] (the low-rank paragraph): the component
+    gates set each span's effective rank, and components are dropped when
+    stored and transferred.  Reading: component i is kept iff it is one of the
+    R_eff = min(R, n) components the truncation holds (R14) and, when eps > 0,
+    its gate m_i >= eps; eps None or <= 0 drops no gated component.  A dropped
+    component is absent from the reconstruction sum, which is the same as
+    giving it sigma_i * m_i = 0.  Returns bool [R]."""
+    m = np.asarray(m, dtype=f64)
+    keep = np.arange(R) < min(R, n)
+    if eps is not None and eps > 0:
+        keep &= m >= eps        # a NaN gate compares false: dropped
+    return keep
+
+
 def reconstruct(U, sm, Vt) -> np.ndarray:
     """[Tech] reconstruction sum: Khat = sum_i m_i sigma_i u_i v_i^T, with the
     gate already folded into sm = sigma * m (R15)."""
@@ -182,6 +201,8 @@ class BatchIndex:
     smv: np.ndarray
     sig_k: np.ndarray         # [L, Hkv, N_S, R] singular values (ungated)
     sig_v: np.ndarray
+    rank_k: Optional[np.ndarray] = None   # [L, Hkv, N_S] kept components (R28)
+    rank_v: Optional[np.ndarray] = None
 
     @property
     def n_spans(self) -> int:
@@ -200,12 +221,15 @@ class BatchIndex:
 def build_index_b(H_b, K_b, V_b, W, gates_b, *, R: int, alpha_sp: float,
                   l_min: int, Hq: int, store: bool = True,
                   layers: Optional[List[int]] = None,
-                  kv_heads: Optional[List[int]] = None) -> BatchIndex:
+                  kv_heads: Optional[List[int]] = None,
+                  gate_eps: Optional[float] = None) -> BatchIndex:
     """Index of one sequence.
 
     H_b [T] fp32; K_b, V_b [L, Hkv, T, d] (bf16 values); W [L, Hq, d', d] fp32;
     gates_b [L, Hkv, 2, S_max, R] or None (m = 1).  Span ordinal j uses gate
-    slot j.  With store=True the stored arrays are rounded to the storage
+    slot j.  gate_eps > 0 drops the components whose gate is below it
+    (kept_components); the dropped ones are stored with sigma * m = 0 and
+    rank_k / rank_v count the kept ones.  With store=True the stored arrays are rounded to the storage
     formats (bf16 rows and factors, fp32 s and sigma*m); with store=False they
     stay fp64 (used by the full-rank pin).  `layers` / `kv_heads` restrict the
     work to a subset (the rest stays zero), for sampled checks at full size.
@@ -228,7 +252,8 @@ def build_index_b(H_b, K_b, V_b, W, gates_b, *, R: int, alpha_sp: float,
                      uk=np.zeros((L, Hkv, ntok, R)), uv=np.zeros((L, Hkv, ntok, R)),
                      vkt=np.zeros((L, Hkv, NS, R, d)), vvt=np.zeros((L, Hkv, NS, R, d)),
                      smk=np.zeros((L, Hkv, NS, R)), smv=np.zeros((L, Hkv, NS, R)),
-                     sig_k=np.zeros((L, Hkv, NS, R)), sig_v=np.zeros((L, Hkv, NS, R)))
+                     sig_k=np.zeros((L, Hkv, NS, R)), sig_v=np.zeros((L, Hkv, NS, R)),
+                     rank_k=np.zeros((L, Hkv, NS), np.int64), rank_v=np.zeros((L, Hkv, NS), np.int64))
     off = idx.tok_off()
     for l in (range(L) if layers is None else layers):
         for g in (range(Hkv) if kv_heads is None else kv_heads):
@@ -245,16 +270,20 @@ def build_index_b(H_b, K_b, V_b, W, gates_b, *, R: int, alpha_sp: float,
                 for which, X in ((0, K), (1, V)):
                     U, sig, Vt = truncated_svd(X[a:a + n], R)
                     m = np.ones(R) if gates_b is None else np.asarray(gates_b[l, g, which, j], f64)
+                    keep = kept_components(m, n, R, gate_eps)
+                    sm = np.where(keep, sig * m, 0.0)
                     if which == 0:
                         idx.uk[l, g, off[j]:off[j] + n] = rb(U)
                         idx.vkt[l, g, j] = rb(Vt)
-                        idx.smk[l, g, j] = rf(sig * m)
+                        idx.smk[l, g, j] = rf(sm)
                         idx.sig_k[l, g, j] = sig
+                        idx.rank_k[l, g, j] = int(keep.sum())
                     else:
                         idx.uv[l, g, off[j]:off[j] + n] = rb(U)
                         idx.vvt[l, g, j] = rb(Vt)
-                        idx.smv[l, g, j] = rf(sig * m)
+                        idx.smv[l, g, j] = rf(sm)
                         idx.sig_v[l, g, j] = sig
+                        idx.rank_v[l, g, j] = int(keep.sum())
     return idx
 
 

@@ -564,3 +564,102 @@ def test_value_gates_do_not_touch_keys():
     out = O.decode_head(q[0, 0, 1], idx, 0, 0, np.ones(idx.n_spans, bool))
     ref = O.full_attention(q[0, 0, 1], K[0, 0, 0], V2)
     assert np.linalg.norm(out - ref) <= 1e-10 * np.linalg.norm(ref)
+
+
+# ------------------------------------------- variable effective rank (R28) ---
+
+def _eps_gates(w, rng, values):
+    """Gates of a one-layer, one-KV-head workload drawn from `values`."""
+    S_max = synth.max_spans(w.T, w.l_min)
+    return rng.choice(np.asarray(values, np.float64), size=(1, w.Hkv, 2, S_max, w.R))
+
+
+def test_gate_eps_error_is_eckart_young_of_the_kept_set():
+    """Gates 1 (kept) or 0.3 (below eps = 0.5, dropped): the reconstruction
+    keeps exactly the surviving exact singular triplets, so its Frobenius error
+    squared is ||A||^2 minus their squared singular values, with the singular
+    values taken from eigvalsh(A^T A), not from the SVD routine."""
+    w, H, K, V, W, q = _small_workload(R=16)
+    rng = np.random.default_rng(28)
+    gates = _eps_gates(w, rng, [1.0, 0.3])
+    idx = O.build_index_b(H[0], K[0], V[0], W, gates, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False, gate_eps=0.5)
+    off = idx.tok_off()
+    checked = 0
+    for j, (a, n) in enumerate(idx.split.spans):
+        for which, X, U, sm, Vt, rank in (
+                (0, K[0, 0, 0], idx.uk, idx.smk, idx.vkt, idx.rank_k),
+                (1, V[0, 0, 0], idx.uv, idx.smv, idx.vvt, idx.rank_v)):
+            A = X[a:a + n]
+            ev = np.sort(np.clip(np.linalg.eigvalsh(A.T @ A), 0, None))[::-1]
+            kept = [i for i in range(w.R) if i < min(w.R, n) and gates[0, 0, which, j, i] >= 0.5]
+            assert rank[0, 0, j] == len(kept)
+            Khat = O.reconstruct(U[0, 0, off[j]:off[j] + n], sm[0, 0, j], Vt[0, 0, j])
+            err2 = float(np.sum((A - Khat) ** 2))
+            want = float(np.sum(A * A)) - float(sum(ev[i] for i in kept))
+            assert abs(err2 - want) <= 1e-9 * float(np.sum(A * A)), (j, which)
+            checked += 1
+    assert checked >= 6
+
+
+@pytest.mark.parametrize("eps", [None, 0.0, -1.0])
+def test_gate_eps_at_or_below_zero_keeps_every_component(eps):
+    """eps None, 0 or negative drops nothing: sigma * m as without eps, and
+    every span keeps min(R, n_S) components."""
+    w, H, K, V, W, q = _small_workload(R=16)
+    gates = _eps_gates(w, np.random.default_rng(5), [0.0, 0.01, 0.4, 0.9])
+    ref = O.build_index_b(H[0], K[0], V[0], W, gates, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq)
+    idx = O.build_index_b(H[0], K[0], V[0], W, gates, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, gate_eps=eps)
+    assert np.array_equal(idx.smk, ref.smk) and np.array_equal(idx.smv, ref.smv)
+    n = idx.split.spans[:, 1]
+    assert np.array_equal(idx.rank_k[0, 0], np.minimum(w.R, n))
+    assert np.array_equal(idx.rank_v[0, 0], np.minimum(w.R, n))
+
+
+def test_dropped_components_are_absent_from_the_attention():
+    """Every span expanded, gates sigmoid(N(0.5, 1)) and eps = 0.5: the decode
+    equals full attention over rows rebuilt from only the components whose
+    gate reaches eps (columns removed, not zeroed), the rest of the cache
+    as stored."""
+    w, H, K, V, W, q = _small_workload(R=16, Hq=2, Hkv=1)
+    rng = np.random.default_rng(9)
+    S_max = synth.max_spans(w.T, w.l_min)
+    gates = 1.0 / (1.0 + np.exp(-(rng.standard_normal((1, 1, 2, S_max, w.R)) + 0.5)))
+    eps = 0.5
+    idx = O.build_index_b(H[0], K[0], V[0], W, gates, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False, gate_eps=eps)
+    full = O.build_index_b(H[0], K[0], V[0], W, gates, R=w.R, alpha_sp=w.alpha_sp,
+                           l_min=w.l_min, Hq=w.Hq, store=False)
+    assert 0 < int(idx.rank_k.sum()) < int(full.rank_k.sum())
+    off = full.tok_off()
+    Kc, Vc = K[0, 0, 0].copy(), V[0, 0, 0].copy()
+    for j, (a, n) in enumerate(full.split.spans):
+        for which, X, U, sm, Vt in ((0, Kc, full.uk, full.smk, full.vkt), (1, Vc, full.uv, full.smv, full.vvt)):
+            cols = [i for i in range(w.R) if gates[0, 0, which, j, i] >= eps]
+            Uj = U[0, 0, off[j]:off[j] + n][:, cols]
+            X[a:a + n] = Uj @ np.diag(sm[0, 0, j][cols]) @ Vt[0, 0, j][cols]
+    for h in range(w.Hq):
+        out = O.decode_head(q[0, 0, h], idx, 0, 0, np.ones(idx.n_spans, bool))
+        ref = O.full_attention(q[0, 0, h], Kc, Vc)
+        assert np.linalg.norm(out - ref) <= 1e-10 * np.linalg.norm(ref)
+
+
+def test_all_components_dropped_is_attention_over_zero_rows():
+    """m = 1 and eps = 2 drop every component: each expanded span is n_S rows
+    of key 0 (logit 0) and value 0, so with every span expanded the output is
+    sum_raw e^l_t v_t / (sum_raw e^l_t + sum_S n_S), l_t = q . k_t / sqrt(d)."""
+    w, H, K, V, W, q = _small_workload(R=16)
+    idx = O.build_index_b(H[0], K[0], V[0], W, None, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False, gate_eps=2.0)
+    assert not idx.rank_k.any() and not idx.rank_v.any()
+    raw = idx.split.raw
+    ntok = int(idx.split.spans[:, 1].sum())
+    for h in range(w.Hq):
+        qh = q[0, 0, h]
+        lg = K[0, 0, 0][raw] @ qh / math.sqrt(w.d)
+        e = np.exp(lg)
+        ref = (e @ V[0, 0, 0][raw]) / (e.sum() + ntok)
+        out = O.decode_head(qh, idx, 0, 0, np.ones(idx.n_spans, bool))
+        assert np.linalg.norm(out - ref) <= 1e-10 * np.linalg.norm(ref)
