@@ -46,8 +46,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def span_alg_bytes(R, d, n):
-    return 4 * R * (n + d) + 8 * R
+def span_alg_bytes(rk, rv, d, n):
+    """Bytes of one span's factors with rk key and rv value components stored:
+    U (n x r), V^T (r x d) in bf16 and sigma * m in fp32, per K and V."""
+    return 2 * (rk + rv) * (n + d) + 4 * (rk + rv)
 
 
 def kernel_source_hash():
@@ -68,9 +70,10 @@ def traffic_from_profile(bytes_per_launch_alg):
     return t.get("bytes_per_launch")
 
 
-def union_alg_bytes(masks, n_spans, span_len, G, R, d):
+def union_alg_bytes(masks, n_spans, span_len, G, ranks, d):
     """Algorithmic factor bytes of one attention launch: for every (b, g), the
-    blobs of the union over the G heads' routed spans.  masks: uint64 [B, Hq, Wd]."""
+    blobs of the union over the G heads' routed spans.  masks: uint64 [B, Hq,
+    Wd]; ranks[b]: the layer's stored ranks, int [Hkv, N_S(b), 2] (K, V)."""
     B, Hq, Wd = masks.shape
     bits = np.unpackbits(masks.astype(">u8").view(np.uint8).reshape(B, Hq, Wd, 8), axis=3)[..., ::-1]
     bits = bits.reshape(B, Hq, Wd * 64).astype(bool)
@@ -78,9 +81,9 @@ def union_alg_bytes(masks, n_spans, span_len, G, R, d):
     off = 0
     for b in range(B):
         ns = int(n_spans[b])
-        lens = span_len[off:off + ns]
-        blob = span_alg_bytes(R, d, lens.astype(np.int64))
+        lens = span_len[off:off + ns].astype(np.int64)
         for g in range(Hq // G):
+            blob = span_alg_bytes(ranks[b][g, :, 0].astype(np.int64), ranks[b][g, :, 1].astype(np.int64), d, lens)
             u = bits[b, g * G:(g + 1) * G, :ns].any(0)
             tot += int(blob[u].sum())
             nun += int(u.sum())
@@ -238,6 +241,9 @@ def main(argv=None):
     ap.add_argument("--prefill", action="store_true",
                     help="time the prefill side instead: the index build of one 128K layer (R = 32) and the "
                          "randomized SVD of all its span matrices alone; prints one JSON line")
+    ap.add_argument("--gate-eps", type=float, default=0.0,
+                    help="build with this gate_eps: components whose gate is below it are not stored "
+                         "(variable effective rank; 0 keeps every component)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 4 plain device copies of MIB MiB each (a known-size kernel that scales "
                          "rocprofv3's FETCH_SIZE / WRITE_SIZE readings) and exit")
@@ -281,12 +287,20 @@ def main(argv=None):
 
     ctx = sl.Context(0, stream=stream)
     t0 = time.time()
-    idx = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM), K, V, H, W, gates)
+    idx = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM, gate_eps=args.gate_eps), K, V, H, W, gates)
     build_s = time.time() - t0
     info = idx.info
     log(f"[bench] index built in {build_s:.2f} s: spans {list(idx.n_spans)[:4]} raw {list(idx.n_raw)[:4]} "
         f"resident {info.resident_bytes / 1e9:.2f} GB factors {info.factor_bytes / 1e9:.2f} GB")
     _, span_len, _ = idx.spans()
+    # stored ranks per (b, l): [Hkv, N_S(b), 2]
+    rk_all = idx.export(fields=["rank"])["rank"]
+    ranks, o = [], 0
+    for b in range(w.B):
+        n = w.L * w.Hkv * int(idx.n_spans[b]) * 2
+        ranks.append(rk_all[o:o + n].reshape(w.L, w.Hkv, int(idx.n_spans[b]), 2))
+        o += n
+    mean_rank = float(rk_all.mean()) if rk_all.size else 0.0
 
     tau = torch.empty(w.L, w.Hq, device=dev)
     if w.tau is not None:
@@ -397,7 +411,7 @@ def main(argv=None):
     fac_bytes, unions = 0, 0
     for s in range(args.steps):
         for l in range(L):
-            fb, nu = union_alg_bytes(mk[s, l][:, 0], idx.n_spans, span_len, w.G, w.R, d)
+            fb, nu = union_alg_bytes(mk[s, l][:, 0], idx.n_spans, span_len, w.G, [r[l] for r in ranks], d)
             fac_bytes += fb
             unions += nu
     launches = args.steps * L
@@ -414,7 +428,8 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "query_heads": Hq, "kv_heads": w.Hkv, "head_dim": d,
-                   "batch": B, "context": w.T, "R": w.R, "dprime": w.dprime,
+                   "batch": B, "context": w.T, "R": w.R, "dprime": w.dprime, "gate_eps": args.gate_eps,
+                   "mean_stored_rank": round(mean_rank, 2),
                    "expand_frac_target": w.frac if w.tau is None else None, "tau": w.tau,
                    "cap": 0 if args.pooled else cap, "pooled_budget_per_layer": budget or None,
                    "factor_tier": "hbm",
@@ -439,7 +454,8 @@ def main(argv=None):
         del idx
         torch.cuda.synchronize()
         t0 = time.time()
-        pidx = ctx.build_index(sl.build_params(w, tier=sl.TIER_PINNED_HOST), K, V, H, W, gates)
+        pidx = ctx.build_index(sl.build_params(w, tier=sl.TIER_PINNED_HOST, gate_eps=args.gate_eps), K, V, H, W,
+                               gates)
         pbuild_s = time.time() - t0
         log(f"[bench] pinned-tier index built in {pbuild_s:.2f} s")
         psteps = min(4, args.steps)

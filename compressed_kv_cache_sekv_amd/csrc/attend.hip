@@ -129,6 +129,9 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
 // span, goes to the wave's LDS buffer instead: asynchronous global->LDS loads
 // (16 bytes per lane, 1 KB per instruction, lane i's bytes land at 16 i)
 // issued with the rest, so it costs no registers and no second round trip.
+// The blob holds nrk (nrv) 16-component blocks of key (value) factors, at most
+// R / 16 each: the registers are sized for R and the blocks past the stored
+// ones are neither loaded nor multiplied (wave-uniform branches).
 template <int D, int R>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
@@ -143,28 +146,33 @@ struct SpanRegs {
   u32x2 uk[4][NR16];
   u32x2 uvt[NR16][4];
   const uint8_t* blob;
-  int n, hm;
+  int n, hm, nrk, nrv;
 
-  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int lane, int grp, uint8_t* lds_vv,
-                                       uint8_t* lds_ck) {
+  __device__ __forceinline__ void load(const uint8_t* b, int n_, int hm_, int ranks, int lane, int grp,
+                                       uint8_t* lds_vv, uint8_t* lds_ck) {
     blob = b;
     n = n_;
     hm = hm_;
-    const bf16_t* pk = (const bf16_t*)(b + Blob::off_vkt(R, D));
-    const uint8_t* pv = b + Blob::off_vv(R, D);
-    const float* sk = (const float*)(b + Blob::off_smk(R, D));
-    const float* sv = (const float*)(b + Blob::off_smv(R, D));
-    const bf16_t* pu = (const bf16_t*)(b + Blob::off_uk(R, D));
-    const bf16_t* pw = (const bf16_t*)(b + Blob::off_uvt(R, D, n_));
+    // stored ranks rk | rv << 16 (multiples of 16), clamped to [16, R]
+    nrk = (NR16 == 1) ? 1 : min(max((ranks & 0xffff) >> 4, 1), NR16);
+    nrv = (NR16 == 1) ? 1 : min(max((int)((uint32_t)ranks >> 20), 1), NR16);
+    const int rk = 16 * nrk, rv = 16 * nrv;
+    const bf16_t* pk = (const bf16_t*)(b + Blob::off_vkt());
+    const uint8_t* pv = b + Blob::off_vv(rk, D);
+    const float* sk = (const float*)(b + Blob::off_smk(rk, rv, D));
+    const float* sv = (const float*)(b + Blob::off_smv(rk, rv, D));
+    const bf16_t* pu = (const bf16_t*)(b + Blob::off_uk(rk, rv, D));
+    const bf16_t* pw = (const bf16_t*)(b + Blob::off_uvt(rk, rv, D, n_));
     const int ntb = Blob::npad(n_) >> 4;
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib)
+      if (ib < nrk)
 #pragma unroll
-      for (int s = 0; s < NS32; ++s) vkt[ib][s] = *(const u32x4*)(pk + ib * 16 * D + s * 512 + lane * 8);
+        for (int s = 0; s < NS32; ++s) vkt[ib][s] = *(const u32x4*)(pk + ib * 16 * D + s * 512 + lane * 8);
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib) {
-      smk[ib] = *(const floatx4*)(sk + 16 * ib + 4 * grp);
-      smv[ib] = *(const floatx4*)(sv + 16 * ib + 4 * grp);
+      if (ib < nrk) smk[ib] = *(const floatx4*)(sk + 16 * ib + 4 * grp);
+      if (ib < nrv) smv[ib] = *(const floatx4*)(sv + 16 * ib + 4 * grp);
     }
     // token blocks past ntb read block ntb - 1 again (in range; never used)
 #pragma unroll
@@ -172,52 +180,59 @@ struct SpanRegs {
       const int tbc = min(tb, ntb - 1);
 #pragma unroll
       for (int kb = 0; kb < NR16; ++kb)
-        uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
+        if (kb < nrk) uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
     }
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib)
+      if (ib < nrv)
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int tbc = min(tb, ntb - 1);
-        uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
-      }
+        for (int tb = 0; tb < 4; ++tb) {
+          const int tbc = min(tb, ntb - 1);
+          uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
+        }
+    // V^V: D rv bf16 = D nrv / 32 KB
 #pragma unroll
     for (int c = 0; c < VV_BYTES / 1024; ++c)
-      __builtin_amdgcn_global_load_lds((const void*)(pv + c * 1024 + lane * 16),
-                                       (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, 0);
+      if (c < D * nrv / 32)
+        __builtin_amdgcn_global_load_lds((const void*)(pv + c * 1024 + lane * 16),
+                                         (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, 0);
     if (CK && ntb > 4) {   // wave-uniform
-      // 512-byte blocks: U^K (tb, kb) at (tb' NR16 + kb), then U^V^T (ib, tb)
-      // at 4 NR16 + ib 4 + tb', tb' = tb - 4; blocks past the span re-read
-      // its last block (in range, multiplied by zero weights)
+      // 512-byte blocks: U^K (tb, kb) at tb' nrk + kb, then U^V^T (ib, tb) at
+      // 4 nrk + 4 ib + tb', tb' = tb - 4; blocks past the span re-read its
+      // last block (in range, multiplied by zero weights).  Two blocks a load;
+      // nrk is 1 or 2 here (R <= 32), so blk / nrk is a shift.
       const uint8_t* uk8 = (const uint8_t*)pu;
       const uint8_t* uv8 = (const uint8_t*)pw;
+      const int sh = nrk - 1;
 #pragma unroll
       for (int c = 0; c < 4 * NR16; ++c) {
-        const int blk = 2 * c + (lane >> 5);
-        int64_t src;
-        if (blk < 4 * NR16) {
-          const int tb = 4 + blk / NR16, kb = blk % NR16;
-          src = (int64_t)(min(tb, ntb - 1) * NR16 + kb) * 512;
-          src += (int64_t)(uk8 - b);
-        } else {
-          const int ib = (blk - 4 * NR16) >> 2, tb = 4 + ((blk - 4 * NR16) & 3);
-          src = (int64_t)(ib * ntb + min(tb, ntb - 1)) * 512;
-          src += (int64_t)(uv8 - b);
+        if (c < 2 * (nrk + nrv)) {
+          const int blk = 2 * c + (lane >> 5);
+          int64_t src;
+          if (blk < 4 * nrk) {
+            const int tb = 4 + (blk >> sh), kb = blk & sh;
+            src = (int64_t)(min(tb, ntb - 1) * nrk + kb) * 512;
+            src += (int64_t)(uk8 - b);
+          } else {
+            const int ib = (blk - 4 * nrk) >> 2, tb = 4 + ((blk - 4 * nrk) & 3);
+            src = (int64_t)(ib * ntb + min(tb, ntb - 1)) * 512;
+            src += (int64_t)(uv8 - b);
+          }
+          __builtin_amdgcn_global_load_lds((const void*)(b + src + (lane & 31) * 16),
+                                           (__attribute__((address_space(3))) void*)(lds_ck + c * 1024), 16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds((const void*)(b + src + (lane & 31) * 16),
-                                         (__attribute__((address_space(3))) void*)(lds_ck + c * 1024), 16, 0, 0);
       }
     }
   }
 };
 
 // One chunk of up to 64 tokens of a routed span: scores, online softmax and
-// the U^V^T p accumulation.
+// the U^V^T p accumulation, over the nrk key and nrv value blocks stored.
 template <int D, int G, int R>
 __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u32x2 (&uvt)[R / 16][4], int tb0,
-                                           int nb, int n, bool act, int grp, const u32x2 (&chi)[R / 16],
-                                           const u32x2 (&clo)[R / 16], float& m, float& l,
-                                           floatx4 (&o)[D / 16], floatx4 (&wacc)[R / 16]) {
+                                           int nb, int n, bool act, int grp, int nrk, int nrv,
+                                           const u32x2 (&chi)[R / 16], const u32x2 (&clo)[R / 16], float& m,
+                                           float& l, floatx4 (&o)[D / 16], floatx4 (&wacc)[R / 16]) {
   constexpr int ND16 = D / 16, NR16 = R / 16;
   floatx4 sc[4];
 #pragma unroll
@@ -225,10 +240,11 @@ __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u
     sc[tb] = floatx4{0, 0, 0, 0};
     if (tb < nb) {
 #pragma unroll
-      for (int kb = 0; kb < NR16; ++kb) {
-        sc[tb] = mfma16(uk[tb][kb], chi[kb], sc[tb]);
-        sc[tb] = mfma16(uk[tb][kb], clo[kb], sc[tb]);
-      }
+      for (int kb = 0; kb < NR16; ++kb)
+        if (kb < nrk) {
+          sc[tb] = mfma16(uk[tb][kb], chi[kb], sc[tb]);
+          sc[tb] = mfma16(uk[tb][kb], clo[kb], sc[tb]);
+        }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tok = 16 * (tb0 + tb) + 4 * grp + r;
@@ -247,10 +263,11 @@ __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u
       u32x2 phi, plo;
       pack4(sc[tb], phi, plo);
 #pragma unroll
-      for (int ib = 0; ib < NR16; ++ib) {
-        wacc[ib] = mfma16(uvt[ib][tb], phi, wacc[ib]);
-        wacc[ib] = mfma16(uvt[ib][tb], plo, wacc[ib]);
-      }
+      for (int ib = 0; ib < NR16; ++ib)
+        if (ib < nrv) {
+          wacc[ib] = mfma16(uvt[ib][tb], phi, wacc[ib]);
+          wacc[ib] = mfma16(uvt[ib][tb], plo, wacc[ib]);
+        }
     }
   }
 }
@@ -262,24 +279,27 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
                                           floatx4 (&o)[D / 16], const uint8_t* lds_vv, const uint8_t* lds_ck) {
   constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
   const int n = sr.n, npad = Blob::npad(n), ntb = npad >> 4;
+  const int nrk = sr.nrk, nrv = sr.nrv;
   // t = V^K^T q; c = t * sigma m^K / sqrt(d), split into bf16 hi + lo
   u32x2 chi[NR16], clo[NR16];
 #pragma unroll
-  for (int ib = 0; ib < NR16; ++ib) {
-    floatx4 t = floatx4{0, 0, 0, 0};
+  for (int ib = 0; ib < NR16; ++ib)
+    if (ib < nrk) {
+      floatx4 t = floatx4{0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < NS32; ++s) t = mfma32(sr.vkt[ib][s], qB[s], t);
-    pack4(t * sr.smk[ib] * scale, chi[ib], clo[ib]);
-  }
+      for (int s = 0; s < NS32; ++s) t = mfma32(sr.vkt[ib][s], qB[s], t);
+      pack4(t * sr.smk[ib] * scale, chi[ib], clo[ib]);
+    }
   const bool act = (hl < G) && ((sr.hm >> hl) & 1);
   floatx4 wacc[NR16];
 #pragma unroll
   for (int ib = 0; ib < NR16; ++ib) wacc[ib] = floatx4{0, 0, 0, 0};
   // first 64 tokens from the preloaded registers, the rest streamed
-  span_chunk<D, G, R>(sr.uk, sr.uvt, 0, min(4, ntb), n, act, grp, chi, clo, m, l, o, wacc);
+  span_chunk<D, G, R>(sr.uk, sr.uvt, 0, min(4, ntb), n, act, grp, nrk, nrv, chi, clo, m, l, o, wacc);
   if (ntb > 4) {
-    const bf16_t* pu = (const bf16_t*)(sr.blob + Blob::off_uk(R, D));
-    const bf16_t* pw = (const bf16_t*)(sr.blob + Blob::off_uvt(R, D, n));
+    const int rk = 16 * nrk, rv = 16 * nrv;
+    const bf16_t* pu = (const bf16_t*)(sr.blob + Blob::off_uk(rk, rv, D));
+    const bf16_t* pw = (const bf16_t*)(sr.blob + Blob::off_uvt(rk, rv, D, n));
     for (int tb0 = 4; tb0 < ntb; tb0 += 4) {
       const int nb = min(4, ntb - tb0);
       u32x2 uk[4][NR16], uvt[NR16][4];
@@ -288,30 +308,34 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
         // the asynchronous copies included)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-          for (int kb = 0; kb < NR16; ++kb) {
-            uk[tb][kb] = *(const u32x2*)(lds_ck + (tb * NR16 + kb) * 512 + lane * 8);
-            uvt[kb][tb] = *(const u32x2*)(lds_ck + (4 * NR16 + kb * 4 + tb) * 512 + lane * 8);
-          }
+          for (int kb = 0; kb < NR16; ++kb)
+            if (kb < nrk) uk[tb][kb] = *(const u32x2*)(lds_ck + (tb * nrk + kb) * 512 + lane * 8);
+#pragma unroll
+          for (int ib = 0; ib < NR16; ++ib)
+            if (ib < nrv) uvt[ib][tb] = *(const u32x2*)(lds_ck + (4 * nrk + ib * 4 + tb) * 512 + lane * 8);
+        }
       } else {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const int tbc = tb0 + min(tb, nb - 1);
 #pragma unroll
-          for (int kb = 0; kb < NR16; ++kb) {
-            uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * NR16 + kb) * 256 + lane * 4);
-            uvt[kb][tb] = *(const u32x2*)(pw + ((int64_t)kb * ntb + tbc) * 256 + lane * 4);
-          }
+          for (int kb = 0; kb < NR16; ++kb)
+            if (kb < nrk) uk[tb][kb] = *(const u32x2*)(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
+#pragma unroll
+          for (int ib = 0; ib < NR16; ++ib)
+            if (ib < nrv) uvt[ib][tb] = *(const u32x2*)(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
         }
       }
-      span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, chi, clo, m, l, o, wacc);
+      span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, nrk, nrv, chi, clo, m, l, o, wacc);
     }
   }
   // o += V^V (sigma m^V . w)
   u32x2 whi[NR16], wlo[NR16];
 #pragma unroll
-  for (int ib = 0; ib < NR16; ++ib) pack4(wacc[ib] * sr.smv[ib], whi[ib], wlo[ib]);
+  for (int ib = 0; ib < NR16; ++ib)
+    if (ib < nrv) pack4(wacc[ib] * sr.smv[ib], whi[ib], wlo[ib]);
   // V^V from the wave's LDS copy: wait for every outstanding load of the
   // wave, the asynchronous copies included
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -319,11 +343,12 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
 #pragma unroll
   for (int db = 0; db < ND16; ++db)
 #pragma unroll
-    for (int kb = 0; kb < NR16; ++kb) {
-      const u32x2 vvv = *(const u32x2*)(pv + ((db * NR16 + kb) * 256 + lane * 4));
-      o[db] = mfma16(vvv, whi[kb], o[db]);
-      o[db] = mfma16(vvv, wlo[kb], o[db]);
-    }
+    for (int kb = 0; kb < NR16; ++kb)
+      if (kb < nrv) {
+        const u32x2 vvv = *(const u32x2*)(pv + ((db * nrv + kb) * 256 + lane * 4));
+        o[db] = mfma16(vvv, whi[kb], o[db]);
+        o[db] = mfma16(vvv, wlo[kb], o[db]);
+      }
 }
 
 // One 32-row step of resident rows for the lane's head: two 16-row key
@@ -437,10 +462,11 @@ void attend_kernel(const AttendArgs a) {
   __shared__ float s_o[4][G][D];
   // per wave: the item's share of the union (span id | active heads << 24
   // by rank within the share), then the wave's own spans in the order it
-  // takes them: blob offset, length, active heads
+  // takes them: blob offset, length, active heads, stored ranks
   __shared__ int32_t s_ln[4][kMaxSpanList];
   __shared__ int64_t s_woff[4][kMaxSpanList];
   __shared__ int32_t s_wn[4][kMaxSpanList];
+  __shared__ int32_t s_wr[4][kMaxSpanList];   // stored ranks rk | rv << 16
   __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
   __shared__ __attribute__((aligned(16))) uint8_t s_ck[4][SpanRegs<D, R>::CK_BYTES];   // per wave
   extern __shared__ uint64_t s_dyn[];
@@ -485,6 +511,8 @@ void attend_kernel(const AttendArgs a) {
   // resident slice: wave w takes steps step_begin + w, + 4, ...; the first
   // one's loads stay in flight during the span bookkeeping below
   const int64_t lg = (int64_t)l * a.Hkv + g;
+  // start of layer l's blobs in `pool`
+  const int64_t lbase = a.layer_off[l] - a.layer_off[a.pool_layer0];
   const bf16_t* Kb = a.kres + bm.res_base + lg * bm.n_res_pad * D;
   const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
   const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
@@ -559,8 +587,8 @@ void attend_kernel(const AttendArgs a) {
   const int ek = (nsh > 0) ? s_ln[wave][min(lane, nsh - 1)] : 0;
   const int Sk = spans ? bm.span_base + (ek & 0xffffff) : 0;
   const int nk = a.span_len[Sk];
-  const int64_t ok = a.span_off[Sk] + (int64_t)(l - a.pool_layer0) * a.layer_bytes + bm.pool_base +
-                     (int64_t)g * bm.pool_lg;
+  const uint2 rfk = a.bref[lg * a.total_spans + Sk];
+  const int64_t ok = lbase + (int64_t)rfk.x * 256;
 
   // resident slice: fold (the span metadata loads are in flight)
   if (t < it.step_end) {
@@ -600,10 +628,12 @@ void attend_kernel(const AttendArgs a) {
     const uint64_t mine = __ballot(lane < nsh && wr == wave);
     const uint32_t olo = __shfl((uint32_t)ok, er), ohi = __shfl((uint32_t)((uint64_t)ok >> 32), er);
     const int ne = __shfl(nk, er), he = (int)((uint32_t)__shfl(ek, er) >> 24);
+    const int rke = __shfl((int)rfk.y, er);
     if ((mine >> lane) & 1ull) {
       const int pos = (int)__popcll(mine & ((1ull << lane) - 1));
       s_woff[wave][pos] = (int64_t)(((uint64_t)ohi << 32) | olo);
       s_wn[wave][pos] = ne | (he << 24);
+      s_wr[wave][pos] = rke;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -611,8 +641,8 @@ void attend_kernel(const AttendArgs a) {
     for (int i = 0; i < nw; ++i) {
       const int nh = s_wn[wave][i];
       SpanRegs<D, R> cur;
-      cur.load(a.pool + uni64(s_woff[wave][i]), uni(nh & 0xffffff), uni((int)((uint32_t)nh >> 24)), lane, grp,
-               s_vv[wave], s_ck[wave]);
+      cur.load(a.pool + uni64(s_woff[wave][i]), uni(nh & 0xffffff), uni((int)((uint32_t)nh >> 24)),
+               uni(s_wr[wave][i]), lane, grp, s_vv[wave], s_ck[wave]);
       span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave], s_ck[wave]);
     }
   }
@@ -806,7 +836,7 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
     auto kern = attend_kernel<D_, G_, R_>;
     const size_t dyn = attend_dyn_lds(G_, a.W);
-    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * 16 * kMaxSpanList +
+    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * 20 * kMaxSpanList +
                              4 * (SpanRegs<D_, R_>::VV_BYTES + SpanRegs<D_, R_>::CK_BYTES);
     if (fixed + dyn > 160 * 1024) return hipErrorInvalidValue;
     if (dyn > 32 * 1024) {

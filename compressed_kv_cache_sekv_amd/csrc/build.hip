@@ -10,11 +10,15 @@
 //  * section 핵심 기여 (Key contributions): the summary and the mean K/V are
 //    surprisal-weighted.
 //  * section 기술 상세 (Technical details): the reconstruction
-//    Khat_S = sum_i m_i sigma_i u_i v_i^T, so sigma_i * m_i is stored.
+//    Khat_S = sum_i m_i sigma_i u_i v_i^T, so sigma_i * m_i is stored; the
+//    components are dropped at storage and transfer, and section 핵심 기여
+//    (Key contributions) has the gates set each span's effective rank: a
+//    component whose gate is below the build's gate_eps is not stored.
 //
-// Kernels: span_split (one workgroup per sequence), pack_raw (raw rows into the
-// resident layouts), summaries (one wave per (b, l, g, span)).  The truncated
-// SVD of the spans is in rsvd.hip.
+// Kernels: span_split (one workgroup per sequence), ranks (stored rank of
+// every span factorization, which sizes the factor pool), pack_raw (raw rows
+// into the resident layouts), summaries (one wave per (b, l, g, span)).  The
+// truncated SVD of the spans is in rsvd.hip.
 #include "common.h"
 
 namespace sekv {
@@ -23,6 +27,47 @@ __device__ __forceinline__ float bf(bf16_t h) { return __uint_as_float((uint32_t
 __device__ __forceinline__ bf16_t to_bf16(float x) {
   const uint32_t u = __float_as_uint(x);
   return (bf16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- ranks ---
+
+// One thread per (b, l, g, span slot): the components kept of the span's K
+// and V factorizations (i < min(R, n) with gate_kept), as stored ranks.  Slots
+// at or past N_S(b) write 0.
+__global__ __launch_bounds__(256) void rank_kernel(const RankArgs a) {
+  const int nbx = (a.S_max + 255) / 256;
+  const int blg = blockIdx.x / nbx;   // (b L + l) Hkv + g
+  const int S = (blockIdx.x - blg * nbx) * 256 + threadIdx.x;
+  const int b = blg / (a.L * a.Hkv);
+  if (S >= a.S_max) return;
+  uint32_t* out = a.ranks + (int64_t)blg * a.S_max + S;
+  if (S >= a.counts[2 * b]) {
+    *out = 0u;
+    return;
+  }
+  const int n = a.span_len[(int64_t)b * a.S_max + S];
+  const int r = min(a.R, n);
+  int kept[2];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    int c = 0;
+    if (a.gates) {
+      const float* m = a.gates + (((int64_t)blg * 2 + which) * a.S_max + S) * a.R;
+      for (int i = 0; i < r; ++i) c += gate_kept(m[i], a.gate_eps);
+    } else {
+      c = gate_kept(1.f, a.gate_eps) ? r : 0;
+    }
+    kept[which] = stored_rank(c);
+  }
+  *out = (uint32_t)kept[0] | ((uint32_t)kept[1] << 16);
+}
+
+hipError_t launch_ranks(const RankArgs& a, hipStream_t st) {
+  if (a.S_max < 1 || a.B * a.L * a.Hkv < 1) return hipSuccess;
+  const int64_t blocks = (int64_t)((a.S_max + 255) / 256) * a.B * a.L * a.Hkv;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rank_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- scans ---
@@ -116,13 +161,11 @@ __global__ __launch_bounds__(1024) void span_split_kernel(const SplitArgs a) {
   int sb = scan1024(nc, s_tmp, &n_spans);
   int32_t* sst = a.span_start + (int64_t)b * a.S_max;
   int32_t* sln = a.span_len + (int64_t)b * a.S_max;
-  float* slg = a.span_logn + (int64_t)b * a.S_max;
   for (int r = r0; r < r1; ++r) {
     const int len = ends[r] - starts[r] + 1;
     if (len >= a.l_min) {
       sst[sb] = starts[r];
       sln[sb] = len;
-      slg[sb] = logf((float)len);
       ++sb;
     }
   }

@@ -50,32 +50,43 @@ __host__ __device__ inline int64_t a16_off(int64_t i, int k, int Kd) {
   return ((i >> 4) * (Kd >> 4) + (k >> 4)) * 256 + lane * 4 + e;
 }
 
-// One span's factor blob (per layer and KV head), n_pad = n rounded up to 16:
-//   VKt  [R][d]   right key factors V^K^T        krow_off(i, dim, d)
-//   VV   [d][R]   right value factors V^V        a16_off(dim, i, R)
-//   smK  [R] fp32 sigma^K * m^K
-//   smV  [R] fp32 sigma^V * m^V
-//   UK   [n_pad][R] left key factors U^K         a16_off(t, i, R)
-//   UVt  [R][n_pad] left value factors U^V^T     a16_off(i, t, n_pad)
-// Rows/cols past n are zero.  Blobs start on 256-byte boundaries.
+// One span's factor blob (per layer and KV head), with rk key and rv value
+// components stored (multiples of 16, the MFMA tile; see BlobRef), n_pad = n
+// rounded up to 16:
+//   VKt  [rk][d]   right key factors V^K^T       krow_off(i, dim, d)
+//   VV   [d][rv]   right value factors V^V       a16_off(dim, i, rv)
+//   smK  [rk] fp32 sigma^K * m^K
+//   smV  [rv] fp32 sigma^V * m^V
+//   UK   [n_pad][rk] left key factors U^K        a16_off(t, i, rk)
+//   UVt  [rv][n_pad] left value factors U^V^T    a16_off(i, t, n_pad)
+// Rows/cols past n and components past the kept ones are zero.  Blobs start
+// on 256-byte boundaries.
 struct Blob {
   static __host__ __device__ inline int npad(int n) { return (n + 15) & ~15; }
-  static __host__ __device__ inline int64_t off_vkt(int, int) { return 0; }
-  static __host__ __device__ inline int64_t off_vv(int R, int D) { return 2LL * R * D; }
-  static __host__ __device__ inline int64_t off_smk(int R, int D) { return 4LL * R * D; }
-  static __host__ __device__ inline int64_t off_smv(int R, int D) { return 4LL * R * D + 4LL * R; }
-  static __host__ __device__ inline int64_t off_uk(int R, int D) { return 4LL * R * D + 8LL * R; }
-  static __host__ __device__ inline int64_t off_uvt(int R, int D, int n) {
-    return off_uk(R, D) + 2LL * npad(n) * R;
+  static __host__ __device__ inline int64_t off_vkt() { return 0; }
+  static __host__ __device__ inline int64_t off_vv(int rk, int D) { return 2LL * rk * D; }
+  static __host__ __device__ inline int64_t off_smk(int rk, int rv, int D) { return 2LL * (rk + rv) * D; }
+  static __host__ __device__ inline int64_t off_smv(int rk, int rv, int D) { return off_smk(rk, rv, D) + 4LL * rk; }
+  static __host__ __device__ inline int64_t off_uk(int rk, int rv, int D) { return off_smv(rk, rv, D) + 4LL * rv; }
+  static __host__ __device__ inline int64_t off_uvt(int rk, int rv, int D, int n) {
+    return off_uk(rk, rv, D) + 2LL * npad(n) * rk;
   }
-  static __host__ __device__ inline int64_t bytes(int R, int D, int n) {
-    return (off_uvt(R, D, n) + 2LL * npad(n) * R + 255) & ~255LL;
-  }
-  // algorithmic bytes of one span: 4R(n + d) + 8R (no padding)
-  static __host__ __device__ inline int64_t alg_bytes(int R, int D, int n) {
-    return 4LL * R * (n + D) + 8LL * R;
+  static __host__ __device__ inline int64_t bytes(int rk, int rv, int D, int n) {
+    return (off_uvt(rk, rv, D, n) + 2LL * npad(n) * rv + 255) & ~255LL;
   }
 };
+
+// Where the blob of (layer l, KV head g, span) sits and what it holds: a
+// uint2 {x: byte offset / 256 within layer l's factor region, y: rk | rv << 16}.
+// Table [L][Hkv][total spans]; the layer's region starts at layer_off[l].
+__host__ __device__ inline int bref_rk(uint2 r) { return (int)(r.y & 0xffffu); }
+__host__ __device__ inline int bref_rv(uint2 r) { return (int)(r.y >> 16); }
+
+// Stored rank of a span's K or V factorization that keeps `kept` components:
+// rounded up to the 16-wide MFMA tile, at least one tile.
+__host__ __device__ inline int stored_rank(int kept) { return kept <= 16 ? 16 : (kept + 15) & ~15; }
+// Component gate test: kept iff eps <= 0 or m >= eps (NaN gates fail it).
+__host__ __device__ inline bool gate_kept(float m, float eps) { return eps <= 0.f || m >= eps; }
 
 // Per-sequence metadata (device copy used by every kernel).
 // Summary keys s of one (b, l, h): s_pad span slots x d4 = d' rounded up to 4
@@ -99,9 +110,6 @@ struct BMeta {
   int64_t tok_base;     // first token of b's spans in the concatenated U order
   int64_t res_base;     // element offset of (b, l=0, g=0) in K/V resident rows
   int64_t s_base;       // element offset of (b, l=0, h=0) in s
-  int64_t pool_base;    // byte offset of (b, g=0) within a layer's factor region
-  int64_t pool_lg;      // bytes per (l, g) factor region of b; the region of
-                        // (b, l, g) starts at l * layer_bytes + pool_base + g * pool_lg
 };
 
 // Routed spans one work item may take (one per lane of a wave).
@@ -131,11 +139,12 @@ struct AttendArgs {
   const bf16_t* vres;
   const float* logn;        // [span] ln n_S
   const int32_t* span_len;  // [span]
-  const int64_t* span_off;  // [span] byte offset of the blob in its (b, l, g) region
+  const uint2* bref;        // [L][Hkv][total_spans] blob references
+  const int64_t* layer_off; // [L + 1] byte offset of each layer's factor region
   const uint8_t* pool;      // factor pool (HBM tier) or staging ring (pinned
                             // tier: the call's layers, blobs at their pool offsets)
   float* part;              // [Lc][n_items][G][D + 2] softmax partials
-  int64_t layer_bytes;      // factor-pool bytes of one layer (all b, g)
+  int64_t total_spans;
   int32_t pool_layer0;      // layer at the start of `pool` (0; the ring: layer_begin)
   int32_t layer_begin, layer_count, n_items;
   int32_t B, L, Hq, Hkv, W, max_spans;
@@ -179,12 +188,13 @@ struct GatherArgs {
   const uint64_t* mask;      // [B][Lc][Hq][W]
   const BMeta* meta;
   const int32_t* span_len;
-  const int64_t* span_off;
+  const uint2* bref;         // [L][Hkv][total_spans] blob references
+  const int64_t* layer_off;  // [L + 1]
   const uint8_t* host_pool;  // device address of the mapped pinned factor pool
-  uint8_t* ring;             // HBM staging ring: layer layer_begin + li at li * layer_bytes
+  uint8_t* ring;             // HBM staging ring: layer l at layer_off[l] - layer_off[layer_begin]
   int2* stat;                // [Lc][B][Hkv]: union spans, union blob bytes / 256 (or NULL)
-  int64_t layer_bytes;
-  int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, R, D, nsplit;
+  int64_t total_spans;
+  int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, D, nsplit;
 };
 
 // ------------------------------------------------------------ launchers ---
@@ -206,7 +216,6 @@ struct SplitArgs {
   const float* H;           // [B][T]
   int32_t* span_start;      // [B][S_max]
   int32_t* span_len;        // [B][S_max]
-  float* span_logn;         // [B][S_max]
   int32_t* raw_pos;         // [B][T]
   int32_t* counts;          // [B][2] (N_S, N_raw)
   int32_t* scratch;         // [B][2][T/2 + 2]
@@ -214,6 +223,18 @@ struct SplitArgs {
   double alpha_sp;
 };
 hipError_t launch_span_split(const SplitArgs& a, hipStream_t st);
+
+// Stored ranks of every span's K and V factorization (span split scratch
+// layout): ranks[((b L + l) Hkv + g) S_max + S] = rk | rv << 16.
+struct RankArgs {
+  const float* gates;       // [B][L][Hkv][2][S_max][R] or NULL (m = 1)
+  const int32_t* span_len;  // [B][S_max]
+  const int32_t* counts;    // [B][2] (N_S, N_raw)
+  uint32_t* ranks;          // [B][L][Hkv][S_max]
+  int32_t B, L, Hkv, R, S_max;
+  float gate_eps;
+};
+hipError_t launch_ranks(const RankArgs& a, hipStream_t st);
 
 struct PackArgs {
   const bf16_t* K;          // [B][L][Hkv][T][D]
@@ -225,12 +246,14 @@ struct PackArgs {
   const int32_t* span_start;  // concatenated over b
   const int32_t* span_len;
   const int32_t* raw_pos;
-  const int64_t* span_off;
+  const uint2* bref;        // [L][Hkv][total_spans] blob references
   bf16_t* kres;
   bf16_t* vres;
   float* s;
   uint8_t* pool;            // device factor destination: one layer's region
-                            // (pool + layer * layer_bytes, or a staging buffer)
+                            // (pool + layer_off[layer], or a staging buffer)
+  int64_t total_spans;
+  float gate_eps;           // components with gate < gate_eps are dropped (if > 0)
   int32_t B, L, Hq, Hkv, D, T, R, dp, S_max;
   int32_t layer;            // layer for the per-layer SVD launch
   int32_t max_raw, max_spans;

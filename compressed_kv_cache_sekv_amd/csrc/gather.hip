@@ -9,9 +9,10 @@
 //
 // The pinned pool is mapped into the device address space and read by the
 // kernel over PCIe.  The HBM ring mirrors the pool's layout for the layers of
-// the call: a blob of layer layer_begin + li lands at its own layer-relative
-// offset in ring layer li, so no placement is computed on the host and the
-// call does not synchronise.  gather_kernel, per (layer, b, KV head, share):
+// the call (layer l's region at layer_off[l] - layer_off[layer_begin]): a blob
+// lands at its own offset within its layer's region, so no placement is
+// computed on the host and the call does not synchronise.  Blobs hold only the
+// components the build kept, so a smaller effective rank moves fewer bytes.  gather_kernel, per (layer, b, KV head, share):
 // forms the union over the G heads' masks and its rank and byte prefix per
 // mask word, and copies its share of the union's blobs; share 0 records the
 // union's size for the call's statistics.
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   __shared__ uint64_t s_uw[kMaxWords];
   __shared__ int32_t s_pre[kMaxWords + 1];      // union spans before word w
   __shared__ int64_t s_bpre[kMaxWords + 1];     // union bytes before word w
-  __shared__ int64_t s_src[kShare];             // blob offset within the layer
+  __shared__ int64_t s_src[kShare];             // blob byte offset within the layer
   __shared__ int32_t s_len[kShare];             // 16-byte chunks
   const int li = blockIdx.y, l = a.layer_begin + li;
   const int j = blockIdx.x % a.nsplit, bg = blockIdx.x / a.nsplit;
@@ -42,14 +43,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   const int64_t rid = ((int64_t)li * a.B + b) * a.Hkv + g;
   const uint64_t* mrow = a.mask + (((int64_t)b * a.layer_count + li) * a.Hq + (int64_t)g * a.G) * a.W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // blob references of (l, g) for b's spans
+  const uint2* bref = a.bref + ((int64_t)l * a.Hkv + g) * a.total_spans + bm.span_base;
+  const int32_t* slen = a.span_len + bm.span_base;
   for (int w = threadIdx.x; w < a.W; w += 256) {
     uint64_t u = 0;
     for (int h = 0; h < a.G; ++h) u |= mrow[(int64_t)h * a.W + w];
     u &= valid_bits(bm.n_spans, w);
     s_uw[w] = u;
     int64_t by = 0;
-    for (uint64_t v = u; v; v &= v - 1)
-      by += Blob::bytes(a.R, a.D, a.span_len[bm.span_base + 64 * w + __builtin_ctzll(v)]);
+    for (uint64_t v = u; v; v &= v - 1) {
+      const int S = 64 * w + __builtin_ctzll(v);
+      const uint2 r = bref[S];
+      by += Blob::bytes(bref_rk(r), bref_rv(r), a.D, slen[S]);
+    }
     s_bpre[w + 1] = by;
     s_pre[w + 1] = __popcll(u);
   }
@@ -84,7 +91,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   }
   __syncthreads();
   const int U = s_pre[a.W];
-  const int64_t region = (int64_t)bm.pool_base + (int64_t)g * bm.pool_lg;   // (b, g) blobs within a layer
   if (j == 0 && threadIdx.x == 0 && a.stat) a.stat[rid] = make_int2(U, (int)(s_bpre[a.W] >> 8));
   const int beg = (int)((int64_t)j * U / a.nsplit), end = (int)((int64_t)(j + 1) * U / a.nsplit);
   const int cnt = min(end - beg, kShare);   // the host keeps shares <= kShare
@@ -95,8 +101,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
     for (uint64_t u = s_uw[w]; u && k < beg + cnt; u &= u - 1) {
       const int S = 64 * w + __builtin_ctzll(u);
       if (k >= beg) {
-        s_src[k - beg] = region + a.span_off[bm.span_base + S];
-        s_len[k - beg] = (int32_t)(Blob::bytes(a.R, a.D, a.span_len[bm.span_base + S]) >> 4);
+        const uint2 r = bref[S];
+        s_src[k - beg] = (int64_t)r.x * 256;
+        s_len[k - beg] = (int32_t)(Blob::bytes(bref_rk(r), bref_rv(r), a.D, slen[S]) >> 4);
       }
       ++k;
     }
@@ -104,8 +111,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   __syncthreads();
   // copy to the same offset of ring layer li, 16 bytes per lane, four loads
   // in flight per lane
-  const uint8_t* src_l = a.host_pool + (int64_t)l * a.layer_bytes;
-  uint8_t* dst_l = a.ring + (int64_t)li * a.layer_bytes;
+  const uint8_t* src_l = a.host_pool + a.layer_off[l];
+  uint8_t* dst_l = a.ring + (a.layer_off[l] - a.layer_off[a.layer_begin]);
   for (int e = 0; e < cnt; ++e) {
     const u32x4* src = (const u32x4*)(src_l + s_src[e]);
     u32x4* dst = (u32x4*)(dst_l + s_src[e]);

@@ -450,6 +450,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   __shared__ float s_sinv[LP];
   __shared__ float s_dinv[LP];
   __shared__ int s_perm[LP];
+  __shared__ int s_slot[LP];
   __shared__ int s_flag[2];
   __shared__ f32x4 s_rot[LP / 2 + 1];
 
@@ -702,10 +703,29 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   }
   __syncthreads();
 
-  // ---- outputs
+  // ---- outputs.  Index build: component i is stored in slot s_slot[i] of
+  // the blob's rk (K) or rv (V) stored components, in order; a component past
+  // min(R, n) or whose gate is below gate_eps is dropped (-1).  Slots past the
+  // kept ones stay zero.
   const int npad = Blob::npad(n);
   uint8_t* blob = nullptr;
-  if (!BATCHED) blob = a.pool + bm.pool_base + (int64_t)g * bm.pool_lg + a.span_off[bm.span_base + S];
+  int rk = R, rv = R;
+  if (!BATCHED) {
+    const uint2 ref = a.bref[((int64_t)a.layer * a.Hkv + g) * a.total_spans + bm.span_base + S];
+    blob = a.pool + (int64_t)ref.x * 256;
+    rk = bref_rk(ref);
+    rv = bref_rv(ref);
+    if (tid == 0) {
+      const int rs = which ? rv : rk;
+      const float* gm = a.gates ? a.gates + mat * (int64_t)R : nullptr;   // this matrix's R gates
+      int c = 0;
+      for (int i = 0; i < R; ++i) {
+        const bool k = i < min(R, n) && gate_kept(gm ? gm[i] : 1.f, a.gate_eps) && c < rs;
+        s_slot[i] = k ? c++ : -1;
+      }
+    }
+    __syncthreads();
+  }
   const int nbi = (re + 3) >> 2;
   for (int c0 = 0; c0 < n; c0 += kNC) {
     if (nch > 1) u_chunk(c0);
@@ -730,8 +750,10 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
         if (BATCHED) {
           a.out_U[(mat * (int64_t)a.max_rows + row) * R + i] = u[e];
         } else {
-          bf16_t* Uo = (bf16_t*)(blob + (which ? Blob::off_uvt(R, D, n) : Blob::off_uk(R, D)));
-          Uo[which ? a16_off(i, row, npad) : a16_off(row, i, R)] = to_bf(u[e]);
+          const int sl = s_slot[i];
+          if (sl < 0) continue;
+          bf16_t* Uo = (bf16_t*)(blob + (which ? Blob::off_uvt(rk, rv, D, n) : Blob::off_uk(rk, rv, D)));
+          Uo[which ? a16_off(sl, row, npad) : a16_off(row, sl, rk)] = to_bf(u[e]);
         }
       }
     }
@@ -751,20 +773,21 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     for (int i = tid; i < R; i += 256) a.out_S[mat * R + i] = (i < re) ? s_sig[i] : 0.f;
     return;
   }
-  // right factors: K -> VKt [R][D] krow layout, V -> VV [D][R] a16 layout
-  bf16_t* Vo = (bf16_t*)(blob + (which ? Blob::off_vv(R, D) : Blob::off_vkt(R, D)));
+  // right factors: K -> VKt [rk][D] krow layout, V -> VV [D][rv] a16 layout
+  bf16_t* Vo = (bf16_t*)(blob + (which ? Blob::off_vv(rk, D) : Blob::off_vkt()));
   for (int idx = tid; idx < D * re; idx += 256) {
     const int i = idx / D, d = idx - i * D;
-    const int64_t o = which ? a16_off(d, i, R) : krow_off(i, d, D);
+    const int sl = s_slot[i];
+    if (sl < 0) continue;
+    const int64_t o = which ? a16_off(d, sl, rv) : krow_off(sl, d, D);
     Vo[o] = to_bf(ZT[i * Y::ZP + d]);
   }
-  float* sm = (float*)(blob + (which ? Blob::off_smv(R, D) : Blob::off_smk(R, D)));
+  float* sm = (float*)(blob + (which ? Blob::off_smv(rk, rv, D) : Blob::off_smk(rk, rv, D)));
   for (int i = tid; i < R; i += 256) {
-    float m = 1.f;
-    if (a.gates)
-      m = a.gates[((((int64_t)b * a.L + a.layer) * a.Hkv + g) * 2 + which) * ((int64_t)a.S_max * R) +
-                  (int64_t)S * R + i];
-    sm[i] = (i < re) ? s_sig[i] * m : 0.f;
+    const int sl = s_slot[i];
+    if (sl < 0) continue;
+    const float m = a.gates ? a.gates[mat * (int64_t)R + i] : 1.f;
+    sm[sl] = (i < re) ? s_sig[i] * m : 0.f;
   }
 }
 

@@ -174,13 +174,18 @@ struct sekv_index {
   int B = 0, L = 0, Hq = 0, Hkv = 0, D = 0, R = 0, dp = 0, G = 0, tier = 0;
   int max_spans = 0, Wd = 0, max_raw = 0;
   int64_t total_spans = 0, total_raw = 0, total_tok = 0;
-  int64_t layer_bytes = 0, pool_bytes = 0;
+  int64_t pool_bytes = 0, max_layer_bytes = 0;
   int64_t kres_elems = 0, s_elems = 0;
   std::vector<BMeta> meta;
   std::vector<int32_t> h_span_len;      // concatenated span lengths
-  std::vector<int64_t> h_span_off;      // concatenated blob offsets in the (b, l, g) region
+  std::vector<float> h_logn;            // ln n_S (host copy of what d_logn holds)
+  // factor blobs: layer l's region at layer_off[l]; within it (b, g, span)
+  // order, sequence b's blobs from region_off[l][b] (b = B: the layer's end)
+  std::vector<int64_t> layer_off;       // [L + 1]
+  std::vector<int64_t> region_off;      // [L][B + 1]
+  std::vector<uint2> h_bref;            // [L][Hkv][total_spans] blob references
   // device
-  DBuf d_meta, d_span_start, d_span_len, d_logn, d_span_off, d_raw_pos;
+  DBuf d_meta, d_span_start, d_span_len, d_logn, d_bref, d_layer_off, d_raw_pos;
   DBuf d_kres, d_vres, d_s, d_W;
   DBuf d_pool;                 // HBM tier
   uint8_t* h_pool = nullptr;   // pinned tier (host address)
@@ -230,6 +235,7 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
   if (need_build_fields) {
     if (p->l_min < 1) return fail(SEKV_EINVAL, "l_min must be >= 1");
     if (!(p->alpha_sp == p->alpha_sp) || std::isinf(p->alpha_sp)) return fail(SEKV_EINVAL, "alpha_sp must be finite");
+    if (std::isnan(p->gate_eps)) return fail(SEKV_EINVAL, "gate_eps is NaN");
     if (p->oversample < 0 || p->oversample > 16) return fail(SEKV_EINVAL, "oversample must be in [0, 16]");
     if (p->power_iters < 0 || p->power_iters > 8) return fail(SEKV_EINVAL, "power_iters must be in [0, 8]");
   }
@@ -250,8 +256,7 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   x->dp = p->dprime; x->G = p->Hq / p->Hkv; x->tier = p->tier;
   x->meta.assign(x->B, BMeta{});
   x->h_span_len = lens;
-  x->h_span_off.assign(lens.size(), 0);
-  int64_t sb = 0, rb = 0, tb = 0, res = 0, sel = 0, pb = 0;
+  int64_t sb = 0, rb = 0, tb = 0, res = 0, sel = 0;
   x->max_spans = 0; x->max_raw = 0;
   for (int b = 0; b < x->B; ++b) {
     BMeta& m = x->meta[b];
@@ -265,15 +270,7 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
     m.tok_base = tb;
     m.res_base = res;
     m.s_base = sel;
-    int64_t off = 0;
-    for (int S = 0; S < m.n_spans; ++S) {
-      x->h_span_off[sb + S] = off;
-      off += Blob::bytes(x->R, x->D, lens[sb + S]);
-      tb += lens[sb + S];
-    }
-    m.pool_lg = off;
-    m.pool_base = pb;
-    pb += off * x->Hkv;
+    for (int S = 0; S < m.n_spans; ++S) tb += lens[sb + S];
     sb += m.n_spans;
     rb += m.n_raw;
     res += (int64_t)x->L * x->Hkv * m.n_res_pad * x->D;
@@ -286,8 +283,6 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   x->total_tok = tb;
   x->kres_elems = res;
   x->s_elems = sel;
-  x->layer_bytes = pb;
-  x->pool_bytes = pb * x->L;
   x->Wd = std::max(1, (x->max_spans + 63) / 64);
   // decode work items: nj per (b, g), each with an equal slice of the
   // resident steps and an equal share of the routed union; nj covers the
@@ -328,6 +323,44 @@ sekv_status plan_layout(sekv_index* x, const sekv_build_params* p, const std::ve
   return SEKV_OK;
 }
 
+// Place the factor blobs of a planned index from their stored ranks (ranks:
+// [L][Hkv][total_spans], rk | rv << 16): per layer, sequences in order, KV
+// heads in order, spans in order, each blob on a 256-byte boundary.
+sekv_status plan_blobs(sekv_index* x, const std::vector<uint32_t>& ranks) {
+  const int64_t tot = x->total_spans;
+  x->h_bref.assign((size_t)x->L * x->Hkv * tot, make_uint2(0u, 0u));
+  x->layer_off.assign((size_t)x->L + 1, 0);
+  x->region_off.assign((size_t)x->L * (x->B + 1), 0);
+  x->max_layer_bytes = 0;
+  int64_t base = 0;
+  for (int l = 0; l < x->L; ++l) {
+    x->layer_off[l] = base;
+    int64_t off = 0;
+    for (int b = 0; b < x->B; ++b) {
+      const BMeta& m = x->meta[b];
+      x->region_off[(size_t)l * (x->B + 1) + b] = off;
+      for (int g = 0; g < x->Hkv; ++g)
+        for (int S = 0; S < m.n_spans; ++S) {
+          const size_t i = ((size_t)l * x->Hkv + g) * tot + m.span_base + S;
+          const uint32_t rr = ranks[i];
+          const int rk = (int)(rr & 0xffffu), rv = (int)(rr >> 16);
+          if (rk < 16 || rv < 16 || rk > x->R || rv > x->R || (rk & 15) || (rv & 15))
+            return fail(SEKV_EHIP, "stored rank (%d, %d) of span %d (b=%d, l=%d, g=%d) outside the R=%d tiles", rk, rv,
+                        S, b, l, g, x->R);
+          if ((off >> 8) > 0xffffffffLL) return fail(SEKV_EUNSUPPORTED, "one layer's factors exceed 1 TiB");
+          x->h_bref[i] = make_uint2((uint32_t)(off >> 8), rr);
+          off += Blob::bytes(rk, rv, x->D, x->h_span_len[m.span_base + S]);
+        }
+    }
+    x->region_off[(size_t)l * (x->B + 1) + x->B] = off;
+    x->max_layer_bytes = std::max(x->max_layer_bytes, off);
+    base += off;
+  }
+  x->layer_off[x->L] = base;
+  x->pool_bytes = base;
+  return SEKV_OK;
+}
+
 // Allocate and clear the device (and pinned) storage of a planned index.
 sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
   const size_t nsp = (size_t)std::max<int64_t>(x->total_spans, 1);
@@ -335,7 +368,8 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
   HIP_TRY(dalloc(x->d_span_start, 4 * nsp));
   HIP_TRY(dalloc(x->d_span_len, 4 * nsp));
   HIP_TRY(dalloc(x->d_logn, 4 * nsp));
-  HIP_TRY(dalloc(x->d_span_off, 8 * nsp));
+  HIP_TRY(dalloc(x->d_bref, sizeof(uint2) * std::max<size_t>(x->h_bref.size(), 1)));
+  HIP_TRY(dalloc(x->d_layer_off, sizeof(int64_t) * x->layer_off.size()));
   HIP_TRY(dalloc(x->d_raw_pos, 4 * (size_t)std::max<int64_t>(x->total_raw, 1)));
   HIP_TRY(dalloc(x->d_kres, 2 * (size_t)x->kres_elems));
   HIP_TRY(dalloc(x->d_vres, 2 * (size_t)x->kres_elems));
@@ -346,7 +380,7 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
   HIP_TRY(hipMemsetAsync(x->d_vres.p, 0, x->d_vres.n, st));
   HIP_TRY(hipMemsetAsync(x->d_s.p, 0, x->d_s.n, st));
   if (x->tier == SEKV_TIER_HBM) {
-    HIP_TRY(dalloc(x->d_pool, (size_t)x->pool_bytes));
+    HIP_TRY(dalloc(x->d_pool, (size_t)std::max<int64_t>(x->pool_bytes, 256)));
     HIP_TRY(hipMemsetAsync(x->d_pool.p, 0, x->d_pool.n, st));
   } else {
     const size_t pb = (size_t)std::max<int64_t>(x->pool_bytes, 256);
@@ -359,12 +393,20 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
     void* dp = nullptr;
     HIP_TRY(hipHostGetDevicePointer(&dp, x->h_pool, 0));
     x->d_host_pool = (const uint8_t*)dp;
-    x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : std::max<int64_t>(x->layer_bytes, 256);
+    x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : std::max<int64_t>(x->max_layer_bytes, 256);
     HIP_TRY(dalloc(x->d_ring, (size_t)x->ring_bytes));
   }
   HIP_TRY(hipMemcpyAsync(x->d_meta.p, x->meta.data(), sizeof(BMeta) * x->B, hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(x->d_span_len.p, x->h_span_len.data(), 4 * x->h_span_len.size(), hipMemcpyHostToDevice, st));
-  HIP_TRY(hipMemcpyAsync(x->d_span_off.p, x->h_span_off.data(), 8 * x->h_span_off.size(), hipMemcpyHostToDevice, st));
+  // ln n_S of the pseudo rows, computed here for built and imported indexes alike
+  x->h_logn.resize(x->h_span_len.size());
+  for (size_t i = 0; i < x->h_span_len.size(); ++i) x->h_logn[i] = logf((float)x->h_span_len[i]);
+  if (!x->h_logn.empty())
+    HIP_TRY(hipMemcpyAsync(x->d_logn.p, x->h_logn.data(), 4 * x->h_logn.size(), hipMemcpyHostToDevice, st));
+  if (!x->h_bref.empty())
+    HIP_TRY(hipMemcpyAsync(x->d_bref.p, x->h_bref.data(), sizeof(uint2) * x->h_bref.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipMemcpyAsync(x->d_layer_off.p, x->layer_off.data(), sizeof(int64_t) * x->layer_off.size(),
+                         hipMemcpyHostToDevice, st));
   HIP_TRY(dalloc(x->d_items, sizeof(WorkItem) * std::max<size_t>(x->items.size(), 1)));
   HIP_TRY(dalloc(x->d_bg_first, 4 * x->bg_first.size()));
   HIP_TRY(hipMemcpyAsync(x->d_items.p, x->items.data(), sizeof(WorkItem) * x->items.size(), hipMemcpyHostToDevice, st));
@@ -377,7 +419,7 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
 void free_index(sekv_index* x) {
   if (!x) return;
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
-  DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_span_off,
+  DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_bref, &x->d_layer_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
                   &x->d_ring, &x->d_gstat, &x->d_items, &x->d_bg_first, &x->d_part,
                   &x->d_score, &x->d_alpha, &x->d_tau_inf};
@@ -562,11 +604,10 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   const int S_max = sekv_max_spans(T, p->l_min);
 
   // ---- span split into scratch
-  DBuf sst, sln, slg, raw, cnt, scr;
-  struct Rel { DBuf* b[6]; ~Rel() { for (DBuf* x : b) x->release(); } } rel{{&sst, &sln, &slg, &raw, &cnt, &scr}};
+  DBuf sst, sln, raw, cnt, scr;
+  struct Rel { DBuf* b[5]; ~Rel() { for (DBuf* x : b) x->release(); } } rel{{&sst, &sln, &raw, &cnt, &scr}};
   HIP_TRY(dalloc(sst, 4 * (size_t)B * std::max(S_max, 1)));
   HIP_TRY(dalloc(sln, 4 * (size_t)B * std::max(S_max, 1)));
-  HIP_TRY(dalloc(slg, 4 * (size_t)B * std::max(S_max, 1)));
   HIP_TRY(dalloc(raw, 4 * (size_t)B * T));
   HIP_TRY(dalloc(cnt, 8 * (size_t)B));
   HIP_TRY(dalloc(scr, 4 * (size_t)B * 2 * (T / 2 + 2)));
@@ -574,7 +615,6 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   sa.H = H;
   sa.span_start = (int32_t*)sst.p;
   sa.span_len = (int32_t*)sln.p;
-  sa.span_logn = (float*)slg.p;
   sa.raw_pos = (int32_t*)raw.p;
   sa.counts = (int32_t*)cnt.p;
   sa.scratch = (int32_t*)scr.p;
@@ -607,14 +647,38 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   x->ctx = c;
   IndexGuard guard{x};
   if ((st = plan_layout(x, p, n_spans, n_raw, lens))) return st;
+  // stored ranks of every span factorization (gates below gate_eps drop their
+  // components), which place the blobs and size the pool
+  {
+    DBuf rk;
+    struct RelR { DBuf* b; ~RelR() { b->release(); } } relr{&rk};
+    const size_t nr = (size_t)B * p->L * p->Hkv * std::max(S_max, 1);
+    HIP_TRY(dalloc(rk, 4 * nr));
+    RankArgs ra{};
+    ra.gates = gates;
+    ra.span_len = (const int32_t*)sln.p;
+    ra.counts = (const int32_t*)cnt.p;
+    ra.ranks = (uint32_t*)rk.p;
+    ra.B = B; ra.L = p->L; ra.Hkv = p->Hkv; ra.R = p->R; ra.S_max = S_max; ra.gate_eps = p->gate_eps;
+    HIP_TRY(launch_ranks(ra, stream));
+    std::vector<uint32_t> hr(nr);
+    HIP_TRY(hipMemcpyAsync(hr.data(), rk.p, 4 * nr, hipMemcpyDeviceToHost, stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+    std::vector<uint32_t> ranks((size_t)p->L * p->Hkv * x->total_spans);
+    for (int b = 0; b < B; ++b)
+      for (int l = 0; l < p->L; ++l)
+        for (int g = 0; g < p->Hkv; ++g)
+          for (int S = 0; S < n_spans[b]; ++S)
+            ranks[((size_t)l * p->Hkv + g) * x->total_spans + x->meta[b].span_base + S] =
+                hr[(((size_t)b * p->L + l) * p->Hkv + g) * S_max + S];
+    if ((st = plan_blobs(x, ranks))) return st;
+  }
   if ((st = alloc_index(x, p->ring_bytes))) return st;
   // compact span tables and raw positions
   for (int b = 0; b < B; ++b) {
     const BMeta& m = x->meta[b];
     if (m.n_spans) {
       HIP_TRY(hipMemcpyAsync((int32_t*)x->d_span_start.p + m.span_base, (int32_t*)sst.p + (size_t)b * S_max,
-                             4 * (size_t)m.n_spans, hipMemcpyDeviceToDevice, stream));
-      HIP_TRY(hipMemcpyAsync((float*)x->d_logn.p + m.span_base, (float*)slg.p + (size_t)b * S_max,
                              4 * (size_t)m.n_spans, hipMemcpyDeviceToDevice, stream));
     }
     if (m.n_raw)
@@ -633,7 +697,9 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   pa.span_start = (const int32_t*)x->d_span_start.p;
   pa.span_len = (const int32_t*)x->d_span_len.p;
   pa.raw_pos = (const int32_t*)x->d_raw_pos.p;
-  pa.span_off = (const int64_t*)x->d_span_off.p;
+  pa.bref = (const uint2*)x->d_bref.p;
+  pa.total_spans = x->total_spans;
+  pa.gate_eps = p->gate_eps;
   pa.kres = (bf16_t*)x->d_kres.p;
   pa.vres = (bf16_t*)x->d_vres.p;
   pa.s = (float*)x->d_s.p;
@@ -645,15 +711,15 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   if (x->tier == SEKV_TIER_HBM) {
     for (int l = 0; l < p->L; ++l) {
       pa.layer = l;
-      pa.pool = (uint8_t*)x->d_pool.p + (size_t)l * x->layer_bytes;
+      pa.pool = (uint8_t*)x->d_pool.p + x->layer_off[l];
       HIP_TRY(launch_rsvd(pa, stream));
     }
     HIP_TRY(hipStreamSynchronize(stream));
   } else {
     // pinned tier: layer l's factors go to HBM stage l % 2 and are copied to
     // the pinned pool on a second stream while layer l + 1 is factored into
-    // the other stage (blob padding is the same in every layer, so the stages
-    // are cleared once)
+    // the other stage (cleared first: the blob layout differs between layers
+    // where the stored ranks do)
     struct Overlap {
       DBuf stage[2];
       hipStream_t copy = nullptr;
@@ -670,8 +736,7 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
     } ov;
     const int nst = p->L > 1 ? 2 : 1;
     for (int k = 0; k < nst; ++k) {
-      HIP_TRY(dalloc(ov.stage[k], (size_t)x->layer_bytes));
-      HIP_TRY(hipMemsetAsync(ov.stage[k].p, 0, ov.stage[k].n, stream));
+      HIP_TRY(dalloc(ov.stage[k], (size_t)std::max<int64_t>(x->max_layer_bytes, 256)));
       HIP_TRY(hipEventCreateWithFlags(&ov.done[k], hipEventDisableTiming));
       HIP_TRY(hipEventCreateWithFlags(&ov.copied[k], hipEventDisableTiming));
     }
@@ -680,12 +745,14 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
       const int k = l % nst;
       pa.layer = l;
       pa.pool = (uint8_t*)ov.stage[k].p;
+      const size_t lbytes = (size_t)(x->layer_off[l + 1] - x->layer_off[l]);
       if (l >= nst) HIP_TRY(hipStreamWaitEvent(stream, ov.copied[k], 0));   // stage k drained
+      if (lbytes) HIP_TRY(hipMemsetAsync(ov.stage[k].p, 0, lbytes, stream));
       HIP_TRY(launch_rsvd(pa, stream));
       HIP_TRY(hipEventRecord(ov.done[k], stream));
       HIP_TRY(hipStreamWaitEvent(ov.copy, ov.done[k], 0));
-      HIP_TRY(hipMemcpyAsync(x->h_pool + (size_t)l * x->layer_bytes, ov.stage[k].p, (size_t)x->layer_bytes,
-                             hipMemcpyDeviceToHost, ov.copy));
+      if (lbytes)
+        HIP_TRY(hipMemcpyAsync(x->h_pool + x->layer_off[l], ov.stage[k].p, lbytes, hipMemcpyDeviceToHost, ov.copy));
       HIP_TRY(hipEventRecord(ov.copied[k], ov.copy));
     }
     HIP_TRY(hipStreamSynchronize(ov.copy));
@@ -751,11 +818,35 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
   x->ctx = c;
   IndexGuard guard{x};
   if ((st = plan_layout(x, p, n_spans, n_raw, lens))) return st;
+  // stored ranks: components up to the last one with nonzero sigma * m (the
+  // rest contribute nothing), in 16-wide tiles
+  {
+    std::vector<uint32_t> ranks((size_t)L * Hkv * x->total_spans, 0u);
+    int64_t spo = 0;
+    auto kept = [&](const float* sm) {
+      int c = 0;
+      for (int i = 0; i < R; ++i)
+        if (sm[i] != 0.f) c = i + 1;
+      return stored_rank(c);
+    };
+    for (int b = 0; b < B; ++b) {
+      const BMeta& m = x->meta[b];
+      for (int l = 0; l < L; ++l)
+        for (int g = 0; g < Hkv; ++g)
+          for (int S = 0; S < m.n_spans; ++S) {
+            const int64_t rsp = spo + ((int64_t)l * Hkv + g) * m.n_spans + S;
+            ranks[((size_t)l * Hkv + g) * x->total_spans + m.span_base + S] =
+                (uint32_t)kept(h->smk + rsp * R) | ((uint32_t)kept(h->smv + rsp * R) << 16);
+          }
+      spo += (int64_t)L * Hkv * m.n_spans;
+    }
+    if ((st = plan_blobs(x, ranks))) return st;
+  }
   if ((st = alloc_index(x, p->ring_bytes))) return st;
   hipStream_t stream = c->stream;
   // pack into the native layouts on the host
   std::vector<bf16_t> kres((size_t)x->kres_elems, 0), vres((size_t)x->kres_elems, 0);
-  std::vector<float> s((size_t)x->s_elems, 0.f), logn((size_t)std::max<int64_t>(tot_sp, 1));
+  std::vector<float> s((size_t)x->s_elems, 0.f);
   std::vector<uint8_t> pool;
   uint8_t* pool_dst;
   if (x->tier == SEKV_TIER_HBM) {
@@ -786,37 +877,35 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
           s[m.s_base + (int64_t)lh * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))] =
               h->s[so + ((int64_t)lh * dp + j) * NS + S];
     so += (int64_t)L * Hq * dp * NS;
-    for (int S = 0; S < NS; ++S) logn[m.span_base + S] = logf((float)lens[m.span_base + S]);
     for (int l = 0; l < L; ++l)
       for (int g = 0; g < Hkv; ++g) {
         const int lg = l * Hkv + g;
         int64_t toff = 0;
         for (int S = 0; S < NS; ++S) {
           const int n = lens[m.span_base + S], np = Blob::npad(n);
-          uint8_t* blob = pool_dst + (int64_t)l * x->layer_bytes + m.pool_base + (int64_t)g * m.pool_lg +
-                          x->h_span_off[m.span_base + S];
-          bf16_t* vkt = (bf16_t*)(blob + Blob::off_vkt(R, D));
-          bf16_t* vv = (bf16_t*)(blob + Blob::off_vv(R, D));
-          float* smk = (float*)(blob + Blob::off_smk(R, D));
-          float* smv = (float*)(blob + Blob::off_smv(R, D));
-          bf16_t* uk = (bf16_t*)(blob + Blob::off_uk(R, D));
-          bf16_t* uvt = (bf16_t*)(blob + Blob::off_uvt(R, D, n));
+          const uint2 rf = x->h_bref[(size_t)lg * x->total_spans + m.span_base + S];
+          const int rk = bref_rk(rf), rv = bref_rv(rf);
+          uint8_t* blob = pool_dst + x->layer_off[l] + (int64_t)rf.x * 256;
+          bf16_t* vkt = (bf16_t*)(blob + Blob::off_vkt());
+          bf16_t* vv = (bf16_t*)(blob + Blob::off_vv(rk, D));
+          float* smk = (float*)(blob + Blob::off_smk(rk, rv, D));
+          float* smv = (float*)(blob + Blob::off_smv(rk, rv, D));
+          bf16_t* uk = (bf16_t*)(blob + Blob::off_uk(rk, rv, D));
+          bf16_t* uvt = (bf16_t*)(blob + Blob::off_uvt(rk, rv, D, n));
           const int64_t rsp = spo + (int64_t)lg * NS + S;   // [L][Hkv][NS] index
-          for (int i = 0; i < R; ++i)
-            for (int d = 0; d < D; ++d) {
-              vkt[krow_off(i, d, D)] = h->vkt[(rsp * R + i) * D + d];
-              vv[a16_off(d, i, R)] = h->vvt[(rsp * R + i) * D + d];
-            }
-          for (int i = 0; i < R; ++i) {
+          for (int i = 0; i < rk; ++i) {
+            for (int d = 0; d < D; ++d) vkt[krow_off(i, d, D)] = h->vkt[(rsp * R + i) * D + d];
             smk[i] = h->smk[rsp * R + i];
+          }
+          for (int i = 0; i < rv; ++i) {
+            for (int d = 0; d < D; ++d) vv[a16_off(d, i, rv)] = h->vvt[(rsp * R + i) * D + d];
             smv[i] = h->smv[rsp * R + i];
           }
           const int64_t ub = tko + (int64_t)lg * ntok + toff;  // [L][Hkv][sum n][R] row
-          for (int t = 0; t < n; ++t)
-            for (int i = 0; i < R; ++i) {
-              uk[a16_off(t, i, R)] = h->uk[(ub + t) * R + i];
-              uvt[a16_off(i, t, np)] = h->uv[(ub + t) * R + i];
-            }
+          for (int t = 0; t < n; ++t) {
+            for (int i = 0; i < rk; ++i) uk[a16_off(t, i, rk)] = h->uk[(ub + t) * R + i];
+            for (int i = 0; i < rv; ++i) uvt[a16_off(i, t, np)] = h->uv[(ub + t) * R + i];
+          }
           toff += n;
         }
       }
@@ -828,7 +917,6 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
   HIP_TRY(hipMemcpyAsync(x->d_s.p, s.data(), 4 * s.size(), hipMemcpyHostToDevice, stream));
   if (tot_sp) {
     HIP_TRY(hipMemcpyAsync(x->d_span_start.p, h->span_start, 4 * (size_t)tot_sp, hipMemcpyHostToDevice, stream));
-    HIP_TRY(hipMemcpyAsync(x->d_logn.p, logn.data(), 4 * (size_t)tot_sp, hipMemcpyHostToDevice, stream));
   }
   if (tot_raw) HIP_TRY(hipMemcpyAsync(x->d_raw_pos.p, h->raw_pos, 4 * (size_t)tot_raw, hipMemcpyHostToDevice, stream));
   HIP_TRY(hipMemcpyAsync(x->d_W.p, h->W, x->d_W.n, hipMemcpyHostToDevice, stream));
@@ -865,21 +953,26 @@ sekv_status export_part(sekv_ctx* c, const sekv_index* x, int bb, int bc, int lb
   const int64_t s0 = m0.s_base, s1 = m1.s_base + (int64_t)x->L * Hq * dp_pad4(dp) * m1.s_pad;
   const int64_t sp0 = m0.span_base, sp1 = m1.span_base + m1.n_spans;
   const int64_t rw0 = m0.raw_base, rw1 = m1.raw_base + m1.n_raw;
-  const int64_t pb0 = m0.pool_base, pb1 = m1.pool_base + (int64_t)Hkv * m1.pool_lg;
   std::vector<bf16_t> kres(want_res ? (size_t)(res1 - res0) : 0), vres(want_res ? (size_t)(res1 - res0) : 0);
   std::vector<float> s(h->s ? (size_t)(s1 - s0) : 0);
   std::vector<int32_t> sst((size_t)std::max<int64_t>(sp1 - sp0, 1)), rp((size_t)std::max<int64_t>(rw1 - rw0, 1));
+  // the sequences' factor blobs, layer by layer: layer lb + l's region from
+  // region_off[lb + l][bb] copied to pool[ppos[l]]
   std::vector<uint8_t> pool;
-  const int64_t preg = pb1 - pb0;   // bytes of the sequences' region in one layer
+  std::vector<int64_t> ppos((size_t)lc + 1, 0);
+  auto reg = [&](int l, int b) { return x->region_off[(size_t)l * (x->B + 1) + b]; };
+  for (int l = 0; l < lc; ++l) ppos[l + 1] = ppos[l] + (reg(lb + l, bb + bc) - reg(lb + l, bb));
   if (want_fac) {
-    pool.resize((size_t)std::max<int64_t>(lc * preg, 1));
-    for (int l = 0; l < lc && preg > 0; ++l) {
-      const size_t src = (size_t)(lb + l) * x->layer_bytes + pb0;
+    pool.resize((size_t)std::max<int64_t>(ppos[lc], 1));
+    for (int l = 0; l < lc; ++l) {
+      const int64_t n = ppos[l + 1] - ppos[l];
+      if (n <= 0) continue;
+      const size_t src = (size_t)(x->layer_off[lb + l] + reg(lb + l, bb));
       if (x->tier == SEKV_TIER_HBM)
-        HIP_TRY(hipMemcpyAsync(pool.data() + (size_t)l * preg, (const uint8_t*)x->d_pool.p + src, (size_t)preg,
+        HIP_TRY(hipMemcpyAsync(pool.data() + ppos[l], (const uint8_t*)x->d_pool.p + src, (size_t)n,
                                hipMemcpyDeviceToHost, stream));
       else
-        memcpy(pool.data() + (size_t)l * preg, x->h_pool + src, (size_t)preg);
+        memcpy(pool.data() + ppos[l], x->h_pool + src, (size_t)n);
     }
   }
   if (want_res) {
@@ -923,35 +1016,42 @@ sekv_status export_part(sekv_ctx* c, const sekv_index* x, int bb, int bc, int lb
             h->s[so + ((int64_t)lh * dp + j) * NS + S] =
                 s[m.s_base - s0 + ((int64_t)lb * Hq + lh) * dp_pad4(dp) * m.s_pad + skey_index(S, j, dp_pad4(dp))];
     so += (int64_t)L * Hq * dp * NS;
-    for (int l = 0; want_fac && l < L; ++l)
+    for (int l = 0; (want_fac || h->rank) && l < L; ++l)
       for (int g = 0; g < Hkv; ++g) {
         const int lg = l * Hkv + g;
         int64_t toff = 0;
         for (int S = 0; S < NS; ++S) {
           const int n = x->h_span_len[m.span_base + S], np = Blob::npad(n);
-          const uint8_t* blob = pool.data() + (int64_t)l * preg + (m.pool_base - pb0) + (int64_t)g * m.pool_lg +
-                                x->h_span_off[m.span_base + S];
-          const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt(R, D));
-          const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(R, D));
-          const float* smk = (const float*)(blob + Blob::off_smk(R, D));
-          const float* smv = (const float*)(blob + Blob::off_smv(R, D));
-          const bf16_t* uk = (const bf16_t*)(blob + Blob::off_uk(R, D));
-          const bf16_t* uvt = (const bf16_t*)(blob + Blob::off_uvt(R, D, n));
+          const uint2 rf = x->h_bref[((size_t)(lb + l) * Hkv + g) * x->total_spans + m.span_base + S];
+          const int rk = bref_rk(rf), rv = bref_rv(rf);
           const int64_t rsp = spo + (int64_t)lg * NS + S;
+          if (h->rank) {
+            h->rank[2 * rsp] = rk;
+            h->rank[2 * rsp + 1] = rv;
+          }
+          if (!want_fac) continue;
+          // components past the stored ones are zero
+          const uint8_t* blob = pool.data() + ppos[l] + ((int64_t)rf.x * 256 - reg(lb + l, bb));
+          const bf16_t* vkt = (const bf16_t*)(blob + Blob::off_vkt());
+          const bf16_t* vv = (const bf16_t*)(blob + Blob::off_vv(rk, D));
+          const float* smk = (const float*)(blob + Blob::off_smk(rk, rv, D));
+          const float* smv = (const float*)(blob + Blob::off_smv(rk, rv, D));
+          const bf16_t* uk = (const bf16_t*)(blob + Blob::off_uk(rk, rv, D));
+          const bf16_t* uvt = (const bf16_t*)(blob + Blob::off_uvt(rk, rv, D, n));
           for (int i = 0; i < R; ++i)
             for (int d = 0; d < D; ++d) {
-              if (h->vkt) h->vkt[(rsp * R + i) * D + d] = vkt[krow_off(i, d, D)];
-              if (h->vvt) h->vvt[(rsp * R + i) * D + d] = vv[a16_off(d, i, R)];
+              if (h->vkt) h->vkt[(rsp * R + i) * D + d] = i < rk ? vkt[krow_off(i, d, D)] : 0;
+              if (h->vvt) h->vvt[(rsp * R + i) * D + d] = i < rv ? vv[a16_off(d, i, rv)] : 0;
             }
           for (int i = 0; i < R; ++i) {
-            if (h->smk) h->smk[rsp * R + i] = smk[i];
-            if (h->smv) h->smv[rsp * R + i] = smv[i];
+            if (h->smk) h->smk[rsp * R + i] = i < rk ? smk[i] : 0.f;
+            if (h->smv) h->smv[rsp * R + i] = i < rv ? smv[i] : 0.f;
           }
           const int64_t ub = tko + (int64_t)lg * ntok + toff;
           for (int t = 0; t < n; ++t)
             for (int i = 0; i < R; ++i) {
-              if (h->uk) h->uk[(ub + t) * R + i] = uk[a16_off(t, i, R)];
-              if (h->uv) h->uv[(ub + t) * R + i] = uvt[a16_off(i, t, np)];
+              if (h->uk) h->uk[(ub + t) * R + i] = i < rk ? uk[a16_off(t, i, rk)] : 0;
+              if (h->uv) h->uv[(ub + t) * R + i] = i < rv ? uvt[a16_off(i, t, np)] : 0;
             }
           toff += n;
         }
@@ -1092,12 +1192,13 @@ size_t part_bytes(const sekv_index* x, int lc) {
   return sizeof(float) * (size_t)lc * std::max<size_t>(x->items.size(), 1) * x->G * (x->D + 2);
 }
 
-// The ring of the pinned tier mirrors the pool: a call over lc layers needs
-// lc whole layers of it.
-sekv_status check_ring(const sekv_index* x, int lc) {
-  if (x->tier == SEKV_TIER_PINNED_HOST && (int64_t)lc * x->layer_bytes > x->ring_bytes)
-    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes holds fewer than the %d layers of this call "
-                "(%lld bytes each)", (long long)x->ring_bytes, lc, (long long)x->layer_bytes);
+// The ring of the pinned tier mirrors the pool: a call over layers
+// [lb, lb + lc) needs those layers' whole factor regions.
+sekv_status check_ring(const sekv_index* x, int lb, int lc) {
+  const int64_t need = x->layer_off[lb + lc] - x->layer_off[lb];
+  if (x->tier == SEKV_TIER_PINNED_HOST && need > x->ring_bytes)
+    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes holds less than the %lld bytes of factors of layers "
+                "[%d, %d)", (long long)x->ring_bytes, (long long)need, lb, lb + lc);
   return SEKV_OK;
 }
 
@@ -1115,13 +1216,14 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
     ga.mask = mask;
     ga.meta = (const BMeta*)x->d_meta.p;
     ga.span_len = (const int32_t*)x->d_span_len.p;
-    ga.span_off = (const int64_t*)x->d_span_off.p;
+    ga.bref = (const uint2*)x->d_bref.p;
+    ga.layer_off = (const int64_t*)x->d_layer_off.p;
     ga.host_pool = x->d_host_pool;
     ga.ring = (uint8_t*)x->d_ring.p;
     ga.stat = gstat;
-    ga.layer_bytes = x->layer_bytes;
+    ga.total_spans = x->total_spans;
     ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
-    ga.W = x->Wd; ga.G = x->G; ga.R = x->R; ga.D = x->D;
+    ga.W = x->Wd; ga.G = x->G; ga.D = x->D;
     ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
     if (stats) HIP_TRY(hipEventRecord(x->ev0, st));
     HIP_TRY(launch_gather(ga, st));
@@ -1136,11 +1238,12 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
   aa.vres = (const bf16_t*)x->d_vres.p;
   aa.logn = (const float*)x->d_logn.p;
   aa.span_len = (const int32_t*)x->d_span_len.p;
-  aa.span_off = (const int64_t*)x->d_span_off.p;
+  aa.bref = (const uint2*)x->d_bref.p;
+  aa.layer_off = (const int64_t*)x->d_layer_off.p;
   aa.pool = pinned ? (const uint8_t*)x->d_ring.p : (const uint8_t*)x->d_pool.p;
   aa.pool_layer0 = pinned ? lb : 0;
   aa.part = part;
-  aa.layer_bytes = x->layer_bytes;
+  aa.total_spans = x->total_spans;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
   aa.max_spans = std::max(x->max_spans, 1);
@@ -1190,7 +1293,7 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
-  if ((st = check_ring(x, lc))) return st;
+  if ((st = check_ring(x, lb, lc))) return st;
   if ((st = set_device(c))) return st;
   HIP_TRY(dgrow(x->d_part, part_bytes(x, lc)));
   int2* gstat = nullptr;

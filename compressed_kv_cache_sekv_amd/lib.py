@@ -46,7 +46,7 @@ class BuildParams(C.Structure):
                 ("d", C.c_int32), ("T", C.c_int32), ("R", C.c_int32), ("dprime", C.c_int32),
                 ("alpha_sp", C.c_float), ("l_min", C.c_int32), ("oversample", C.c_int32),
                 ("power_iters", C.c_int32), ("seed", C.c_uint64), ("tier", C.c_int32),
-                ("ring_bytes", C.c_int64)]
+                ("ring_bytes", C.c_int64), ("gate_eps", C.c_float)]
 
 
 class IndexInfo(C.Structure):
@@ -68,7 +68,7 @@ class HostIndex(C.Structure):
 
 
 class HostIndexOut(C.Structure):
-    _fields_ = [(f, C.c_void_p) for f in _HOST_FIELDS]
+    _fields_ = [(f, C.c_void_p) for f in _HOST_FIELDS] + [("rank", C.c_void_p)]
 
 
 class Stats(C.Structure):
@@ -139,12 +139,13 @@ def validate_params(p: BuildParams) -> int:
     return lib().sekv_validate_params(C.byref(p))
 
 
-def build_params(w, tier: Optional[int] = None, ring_bytes: int = 0) -> BuildParams:
+def build_params(w, tier: Optional[int] = None, ring_bytes: int = 0, gate_eps: float = 0.0) -> BuildParams:
     """BuildParams from a synth.Workload-like object."""
     t = {"hbm": TIER_HBM, "pinned": TIER_PINNED_HOST}[w.tier] if tier is None else tier
     return BuildParams(B=w.B, L=w.L, Hq=w.Hq, Hkv=w.Hkv, d=w.d, T=w.T, R=w.R, dprime=w.dprime,
                        alpha_sp=w.alpha_sp, l_min=w.l_min, oversample=w.oversample,
-                       power_iters=w.power_iters, seed=w.seed, tier=t, ring_bytes=ring_bytes)
+                       power_iters=w.power_iters, seed=w.seed, tier=t, ring_bytes=ring_bytes,
+                       gate_eps=gate_eps)
 
 
 class Context:
@@ -197,7 +198,8 @@ class Context:
 
     def import_index(self, p: BuildParams, arrays: dict) -> "Index":
         """arrays: numpy arrays in the logical layout of sekv_host_index."""
-        keep = {k: np.ascontiguousarray(v) for k, v in arrays.items()}
+        keep = {k: np.ascontiguousarray(v) for k, v in arrays.items()
+                if k in _HOST_FIELDS or k in ("n_spans", "n_raw", "W")}
         hi = HostIndex(**{k: (v.ctypes.data if v.size else None) for k, v in keep.items()})
         h = C.c_void_p()
         check(lib().sekv_index_import(self.h, C.byref(p), C.byref(hi), C.byref(h)))
@@ -283,7 +285,8 @@ class Index:
                       s=(lc * Hq * dp * NS, np.float32),
                       uk=(lc * Hkv * NT * R, u16), uv=(lc * Hkv * NT * R, u16),
                       vkt=(lc * Hkv * NS * R * d, u16), vvt=(lc * Hkv * NS * R * d, u16),
-                      smk=(lc * Hkv * NS * R, np.float32), smv=(lc * Hkv * NS * R, np.float32))
+                      smk=(lc * Hkv * NS * R, np.float32), smv=(lc * Hkv * NS * R, np.float32),
+                      rank=(lc * Hkv * NS * 2, np.int32))
         out = {k: np.zeros(n, t) for k, (n, t) in shapes.items() if fields is None or k in fields}
         ho = HostIndexOut(**{k: (v.ctypes.data if v.size else None) for k, v in out.items()})
         check(lib().sekv_index_export_part(self.ctx.h, self.h, int(seq_begin), int(bc), int(layer_begin), int(lc),

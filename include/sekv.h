@@ -74,9 +74,19 @@ typedef struct {
   int32_t power_iters;  /* randomized-SVD power iterations q                     */
   uint64_t seed;        /* Gaussian test matrices: Philox4x32-10 keyed by seed   */
   int32_t tier;         /* sekv_tier                                             */
-  int64_t ring_bytes;   /* pinned tier: HBM staging ring size, 0 = one layer's
-                           whole factor set; a decode call over n layers needs
-                           n layers' worth (the ring mirrors the pool layout)     */
+  int64_t ring_bytes;   /* pinned tier: HBM staging ring size, 0 = the largest
+                           layer's whole factor set; a decode call over layers
+                           [lb, lb + n) needs their factor bytes (the ring
+                           mirrors the pool layout)                              */
+  float gate_eps;       /* variable effective rank ([Contrib], dual resolution;
+                           [Tech], low-rank paragraph: the gates set each span's
+                           effective rank and components are dropped at storage
+                           and transfer): when > 0, component i of a span's K
+                           (V) factorization is stored only if its gate
+                           m_i >= gate_eps.  <= 0 keeps every component.  Each
+                           blob keeps min(R, n_S) components at most, padded
+                           with zero components to a multiple of 16 (>= 16).
+                           NaN is rejected (EINVAL).                             */
 } sekv_build_params;
 
 /* Index summary. */
@@ -106,7 +116,10 @@ typedef struct {
  *   smk, smv               fp32  [L][Hkv][N_S(b)][R]     sigma_i * m_i
  * plus W, fp32 [L][Hq][d'][d], the routing projection (not per b).
  * Import reads these (host, const); export writes them into caller buffers
- * sized from sekv_index_info / sekv_index_counts. */
+ * sized from sekv_index_info / sekv_index_counts.  The stored rank of each
+ * imported K (V) factorization is the number of components up to its last
+ * nonzero sigma_i * m_i, rounded up to 16: trailing zero components are
+ * not stored (they contribute nothing). */
 typedef struct {
   const int32_t* n_spans;     /* [B] */
   const int32_t* n_raw;       /* [B] */
@@ -138,6 +151,9 @@ typedef struct {
   uint16_t* vvt;
   float* smk;
   float* smv;
+  int32_t* rank;        /* [L][Hkv][N_S(b)][2]: stored components (K, V) of each
+                           blob, multiples of 16; components past them export
+                           as zeros.  Nullable, like every member.               */
 } sekv_host_index_out;
 
 /* Per-call decode statistics.  The gather fields are filled for the pinned

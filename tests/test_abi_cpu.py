@@ -107,3 +107,33 @@ def test_mask_packing_roundtrip():
     m = pack_mask(z, 1, 1, 2, 3)
     assert m[0, 0, 1, 0] == 1 and m[0, 0, 1, 1] == 1 and m[0, 0, 1, 2] == 0
     assert np.array_equal(unpack_mask(m[0, 0, 0], 130), z[(0, 0, 0)])
+
+
+def test_struct_layouts_match_the_header(L, tmp_path):
+    """The binding's ctypes structures against the C compiler's own layout of
+    the header's structs (size and every member offset)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"sekv_build_params": L.BuildParams, "sekv_index_info": L.IndexInfo,
+               "sekv_host_index": L.HostIndex, "sekv_host_index_out": L.HostIndexOut, "sekv_stats": L.Stats}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sekv.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, f, v = line.split()
+        got[(cname, f)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

@@ -27,17 +27,25 @@ def test_union_bytes_against_brute_force():
     z = rng.random((B, Hq, Wd * 64)) < 0.2
     for b in range(B):
         z[b, :, n_spans[b]:] = False
-    got, unions = bench.union_alg_bytes(_pack(z), n_spans, span_len, G, R, d)
-    want, cnt, off = 0, 0, 0
-    for b in range(B):
-        for g in range(Hq // G):
-            for S in range(int(n_spans[b])):
-                if any(z[b, h, S] for h in range(g * G, (g + 1) * G)):
-                    n = int(span_len[off + S])
-                    want += 4 * R * (n + d) + 8 * R      # U^K, U^V (n x R), V^K, V^V (d x R) bf16; sigma m fp32
-                    cnt += 1
-        off += int(n_spans[b])
-    assert (got, unions) == (want, cnt)
+    # stored ranks (K, V) per (b, g, span): R everywhere, then ragged
+    for ragged in (False, True):
+        ranks = [np.full((Hq // G, int(n), 2), R, np.int64) if not ragged else
+                 16 * rng.integers(1, 5, (Hq // G, int(n), 2)) for n in n_spans]
+        got, unions = bench.union_alg_bytes(_pack(z), n_spans, span_len, G, ranks, d)
+        want, cnt, off = 0, 0, 0
+        for b in range(B):
+            for g in range(Hq // G):
+                for S in range(int(n_spans[b])):
+                    if any(z[b, h, S] for h in range(g * G, (g + 1) * G)):
+                        n = int(span_len[off + S])
+                        rk, rv = (int(x) for x in ranks[b][g, S])
+                        # U (n x r) and V (d x r) in bf16, sigma m (r) in fp32, for K and for V
+                        want += 2 * rk * (n + d) + 4 * rk + 2 * rv * (n + d) + 4 * rv
+                        if not ragged:
+                            assert 2 * rk * (n + d) + 4 * rk + 2 * rv * (n + d) + 4 * rv == 4 * R * (n + d) + 8 * R
+                        cnt += 1
+            off += int(n_spans[b])
+        assert (got, unions) == (want, cnt)
 
 
 def test_traffic_lookup_is_keyed_to_the_kernel_source(tmp_path, monkeypatch):

@@ -105,7 +105,13 @@ def test_import_export_roundtrip(ctx, sl):
     idx = ctx.import_index(sl.build_params(c.w), arrays)
     ex = idx.export()
     for k, v in ex.items():
-        assert np.array_equal(v, arrays[k].ravel()), k
+        if k != "rank":
+            assert np.array_equal(v, arrays[k].ravel()), k
+    # stored ranks: up to the last nonzero sigma * m, in 16-wide tiles
+    for key, col in (("smk", 0), ("smv", 1)):
+        sm = arrays[key].reshape(-1, c.w.R)
+        last = np.where(sm != 0, np.arange(1, c.w.R + 1), 0).max(1)
+        assert np.array_equal(ex["rank"].reshape(-1, 2)[:, col], np.maximum(16, (last + 15) // 16 * 16))
     # one layer at a time: the slices of the whole export
     w, i = c.w, c.idxs[0]
     per_l = {"k_res": w.Hkv * (i.n_raw + i.n_spans) * w.d, "v_res": w.Hkv * (i.n_raw + i.n_spans) * w.d,
