@@ -472,7 +472,7 @@ void attend_kernel(const AttendArgs a) {
   extern __shared__ uint64_t s_dyn[];
 
   const WorkItem it = a.items[blockIdx.x];
-  const int lc = blockIdx.y, l = a.layer_begin + lc;
+  const int lc = a.lc_first + blockIdx.y, l = a.layer_begin + lc;
   const int b = it.b, g = it.g;
   const BMeta bm = a.meta[b];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -831,7 +831,8 @@ hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
 
 hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t st, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {
-  if (a.W > 1024) return hipErrorInvalidValue;
+  if (a.W > 1024 || a.lc_first < 0 || a.lc_count < 1 || a.lc_first + a.lc_count > a.layer_count)
+    return hipErrorInvalidValue;
   return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
     auto kern = attend_kernel<D_, G_, R_>;
@@ -844,10 +845,10 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
       if (e != hipSuccess) return e;
     }
     if (ev_start)
-      hipExtLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), (uint32_t)dyn, st, ev_start, ev_stop, 0u,
+      hipExtLaunchKernelGGL(kern, dim3(a.n_items, a.lc_count), dim3(256), (uint32_t)dyn, st, ev_start, ev_stop, 0u,
                             a);
     else
-      hipLaunchKernelGGL(kern, dim3(a.n_items, a.layer_count), dim3(256), dyn, st, a);
+      hipLaunchKernelGGL(kern, dim3(a.n_items, a.lc_count), dim3(256), dyn, st, a);
     return hipGetLastError();
   });
 }

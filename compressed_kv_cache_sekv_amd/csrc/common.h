@@ -145,8 +145,9 @@ struct AttendArgs {
                             // tier: the call's layers, blobs at their pool offsets)
   float* part;              // [Lc][n_items][G][D + 2] softmax partials
   int64_t total_spans;
-  int32_t pool_layer0;      // layer at the start of `pool` (0; the ring: layer_begin)
+  int32_t pool_layer0;      // layer whose region starts `pool` (0; a ring slot: its layer)
   int32_t layer_begin, layer_count, n_items;
+  int32_t lc_first, lc_count;   // this launch: layers [lc_first, lc_first + lc_count) of the call
   int32_t B, L, Hq, Hkv, W, max_spans;
   float scale;              // 1/sqrt(d)
 };
@@ -191,10 +192,12 @@ struct GatherArgs {
   const uint2* bref;         // [L][Hkv][total_spans] blob references
   const int64_t* layer_off;  // [L + 1]
   const uint8_t* host_pool;  // device address of the mapped pinned factor pool
-  uint8_t* ring;             // HBM staging ring: layer l at layer_off[l] - layer_off[layer_begin]
+  uint8_t* ring;             // HBM staging ring (slot): layer l at layer_off[l] - layer_off[ring_layer0]
   int2* stat;                // [Lc][B][Hkv]: union spans, union blob bytes / 256 (or NULL)
   int64_t total_spans;
   int32_t layer_begin, layer_count, B, Hq, Hkv, W, G, D, nsplit;
+  int32_t lc_first, lc_count;   // this launch: layers [lc_first, lc_first + lc_count) of the call
+  int32_t ring_layer0;      // layer whose region starts `ring`
 };
 
 // ------------------------------------------------------------ launchers ---

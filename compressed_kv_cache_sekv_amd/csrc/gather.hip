@@ -9,7 +9,7 @@
 //
 // The pinned pool is mapped into the device address space and read by the
 // kernel over PCIe.  The HBM ring mirrors the pool's layout for the layers of
-// the call (layer l's region at layer_off[l] - layer_off[layer_begin]): a blob
+// one launch (layer l's region at layer_off[l] - layer_off[ring_layer0]): a blob
 // lands at its own offset within its layer's region, so no placement is
 // computed on the host and the call does not synchronise.  Blobs hold only the
 // components the build kept, so a smaller effective rank moves fewer bytes.  gather_kernel, per (layer, b, KV head, share):
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   __shared__ int64_t s_bpre[kMaxWords + 1];     // union bytes before word w
   __shared__ int64_t s_src[kShare];             // blob byte offset within the layer
   __shared__ int32_t s_len[kShare];             // 16-byte chunks
-  const int li = blockIdx.y, l = a.layer_begin + li;
+  const int li = a.lc_first + blockIdx.y, l = a.layer_begin + li;
   const int j = blockIdx.x % a.nsplit, bg = blockIdx.x / a.nsplit;
   const int b = bg / a.Hkv, g = bg - b * a.Hkv;
   const BMeta bm = a.meta[b];
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   // copy to the same offset of ring layer li, 16 bytes per lane, four loads
   // in flight per lane
   const uint8_t* src_l = a.host_pool + a.layer_off[l];
-  uint8_t* dst_l = a.ring + (a.layer_off[l] - a.layer_off[a.layer_begin]);
+  uint8_t* dst_l = a.ring + (a.layer_off[l] - a.layer_off[a.ring_layer0]);
   for (int e = 0; e < cnt; ++e) {
     const u32x4* src = (const u32x4*)(src_l + s_src[e]);
     u32x4* dst = (u32x4*)(dst_l + s_src[e]);
@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(gather_kernel, dim3(a.B * a.Hkv * a.nsplit, a.layer_count), dim3(256), 0, st, a);
+  if (a.lc_first < 0 || a.lc_count < 1 || a.lc_first + a.lc_count > a.layer_count) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_kernel, dim3(a.B * a.Hkv * a.nsplit, a.lc_count), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -200,7 +200,11 @@ struct sekv_index {
   DBuf d_items, d_bg_first, d_part;
   // routing scratch: scores ranked by the budget kernels; alpha for calibration
   DBuf d_score, d_alpha, d_tau_inf;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  // pinned tier: the copy stream the gathers of multi-layer calls run on, the
+  // events that order them against the attention, and gather timing events
+  hipStream_t copy = nullptr;
+  hipEvent_t ev_call = nullptr, ev_ready[2] = {nullptr, nullptr}, ev_free[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> gev;
 };
 
 namespace {
@@ -393,7 +397,8 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
     void* dp = nullptr;
     HIP_TRY(hipHostGetDevicePointer(&dp, x->h_pool, 0));
     x->d_host_pool = (const uint8_t*)dp;
-    x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : std::max<int64_t>(x->max_layer_bytes, 256);
+    // two layer slots by default: a multi-layer call gathers one layer ahead
+    x->ring_bytes = ring_bytes_req > 0 ? ring_bytes_req : 2 * std::max<int64_t>((x->max_layer_bytes + 255) & ~255LL, 256);
     HIP_TRY(dalloc(x->d_ring, (size_t)x->ring_bytes));
   }
   HIP_TRY(hipMemcpyAsync(x->d_meta.p, x->meta.data(), sizeof(BMeta) * x->B, hipMemcpyHostToDevice, st));
@@ -411,22 +416,31 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
   HIP_TRY(dalloc(x->d_bg_first, 4 * x->bg_first.size()));
   HIP_TRY(hipMemcpyAsync(x->d_items.p, x->items.data(), sizeof(WorkItem) * x->items.size(), hipMemcpyHostToDevice, st));
   HIP_TRY(hipMemcpyAsync(x->d_bg_first.p, x->bg_first.data(), 4 * x->bg_first.size(), hipMemcpyHostToDevice, st));
-  HIP_TRY(hipEventCreate(&x->ev0));
-  HIP_TRY(hipEventCreate(&x->ev1));
+  if (x->tier == SEKV_TIER_PINNED_HOST) {
+    HIP_TRY(hipStreamCreateWithFlags(&x->copy, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&x->ev_call, hipEventDisableTiming));
+    for (int k = 0; k < 2; ++k) {
+      HIP_TRY(hipEventCreateWithFlags(&x->ev_ready[k], hipEventDisableTiming));
+      HIP_TRY(hipEventCreateWithFlags(&x->ev_free[k], hipEventDisableTiming));
+    }
+  }
   return SEKV_OK;
 }
 
 void free_index(sekv_index* x) {
   if (!x) return;
   if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
+  if (x->copy) (void)hipStreamSynchronize(x->copy);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_bref, &x->d_layer_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
                   &x->d_ring, &x->d_gstat, &x->d_items, &x->d_bg_first, &x->d_part,
                   &x->d_score, &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
-  if (x->ev0) (void)hipEventDestroy(x->ev0);
-  if (x->ev1) (void)hipEventDestroy(x->ev1);
+  if (x->copy) (void)hipStreamDestroy(x->copy);
+  for (hipEvent_t e : {x->ev_call, x->ev_ready[0], x->ev_ready[1], x->ev_free[0], x->ev_free[1]})
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : x->gev) (void)hipEventDestroy(e);
   x->magic = DEAD_MAGIC;
   delete x;
 }
@@ -1192,43 +1206,37 @@ size_t part_bytes(const sekv_index* x, int lc) {
   return sizeof(float) * (size_t)lc * std::max<size_t>(x->items.size(), 1) * x->G * (x->D + 2);
 }
 
-// The ring of the pinned tier mirrors the pool: a call over layers
-// [lb, lb + lc) needs those layers' whole factor regions.
-sekv_status check_ring(const sekv_index* x, int lb, int lc) {
-  const int64_t need = x->layer_off[lb + lc] - x->layer_off[lb];
-  if (x->tier == SEKV_TIER_PINNED_HOST && need > x->ring_bytes)
-    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes holds less than the %lld bytes of factors of layers "
-                "[%d, %d)", (long long)x->ring_bytes, (long long)need, lb, lb + lc);
+// The staging ring of the pinned tier holds one or two layer slots, each a
+// mirror of one layer's factor region (blobs at their offsets within it).
+int64_t ring_slot_bytes(const sekv_index* x) { return (x->max_layer_bytes + 255) & ~255LL; }
+int ring_slots(const sekv_index* x) {
+  const int64_t sb = std::max<int64_t>(ring_slot_bytes(x), 256);
+  return (int)std::min<int64_t>(2, x->ring_bytes / sb);
+}
+
+sekv_status check_ring(const sekv_index* x) {
+  if (x->tier == SEKV_TIER_PINNED_HOST && ring_slots(x) < 1)
+    return fail(SEKV_ECAPACITY, "staging ring of %lld bytes holds less than one layer's factors (%lld bytes)",
+                (long long)x->ring_bytes, (long long)ring_slot_bytes(x));
   return SEKV_OK;
 }
 
 // Gather (pinned tier), attention items writing their partials to `part`,
 // merge into out.  Asynchronous unless stats are asked for on the pinned tier
-// (then the union sizes and the gather time are read back).
+// (then the union sizes and the gather times are read back).
+//
+// Pinned tier: layer li of the call is gathered into ring slot li % slots and
+// attended from there.  With two slots and more than one layer the gathers run
+// on the index's copy stream, one layer ahead: layer li + 1 crosses PCIe while
+// layer li is attended ([Method] Fig. 2: asynchronous transfer overlapped with
+// the pipeline), and the gather into a slot waits for the attention of the
+// layer that used it before.
 sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q, const uint64_t* mask, float* out,
                        sekv_stats* stats, float* part, int2* gstat, bool timed) {
   if (stats) memset(stats, 0, sizeof *stats);
   const int n_items = (int)x->items.size();
   hipStream_t st = c->stream;
   const bool pinned = x->tier == SEKV_TIER_PINNED_HOST;
-  if (pinned) {
-    GatherArgs ga{};
-    ga.mask = mask;
-    ga.meta = (const BMeta*)x->d_meta.p;
-    ga.span_len = (const int32_t*)x->d_span_len.p;
-    ga.bref = (const uint2*)x->d_bref.p;
-    ga.layer_off = (const int64_t*)x->d_layer_off.p;
-    ga.host_pool = x->d_host_pool;
-    ga.ring = (uint8_t*)x->d_ring.p;
-    ga.stat = gstat;
-    ga.total_spans = x->total_spans;
-    ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
-    ga.W = x->Wd; ga.G = x->G; ga.D = x->D;
-    ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
-    if (stats) HIP_TRY(hipEventRecord(x->ev0, st));
-    HIP_TRY(launch_gather(ga, st));
-    if (stats) HIP_TRY(hipEventRecord(x->ev1, st));
-  }
   AttendArgs aa{};
   aa.q = (const bf16_t*)q;
   aa.mask = mask;
@@ -1240,21 +1248,76 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
   aa.span_len = (const int32_t*)x->d_span_len.p;
   aa.bref = (const uint2*)x->d_bref.p;
   aa.layer_off = (const int64_t*)x->d_layer_off.p;
-  aa.pool = pinned ? (const uint8_t*)x->d_ring.p : (const uint8_t*)x->d_pool.p;
-  aa.pool_layer0 = pinned ? lb : 0;
+  aa.pool = (const uint8_t*)x->d_pool.p;
+  aa.pool_layer0 = 0;
   aa.part = part;
   aa.total_spans = x->total_spans;
   aa.layer_begin = lb; aa.layer_count = lc; aa.n_items = n_items;
+  aa.lc_first = 0; aa.lc_count = lc;
   aa.B = x->B; aa.L = x->L; aa.Hq = x->Hq; aa.Hkv = x->Hkv; aa.W = x->Wd;
   aa.max_spans = std::max(x->max_spans, 1);
   aa.scale = 1.0f / sqrtf((float)x->D);
-  if (n_items > 0) {
-    size_t slot = 0;
+  auto attend = [&]() -> sekv_status {
+    if (n_items <= 0) return SEKV_OK;
     if (timed) {
+      size_t slot = 0;
       HIP_TRY(c->t_attend.reserve(&slot));
       HIP_TRY(launch_attend(aa, x->D, x->G, x->R, st, c->t_attend.ev[slot], c->t_attend.ev[slot + 1]));
     } else {
       HIP_TRY(launch_attend(aa, x->D, x->G, x->R, st));
+    }
+    return SEKV_OK;
+  };
+  sekv_status rs;
+  if (!pinned) {
+    if ((rs = attend())) return rs;
+  } else {
+    GatherArgs ga{};
+    ga.mask = mask;
+    ga.meta = (const BMeta*)x->d_meta.p;
+    ga.span_len = (const int32_t*)x->d_span_len.p;
+    ga.bref = (const uint2*)x->d_bref.p;
+    ga.layer_off = (const int64_t*)x->d_layer_off.p;
+    ga.host_pool = x->d_host_pool;
+    ga.stat = gstat;
+    ga.total_spans = x->total_spans;
+    ga.layer_begin = lb; ga.layer_count = lc; ga.B = x->B; ga.Hq = x->Hq; ga.Hkv = x->Hkv;
+    ga.W = x->Wd; ga.G = x->G; ga.D = x->D;
+    ga.nsplit = std::max(1, (x->max_spans + gather_share() - 1) / gather_share());
+    const int slots = ring_slots(x);
+    const bool overlap = slots >= 2 && lc >= 2;
+    hipStream_t gs = overlap ? x->copy : st;
+    if (stats && x->gev.size() < (size_t)2 * lc) {
+      while (x->gev.size() < (size_t)2 * lc) {
+        hipEvent_t e = nullptr;
+        HIP_TRY(hipEventCreate(&e));
+        x->gev.push_back(e);
+      }
+    }
+    if (overlap) {   // the copy stream starts after the work already on the call's stream (the masks)
+      HIP_TRY(hipEventRecord(x->ev_call, st));
+      HIP_TRY(hipStreamWaitEvent(gs, x->ev_call, 0));
+    }
+    for (int li = 0; li < lc; ++li) {
+      const int k = li % slots;
+      const int l = lb + li;
+      uint8_t* ring = (uint8_t*)x->d_ring.p + (size_t)k * ring_slot_bytes(x);
+      ga.ring = ring;
+      ga.ring_layer0 = l;
+      ga.lc_first = li; ga.lc_count = 1;
+      if (overlap && li >= slots) HIP_TRY(hipStreamWaitEvent(gs, x->ev_free[k], 0));
+      if (stats) HIP_TRY(hipEventRecord(x->gev[2 * li], gs));
+      HIP_TRY(launch_gather(ga, gs));
+      if (stats) HIP_TRY(hipEventRecord(x->gev[2 * li + 1], gs));
+      if (overlap) {
+        HIP_TRY(hipEventRecord(x->ev_ready[k], gs));
+        HIP_TRY(hipStreamWaitEvent(st, x->ev_ready[k], 0));
+      }
+      aa.pool = ring;
+      aa.pool_layer0 = l;
+      aa.lc_first = li; aa.lc_count = 1;
+      if ((rs = attend())) return rs;
+      if (overlap) HIP_TRY(hipEventRecord(x->ev_free[k], st));
     }
   }
   MergeArgs mg{};
@@ -1274,11 +1337,15 @@ sekv_status decode_run(sekv_ctx* c, sekv_index* x, int lb, int lc, const void* q
       un += (uint64_t)v.x;
       by += (uint64_t)v.y << 8;
     }
-    float ms = 0.f;
-    HIP_TRY(hipEventElapsedTime(&ms, x->ev0, x->ev1));
+    double ms = 0.0;
+    for (int li = 0; li < lc; ++li) {
+      float m = 0.f;
+      HIP_TRY(hipEventElapsedTime(&m, x->gev[2 * li], x->gev[2 * li + 1]));
+      ms += m;
+    }
     stats->union_spans = un;
     stats->pcie_bytes = by;
-    stats->pcie_copies = 1;
+    stats->pcie_copies = (uint64_t)lc;
     stats->pcie_ms = ms;
   }
   return SEKV_OK;
@@ -1293,7 +1360,7 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
-  if ((st = check_ring(x, lb, lc))) return st;
+  if ((st = check_ring(x))) return st;
   if ((st = set_device(c))) return st;
   HIP_TRY(dgrow(x->d_part, part_bytes(x, lc)));
   int2* gstat = nullptr;

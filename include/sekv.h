@@ -74,10 +74,12 @@ typedef struct {
   int32_t power_iters;  /* randomized-SVD power iterations q                     */
   uint64_t seed;        /* Gaussian test matrices: Philox4x32-10 keyed by seed   */
   int32_t tier;         /* sekv_tier                                             */
-  int64_t ring_bytes;   /* pinned tier: HBM staging ring size, 0 = the largest
-                           layer's whole factor set; a decode call over layers
-                           [lb, lb + n) needs their factor bytes (the ring
-                           mirrors the pool layout)                              */
+  int64_t ring_bytes;   /* pinned tier: HBM staging ring size, 0 = two slots of
+                           the largest layer's whole factor set.  Each slot
+                           mirrors one layer's region of the pool; one slot is
+                           required (ECAPACITY otherwise), and with two a call
+                           over several layers gathers the next layer while the
+                           current one is attended                               */
   float gate_eps;       /* variable effective rank ([Contrib], dual resolution;
                            [Tech], low-rank paragraph: the gates set each span's
                            effective rank and components are dropped at storage
@@ -161,8 +163,10 @@ typedef struct {
 typedef struct {
   uint64_t union_spans;    /* sum over (b, l, g) of |union of the G heads' z|   */
   uint64_t pcie_bytes;     /* bytes moved host -> HBM ring (padded blobs)        */
-  uint64_t pcie_copies;    /* gather kernel launches                             */
-  double pcie_ms;          /* stream time of the gather kernel (HIP events)      */
+  uint64_t pcie_copies;    /* gather kernel launches (one per layer)             */
+  double pcie_ms;          /* summed stream time of the gather launches (HIP
+                              events around each); overlapped with attention
+                              when the call gathers one layer ahead             */
 } sekv_stats;
 
 /* ---------------------------------------------------------------- lifecycle */
@@ -324,13 +328,17 @@ sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
  * Pinned tier: the routed union's factor blobs are first gathered from the
  * mapped pinned pool into the HBM staging ring by a kernel reading them over
  * PCIe ([Method] Stage 2: the factors are fetched from the CPU
- * asynchronously).  The ring mirrors the pool layout of the call's layers (a
- * blob sits at its own pool offset), so it must hold layer_count whole layers
- * of factors (SEKV_ECAPACITY otherwise, before any device work), nothing is
- * placed on the host and the call does not synchronise, except when stats is
- * non-NULL on the pinned tier (to read back the union sizes and the gather
- * time).  The index owns the partials buffer (grown on first use): calls on
- * one context are ordered on its stream. */
+ * asynchronously).  Each ring slot mirrors one layer's pool region (a blob
+ * sits at its own offset), so nothing is placed on the host; the ring must
+ * hold one slot (SEKV_ECAPACITY otherwise, before any device work).  With two
+ * slots and layer_count > 1 the gathers run on the index's own stream one
+ * layer ahead of the attention ([Method] Fig. 2: asynchronous transfer
+ * overlapped with the decode pipeline), ordered by events against the call's
+ * stream: the call's results are still complete when its stream is.  The
+ * call does not synchronise, except when stats is non-NULL on the pinned
+ * tier (to read back the union sizes and the gather times).  The index owns
+ * the partials buffer (grown on first use): calls on one context are ordered
+ * on its stream. */
 sekv_status sekv_decode_attend(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                                int32_t layer_count, const void* q, const uint64_t* mask,
                                float* out, sekv_stats* stats);

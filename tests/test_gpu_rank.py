@@ -153,22 +153,50 @@ def _check_against_export(idx, w, q, tau, words, out, lb, lc, label):
     assert worst <= SC.REL_L2
 
 
-@pytest.mark.parametrize("tier", [0, 1], ids=["hbm", "pinned"])
-def test_ragged_decode_against_oracle_per_layer_calls(ctx, sl, tier):
+def _union_blob_bytes(idx, w, words, lb, lc):
+    """Bytes the gather must move for these masks: the padded blobs of each
+    (b, l, g) union, from the exported ranks and span lengths."""
+    rk = idx.export(layer_begin=lb, layer_count=lc, fields=["rank"])["rank"]
+    lens = idx.span_lengths()
+    tot, so, ro = 0, 0, 0
+    for b in range(w.B):
+        ns = int(idx.n_spans[b])
+        r = rk[ro:ro + lc * w.Hkv * ns * 2].reshape(lc, w.Hkv, ns, 2)
+        for l in range(lc):
+            for g in range(w.Hkv):
+                u = np.zeros(ns, bool)
+                for h in range(g * w.G, (g + 1) * w.G):
+                    u |= SC.unpack_mask(words[b, l, h], ns)
+                n = lens[so:so + ns][u].astype(np.int64)
+                tot += int(blob_bytes(r[l, g, u, 0], r[l, g, u, 1], w.d, n).sum())
+        so += ns
+        ro += lc * w.Hkv * ns * 2
+    return tot
+
+
+@pytest.mark.parametrize("tier,slots", [(0, 0), (1, 2), (1, 1)], ids=["hbm", "pinned-2slots", "pinned-1slot"])
+def test_ragged_decode_against_oracle_per_layer_calls(ctx, sl, tier, slots):
     """Two layers whose blob layouts differ, decoded one layer per call (the
-    second call starts at layer 1) and both layers in one call."""
+    second call starts at layer 1) and both layers in one call: on the pinned
+    tier with two ring slots (the second layer gathered while the first is
+    attended) and with one (gather and attend in turn)."""
     w = W2L
-    # pinned: a ring for both layers, so the two-layer call fits
-    idx = build(ctx, sl, w, EPS, tier=tier, ring_bytes=(1 << 30) if tier == 1 else 0)
+    idx = build(ctx, sl, w, EPS, tier=tier)
+    if slots == 1:
+        one = idx.info.ring_bytes // 2     # the default ring holds two slots
+        idx.free()
+        idx = build(ctx, sl, w, EPS, tier=tier, ring_bytes=one)
     q = synth.query(w, 0)
     tau = calibrated_tau(idx, w)
     for lb, lc in ((0, 1), (1, 1), (0, 2)):
         mask = _route(idx, w, q, tau, lb, lc)
         out, st = _decode(idx, w, q, mask, lb, lc, stats=tier == 1)
         words = mask.cpu().numpy().view(np.uint64)
-        _check_against_export(idx, w, q, tau, words, out, lb, lc, f"tier {tier} layers [{lb}, {lb + lc})")
+        _check_against_export(idx, w, q, tau, words, out, lb, lc, f"tier {tier} slots {slots} layers [{lb}, {lb + lc})")
         if tier == 1:
-            assert st.pcie_bytes > 0
+            assert st.pcie_copies == lc
+            assert st.pcie_bytes == _union_blob_bytes(idx, w, words, lb, lc)
+            print(f"[rank] gather of layers [{lb}, {lb + lc}): {st.pcie_bytes} bytes in {st.pcie_ms:.3f} ms")
     idx.free()
 
 
