@@ -20,6 +20,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <unordered_set>
 #include <vector>
 
 #include "sekv.h"
@@ -41,17 +42,36 @@ sekv_status fail(sekv_status st, const char* fmt, ...) {
   return st;
 }
 
+// On a failing HIP call: reset the runtime's last-error state (so that the
+// caller's next HIP call does not report this failure again), then return.
 #define HIP_TRY(expr)                                                                    \
   do {                                                                                   \
     hipError_t e_ = (expr);                                                              \
-    if (e_ != hipSuccess)                                                                \
+    if (e_ != hipSuccess) {                                                              \
+      (void)hipGetLastError();                                                           \
       return fail(e_ == hipErrorOutOfMemory ? SEKV_ENOMEM : SEKV_EHIP, "%s: %s (%s:%d)", \
                   #expr, hipGetErrorString(e_), __FILE__, __LINE__);                     \
+    }                                                                                    \
   } while (0)
 
 constexpr uint32_t CTX_MAGIC = 0x53454b43u;   // "SEKC"
 constexpr uint32_t IDX_MAGIC = 0x53454b49u;   // "SEKI"
 constexpr uint32_t DEAD_MAGIC = 0xdeadbeefu;
+
+// Handles handed out and not yet destroyed or freed.  A call checks its
+// handles here before reading them, so a destroyed context or a freed index
+// is refused (SEKV_ESTATE) without touching freed memory.
+std::mutex g_live_mu;
+std::unordered_set<const void*> g_live;
+bool is_live(const void* p) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  return p && g_live.count(p) != 0;
+}
+void set_live(const void* p, bool on) {
+  std::lock_guard<std::mutex> lk(g_live_mu);
+  if (on) g_live.insert(p);
+  else g_live.erase(p);
+}
 
 // Work decomposition of the decode kernel: at most kStepsPerItem resident
 // 32-row steps (two per wave) and kSpansPerItem compressed spans of the
@@ -211,7 +231,7 @@ namespace {
 
 sekv_status check_ctx(const sekv_ctx* c) {
   if (!c) return fail(SEKV_EINVAL, "null context");
-  if (c->magic != CTX_MAGIC) return fail(SEKV_ESTATE, "context is not live");
+  if (!is_live(c) || c->magic != CTX_MAGIC) return fail(SEKV_ESTATE, "context is not live");
   return SEKV_OK;
 }
 
@@ -219,7 +239,7 @@ sekv_status check_idx(const sekv_ctx* c, const sekv_index* x) {
   sekv_status st = check_ctx(c);
   if (st) return st;
   if (!x) return fail(SEKV_EINVAL, "null index");
-  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  if (!is_live(x) || x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
   if (x->ctx != c) return fail(SEKV_ESTATE, "index belongs to another context");
   return SEKV_OK;
 }
@@ -391,6 +411,7 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
     hipError_t e = hipHostMalloc((void**)&x->h_pool, pb, hipHostMallocPortable | hipHostMallocMapped);
     if (e != hipSuccess) {
       x->h_pool = nullptr;
+      (void)hipGetLastError();
       return fail(SEKV_ENOMEM, "pinned host pool of %zu bytes: %s", pb, hipGetErrorString(e));
     }
     memset(x->h_pool, 0, pb);
@@ -429,7 +450,8 @@ sekv_status alloc_index(sekv_index* x, int64_t ring_bytes_req) {
 
 void free_index(sekv_index* x) {
   if (!x) return;
-  if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
+  set_live(x, false);
+  if (x->ctx && is_live(x->ctx) && x->ctx->magic == CTX_MAGIC) (void)hipStreamSynchronize(x->ctx->stream);
   if (x->copy) (void)hipStreamSynchronize(x->copy);
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_bref, &x->d_layer_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
@@ -491,12 +513,14 @@ extern "C" sekv_status sekv_create(int32_t device, void* stream, sekv_ctx** out)
   sekv_ctx* c = new sekv_ctx();
   c->device = device;
   c->stream = (hipStream_t)stream;
+  set_live(c, true);
   *out = c;
   return SEKV_OK;
 }
 
 extern "C" void sekv_destroy(sekv_ctx* c) {
-  if (!c || c->magic != CTX_MAGIC) return;
+  if (!c || !is_live(c) || c->magic != CTX_MAGIC) return;
+  set_live(c, false);
   (void)hipSetDevice(c->device);
   (void)hipStreamSynchronize(c->stream);
   c->t_route.release();
@@ -571,7 +595,7 @@ extern "C" sekv_status sekv_rsvd_batched(sekv_ctx* c, int32_t count, const void*
 
 extern "C" sekv_status sekv_index_get_info(const sekv_index* x, sekv_index_info* info) {
   if (!x || !info) return fail(SEKV_EINVAL, "null argument");
-  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  if (!is_live(x) || x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
   info->B = x->B; info->L = x->L; info->Hq = x->Hq; info->Hkv = x->Hkv; info->d = x->D;
   info->R = x->R; info->dprime = x->dp; info->tier = x->tier;
   info->max_spans = x->max_spans;
@@ -587,7 +611,7 @@ extern "C" sekv_status sekv_index_get_info(const sekv_index* x, sekv_index_info*
 
 extern "C" sekv_status sekv_index_counts(const sekv_index* x, int32_t* n_spans, int32_t* n_raw) {
   if (!x || !n_spans || !n_raw) return fail(SEKV_EINVAL, "null argument");
-  if (x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
+  if (!is_live(x) || x->magic != IDX_MAGIC) return fail(SEKV_ESTATE, "index is not live");
   for (int b = 0; b < x->B; ++b) {
     n_spans[b] = x->meta[b].n_spans;
     n_raw[b] = x->meta[b].n_raw;
@@ -596,8 +620,8 @@ extern "C" sekv_status sekv_index_counts(const sekv_index* x, int32_t* n_spans, 
 }
 
 extern "C" void sekv_index_free(sekv_index* x) {
-  if (!x || x->magic != IDX_MAGIC) return;
-  if (x->ctx && x->ctx->magic == CTX_MAGIC) (void)hipSetDevice(x->ctx->device);
+  if (!x || !is_live(x) || x->magic != IDX_MAGIC) return;
+  if (x->ctx && is_live(x->ctx) && x->ctx->magic == CTX_MAGIC) (void)hipSetDevice(x->ctx->device);
   free_index(x);
 }
 
@@ -773,6 +797,7 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
     HIP_TRY(hipStreamSynchronize(stream));
   }
   guard.x = nullptr;
+  set_live(x, true);
   *out = x;
   return SEKV_OK;
 }
@@ -938,6 +963,7 @@ extern "C" sekv_status sekv_index_import(sekv_ctx* c, const sekv_build_params* p
     HIP_TRY(hipMemcpyAsync(x->d_pool.p, pool.data(), pool.size(), hipMemcpyHostToDevice, stream));
   HIP_TRY(hipStreamSynchronize(stream));
   guard.x = nullptr;
+  set_live(x, true);
   *out = x;
   return SEKV_OK;
 }
