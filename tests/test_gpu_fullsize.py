@@ -293,3 +293,67 @@ def test_70b_batch32_64k_sampled(ctx, sl):
     assert contract <= SC.REL_L2
     assert gap <= SVD_GAP
     idx.free()
+
+
+@pytest.mark.timeout(900)
+def test_70b_batch32_64k_gate_eps_sampled(ctx, sl):
+    """The full 70B-shaped batch built with gate_eps = 0.75 (components whose
+    gate is below it are not stored): the stored ranks of sampled (sequence,
+    KV head) units bit-exact against the oracle's kept counts, and the
+    contract on those units: masks against the oracle routing the library's
+    exported index, decode within 5e-3 of the oracle decoding it."""
+    eps = 0.75
+    w = synth.WORKLOADS["llama70b_b32_64k"]
+    G = w.G
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, l, "cuda") for l in range(w.L)])
+    S_max = synth.max_spans(w.T, w.l_min)
+    gates = torch.stack([torch.stack([synth.gates(w, b, l, S_max, "cuda") for l in range(w.L)])
+                         for b in range(w.B)])
+    q = synth.query(w, 0, "cuda")
+    idx = ctx.build_index(sl.build_params(w, gate_eps=eps), K, V, H, W, gates)
+    tau = torch.zeros(w.L, w.Hq, device="cuda")
+    idx.calibrate_tau(0, w.L, synth.calibration_query(w, "cuda"), w.frac, tau)
+    Wd = idx.mask_words
+    mask = torch.zeros(w.B, w.L, w.Hq, Wd, dtype=torch.int64, device="cuda")
+    idx.route(0, w.L, q, tau, 0, mask, None)
+    out = torch.zeros(w.B, w.L, w.Hq, w.d, device="cuda")
+    idx.decode_attend(0, w.L, q, mask, out)
+    torch.cuda.synchronize()
+    words = mask.cpu().numpy().view(np.uint64)
+    out = out.cpu().double().numpy()
+    tau = tau.cpu().double().numpy()
+    Wn = W.cpu().double().numpy()
+    qn = q.cpu()
+    gn = gates.cpu()
+    lens_all = idx.span_lengths()
+    units = [(b, (3 * b + 1) % w.Hkv) for b in range(0, w.B, 2)]
+    contract, pairs, excl, checked = 0.0, 0, 0, 0
+    for b, g in units:
+        ex = idx.export(0, 1, seq_begin=b, seq_count=1)
+        ns = int(idx.n_spans[b])
+        lens = lens_all[int(idx.n_spans[:b].sum()):][:ns]
+        rk = ex["rank"].reshape(w.L, w.Hkv, ns, 2)[0, g]
+        for S in range(ns):
+            for which in range(2):
+                k = int(O.kept_components(gn[b, 0, g, which, S].double().numpy(), int(lens[S]), w.R, eps).sum())
+                assert rk[S, which] == (16 if k <= 16 else 16 * ((k + 15) // 16)), (b, g, S, which)
+                checked += 1
+        lib = SC.index_from_export(ex, idx.n_spans[b:b + 1], idx.n_raw[b:b + 1], w.L, w.Hq, w.Hkv, w.d, w.R,
+                                   w.dprime, kv_head=g)
+        keys = [(0, 0, hh) for hh in range(G)]
+        sub = lambda a: a[:, g * G:(g + 1) * G]
+        qb = qn[b:b + 1, :, g * G:(g + 1) * G].double().numpy()
+        ref = SC.route_ref(lib, sub(Wn), qb, sub(tau), keys=keys)
+        p, e = SC.check_masks(lambda k: words[b, 0, g * G + k[2]], ref, f"70b eps unit ({b}, {g})")
+        pairs += p
+        excl += e
+        for hh in range(G):
+            zg = SC.unpack_mask(words[b, 0, g * G + hh], lib[0].n_spans)
+            o = O.decode_head(qb[0, 0, hh], lib[0], 0, 0, zg)
+            contract = max(contract, SC.rel_l2(out[b, 0, g * G + hh], o))
+    print(f"[70b b32 eps {eps}] {len(units)} units: {checked} stored ranks exact, {pairs} routing pairs "
+          f"({excl} excluded), library vs oracle on the library's index {contract:.3e}; factor pool "
+          f"{idx.info.factor_bytes / 1e9:.2f} GB", flush=True)
+    assert contract <= SC.REL_L2
+    idx.free()

@@ -200,14 +200,22 @@ def test_ragged_decode_against_oracle_per_layer_calls(ctx, sl, tier, slots):
     idx.free()
 
 
-def test_ragged_decode_against_oracle_batch(ctx, sl):
+@pytest.mark.parametrize("eps", [EPS, 2.0])
+def test_ragged_decode_against_oracle_batch(ctx, sl, eps):
+    """The 70B-shaped pair of sequences at gate_eps 0.5, and at 2.0, where
+    every gate is below eps: each blob then stores one tile of zero
+    components, every expanded span contributes rows of key 0 and value 0."""
     w = W70
-    idx = build(ctx, sl, w, EPS)
+    idx = build(ctx, sl, w, eps)
+    if eps > 1:
+        ex = idx.export(fields=["rank", "smk", "smv"])
+        assert (ex["rank"] == 16).all() and not ex["smk"].any() and not ex["smv"].any()
     q = synth.query(w, 0)
     tau = calibrated_tau(idx, w)
     mask = _route(idx, w, q, tau, 0, 1)
     out, _ = _decode(idx, w, q, mask, 0, 1)
-    _check_against_export(idx, w, q, tau, mask.cpu().numpy().view(np.uint64), out, 0, 1, "70B-shaped batch")
+    _check_against_export(idx, w, q, tau, mask.cpu().numpy().view(np.uint64), out, 0, 1,
+                          f"70B-shaped batch, gate_eps {eps}")
     idx.free()
 
 
