@@ -14,15 +14,22 @@ step_ms     = p10 / median / p90 of the K per-step durations, from a pass of
               the same steps with an event after each (the timed region
               holds the K steps alone)
 roofline    = the attention kernel's algorithmic bytes per launch (resident
-              K/V rows, the factor blobs of the routed union, queries, masks)
-              over its mean launch time from HIP events in the timed region,
-              against MI355X's 8 TB/s HBM peak
+              K/V rows, the factor blobs of the routed union at their stored
+              ranks, queries, masks) over its mean launch time, against
+              MI355X's 8 TB/s HBM peak.  The launch time comes from HIP events
+              recorded in each attention launch's own dispatch packet, in an
+              instrumented pass over the same steps on the same stream (the
+              timed region itself carries no events); `traffic` is the
+              committed rocprofv3 FETCH_SIZE + WRITE_SIZE reading for the same
+              kernel source, or null
 cpu_baseline= the fp64 CPU oracle (BLAS on the process's cores; a one-thread
               run beside it), on a bounded sample of the
               same workload (one layer x one KV head), scaled to a full step
 pcie        = the same decode with span factors in pinned host memory and the
-              routed union gathered into an HBM ring (PCIe bytes and time per
-              step, reported beside the value, never as it)
+              routed union gathered into an HBM ring slot (PCIe bytes and time
+              per step; query-tokens/s including PCIe for per-layer calls and
+              for one call over all layers; reported beside the value, never
+              as it)
 """
 from __future__ import annotations
 
