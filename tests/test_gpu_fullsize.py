@@ -357,3 +357,60 @@ def test_70b_batch32_64k_gate_eps_sampled(ctx, sl):
           f"{idx.info.factor_bytes / 1e9:.2f} GB", flush=True)
     assert contract <= SC.REL_L2
     idx.free()
+
+
+@pytest.mark.timeout(900)
+def test_rsvd_full_128k_layer_quality(ctx, sl):
+    """The randomized SVD on every span matrix of one 128K layer of the
+    prefill workload (8 KV heads, K and V: 42,048 matrices; R = 32,
+    oversampling 8, 2 power iterations), each against its exact Eckart-Young
+    optimum (R19: err <= 1.05 opt + 1e-5 |A|), with sorted nonnegative
+    singular values and orthonormal factors."""
+    w = synth.WORKLOADS["prefill_8b_128k"]
+    H, K, V = synth.kv_cache(w, device="cuda")
+    sp = O.span_split(H[0].cpu().numpy(), w.alpha_sp, w.l_min)
+    starts = sp.spans[:, 0]
+    lens = sp.spans[:, 1].astype(np.int64)
+    # matrices in (g, K|V, span) order, rows gathered on the device
+    idx_rows = torch.from_numpy(np.concatenate([np.arange(a, a + n) for a, n in sp.spans])).cuda()
+    blocks = []
+    for g in range(w.Hkv):
+        for X in (K, V):
+            blocks.append(X[0, 0, g].index_select(0, idx_rows))
+    A = torch.cat(blocks).contiguous()
+    rows_np = np.tile(lens, 2 * w.Hkv).astype(np.int32)
+    cnt = len(rows_np)
+    row_off = np.concatenate([[0], np.cumsum(rows_np[:-1].astype(np.int64))]) * w.d
+    mr = int(rows_np.max())
+    U = torch.zeros(cnt, mr, w.R, device="cuda")
+    S = torch.zeros(cnt, w.R, device="cuda")
+    Vt = torch.zeros(cnt, w.R, w.d, device="cuda")
+    ctx.rsvd_batched(A, torch.from_numpy(row_off).cuda(), torch.from_numpy(rows_np).cuda(), mr, w.d, w.R,
+                     w.oversample, w.power_iters, w.seed, U, S, Vt)
+    torch.cuda.synchronize()
+    print(f"[rsvd full layer] {cnt} matrices factored", flush=True)
+    Ah = A.double().cpu().numpy()
+    Uh, Sh, Vh = U.cpu().numpy(), S.cpu().double().numpy(), Vt.cpu().double().numpy()
+    worst, worst_orth, done = 0.0, 0.0, 0
+    for n in np.unique(rows_np):
+        ms = np.flatnonzero(rows_np == n)
+        Am = np.stack([Ah[row_off[m] // w.d:row_off[m] // w.d + n] for m in ms])       # [c, n, d]
+        Um = Uh[ms, :n].astype(np.float64)
+        rec = np.matmul(Um * Sh[ms][:, None, :], Vh[ms])
+        err = np.sqrt(((Am - rec) ** 2).sum(axis=(1, 2)))
+        sv = np.linalg.svd(Am, compute_uv=False)                                         # exact, descending
+        opt = np.sqrt((sv[:, w.R:] ** 2).sum(1)) if sv.shape[1] > w.R else np.zeros(len(ms))
+        nrm = np.sqrt((Am ** 2).sum(axis=(1, 2)))
+        worst = max(worst, float((err / (1.05 * opt + 1e-5 * nrm)).max()))
+        r = min(w.R, int(n))
+        assert (np.diff(Sh[ms, :r], axis=1) <= 1e-6 * Sh[ms, :1]).all() and (Sh[ms] >= 0).all()
+        for j, m in enumerate(ms):
+            k = int((Sh[m] > 0).sum())
+            worst_orth = max(worst_orth, np.abs(Um[j, :, :k].T @ Um[j, :, :k] - np.eye(k)).max(),
+                             np.abs(Vh[m, :k] @ Vh[m, :k].T - np.eye(k)).max())
+        done += len(ms)
+    assert done == cnt
+    print(f"[rsvd full layer] {cnt} matrices: worst err / (1.05 opt + 1e-5 |A|) = {worst:.4f}; "
+          f"worst orthonormality {worst_orth:.2e}", flush=True)
+    assert worst <= 1.0
+    assert worst_orth <= 1e-4
