@@ -107,7 +107,7 @@ __device__ __forceinline__ void tri_decode(int e, int& r, int& c) {
 // three; for wider sketches 16 rows save too little LDS to add one).
 template <int LP>
 struct Chunk {
-  static constexpr int NC = LP <= 32 ? 16 : 32;
+  static constexpr int NC = LP <= 48 ? 16 : 32;
   static constexpr int NRT = NC / 16;   // 16-row tiles per chunk
 };
 
@@ -118,8 +118,13 @@ struct Chunk {
 //            bf16 [kNRT][LP/16][64][4] each (range finder),
 //       or CT float [LP][kNC + 4] (a chunk of A Z or of U'),
 //       or Lf float [LP][LP] (Cholesky factor, fp32 copy, during orth)
-//   G   double [LP][LP]  Gram / Cholesky factor (lower), L^-1 (upper);
-//       or T float [LP][LP + 1] and E^T float [LP][LP + 4] (Jacobi)
+//   G   double [JP][JP]  Gram / Cholesky factor (lower), L^-1 (upper);
+//       or T float [JP][JP + 1] (Jacobi), with E^T float [JP][EP] in X when
+//       it fits there (X is idle during the Jacobi), else after T.
+//   JP = the largest sketch width min(R + p, d) rounded up to even, so the
+//   small-matrix region is sized by the sketch, not by its 16-wide padding
+//   (at R = 32, p = 8: 40 instead of 48; this region decides how many
+//   workgroups share a CU).
 template <int D, int LP>
 struct Lay {
   static constexpr int kNC = Chunk<LP>::NC;
@@ -138,10 +143,32 @@ struct Lay {
   static constexpr size_t x_end = ((x_end1 > x_end2 ? x_end1 : x_end2) > x_end3
                                        ? (x_end1 > x_end2 ? x_end1 : x_end2) : x_end3);
   static constexpr size_t g = (x_end + 15) & ~(size_t)15;
-  static constexpr size_t g_bytes1 = (size_t)LP * LP * 8;
-  static constexpr size_t g_bytes2 = (size_t)LP * (LP + 1) * 4 + (size_t)LP * (LP + 4) * 4;
-  static constexpr size_t bytes = g + (g_bytes1 > g_bytes2 ? g_bytes1 : g_bytes2);
 };
+
+// The runtime part of the layout: pitches of the small matrices for sketch
+// widths up to lmax (<= LP), where E^T goes, and the workgroup's LDS bytes.
+struct SmallLay {
+  int jp, tp, ep;      // G pitch and Jacobi size (even), T pitch, E^T pitch
+  size_t et;           // byte offset of E^T
+  size_t bytes;        // dynamic LDS of the workgroup
+};
+template <int D, int LP>
+__host__ __device__ inline SmallLay small_lay(int lmax) {
+  using Y = Lay<D, LP>;
+  SmallLay r;
+  r.jp = lmax + (lmax & 1);
+  r.tp = r.jp + 1;
+  r.ep = ((r.jp + 3) & ~3) + 4;
+  const size_t gb = (size_t)r.jp * r.jp * 8, tb = (size_t)r.jp * r.tp * 4, eb = (size_t)r.jp * r.ep * 4;
+  if (eb <= Y::g - Y::x) {
+    r.et = Y::x;
+    r.bytes = Y::g + (gb > tb ? gb : tb);
+  } else {
+    r.et = Y::g + ((tb + 15) & ~(size_t)15);
+    r.bytes = r.et + eb > Y::g + gb ? r.et + eb : Y::g + gb;
+  }
+  return r;
+}
 
 // Stage rows [c0, c0 + kNC) of A (rows >= n read as zero) into Ar and, for
 // the range finder, into the transposed operand tiles At.
@@ -269,25 +296,24 @@ __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
 // updated).  Afterwards L_jk = G[j][k] * dinv[k] (j > k), L_kk = 1 / dinv[k];
 // a pivot at or below 1e-14 of the largest diagonal marks a dependent
 // column: dinv = 0 there.
-template <int LP>
-__device__ void cholesky64(double* G, int m, float* dinv) {
+__device__ void cholesky64(double* G, int m, int GP, float* dinv) {
   double maxd = 0.0;
-  for (int i = 0; i < m; ++i) maxd = fmax(maxd, G[i * LP + i]);
+  for (int i = 0; i < m; ++i) maxd = fmax(maxd, G[i * GP + i]);
   const double tol = 1e-14 * maxd;
   __syncthreads();
   // thread t updates row k + 1 + (t >> 2) of the trailing block, columns
   // k + 1 + (t & 3) + 4 jj up to the diagonal
   for (int k = 0; k < m; ++k) {
-    const double dk = G[k * LP + k];
+    const double dk = G[k * GP + k];
     const double inv = (dk > tol && dk > 0.0) ? 1.0 / dk : 0.0;
     for (int i = k + 1 + (threadIdx.x >> 2); i < m; i += 64) {
-      const double f = G[i * LP + k] * inv;
-      for (int j = k + 1 + (threadIdx.x & 3); j <= i; j += 4) G[i * LP + j] -= f * G[j * LP + k];
+      const double f = G[i * GP + k] * inv;
+      for (int j = k + 1 + (threadIdx.x & 3); j <= i; j += 4) G[i * GP + j] -= f * G[j * GP + k];
     }
     __syncthreads();
   }
   for (int k = threadIdx.x; k < m; k += 256) {
-    const double dk = G[k * LP + k];
+    const double dk = G[k * GP + k];
     dinv[k] = (dk > tol && dk > 0.0) ? (float)(1.0 / sqrt(dk)) : 0.f;
   }
   __syncthreads();
@@ -296,7 +322,7 @@ __device__ void cholesky64(double* G, int m, float* dinv) {
 // Orthonormalise the first m rows of ZT (columns of Z, length D) in place:
 // Cholesky-QR, Z <- Z L^-T.  Rows m..LP-1 of ZT are zero on entry and exit.
 template <int D, int LP>
-__device__ void orthonormalize(uint8_t* lds, int m, float* dinv) {
+__device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
   using Y = Lay<D, LP>;
   float* ZT = (float*)(lds + Y::zt);
   double* G = (double*)(lds + Y::g);
@@ -322,16 +348,16 @@ __device__ void orthonormalize(uint8_t* lds, int m, float* dinv) {
       }
     }
     const int i0 = 2 * bi, j0 = 2 * bj;
-    G[i0 * LP + j0] = g00; G[j0 * LP + i0] = g00;
-    G[i0 * LP + j0 + 1] = g01; G[(j0 + 1) * LP + i0] = g01;
-    G[(i0 + 1) * LP + j0] = g10; G[j0 * LP + i0 + 1] = g10;
-    G[(i0 + 1) * LP + j0 + 1] = g11; G[(j0 + 1) * LP + i0 + 1] = g11;
+    G[i0 * GP + j0] = g00; G[j0 * GP + i0] = g00;
+    G[i0 * GP + j0 + 1] = g01; G[(j0 + 1) * GP + i0] = g01;
+    G[(i0 + 1) * GP + j0] = g10; G[j0 * GP + i0 + 1] = g10;
+    G[(i0 + 1) * GP + j0 + 1] = g11; G[(j0 + 1) * GP + i0 + 1] = g11;
   }
   __syncthreads();
-  cholesky64<LP>(G, m, dinv);
+  cholesky64(G, m, GP, dinv);
   for (int e = threadIdx.x; e < LP * LP; e += 256) {
     const int k = e / LP, j = e - k * LP;
-    Lf[e] = (j < k && k < m) ? (float)G[k * LP + j] * dinv[j] : 0.f;
+    Lf[e] = (j < k && k < m) ? (float)G[k * GP + j] * dinv[j] : 0.f;
   }
   __syncthreads();
   if (threadIdx.x < D) {
@@ -357,18 +383,16 @@ __device__ void orthonormalize(uint8_t* lds, int m, float* dinv) {
 }
 
 // Cyclic Jacobi eigen-decomposition of the symmetric l x l matrix T (pitch
-// LP + 1; rows and columns l..LP-1 zero).  Eigenvectors are accumulated as
-// the rows of ET (pitch LP + 4): row p of ET is column p of E.  The disjoint
+// TP; rows and columns l..JP-1 zero, JP even >= l).  Eigenvectors are
+// accumulated as the rows of ET (pitch EP): row p of ET is column p of E.  The disjoint
 // pairs of a round (round-robin ordering) rotate together; each 2 x 2 block
 // of T and each 4-element piece of a pair of ET rows is one work item.
-template <int LP>
-__device__ void jacobi(float* T, float* ET, int l, f32x4* rot, int* flag) {
-  constexpr int TP = LP + 1, EP = LP + 4;
+__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* flag) {
   const int m = l + (l & 1);
   const int np = m >> 1;
   const int nrc = (l + 3) >> 2;
   const float inv_np = 1.f / (float)max(np, 1), inv_nrc = 1.f / (float)max(nrc, 1);
-  for (int i = threadIdx.x; i < LP * EP; i += 256) ET[i] = (i / EP == i % EP) ? 1.f : 0.f;
+  for (int i = threadIdx.x; i < JP * EP; i += 256) ET[i] = (i / EP == i % EP) ? 1.f : 0.f;
   __syncthreads();
   for (int sweep = 0; sweep < 12; ++sweep) {
     if (threadIdx.x == 0) flag[0] = 0;
@@ -443,9 +467,11 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   float* ZT = (float*)(lds + Y::zt);
   bf16_t* Ar = (bf16_t*)(lds + Y::x);
   float* CT = (float*)(lds + Y::ct);
-  double* G = (double*)(lds + Y::g);
-  float* Tm = (float*)(lds + Y::g);          // pitch LP + 1
-  float* ET = Tm + LP * (LP + 1);             // pitch LP + 4
+  const SmallLay SL = small_lay<D, LP>(min(a.R + a.oversample, D));
+  const int GP = SL.jp, TP = SL.tp;
+  double* G = (double*)(lds + Y::g);          // pitch GP
+  float* Tm = (float*)(lds + Y::g);           // pitch TP
+  float* ET = (float*)(lds + SL.et);          // pitch SL.ep
   __shared__ float s_sig[LP];
   __shared__ float s_sinv[LP];
   __shared__ float s_dinv[LP];
@@ -485,17 +511,17 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     __syncthreads();
     for (int it = 0; it <= a.power_iters; ++it) {
       range_step<D, LP>(A, n, lds);
-      orthonormalize<D, LP>(lds, l, s_dinv);
+      orthonormalize<D, LP>(lds, l, GP, s_dinv);
     }
-    orthonormalize<D, LP>(lds, l, s_dinv);
+    orthonormalize<D, LP>(lds, l, GP, s_dinv);
   } else if (n <= D) {
     for (int i = tid; i < LP * D; i += 256) {
       const int j = i / D, d = i - j * D;
       ZT[j * Y::ZP + d] = (j < n) ? bfv(A[(int64_t)j * D + d]) : 0.f;
     }
     __syncthreads();
-    orthonormalize<D, LP>(lds, l, s_dinv);
-    orthonormalize<D, LP>(lds, l, s_dinv);
+    orthonormalize<D, LP>(lds, l, GP, s_dinv);
+    orthonormalize<D, LP>(lds, l, GP, s_dinv);
   } else {
     for (int i = tid; i < LP * D; i += 256) {
       const int j = i / D, d = i - j * D;
@@ -544,7 +570,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
       }
       __syncthreads();
     }
-    for (int i = tid; i < LP * (LP + 1); i += 256) Tm[i] = 0.f;
+    for (int i = tid; i < SL.jp * TP; i += 256) Tm[i] = 0.f;
     __syncthreads();
 #pragma unroll
     for (int bb = 0; bb < MAXB; ++bb) {
@@ -553,7 +579,6 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
         int bj, bi;
         tri_decode(t, bj, bi);
         const int i0 = 2 * bi, j0 = 2 * bj;
-        constexpr int TP = LP + 1;
         Tm[i0 * TP + j0] = (float)acc[bb][0]; Tm[j0 * TP + i0] = (float)acc[bb][0];
         Tm[i0 * TP + j0 + 1] = (float)acc[bb][1]; Tm[(j0 + 1) * TP + i0] = (float)acc[bb][1];
         Tm[(i0 + 1) * TP + j0] = (float)acc[bb][2]; Tm[j0 * TP + i0 + 1] = (float)acc[bb][2];
@@ -562,14 +587,14 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
-  jacobi<LP>(Tm, ET, l, s_rot, s_flag);
+  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
   for (int i = tid; i < l; i += 256) {
-    const float ti = Tm[i * (LP + 1) + i];
+    const float ti = Tm[i * TP + i];
     int rank = 0;
     for (int j = 0; j < l; ++j) {
-      const float tj = Tm[j * (LP + 1) + j];
+      const float tj = Tm[j * TP + j];
       rank += (tj > ti) || (tj == ti && j < i);
     }
     s_perm[rank] = i;
@@ -577,10 +602,10 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   __syncthreads();
   if (tid == 0) {
     const int r = min(R, l);
-    const float top = sqrtf(fmaxf(Tm[s_perm[0] * (LP + 1) + s_perm[0]], 0.f));
+    const float top = sqrtf(fmaxf(Tm[s_perm[0] * TP + s_perm[0]], 0.f));
     int re = 0;
     for (int i = 0; i < r; ++i) {
-      const float sg = sqrtf(fmaxf(Tm[s_perm[i] * (LP + 1) + s_perm[i]], 0.f));
+      const float sg = sqrtf(fmaxf(Tm[s_perm[i] * TP + s_perm[i]], 0.f));
       const bool keep = sg > 1e-6f * top && sg > 0.f;
       s_sig[i] = keep ? sg : 0.f;
       s_sinv[i] = keep ? 1.f / sg : 0.f;
@@ -611,7 +636,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
         for (int k = 0; k < l; ++k) {
           const f32x4 z = *(const f32x4*)(ZT + k * Y::ZP + d0);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[bb][e] += z * ET[col[bb][e] * (LP + 4) + k];
+          for (int e = 0; e < 4; ++e) v[bb][e] += z * ET[col[bb][e] * SL.ep + k];
         }
       }
     }
@@ -681,24 +706,24 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
         int bj, bi;
         tri_decode(t, bj, bi);
         const int i0 = 2 * bi, j0 = 2 * bj;
-        G[i0 * LP + j0] = acc[bb][0]; G[j0 * LP + i0] = acc[bb][0];
-        G[i0 * LP + j0 + 1] = acc[bb][1]; G[(j0 + 1) * LP + i0] = acc[bb][1];
-        G[(i0 + 1) * LP + j0] = acc[bb][2]; G[j0 * LP + i0 + 1] = acc[bb][2];
-        G[(i0 + 1) * LP + j0 + 1] = acc[bb][3]; G[(j0 + 1) * LP + i0 + 1] = acc[bb][3];
+        G[i0 * GP + j0] = acc[bb][0]; G[j0 * GP + i0] = acc[bb][0];
+        G[i0 * GP + j0 + 1] = acc[bb][1]; G[(j0 + 1) * GP + i0] = acc[bb][1];
+        G[(i0 + 1) * GP + j0] = acc[bb][2]; G[j0 * GP + i0 + 1] = acc[bb][2];
+        G[(i0 + 1) * GP + j0 + 1] = acc[bb][3]; G[(j0 + 1) * GP + i0 + 1] = acc[bb][3];
       }
     }
     __syncthreads();
   }
-  cholesky64<LP>(G, re, s_dinv);
+  cholesky64(G, re, GP, s_dinv);
   // L^-1 (lower), column j by thread j, stored transposed in G's upper triangle:
   // Linv[i][j] at G[j][i] (i > j); Linv[j][j] = dinv[j]
   if (tid < re) {
     const int j = tid;
     const float dj = s_dinv[j];
     for (int i = j + 1; i < re; ++i) {
-      float accv = (float)G[i * LP + j] * s_dinv[j] * dj;
-      for (int k = j + 1; k < i; ++k) accv += (float)G[i * LP + k] * s_dinv[k] * (float)G[j * LP + k];
-      G[j * LP + i] = (double)(-accv * s_dinv[i]);
+      float accv = (float)G[i * GP + j] * s_dinv[j] * dj;
+      for (int k = j + 1; k < i; ++k) accv += (float)G[i * GP + k] * s_dinv[k] * (float)G[j * GP + k];
+      G[j * GP + i] = (double)(-accv * s_dinv[i]);
     }
   }
   __syncthreads();
@@ -740,7 +765,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = i0 + e;
-          if (i < re && j <= i) u[e] += up * (j == i ? s_dinv[i] : (float)G[j * LP + i]);
+          if (i < re && j <= i) u[e] += up * (j == i ? s_dinv[i] : (float)G[j * GP + i]);
         }
       }
 #pragma unroll
@@ -793,7 +818,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
 
 template <int D, int LP, bool BATCHED>
 hipError_t launch_lp(const PackArgs& a, dim3 grid, hipStream_t st) {
-  const size_t lds = Lay<D, LP>::bytes;
+  const size_t lds = small_lay<D, LP>(min(a.R + a.oversample, D)).bytes;
   hipError_t e = hipFuncSetAttribute((const void*)rsvd_mfma_kernel<D, LP, BATCHED>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
