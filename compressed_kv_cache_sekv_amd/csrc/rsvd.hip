@@ -25,8 +25,10 @@
 // the range finder, three (fp32 accuracy) for the Rayleigh-Ritz and U.
 // Orthonormalisation is Cholesky-QR with an fp64 Gram matrix and fp64
 // factorisation (columns whose pivot falls below 1e-14 of the largest are
-// dropped as numerically dependent); the basis of the last step gets a
-// second pass.  Grams of C and U accumulate fp32 products in fp64.
+// dropped as numerically dependent); one pass per step keeps the basis
+// orthonormal to ~5e-6 at these sketch widths (the exact-range case, whose
+// Gram is that of A itself, gets a second pass).  Grams of C and U
+// accumulate fp32 products in fp64.
 //
 // Omega ~ N(0, 1) from Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
 // "Parallel random numbers: as easy as 1, 2, 3", SC 2011) keyed by the seed
@@ -292,27 +294,53 @@ __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
 }
 
 // In-place Cholesky (LDL^T form) of the leading m x m block of the symmetric
-// fp64 matrix G (both triangles filled on entry; the lower triangle is
-// updated).  Afterwards L_jk = G[j][k] * dinv[k] (j > k), L_kk = 1 / dinv[k];
-// a pivot at or below 1e-14 of the largest diagonal marks a dependent
-// column: dinv = 0 there.
+// fp64 matrix G (pitch GP; both triangles filled on entry; the lower
+// triangle is updated).  Afterwards L_jk = G[j][k] * dinv[k] (j > k), L_kk =
+// 1 / dinv[k]; a pivot at or below 1e-14 of the largest diagonal marks a
+// dependent column: dinv = 0 there.
+//
+// Right-looking, two columns per barrier: step (k, k + 1) applies both
+// rank-one updates to the trailing block (rows and columns >= k + 2) at once,
+// forming column k + 1 after the first update on the fly from the old
+// values; that column is written back during the next step (nothing reads it
+// there), so the columns being read are never written within a step.
 __device__ void cholesky64(double* G, int m, int GP, float* dinv) {
   double maxd = 0.0;
   for (int i = 0; i < m; ++i) maxd = fmax(maxd, G[i * GP + i]);
   const double tol = 1e-14 * maxd;
+  const int tid = threadIdx.x;
   __syncthreads();
-  // thread t updates row k + 1 + (t >> 2) of the trailing block, columns
-  // k + 1 + (t & 3) + 4 jj up to the diagonal
-  for (int k = 0; k < m; ++k) {
-    const double dk = G[k * GP + k];
-    const double inv = (dk > tol && dk > 0.0) ? 1.0 / dk : 0.0;
-    for (int i = k + 1 + (threadIdx.x >> 2); i < m; i += 64) {
-      const double f = G[i * GP + k] * inv;
-      for (int j = k + 1 + (threadIdx.x & 3); j <= i; j += 4) G[i * GP + j] -= f * G[j * GP + k];
+  auto pivot_inv = [&](double d) { return (d > tol && d > 0.0) ? 1.0 / d : 0.0; };
+  // write back column c (the second of step (c - 1, c)) after its update by column c - 1
+  auto write_back = [&](int c) {
+    const double a = G[c * GP + c - 1], inv0 = pivot_inv(G[(c - 1) * GP + c - 1]);
+    for (int i = c + tid; i < m; i += 256)
+      G[i * GP + c] -= G[i * GP + c - 1] * a * inv0;   // i == c: the diagonal, a * a * inv0
+  };
+  for (int k = 0; k < m; k += 2) {
+    if (k >= 2) write_back(k - 1);
+    if (k + 1 < m) {
+      const double inv0 = pivot_inv(G[k * GP + k]);
+      const double a = G[(k + 1) * GP + k];
+      const double inv1 = pivot_inv(G[(k + 1) * GP + k + 1] - a * a * inv0);
+      for (int i = k + 2 + (tid >> 2); i < m; i += 64) {
+        const double ci0 = G[i * GP + k];
+        const double ci1 = G[i * GP + k + 1] - ci0 * a * inv0;
+        const double f0 = ci0 * inv0, f1 = ci1 * inv1;
+        for (int j = k + 2 + (tid & 3); j <= i; j += 4) {
+          const double cj0 = G[j * GP + k];
+          const double cj1 = G[j * GP + k + 1] - cj0 * a * inv0;
+          G[i * GP + j] -= f0 * cj0 + f1 * cj1;
+        }
+      }
     }
     __syncthreads();
   }
-  for (int k = threadIdx.x; k < m; k += 256) {
+  if (m >= 2 && (m & 1) == 0) {   // the last step's second column
+    write_back(m - 1);
+    __syncthreads();
+  }
+  for (int k = tid; k < m; k += 256) {
     const double dk = G[k * GP + k];
     dinv[k] = (dk > tol && dk > 0.0) ? (float)(1.0 / sqrt(dk)) : 0.f;
   }
@@ -513,7 +541,6 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
       range_step<D, LP>(A, n, lds);
       orthonormalize<D, LP>(lds, l, GP, s_dinv);
     }
-    orthonormalize<D, LP>(lds, l, GP, s_dinv);
   } else if (n <= D) {
     for (int i = tid; i < LP * D; i += 256) {
       const int j = i / D, d = i - j * D;
