@@ -415,12 +415,19 @@ __device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
 // accumulated as the rows of ET (pitch EP): row p of ET is column p of E.  The disjoint
 // pairs of a round (round-robin ordering) rotate together; each 2 x 2 block
 // of T and each 4-element piece of a pair of ET rows is one work item.
-__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* flag) {
+__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* flag,
+                       uint16_t* blk) {
   const int m = l + (l & 1);
   const int np = m >> 1;
   const int nrc = (l + 3) >> 2;
-  const float inv_np = 1.f / (float)max(np, 1), inv_nrc = 1.f / (float)max(nrc, 1);
+  const int nblk = np * (np + 1) / 2;   // pairs of pairs k1 <= k2
+  const float inv_nrc = 1.f / (float)max(nrc, 1);
   for (int i = threadIdx.x; i < JP * EP; i += 256) ET[i] = (i / EP == i % EP) ? 1.f : 0.f;
+  for (int t = threadIdx.x; t < nblk; t += 256) {
+    int k2, k1;
+    tri_decode(t, k2, k1);
+    blk[t] = (uint16_t)(k1 | (k2 << 8));
+  }
   __syncthreads();
   for (int sweep = 0; sweep < 12; ++sweep) {
     if (threadIdx.x == 0) flag[0] = 0;
@@ -447,9 +454,10 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
         rot[k] = f32x4{c, s, __int_as_float(p), __int_as_float(q)};
       }
       __syncthreads();
-      for (int t = threadIdx.x; t < np * np; t += 256) {
-        const int k2 = (int)(((float)t + 0.5f) * inv_np);
-        const int k1 = t - k2 * np;
+      // T is symmetric: each pair of pairs k1 <= k2 updates its 2 x 2 block
+      // and writes the transposed block too
+      for (int t = threadIdx.x; t < nblk; t += 256) {
+        const int kk = blk[t], k1 = kk & 255, k2 = kk >> 8;
         const f32x4 r1 = rot[k1], r2 = rot[k2];
         const float c1 = r1[0], s1 = r1[1], c2 = r2[0], s2 = r2[1];
         const int p1 = __float_as_int(r1[2]), q1 = __float_as_int(r1[3]);
@@ -465,6 +473,12 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
         T[p1 * TP + q2] = z01;
         T[q1 * TP + p2] = z10;
         T[q1 * TP + q2] = z11;
+        if (k1 != k2) {
+          T[p2 * TP + p1] = z00;
+          T[q2 * TP + p1] = z01;
+          T[p2 * TP + q1] = z10;
+          T[q2 * TP + q1] = z11;
+        }
       }
       for (int t = threadIdx.x; t < np * nrc; t += 256) {
         const int k = (int)(((float)t + 0.5f) * inv_nrc);
@@ -507,6 +521,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   __shared__ int s_slot[LP];
   __shared__ int s_flag[2];
   __shared__ f32x4 s_rot[LP / 2 + 1];
+  __shared__ uint16_t s_blk[(LP / 2) * (LP / 2 + 1) / 2];
 
   int S = 0, b = 0, g = 0, which = 0, n;
   const bf16_t* A;
@@ -614,7 +629,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
-  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag);
+  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag, s_blk);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
   for (int i = tid; i < l; i += 256) {
