@@ -443,9 +443,13 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
         float c = 1.f, s = 0.f;
         if (p < l && q < l) {
           const float apq = T[p * TP + q], app = T[p * TP + p], aqq = T[q * TP + q];
-          if (fabsf(apq) > 1e-7f * sqrtf(fabsf(app * aqq)) && fabsf(apq) > 1e-30f) {
-            const float th = (aqq - app) / (2.f * apq);
-            const float t = (th >= 0.f ? 1.f : -1.f) / (fabsf(th) + sqrtf(1.f + th * th));
+          // rotate when |apq| > 1e-7 sqrt|app aqq| (squared: no root); the
+          // angle from hardware reciprocal and root, since c and s are then
+          // formed from t as an exact rotation (c^2 + s^2 = 1 to rounding)
+          if (apq * apq > 1e-14f * fabsf(app * aqq) && fabsf(apq) > 1e-30f) {
+            const float th = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+            const float t = (th >= 0.f ? 1.f : -1.f) *
+                            __builtin_amdgcn_rcpf(fabsf(th) + __builtin_amdgcn_sqrtf(1.f + th * th));
             c = rsqrtf(1.f + t * t);
             s = t * c;
             flag[0] = 1;
