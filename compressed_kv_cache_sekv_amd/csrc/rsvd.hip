@@ -416,7 +416,7 @@ __device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
 // pairs of a round (round-robin ordering) rotate together; each 2 x 2 block
 // of T and each 4-element piece of a pair of ET rows is one work item.
 __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* flag,
-                       uint16_t* blk) {
+                       uint16_t* blk, int* rflag) {
   const int m = l + (l & 1);
   const int np = m >> 1;
   const int nrc = (l + 3) >> 2;
@@ -428,11 +428,15 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
     tri_decode(t, k2, k1);
     blk[t] = (uint16_t)(k1 | (k2 << 8));
   }
+  // rflag[r & 1]: a pair of round r rotates (a round without rotation skips
+  // its updates); the other slot is cleared during the round for the next
+  if (threadIdx.x < 2) rflag[threadIdx.x] = 0;
   __syncthreads();
+  int r_all = 0;
   for (int sweep = 0; sweep < 12; ++sweep) {
     if (threadIdx.x == 0) flag[0] = 0;
     __syncthreads();
-    for (int rnd = 0; rnd + 1 < m; ++rnd) {
+    for (int rnd = 0; rnd + 1 < m; ++rnd, ++r_all) {
       if (threadIdx.x < np) {
         const int k = threadIdx.x;
         int pp = k - 1 + rnd;
@@ -453,11 +457,18 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
             c = rsqrtf(1.f + t * t);
             s = t * c;
             flag[0] = 1;
+            rflag[r_all & 1] = 1;
           }
         }
         rot[k] = f32x4{c, s, __int_as_float(p), __int_as_float(q)};
       }
       __syncthreads();
+      const bool rotates = rflag[r_all & 1] != 0;
+      if (threadIdx.x == 0) rflag[(r_all + 1) & 1] = 0;
+      if (!rotates) {
+        __syncthreads();
+        continue;
+      }
       // T is symmetric: each pair of pairs k1 <= k2 updates its 2 x 2 block
       // and writes the transposed block too
       for (int t = threadIdx.x; t < nblk; t += 256) {
@@ -526,6 +537,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   __shared__ int s_flag[2];
   __shared__ f32x4 s_rot[LP / 2 + 1];
   __shared__ uint16_t s_blk[(LP / 2) * (LP / 2 + 1) / 2];
+  __shared__ int s_rflag[2];
 
   int S = 0, b = 0, g = 0, which = 0, n;
   const bf16_t* A;
@@ -633,7 +645,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
-  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag, s_blk);
+  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag, s_blk, s_rflag);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
   for (int i = tid; i < l; i += 256) {
