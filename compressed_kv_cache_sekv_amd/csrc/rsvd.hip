@@ -151,7 +151,8 @@ struct Lay {
 // widths up to lmax (<= LP), where E^T goes, and the workgroup's LDS bytes.
 struct SmallLay {
   int jp, tp, ep;      // G pitch and Jacobi size (even), T pitch, E^T pitch
-  size_t et;           // byte offset of E^T
+  size_t et;           // byte offset of E^T, followed by the Jacobi's rotation
+                       // list (jp / 2 + 1 f32x4) and pair table (uint16)
   size_t bytes;        // dynamic LDS of the workgroup
 };
 template <int D, int LP>
@@ -161,7 +162,9 @@ __host__ __device__ inline SmallLay small_lay(int lmax) {
   r.jp = lmax + (lmax & 1);
   r.tp = r.jp + 1;
   r.ep = ((r.jp + 3) & ~3) + 4;
-  const size_t gb = (size_t)r.jp * r.jp * 8, tb = (size_t)r.jp * r.tp * 4, eb = (size_t)r.jp * r.ep * 4;
+  const int np = r.jp / 2;
+  const size_t gb = (size_t)r.jp * r.jp * 8, tb = (size_t)r.jp * r.tp * 4;
+  const size_t eb = (size_t)r.jp * r.ep * 4 + (size_t)(np + 1) * 16 + (((size_t)np * (np + 1) + 15) & ~(size_t)15);
   if (eb <= Y::g - Y::x) {
     r.et = Y::x;
     r.bytes = Y::g + (gb > tb ? gb : tb);
@@ -535,8 +538,6 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   __shared__ int s_perm[LP];
   __shared__ int s_slot[LP];
   __shared__ int s_flag[2];
-  __shared__ f32x4 s_rot[LP / 2 + 1];
-  __shared__ uint16_t s_blk[(LP / 2) * (LP / 2 + 1) / 2];
   __shared__ int s_rflag[2];
 
   int S = 0, b = 0, g = 0, which = 0, n;
@@ -645,6 +646,9 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
+  // the rotation list and pair table follow E^T (the staging region is idle)
+  f32x4* s_rot = (f32x4*)(ET + (size_t)SL.jp * SL.ep);
+  uint16_t* s_blk = (uint16_t*)(s_rot + SL.jp / 2 + 1);
   jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag, s_blk, s_rflag);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
