@@ -122,7 +122,8 @@ struct Chunk {
 //       or Lf float [LP][LP] (Cholesky factor, fp32 copy, during orth)
 //   G   double [JP][JP]  Gram / Cholesky factor (lower), L^-1 (upper);
 //       or T float [JP][JP + 1] (Jacobi), with E^T float [JP][EP] in X when
-//       it fits there (X is idle during the Jacobi), else after T.
+//       it fits there (X is idle during the Jacobi), else after T;
+//       finally Lt float [LP][LP] (L^-T for U, at least this many bytes).
 //   JP = the largest sketch width min(R + p, d) rounded up to even, so the
 //   small-matrix region is sized by the sketch, not by its 16-wide padding
 //   (at R = 32, p = 8: 40 instead of 48; this region decides how many
@@ -172,6 +173,9 @@ __host__ __device__ inline SmallLay small_lay(int lmax) {
     r.et = Y::g + ((tb + 15) & ~(size_t)15);
     r.bytes = r.et + eb > Y::g + gb ? r.et + eb : Y::g + gb;
   }
+  // the fp32 L^-T table of the U step, [LP][LP] over the G region
+  const size_t lt = (size_t)LP * LP * 4;
+  if (r.bytes < Y::g + lt) r.bytes = Y::g + lt;
   return r;
 }
 
@@ -560,7 +564,6 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = a.R;
   const int l = min(R + a.oversample, min(n, D));
-  const int nch = (n + kNC - 1) / kNC;
 
   // ---- orthonormal basis Z of the (approximate) dominant right singular subspace
   if (l < min(n, D)) {
@@ -813,38 +816,100 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
-  const int nbi = (re + 3) >> 2;
-  for (int c0 = 0; c0 < n; c0 += kNC) {
-    if (nch > 1) u_chunk(c0);
-    for (int t = tid; t < kNC * nbi; t += 256) {
-      const int r = t % kNC, i0 = 4 * (t / kNC);
-      const int row = c0 + r;
-      if (row >= n) continue;
-      float u[4] = {0.f, 0.f, 0.f, 0.f};
-      const int jmax = min(i0 + 4, re);
-      for (int j = 0; j < jmax; ++j) {
-        const float up = CT[j * Y::CTP + r];
+  // right factors and sigma (m)
+  if (BATCHED) {
+    float* Vo = a.out_Vt + mat * (int64_t)R * D;
+    for (int idx = tid; idx < R * D; idx += 256) {
+      const int i = idx / D, d = idx - i * D;
+      Vo[idx] = (i < re) ? ZT[i * Y::ZP + d] : 0.f;
+    }
+    for (int i = tid; i < R; i += 256) a.out_S[mat * R + i] = (i < re) ? s_sig[i] : 0.f;
+  } else {
+    // K -> VKt [rk][D] krow layout, V -> VV [D][rv] a16 layout
+    bf16_t* Vo = (bf16_t*)(blob + (which ? Blob::off_vv(rk, D) : Blob::off_vkt()));
+    for (int idx = tid; idx < D * re; idx += 256) {
+      const int i = idx / D, d = idx - i * D;
+      const int sl = s_slot[i];
+      if (sl < 0) continue;
+      const int64_t o = which ? a16_off(d, sl, rv) : krow_off(sl, d, D);
+      Vo[o] = to_bf(ZT[i * Y::ZP + d]);
+    }
+    float* sm = (float*)(blob + (which ? Blob::off_smv(rk, rv, D) : Blob::off_smk(rk, rv, D)));
+    for (int i = tid; i < R; i += 256) {
+      const int sl = s_slot[i];
+      if (sl < 0) continue;
+      const float m = a.gates ? a.gates[mat * (int64_t)R + i] : 1.f;
+      sm[sl] = (i < re) ? s_sig[i] * m : 0.f;
+    }
+  }
+
+  // L^-T as an fp32 table over the G region: Lt[k][i] = Linv[i][k] for
+  // k <= i < re, else 0 (read from G into registers, then written over it)
+  float* Lt = (float*)G;
+  {
+    constexpr int NE = (LP * LP + 255) / 256;
+    float lt[NE];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          if (i < re && j <= i) u[e] += up * (j == i ? s_dinv[i] : (float)G[j * GP + i]);
+    for (int c = 0; c < NE; ++c) {
+      const int e = tid + 256 * c, k = e / LP, i = e - k * LP;
+      lt[c] = (e < LP * LP && i < re && k <= i) ? (k == i ? s_dinv[i] : (float)G[k * GP + i]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NE; ++c)
+      if (tid + 256 * c < LP * LP) Lt[tid + 256 * c] = lt[c];
+    __syncthreads();
+  }
+
+  // ---- U = U' L^-T, one staged chunk of rows at a time: U' as in the Gram
+  // pass (the same products, so the same values), then the triangular factor
+  // on the fp32 MFMA (16x16x4: A[i][k] and B[k][j] at lane i (j) + 16 k).
+  {
+    constexpr int NT = (kNRT * NJT + 3) / 4;   // output tiles per wave
+    const int kend = (re + 3) & ~3;            // rows re.. of CT and Lt are zero
+    for (int c0 = 0; c0 < n; c0 += kNC) {
+      u_chunk(c0);
+      f32x4 ut[NT];
+#pragma unroll
+      for (int q = 0; q < NT; ++q) {
+        ut[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int t = wave + 4 * q;
+        if (t < kNRT * NJT) {
+          const int rt = t / NJT, jt = t - rt * NJT;
+          for (int k0 = 0; k0 < kend; k0 += 4) {
+            const int k = k0 + (lane >> 4);
+            const float av = CT[k * Y::CTP + rt * 16 + (lane & 15)];
+            const float bv = Lt[k * LP + jt * 16 + (lane & 15)];
+            ut[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, ut[q], 0, 0, 0);
+          }
         }
       }
+      __syncthreads();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        if (i >= re) continue;
+      for (int q = 0; q < NT; ++q) {
+        const int t = wave + 4 * q;
+        if (t < kNRT * NJT) {
+          const int rt = t / NJT, jt = t - rt * NJT;
+          *(f32x4*)(CT + (jt * 16 + (lane & 15)) * Y::CTP + rt * 16 + 4 * (lane >> 4)) = ut[q];
+        }
+      }
+      __syncthreads();
+      for (int t = tid; t < kNC * re; t += 256) {
+        const int i = t / kNC, r = t - i * kNC;
+        const int row = c0 + r;
+        if (row >= n) continue;
+        const float u = CT[i * Y::CTP + r];
         if (BATCHED) {
-          a.out_U[(mat * (int64_t)a.max_rows + row) * R + i] = u[e];
+          a.out_U[(mat * (int64_t)a.max_rows + row) * R + i] = u;
         } else {
           const int sl = s_slot[i];
           if (sl < 0) continue;
           bf16_t* Uo = (bf16_t*)(blob + (which ? Blob::off_uvt(rk, rv, D, n) : Blob::off_uk(rk, rv, D)));
-          Uo[which ? a16_off(sl, row, npad) : a16_off(row, sl, rk)] = to_bf(u[e]);
+          Uo[which ? a16_off(sl, row, npad) : a16_off(row, sl, rk)] = to_bf(u);
         }
       }
+      __syncthreads();
     }
-    if (nch > 1) __syncthreads();
   }
   if (BATCHED) {
     float* Uo = a.out_U + mat * (int64_t)a.max_rows * R;
@@ -852,29 +917,6 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
       const int row = idx / R, i = idx - row * R;
       if (row >= n || i >= re) Uo[idx] = 0.f;
     }
-    float* Vo = a.out_Vt + mat * (int64_t)R * D;
-    for (int idx = tid; idx < R * D; idx += 256) {
-      const int i = idx / D, d = idx - i * D;
-      Vo[idx] = (i < re) ? ZT[i * Y::ZP + d] : 0.f;
-    }
-    for (int i = tid; i < R; i += 256) a.out_S[mat * R + i] = (i < re) ? s_sig[i] : 0.f;
-    return;
-  }
-  // right factors: K -> VKt [rk][D] krow layout, V -> VV [D][rv] a16 layout
-  bf16_t* Vo = (bf16_t*)(blob + (which ? Blob::off_vv(rk, D) : Blob::off_vkt()));
-  for (int idx = tid; idx < D * re; idx += 256) {
-    const int i = idx / D, d = idx - i * D;
-    const int sl = s_slot[i];
-    if (sl < 0) continue;
-    const int64_t o = which ? a16_off(d, sl, rv) : krow_off(sl, d, D);
-    Vo[o] = to_bf(ZT[i * Y::ZP + d]);
-  }
-  float* sm = (float*)(blob + (which ? Blob::off_smv(rk, rv, D) : Blob::off_smk(rk, rv, D)));
-  for (int i = tid; i < R; i += 256) {
-    const int sl = s_slot[i];
-    if (sl < 0) continue;
-    const float m = a.gates ? a.gates[mat * (int64_t)R + i] : 1.f;
-    sm[sl] = (i < re) ? s_sig[i] * m : 0.f;
   }
 }
 
