@@ -119,7 +119,7 @@ struct Chunk {
 //       then At bf16 [D/16][kNRT][64][4] (A^T operand) + Yb hi/lo
 //            bf16 [kNRT][LP/16][64][4] each (range finder),
 //       or CT float [LP][kNC + 4] (a chunk of A Z or of U'),
-//       or Lf float [LP][LP] (Cholesky factor, fp32 copy, during orth)
+//       or Lf float [LP][LP] (Cholesky factor transposed, fp32, during orth)
 //   G   double [JP][JP]  Gram / Cholesky factor (lower), L^-1 (upper);
 //       or T float [JP][JP + 1] (Jacobi), with E^T float [JP][EP] in X when
 //       it fits there (X is idle during the Jacobi), else after T;
@@ -312,22 +312,28 @@ __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
 // values; that column is written back during the next step (nothing reads it
 // there), so the columns being read are never written within a step.
 __device__ void cholesky64(double* G, int m, int GP, float* dinv) {
+  // largest diagonal: each wave reads it in parallel and reduces by shuffles
   double maxd = 0.0;
-  for (int i = 0; i < m; ++i) maxd = fmax(maxd, G[i * GP + i]);
+  for (int i = threadIdx.x & 63; i < m; i += 64) maxd = fmax(maxd, G[i * GP + i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) maxd = fmax(maxd, __shfl_xor(maxd, o));
   const double tol = 1e-14 * maxd;
   const int tid = threadIdx.x;
   __syncthreads();
   auto pivot_inv = [&](double d) { return (d > tol && d > 0.0) ? 1.0 / d : 0.0; };
-  // write back column c (the second of step (c - 1, c)) after its update by column c - 1
-  auto write_back = [&](int c) {
-    const double a = G[c * GP + c - 1], inv0 = pivot_inv(G[(c - 1) * GP + c - 1]);
+  // write back column c (the second of step (c - 1, c)) after its update by
+  // column c - 1, whose pivot inverse inv0 the previous step formed
+  auto write_back = [&](int c, double inv0) {
+    const double a = G[c * GP + c - 1];
     for (int i = c + tid; i < m; i += 256)
       G[i * GP + c] -= G[i * GP + c - 1] * a * inv0;   // i == c: the diagonal, a * a * inv0
   };
+  double inv_prev = 0.0;   // pivot inverse of the first column of the previous step
   for (int k = 0; k < m; k += 2) {
-    if (k >= 2) write_back(k - 1);
+    if (k >= 2) write_back(k - 1, inv_prev);
     if (k + 1 < m) {
       const double inv0 = pivot_inv(G[k * GP + k]);
+      inv_prev = inv0;
       const double a = G[(k + 1) * GP + k];
       const double inv1 = pivot_inv(G[(k + 1) * GP + k + 1] - a * a * inv0);
       for (int i = k + 2 + (tid >> 2); i < m; i += 64) {
@@ -344,7 +350,7 @@ __device__ void cholesky64(double* G, int m, int GP, float* dinv) {
     __syncthreads();
   }
   if (m >= 2 && (m & 1) == 0) {   // the last step's second column
-    write_back(m - 1);
+    write_back(m - 1, inv_prev);
     __syncthreads();
   }
   for (int k = tid; k < m; k += 256) {
@@ -390,8 +396,9 @@ __device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
   }
   __syncthreads();
   cholesky64(G, m, GP, dinv);
+  // Lf[j][k] = L[k][j] (j < k < m): row j holds the multipliers of column j
   for (int e = threadIdx.x; e < LP * LP; e += 256) {
-    const int k = e / LP, j = e - k * LP;
+    const int j = e / LP, k = e - j * LP;
     Lf[e] = (j < k && k < m) ? (float)G[k * GP + j] * dinv[j] : 0.f;
   }
   __syncthreads();
@@ -406,7 +413,7 @@ __device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
         const float zj = w[j] * dinv[j];
         w[j] = zj;
 #pragma unroll
-        for (int k = j + 1; k < LP; ++k) w[k] -= Lf[k * LP + j] * zj;
+        for (int k = j + 1; k < LP; ++k) w[k] -= Lf[j * LP + k] * zj;
       } else {
         w[j] = 0.f;
       }
