@@ -238,7 +238,7 @@ __device__ __forceinline__ f32x4 az_tile(const bf16_t* Ar, const float* ZT, int 
 
 // ZT <- rows of A^T (A Z) (all columns of Z; unused columns of Z are zero).
 template <int D, int LP>
-__device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
+__device__ __forceinline__ void range_step_body(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
   constexpr int kNC = Chunk<LP>::NC, kNRT = Chunk<LP>::NRT;
   using Y = Lay<D, LP>;
   constexpr int NJT = LP / 16, NDT = D / 16, DTW = (NDT + 3) / 4;
@@ -298,6 +298,16 @@ __device__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
     }
   }
   __syncthreads();
+}
+
+template <int D, int LP>
+__device__ __noinline__ void range_step_call(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
+  range_step_body<D, LP>(A, n, lds);
+}
+template <int D, int LP>
+__device__ __forceinline__ void range_step(const bf16_t* __restrict__ A, int n, uint8_t* lds) {
+  if constexpr (LP >= 48) range_step_body<D, LP>(A, n, lds);
+  else range_step_call<D, LP>(A, n, lds);
 }
 
 // In-place Cholesky (LDL^T form) of the leading m x m block of the symmetric
@@ -363,7 +373,7 @@ __device__ void cholesky64(double* G, int m, int GP, float* dinv) {
 // Orthonormalise the first m rows of ZT (columns of Z, length D) in place:
 // Cholesky-QR, Z <- Z L^-T.  Rows m..LP-1 of ZT are zero on entry and exit.
 template <int D, int LP>
-__device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
+__device__ __forceinline__ void orthonormalize_body(uint8_t* lds, int m, int GP, float* dinv) {
   using Y = Lay<D, LP>;
   float* ZT = (float*)(lds + Y::zt);
   double* G = (double*)(lds + Y::g);
@@ -422,6 +432,20 @@ __device__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
     for (int j = 0; j < LP; ++j) ZT[j * Y::ZP + d] = w[j];
   }
   __syncthreads();
+}
+
+template <int D, int LP>
+__device__ __noinline__ void orthonormalize_call(uint8_t* lds, int m, int GP, float* dinv) {
+  orthonormalize_body<D, LP>(lds, m, GP, dinv);
+}
+// Inlined into the kernel for sketches of 48 columns and more (measured 18.4
+// -> 18.0 ms per 128K layer at R = 32, and fewer registers than the call
+// needs); a call for narrower ones, whose kernels would otherwise grow past
+// the 128 registers that four workgroups per CU allow.
+template <int D, int LP>
+__device__ __forceinline__ void orthonormalize(uint8_t* lds, int m, int GP, float* dinv) {
+  if constexpr (LP >= 48) orthonormalize_body<D, LP>(lds, m, GP, dinv);
+  else orthonormalize_call<D, LP>(lds, m, GP, dinv);
 }
 
 // Cyclic Jacobi eigen-decomposition of the symmetric l x l matrix T (pitch
