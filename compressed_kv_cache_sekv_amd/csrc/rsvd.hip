@@ -453,8 +453,8 @@ __device__ __forceinline__ void orthonormalize(uint8_t* lds, int m, int GP, floa
 // accumulated as the rows of ET (pitch EP): row p of ET is column p of E.  The disjoint
 // pairs of a round (round-robin ordering) rotate together; each 2 x 2 block
 // of T and each 4-element piece of a pair of ET rows is one work item.
-__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* flag,
-                       uint16_t* blk, int* rflag) {
+__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, uint16_t* blk,
+                       int* rflag) {
   const int m = l + (l & 1);
   const int np = m >> 1;
   const int nrc = (l + 3) >> 2;
@@ -472,8 +472,21 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
   __syncthreads();
   int r_all = 0;
   for (int sweep = 0; sweep < 12; ++sweep) {
-    if (threadIdx.x == 0) flag[0] = 0;
-    __syncthreads();
+    // a sweep rotates iff some pair meets the rotation test on the sweep's
+    // starting T (a round without rotation leaves T as it was): after the
+    // first sweep, one pass over the pairs decides it instead of a sweep of
+    // rounds that all skip
+    if (sweep > 0) {
+      int need = 0;
+      for (int e = threadIdx.x; e < l * l; e += 256) {
+        const int p = e / l, q = e - p * l;
+        if (p < q) {
+          const float apq = T[p * TP + q], app = T[p * TP + p], aqq = T[q * TP + q];
+          need |= (apq * apq > 1e-14f * fabsf(app * aqq) && fabsf(apq) > 1e-30f);
+        }
+      }
+      if (!__syncthreads_or(need)) break;
+    }
     for (int rnd = 0; rnd + 1 < m; ++rnd, ++r_all) {
       if (threadIdx.x < np) {
         const int k = threadIdx.x;
@@ -494,7 +507,6 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
                             __builtin_amdgcn_rcpf(fabsf(th) + __builtin_amdgcn_sqrtf(1.f + th * th));
             c = rsqrtf(1.f + t * t);
             s = t * c;
-            flag[0] = 1;
             rflag[r_all & 1] = 1;
           }
         }
@@ -546,9 +558,6 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
       }
       __syncthreads();
     }
-    const int any = flag[0];
-    __syncthreads();
-    if (!any) break;
   }
 }
 
@@ -683,7 +692,7 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
   // the rotation list and pair table follow E^T (the staging region is idle)
   f32x4* s_rot = (f32x4*)(ET + (size_t)SL.jp * SL.ep);
   uint16_t* s_blk = (uint16_t*)(s_rot + SL.jp / 2 + 1);
-  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_flag, s_blk, s_rflag);
+  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_blk, s_rflag);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
   for (int i = tid; i < l; i += 256) {
