@@ -244,58 +244,107 @@ __device__ __forceinline__ bf16_t f64_to_bf16(double x) {
 // row in bf16, and s^(l,h) = W^(l,h) kbar in fp64 from the unrounded kbar,
 // stored fp32, for the G query heads of KV head g.  grid (ceil(max_spans/4),
 // B, L*Hkv).
+//  * Means: a row of d bf16 is d / 8 lanes of 16 bytes, so one load covers
+//    64 / (d / 8) rows; each lane keeps kU loads of K and of V in flight (16
+//    rows a round at d = 128), accumulates its 8 dims in fp64, and the row
+//    slots are summed by shuffles at the end.
+//  * s: thread o takes output (head, j) for all four spans of the workgroup,
+//    so each W row is read once per workgroup (16-byte loads, 8 in flight),
+//    summed over d in order as before.
 __global__ __launch_bounds__(256) void summaries_kernel(const PackArgs a) {
+  constexpr int kU = 4;
   __shared__ double s_k[4][128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int S = blockIdx.x * 4 + wave, b = blockIdx.y, lg = blockIdx.z;
+  const int S0 = blockIdx.x * 4, S = S0 + wave, b = blockIdx.y, lg = blockIdx.z;
   const int l = lg / a.Hkv, g = lg - l * a.Hkv, D = a.D;
   const BMeta bm = a.meta[b];
-  const bool live = S < bm.n_spans;
-  if (live) {
+  const int CL = D >> 3, RS = 64 / CL;   // lanes per row, rows per load
+  const int c = lane % CL, rs = lane / CL;
+  if (S < bm.n_spans) {
     const int start = a.span_start[bm.span_base + S], n = a.span_len[bm.span_base + S];
     const float* H = a.H + (int64_t)b * a.T + start;
-    const int64_t src = (((int64_t)b * a.L * a.Hkv + lg) * a.T + start) * D;
+    const int64_t src = (((int64_t)b * a.L * a.Hkv + lg) * a.T + start) * D + 8 * c;
     const bf16_t* K = a.K + src;
     const bf16_t* V = a.V + src;
-    const int per = D >> 6;  // dims per lane: 1 (d=64) or 2 (d=128)
-    double ak[2] = {0.0, 0.0}, av[2] = {0.0, 0.0}, ws = 0.0;
-    for (int t = 0; t < n; ++t) {
-      const double w = (double)H[t];
-      ws += w;
-      for (int e = 0; e < per; ++e) {
-        ak[e] += w * (double)bf(K[(int64_t)t * D + per * lane + e]);
-        av[e] += w * (double)bf(V[(int64_t)t * D + per * lane + e]);
-      }
-    }
-    if (ws == 0.0) {
-      ws = (double)n;
-      ak[0] = ak[1] = av[0] = av[1] = 0.0;
-      for (int t = 0; t < n; ++t)
-        for (int e = 0; e < per; ++e) {
-          ak[e] += (double)bf(K[(int64_t)t * D + per * lane + e]);
-          av[e] += (double)bf(V[(int64_t)t * D + per * lane + e]);
+    double ak[8], av[8], ws;
+    auto accumulate = [&](bool uniform) {
+      ws = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ak[e] = av[e] = 0.0;
+      for (int t0 = 0; t0 < n; t0 += kU * RS) {
+        uint4 kv[kU], vv[kU];
+        float hv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {   // rows past the span re-read its last row (unused)
+          const int t = min(t0 + rs + u * RS, n - 1);
+          kv[u] = *(const uint4*)(K + (int64_t)t * D);
+          vv[u] = *(const uint4*)(V + (int64_t)t * D);
+          hv[u] = H[t];
         }
-    }
-    const int64_t dst = bm.res_base + (int64_t)lg * bm.n_res_pad * D;
-    const int prow = bm.n_raw + S;
-    for (int e = 0; e < per; ++e) {
-      const int dim = per * lane + e;
-      const double kb = ak[e] / ws, vb = av[e] / ws;
-      s_k[wave][dim] = kb;
-      a.kres[dst + krow_off(prow, dim, D)] = f64_to_bf16(kb);
-      a.vres[dst + vrow_off(prow, dim, D)] = f64_to_bf16(vb);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          if (t0 + rs + u * RS >= n) continue;
+          const double w = uniform ? 1.0 : (double)hv[u];
+          ws += w;
+          const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+          const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t kb = (e & 1) ? (kw[e >> 1] & 0xffff0000u) : (kw[e >> 1] << 16);
+            const uint32_t vb = (e & 1) ? (vw[e >> 1] & 0xffff0000u) : (vw[e >> 1] << 16);
+            ak[e] += w * (double)__uint_as_float(kb);
+            av[e] += w * (double)__uint_as_float(vb);
+          }
+        }
+      }
+      for (int o = CL; o < 64; o <<= 1) {   // sum the row slots
+        ws += __shfl_xor(ws, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ak[e] += __shfl_xor(ak[e], o);
+          av[e] += __shfl_xor(av[e], o);
+        }
+      }
+    };
+    accumulate(false);
+    if (ws == 0.0) accumulate(true);   // the same in every lane
+    if (rs == 0) {
+      const int64_t dst = bm.res_base + (int64_t)lg * bm.n_res_pad * D;
+      const int prow = bm.n_raw + S;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int dim = 8 * c + e;
+        const double kb = ak[e] / ws, vb = av[e] / ws;
+        s_k[wave][dim] = kb;
+        a.kres[dst + krow_off(prow, dim, D)] = f64_to_bf16(kb);
+        a.vres[dst + vrow_off(prow, dim, D)] = f64_to_bf16(vb);
+      }
     }
   }
   __syncthreads();
-  if (!live) return;
-  const int G = a.Hq / a.Hkv;
-  for (int o = lane; o < G * a.dp; o += 64) {
+  const int nlive = min(4, bm.n_spans - S0);
+  if (nlive <= 0) return;
+  const int G = a.Hq / a.Hkv, d4 = dp_pad4(a.dp);
+  for (int o = threadIdx.x; o < G * a.dp; o += 256) {
     const int hh = g * G + o / a.dp, j = o - (o / a.dp) * a.dp;
-    const float* w = a.W + (((int64_t)l * a.Hq + hh) * a.dp + j) * D;
-    double acc = 0.0;
-    for (int d = 0; d < D; ++d) acc += (double)w[d] * s_k[wave][d];
-    const int d4 = dp_pad4(a.dp);
-    a.s[bm.s_base + ((int64_t)l * a.Hq + hh) * d4 * bm.s_pad + skey_index(S, j, d4)] = (float)acc;
+    const float4* w4 = (const float4*)(a.W + (((int64_t)l * a.Hq + hh) * a.dp + j) * D);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int q0 = 0; q0 < D / 4; q0 += 8) {
+      float4 wv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) wv[u] = w4[q0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int d = 4 * (q0 + u);
+        const float wx[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int sp = 0; sp < 4; ++sp) acc[sp] += (double)wx[e] * s_k[sp][d + e];
+      }
+    }
+    for (int sp = 0; sp < nlive; ++sp)
+      a.s[bm.s_base + ((int64_t)l * a.Hq + hh) * d4 * bm.s_pad + skey_index(S0 + sp, j, d4)] = (float)acc[sp];
   }
 }
 

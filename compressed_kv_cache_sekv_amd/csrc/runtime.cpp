@@ -229,6 +229,10 @@ struct sekv_index {
 
 namespace {
 
+// The kernels read q, K, V and W with 16-byte vector loads and the masks as
+// 64-bit words.
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
 sekv_status check_ctx(const sekv_ctx* c) {
   if (!c) return fail(SEKV_EINVAL, "null context");
   if (!is_live(c) || c->magic != CTX_MAGIC) return fail(SEKV_ESTATE, "context is not live");
@@ -636,6 +640,8 @@ extern "C" sekv_status sekv_build_index(sekv_ctx* c, const sekv_build_params* p,
   *out = nullptr;
   if ((st = check_shape(p, true))) return st;
   if (!K || !V || !H || !W) return fail(SEKV_EINVAL, "null K, V, H or W");
+  if (!aligned(K, 16) || !aligned(V, 16) || !aligned(W, 16))
+    return fail(SEKV_EINVAL, "K, V and W must be 16-byte aligned");
   if ((st = set_device(c))) return st;
   hipStream_t stream = c->stream;
   const int B = p->B, T = p->T;
@@ -1125,6 +1131,7 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !tau || !mask) return fail(SEKV_EINVAL, "null q, tau or mask");
+  if (!aligned(q, 16) || !aligned(mask, 8)) return fail(SEKV_EINVAL, "q must be 16-byte and mask 8-byte aligned");
   if (cap < 0) return fail(SEKV_EINVAL, "cap < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
@@ -1156,6 +1163,7 @@ extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int3
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !tau || !mask) return fail(SEKV_EINVAL, "null q, tau or mask");
+  if (!aligned(q, 16) || !aligned(mask, 8)) return fail(SEKV_EINVAL, "q must be 16-byte and mask 8-byte aligned");
   if (budget < 0) return fail(SEKV_EINVAL, "budget < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
@@ -1188,6 +1196,7 @@ extern "C" sekv_status sekv_calibrate_tau(sekv_ctx* c, const sekv_index* xc, int
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q_cal || !tau_out) return fail(SEKV_EINVAL, "null q_cal or tau_out");
+  if (!aligned(q_cal, 16)) return fail(SEKV_EINVAL, "q_cal must be 16-byte aligned");
   if (!(frac >= 0.f && frac <= 1.f)) return fail(SEKV_EINVAL, "frac must be in [0, 1]");
   if (x->total_spans < 2) return fail(SEKV_EINVAL, "calibration needs at least 2 spans");
   if ((st = set_device(c))) return st;
@@ -1386,6 +1395,7 @@ extern "C" sekv_status sekv_decode_attend(sekv_ctx* c, const sekv_index* xc, int
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if (!aligned(q, 16) || !aligned(mask, 8)) return fail(SEKV_EINVAL, "q must be 16-byte and mask 8-byte aligned");
   if ((st = check_ring(x))) return st;
   if ((st = set_device(c))) return st;
   HIP_TRY(dgrow(x->d_part, part_bytes(x, lc)));
@@ -1405,6 +1415,7 @@ extern "C" sekv_status sekv_decode_attend_noalloc(sekv_ctx* c, const sekv_index*
   if (st) return st;
   if ((st = check_layers(x, lb, lc))) return st;
   if (!q || !mask || !out) return fail(SEKV_EINVAL, "null q, mask or out");
+  if (!aligned(q, 16) || !aligned(mask, 8)) return fail(SEKV_EINVAL, "q must be 16-byte and mask 8-byte aligned");
   if (x->tier != SEKV_TIER_HBM)
     return fail(SEKV_EUNSUPPORTED, "the no-allocation decode serves the HBM tier only");
   const size_t need = part_bytes(x, lc);

@@ -200,9 +200,11 @@ sekv_status sekv_validate_params(const sekv_build_params* p);
  * and KV head, computed by randomized subspace iteration ([Method]: the
  * randomized truncated SVD that parallelises prefill; [Tech]).  Anchors and
  * runs shorter than l_min stay raw ([Method]).
- *   K, V   device bf16 [B][L][Hkv][T][d]
+ *   K, V   device bf16 [B][L][Hkv][T][d], 16-byte aligned
  *   H      device fp32 [B][T]  token surprisal (>= 0, finite)
- *   W      device fp32 [L][Hq][d'][d]  routing projection (copied into the index)
+ *   W      device fp32 [L][Hq][d'][d]  routing projection (copied into the
+ *          index), 16-byte aligned
+ *   (a misaligned K, V or W is SEKV_EINVAL, refused before any work)
  *   gates  device fp32 [B][L][Hkv][2 (K|V)][S_max][R] component gates m, span
  *          ordinal S using slot S, S_max = sekv_max_spans(T, l_min); or NULL
  *          for m = 1.  sigma*m is stored.
@@ -272,10 +274,11 @@ void sekv_index_free(sekv_index* idx);
  * expansions keeps the cap largest a_S (the order of alpha), ties to the
  * lower span index ([Tech]: spans taken in descending alpha until the budget
  * holds).
- *   q      device bf16 [B][layer_count][Hq][d]
+ *   q      device bf16 [B][layer_count][Hq][d], 16-byte aligned
  *   tau    device fp32 [layer_count][Hq]  (+-inf allowed)
- *   mask   device uint64 [B][layer_count][Hq][mask_words]; bit j of word w is
- *          z of span 64w + j; bits at or past N_S(b) are 0
+ *   mask   device uint64 [B][layer_count][Hq][mask_words], 8-byte aligned;
+ *          bit j of word w is z of span 64w + j; bits at or past N_S(b) are 0
+ *   (a misaligned q or mask is SEKV_EINVAL, refused before any work)
  *   alpha  device fp32 [B][layer_count][Hq][mask_words * 64], 16-byte
  *          aligned (SEKV_EINVAL otherwise), or NULL: sigmoid(a_S) in fp32,
  *          for inspection; entries at or past N_S(b) are unspecified
@@ -306,7 +309,8 @@ sekv_status sekv_route_pooled(sekv_ctx* ctx, const sekv_index* idx, int32_t laye
  * N_S(b)) of the (b, span) pairs exceed it: the midpoint of the k-th and
  * (k+1)-th largest alpha, k clipped to [1, sum_b N_S(b) - 1].  The pages learn
  * tau; this stands in for the learned value on synthetic workloads.
- *   q_cal  device bf16 [B][layer_count][Hq][d];  tau_out device fp32 [layer_count][Hq] */
+ *   q_cal  device bf16 [B][layer_count][Hq][d], 16-byte aligned (SEKV_EINVAL
+ *          otherwise);  tau_out device fp32 [layer_count][Hq] */
 sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t layer_begin,
                                int32_t layer_count, const void* q_cal, float frac,
                                float* tau_out);
@@ -317,9 +321,10 @@ sekv_status sekv_calibrate_tau(sekv_ctx* ctx, const sekv_index* idx, int32_t lay
  * Khat = U^K diag(sigma m) V^K^T, Vhat likewise, of each span with z = 1.  The
  * reconstruction is evaluated in factored form and never materialised.
  * Softmax scale 1/sqrt(d).
- *   q      device bf16 [B][layer_count][Hq][d]
- *   mask   device uint64 [B][layer_count][Hq][mask_words] (from sekv_route or
- *          the caller)
+ *   q      device bf16 [B][layer_count][Hq][d], 16-byte aligned
+ *   mask   device uint64 [B][layer_count][Hq][mask_words], 8-byte aligned
+ *          (from sekv_route or the caller); a misaligned q or mask is
+ *          SEKV_EINVAL, refused before any work
  *   out    device fp32 [B][layer_count][Hq][d]
  *   stats  host, or NULL
  * Work: the attention kernel's workgroups each take a slice of the resident

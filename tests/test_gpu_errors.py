@@ -105,3 +105,43 @@ def test_ring_larger_than_the_device_is_enomem(sl, case):
     assert torch.isfinite(out).all()
     idx.free()
     ctx.close()
+
+
+def test_misaligned_inputs_are_refused(sl, case):
+    """The kernels read q, K, V and W with 16-byte loads and the masks as
+    64-bit words: a pointer off that alignment is SEKV_EINVAL, refused on the
+    host before any work, and the context keeps working."""
+    EINVAL = 1
+    w = case.w
+    ctx = sl.Context(0)
+    idx = ctx.import_index(sl.build_params(w), SC.import_arrays(case))
+    q, tau, mask, out = _decode_args(idx, w)
+    qb = torch.zeros(q.numel() + 8, dtype=torch.bfloat16, device="cuda")   # q at +2 bytes
+    mb = torch.zeros(mask.numel() + 1, dtype=torch.int64, device="cuda")    # mask at +4 bytes
+    L = sl.lib()
+    assert L.sekv_route(ctx.h, idx.h, 0, w.L, qb.data_ptr() + 2, tau.data_ptr(), 0, mask.data_ptr(), None) == EINVAL
+    assert b"aligned" in L.sekv_last_error()
+    assert L.sekv_route(ctx.h, idx.h, 0, w.L, q.data_ptr(), tau.data_ptr(), 0, mb.data_ptr() + 4, None) == EINVAL
+    assert L.sekv_route_pooled(ctx.h, idx.h, 0, w.L, qb.data_ptr() + 2, tau.data_ptr(), 0, mask.data_ptr(),
+                               None) == EINVAL
+    assert L.sekv_decode_attend(ctx.h, idx.h, 0, w.L, qb.data_ptr() + 2, mask.data_ptr(), out.data_ptr(),
+                                None) == EINVAL
+    assert L.sekv_decode_attend_noalloc(ctx.h, idx.h, 0, w.L, q.data_ptr(), mb.data_ptr() + 4, out.data_ptr(),
+                                        None) == EINVAL
+    assert L.sekv_calibrate_tau(ctx.h, idx.h, 0, w.L, qb.data_ptr() + 2, C.c_float(0.1), tau.data_ptr()) == EINVAL
+    # the build: K off by 2 bytes
+    H, K, V, W, _ = SC.make_inputs(w)
+    Kb = torch.zeros(K.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    Vd, Hd, Wd = V.cuda().contiguous(), H.cuda().contiguous(), W.cuda().contiguous()
+    hx = C.c_void_p()
+    p = sl.build_params(w)
+    assert L.sekv_build_index(ctx.h, C.byref(p), C.c_void_p(Kb.data_ptr() + 2), C.c_void_p(Vd.data_ptr()),
+                              C.c_void_p(Hd.data_ptr()), C.c_void_p(Wd.data_ptr()), None, C.byref(hx)) == EINVAL
+    assert not hx.value
+    # aligned calls still work
+    idx.route(0, w.L, q, tau, 0, mask)
+    idx.decode_attend(0, w.L, q, mask, out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    idx.free()
+    ctx.close()
