@@ -153,7 +153,7 @@ struct Lay {
 struct SmallLay {
   int jp, tp, ep;      // G pitch and Jacobi size (even), T pitch, E^T pitch
   size_t et;           // byte offset of E^T, followed by the Jacobi's rotation
-                       // list (jp / 2 + 1 f32x4) and pair table (uint16)
+                       // list (jp / 2 + 1 f32x4)
   size_t bytes;        // dynamic LDS of the workgroup
 };
 template <int D, int LP>
@@ -165,7 +165,7 @@ __host__ __device__ inline SmallLay small_lay(int lmax) {
   r.ep = ((r.jp + 3) & ~3) + 4;
   const int np = r.jp / 2;
   const size_t gb = (size_t)r.jp * r.jp * 8, tb = (size_t)r.jp * r.tp * 4;
-  const size_t eb = (size_t)r.jp * r.ep * 4 + (size_t)(np + 1) * 16 + (((size_t)np * (np + 1) + 15) & ~(size_t)15);
+  const size_t eb = (size_t)r.jp * r.ep * 4 + (size_t)(np + 1) * 16;
   if (eb <= Y::g - Y::x) {
     r.et = Y::x;
     r.bytes = Y::g + (gb > tb ? gb : tb);
@@ -453,18 +453,30 @@ __device__ __forceinline__ void orthonormalize(uint8_t* lds, int m, int GP, floa
 // accumulated as the rows of ET (pitch EP): row p of ET is column p of E.  The disjoint
 // pairs of a round (round-robin ordering) rotate together; each 2 x 2 block
 // of T and each 4-element piece of a pair of ET rows is one work item.
-__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, uint16_t* blk,
-                       int* rflag) {
+template <int LP>
+__device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4* rot, int* rflag) {
+  constexpr int NPM = LP / 2;                                 // pairs at most
+  constexpr int TT = (NPM * (NPM + 1) / 2 + 255) / 256;       // T blocks per thread
+  constexpr int TE = (NPM * ((LP + 3) / 4) + 255) / 256;      // E^T pieces per thread
   const int m = l + (l & 1);
   const int np = m >> 1;
   const int nrc = (l + 3) >> 2;
   const int nblk = np * (np + 1) / 2;   // pairs of pairs k1 <= k2
-  const float inv_nrc = 1.f / (float)max(nrc, 1);
   for (int i = threadIdx.x; i < JP * EP; i += 256) ET[i] = (i / EP == i % EP) ? 1.f : 0.f;
-  for (int t = threadIdx.x; t < nblk; t += 256) {
-    int k2, k1;
-    tri_decode(t, k2, k1);
-    blk[t] = (uint16_t)(k1 | (k2 << 8));
+  // this thread's tasks, the same every round: T blocks t = tid + 256 u
+  // (k1 | k2 << 8) and E^T pieces (pair k | first row r0 << 8); -1 for none
+  int tk[TT], te[TE];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) {
+    const int t = threadIdx.x + 256 * u;
+    int k2 = 0, k1 = 0;
+    if (t < nblk) tri_decode(t, k2, k1);
+    tk[u] = (t < nblk) ? (k1 | (k2 << 8)) : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < TE; ++u) {
+    const int t = threadIdx.x + 256 * u, k = t / max(nrc, 1);
+    te[u] = (t < np * nrc) ? (k | ((4 * (t - k * nrc)) << 8)) : -1;
   }
   // rflag[r & 1]: a pair of round r rotates (a round without rotation skips
   // its updates); the other slot is cleared during the round for the next
@@ -513,7 +525,17 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
         rot[k] = f32x4{c, s, __int_as_float(p), __int_as_float(q)};
       }
       __syncthreads();
+      // the round flag and the rotations of this thread's tasks, read together
       const bool rotates = rflag[r_all & 1] != 0;
+      f32x4 ra[TT], rb[TT], rc[TE];
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        const int kk = tk[u] < 0 ? 0 : tk[u];
+        ra[u] = rot[kk & 255];
+        rb[u] = rot[kk >> 8];
+      }
+#pragma unroll
+      for (int u = 0; u < TE; ++u) rc[u] = rot[(te[u] < 0 ? 0 : te[u]) & 255];
       if (threadIdx.x == 0) rflag[(r_all + 1) & 1] = 0;
       if (!rotates) {
         __syncthreads();
@@ -521,9 +543,11 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
       }
       // T is symmetric: each pair of pairs k1 <= k2 updates its 2 x 2 block
       // and writes the transposed block too
-      for (int t = threadIdx.x; t < nblk; t += 256) {
-        const int kk = blk[t], k1 = kk & 255, k2 = kk >> 8;
-        const f32x4 r1 = rot[k1], r2 = rot[k2];
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        if (tk[u] < 0) continue;
+        const int k1 = tk[u] & 255, k2 = tk[u] >> 8;
+        const f32x4 r1 = ra[u], r2 = rb[u];
         const float c1 = r1[0], s1 = r1[1], c2 = r2[0], s2 = r2[1];
         const int p1 = __float_as_int(r1[2]), q1 = __float_as_int(r1[3]);
         const int p2 = __float_as_int(r2[2]), q2 = __float_as_int(r2[3]);
@@ -545,10 +569,11 @@ __device__ void jacobi(float* T, float* ET, int l, int JP, int TP, int EP, f32x4
           T[q2 * TP + q1] = z11;
         }
       }
-      for (int t = threadIdx.x; t < np * nrc; t += 256) {
-        const int k = (int)(((float)t + 0.5f) * inv_nrc);
-        const int r0 = 4 * (t - k * nrc);
-        const f32x4 rk = rot[k];
+#pragma unroll
+      for (int u = 0; u < TE; ++u) {
+        if (te[u] < 0) continue;
+        const int r0 = te[u] >> 8;
+        const f32x4 rk = rc[u];
         if (rk[1] == 0.f) continue;
         f32x4* ep = (f32x4*)(ET + __float_as_int(rk[2]) * EP + r0);
         f32x4* eq = (f32x4*)(ET + __float_as_int(rk[3]) * EP + r0);
@@ -689,10 +714,9 @@ __global__ __launch_bounds__(256) void rsvd_mfma_kernel(const PackArgs a) {
     }
     __syncthreads();
   }
-  // the rotation list and pair table follow E^T (the staging region is idle)
+  // the rotation list follows E^T (the staging region is idle)
   f32x4* s_rot = (f32x4*)(ET + (size_t)SL.jp * SL.ep);
-  uint16_t* s_blk = (uint16_t*)(s_rot + SL.jp / 2 + 1);
-  jacobi(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_blk, s_rflag);
+  jacobi<LP>(Tm, ET, l, SL.jp, TP, SL.ep, s_rot, s_rflag);
 
   // ---- order eigenpairs by decreasing eigenvalue (ties: lower index first)
   for (int i = tid; i < l; i += 256) {
