@@ -113,21 +113,143 @@ __device__ double sum1024(double v, double* s_d) {
 // mu and sigma: mean and population std of the sequence's surprisal in fp64;
 // anchors: H_t > mu + alpha_sp*sigma (strict); spans: maximal anchor-free runs
 // of at least l_min tokens; raw: anchors and the tokens of shorter runs.
+// One 1024-thread workgroup per sequence.
+
+// The anchor threshold mu + alpha_sp * sigma of one sequence (fixed-order sums).
+__device__ double split_threshold(const float* H, int T, double alpha_sp, double* s_d) {
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < T; i += 1024) acc += (double)H[i];
+  const double mu = sum1024(acc, s_d) / (double)T;
+  acc = 0.0;
+  for (int i = threadIdx.x; i < T; i += 1024) {
+    const double dv = (double)H[i] - mu;
+    acc += dv * dv;
+  }
+  const double sigma = sqrt(sum1024(acc, s_d) / (double)T);
+  return mu + alpha_sp * sigma;
+}
+
+// Sequences of up to kSplitBitsT tokens: the anchor test is evaluated once,
+// with coalesced loads, into a bitmap in LDS (bit j of word w: token 32 w + j);
+// thread t then takes whole words of tokens and forms run starts, run ends and
+// raw tokens with word operations (a start: a non-anchor token at 0 or after
+// an anchor; an end: a non-anchor token at T - 1 or before an anchor).
+constexpr int kSplitBitsT = 262144;   // 32 KB of bitmap
+
+__global__ __launch_bounds__(1024) void span_split_bits_kernel(const SplitArgs a) {
+  extern __shared__ uint32_t s_anc[];   // [2 ceil(T / 64)]
+  __shared__ double s_d[16];
+  __shared__ int s_tmp[17];
+  const int b = blockIdx.x, T = a.T, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* H = a.H + (int64_t)b * T;
+  const double thr = split_threshold(H, T, a.alpha_sp, s_d);
+  const int NW = (T + 31) >> 5, NWP = 2 * ((T + 63) >> 6);   // words used, words held
+  for (int i0 = 0; i0 < T; i0 += 1024) {
+    const int i = i0 + tid;
+    const uint64_t bal = __ballot(i < T && (double)H[i] > thr);
+    if (lane == 0 && (i0 >> 5) + 2 * wave < NWP) {
+      const int w = (i0 >> 5) + 2 * wave;
+      s_anc[w] = (uint32_t)bal;
+      s_anc[w + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  __syncthreads();
+  // this thread's words [w0, w1)
+  const int CW = (NW + 1023) / 1024;
+  const int w0 = min(NW, tid * CW), w1 = min(NW, w0 + CW);
+  auto valid = [&](int w) -> uint32_t {   // bits of tokens < T
+    const int left = T - 32 * w;
+    return left >= 32 ? 0xffffffffu : ((1u << left) - 1u);
+  };
+  auto starts_of = [&](int w) -> uint32_t {
+    const uint32_t an = s_anc[w];
+    const uint32_t prev = (w == 0) ? 1u : (s_anc[w - 1] >> 31);   // token -1 counts as an anchor
+    return ~an & valid(w) & ((an << 1) | prev);
+  };
+  auto ends_of = [&](int w) -> uint32_t {
+    const uint32_t an = s_anc[w];
+    uint32_t next = (an >> 1) | ((w + 1 < NW) ? (s_anc[w + 1] << 31) : 0u);
+    if (32 * w + 31 >= T - 1) next |= 1u << (T - 1 - 32 * w);   // token T counts as an anchor
+    return ~an & valid(w) & next;
+  };
+  int ns = 0, ne = 0;
+  for (int w = w0; w < w1; ++w) {
+    ns += __popc(starts_of(w));
+    ne += __popc(ends_of(w));
+  }
+  int nruns, nruns2;
+  const int bs = scan1024(ns, s_tmp, &nruns);
+  const int be = scan1024(ne, s_tmp, &nruns2);
+  int32_t* starts = a.scratch + (int64_t)b * 2 * (T / 2 + 2);
+  int32_t* ends = starts + (T / 2 + 2);
+  {
+    int ks = bs, ke = be;
+    for (int w = w0; w < w1; ++w) {
+      for (uint32_t x = starts_of(w); x; x &= x - 1) starts[ks++] = 32 * w + __ffs(x) - 1;
+      for (uint32_t x = ends_of(w); x; x &= x - 1) ends[ke++] = 32 * w + __ffs(x) - 1;
+    }
+  }
+  __syncthreads();
+  // compressed runs -> span table, in run order
+  const int Cr = (nruns + 1023) / 1024;
+  const int r0 = min(nruns, tid * Cr), r1 = min(nruns, r0 + Cr);
+  int nc = 0;
+  for (int r = r0; r < r1; ++r) nc += (ends[r] - starts[r] + 1 >= a.l_min);
+  int n_spans;
+  int sb = scan1024(nc, s_tmp, &n_spans);
+  int32_t* sst = a.span_start + (int64_t)b * a.S_max;
+  int32_t* sln = a.span_len + (int64_t)b * a.S_max;
+  for (int r = r0; r < r1; ++r) {
+    const int len = ends[r] - starts[r] + 1;
+    if (len >= a.l_min) {
+      sst[sb] = starts[r];
+      sln[sb] = len;
+      ++sb;
+    }
+  }
+  // raw bits of word w: its anchors and the tokens of short runs; run is the
+  // index of the last run started before the word, and moves past the word's
+  // starts
+  auto raw_of = [&](int w, int& run) -> uint32_t {
+    const uint32_t an = s_anc[w] & valid(w);
+    uint32_t raw = an, rem = ~s_anc[w] & valid(w), st = starts_of(w);
+    while (rem) {
+      const int nb = st ? __ffs(st) - 1 : 32;   // the next start in the word
+      const uint32_t seg = (nb >= 32) ? rem : (rem & ((1u << nb) - 1u));
+      if (seg && ends[run] - starts[run] + 1 < a.l_min) raw |= seg;
+      rem &= ~seg;
+      if (!st) break;
+      ++run;
+      st &= st - 1;
+    }
+    return raw;
+  };
+  int nraw = 0;
+  {
+    int run = bs - 1;   // the last run that started before w0
+    for (int w = w0; w < w1; ++w) nraw += __popc(raw_of(w, run));
+  }
+  int n_raw;
+  int rb = scan1024(nraw, s_tmp, &n_raw);
+  int32_t* rp = a.raw_pos + (int64_t)b * T;
+  {
+    int run = bs - 1;
+    for (int w = w0; w < w1; ++w)
+      for (uint32_t x = raw_of(w, run); x; x &= x - 1) rp[rb++] = 32 * w + __ffs(x) - 1;
+  }
+  if (tid == 0) {
+    a.counts[2 * b] = n_spans;
+    a.counts[2 * b + 1] = n_raw;
+  }
+}
+
+// Longer sequences: each thread walks a contiguous chunk of tokens.
 __global__ __launch_bounds__(1024) void span_split_kernel(const SplitArgs a) {
   __shared__ double s_d[16];
   __shared__ int s_tmp[17];
   const int b = blockIdx.x, T = a.T, tid = threadIdx.x;
   const float* H = a.H + (int64_t)b * T;
-  double acc = 0.0;
-  for (int i = tid; i < T; i += 1024) acc += (double)H[i];
-  const double mu = sum1024(acc, s_d) / (double)T;
-  acc = 0.0;
-  for (int i = tid; i < T; i += 1024) {
-    const double dv = (double)H[i] - mu;
-    acc += dv * dv;
-  }
-  const double sigma = sqrt(sum1024(acc, s_d) / (double)T);
-  const double thr = mu + a.alpha_sp * sigma;
+  const double thr = split_threshold(H, T, a.alpha_sp, s_d);
   auto anc = [&](int i) -> bool { return (double)H[i] > thr; };
 
   const int C = (T + 1023) / 1024;
@@ -197,7 +319,12 @@ __global__ __launch_bounds__(1024) void span_split_kernel(const SplitArgs a) {
 }
 
 hipError_t launch_span_split(const SplitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(span_split_kernel, dim3(a.B), dim3(1024), 0, st, a);
+  if (a.T <= kSplitBitsT) {
+    const size_t lds = sizeof(uint32_t) * 2 * (size_t)((a.T + 63) / 64);
+    hipLaunchKernelGGL(span_split_bits_kernel, dim3(a.B), dim3(1024), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(span_split_kernel, dim3(a.B), dim3(1024), 0, st, a);
+  }
   return hipGetLastError();
 }
 
