@@ -14,6 +14,8 @@ times (one layer per call, the 8B-shaped 128K layer of the 32-layer stack).
   the pooled masks.
 * The largest span count the mask layout holds (65535 spans of 8 tokens):
   masks without and with a cap, decode, and the library's own split.
+* The library's split of 262144 and 262145 tokens (the two sides of its
+  LDS-bitmap limit) against the oracle's.
 * 70B-shaped layer, 32 sequences of 65536 tokens (64 query / 8 KV heads,
   R = 64): the library builds the whole index on the GPU from inputs drawn on
   the GPU; the span table of every sequence is checked against the oracle's
@@ -125,6 +127,24 @@ def test_max_span_count(ctx, sl):
     assert np.array_equal(start, idxs[0].split.spans[:, 0]) and np.array_equal(length, idxs[0].split.spans[:, 1])
     assert np.array_equal(raw, idxs[0].split.raw)
     lib_idx.free()
+
+
+@pytest.mark.parametrize("T", [262144, 262145])
+def test_split_on_both_sides_of_the_bitmap_limit(ctx, sl, T):
+    """The span split keeps its anchor bitmap in LDS for sequences of up to
+    262144 tokens and walks the tokens one by one beyond that: on both sides
+    of the limit the library's span table and raw positions equal the
+    oracle's split of the same surprisal."""
+    w = synth.WORKLOADS["tiny_2k"].scaled(T=T)
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = synth.routing_w(w, 0, "cuda")[None].contiguous()
+    ref = O.span_split(H[0].cpu().numpy(), w.alpha_sp, w.l_min)
+    idx = ctx.build_index(sl.build_params(w), K, V, H, W)
+    start, length, raw = idx.spans()
+    print(f"[split] T = {T}: {len(start)} spans, {len(raw)} raw tokens", flush=True)
+    assert np.array_equal(start, ref.spans[:, 0]) and np.array_equal(length, ref.spans[:, 1])
+    assert np.array_equal(raw, ref.raw)
+    idx.free()
 
 
 def test_import_beyond_the_mask_layout_is_refused(ctx, sl):
