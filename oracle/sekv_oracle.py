@@ -28,9 +28,10 @@ against brute force; the pooled budget against brute force and against the
 per-head cap on a one-head pool; calibration by counting; dropped components
 (gate below eps) against the Eckart-Young error of the kept set, against a
 reconstruction that leaves them out, and, all dropped, against the closed
-form of attention over zero rows.  Unpinned: absolute decode
-outputs at generic tau (no worked example is printed on the pages); they stand
-on the pinned pieces.
+form of attention over zero rows; decode at truncated rank with a mixed
+per-head z against attention over rows projected onto their top-R
+eigenvectors of A^T A (numpy eigh) and mean copies.  The pages print no
+worked example, so no pin holds an absolute output value from them.
 """
 from __future__ import annotations
 

@@ -507,6 +507,41 @@ def test_mixed_expansion_per_head_with_exact_factors():
         assert np.linalg.norm(out - ref) <= 1e-10 * np.linalg.norm(ref)
 
 
+def _projected(A, R):
+    """Rank-R Eckart-Young approximation of A as A P with P the projector on
+    the top-R eigenvectors of A^T A (numpy eigh, not the oracle's SVD)."""
+    ev, Q = np.linalg.eigh(A.T @ A)
+    top = Q[:, np.argsort(ev)[::-1][:min(R, A.shape[0], A.shape[1])]]
+    return A @ top @ top.T
+
+
+def test_truncated_rank_mixed_expansion_is_attention_over_projected_rows():
+    """Generic tau at truncated rank (R < n_S on most spans), m = 1: an expanded
+    span contributes its rows projected onto their top-R right singular
+    subspace, any other span n_S copies of its weighted mean, each raw token its
+    own row; the decode is plain softmax attention over that context.  The
+    projector comes from an eigen-decomposition of A^T A, so a dropped
+    component, a wrong sigma or a misplaced token offset in the factored
+    index would all show."""
+    w, H, K, V, W, q = _small_workload(T=900, R=3, Hq=4, Hkv=2, d=32, rank=6)
+    idx = O.build_index_b(H[0], K[0], V[0], W, None, R=w.R, alpha_sp=w.alpha_sp,
+                          l_min=w.l_min, Hq=w.Hq, store=False)
+    assert sum(n > w.R for _, n in idx.split.spans) >= 3
+    rng = np.random.default_rng(21)
+    for h in range(w.Hq):
+        g = h // w.G
+        z = rng.random(idx.n_spans) < 0.5
+        z[0], z[-1] = True, False
+        K2, V2 = _mean_replaced(K[0, 0, g], V[0, 0, g], H[0], idx.split, ~z)
+        for j, (a, n) in enumerate(idx.split.spans):
+            if z[j]:
+                K2[a:a + n] = _projected(K[0, 0, g, a:a + n], w.R)
+                V2[a:a + n] = _projected(V[0, 0, g, a:a + n], w.R)
+        out = O.decode_head(q[0, 0, h], idx, 0, g, z)
+        ref = O.full_attention(q[0, 0, h], K2, V2)
+        assert np.linalg.norm(out - ref) <= 1e-9 * np.linalg.norm(ref)
+
+
 def test_gates_scale_components():
     """Gate 0 on every component of an expanded span zeroes its rows' keys and
     values (logit 0, value 0); gate 1 with full rank is exact."""
