@@ -267,7 +267,7 @@ sekv_status check_shape(const sekv_build_params* p, bool need_build_fields) {
     if (p->oversample < 0 || p->oversample > 16) return fail(SEKV_EINVAL, "oversample must be in [0, 16]");
     if (p->power_iters < 0 || p->power_iters > 8) return fail(SEKV_EINVAL, "power_iters must be in [0, 8]");
   }
-  const int64_t smax = (int64_t)(p->T + 1) / (p->l_min > 0 ? p->l_min + 1 : 2);
+  const int64_t smax = ((int64_t)p->T + 1) / (p->l_min > 0 ? (int64_t)p->l_min + 1 : 2);
   if ((smax + 63) / 64 > kMaxWords) return fail(SEKV_EUNSUPPORTED, "T too large for l_min (more than 65536 spans possible)");
   return SEKV_OK;
 }
