@@ -4,11 +4,16 @@
  * returns before any kernel launch: parameter validation, null arguments,
  * the span bound, a context on a device that may not exist, and a sweep of
  * random and extreme parameter values through the validation arithmetic.
+ * With a device present it also imports a small ragged index from host
+ * arrays into each tier, reads it back and compares every array bit for bit,
+ * and checks use after free: the host packing and unpacking code runs under
+ * the sanitizers (no kernel is launched).
  * Prints "host checks passed: N" and exits 0, or lists the failures and
  * exits 1; a sanitizer report aborts the run. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "sekv.h"
@@ -57,7 +62,7 @@ static void check_validation(void) {
   p = valid_params(); p.B = 32; p.Hq = 64; p.T = 65536; p.R = 64;
   CHECK(sekv_validate_params(&p) == SEKV_OK, "the 70B-shaped batch validates");
 
-  struct { const char* what; int32_t* field; int32_t value; int status; } ic[] = {
+  struct { const char* what; int32_t* field; int32_t value; sekv_status status; } ic[] = {
       {"Hkv not dividing Hq", &p.Hkv, 7, SEKV_EINVAL},
       {"d = 96", &p.d, 96, SEKV_EUNSUPPORTED},
       {"R above d", &p.R, 256, SEKV_EINVAL},
@@ -171,12 +176,120 @@ static void check_null_arguments(void) {
   sekv_index_free(NULL);
 }
 
+/* bf16 bit pattern of a value in [-1, 1) (exactly representable) */
+static uint16_t rand_bf16(void) {
+  const float f = (float)((int32_t)next_u32()) * (1.0f / 2147483648.0f);
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+static float rand_sigma(void) { return 0.25f + (float)(next_u32() >> 8) * (1.0f / 16777216.0f); }
+
+/* import -> export round trip of a two-sequence, two-layer index (G = 2,
+ * d = 64, R = 16, d' = 8, T = 100) with random span partitions */
+static void check_roundtrip(sekv_ctx* c, int tier) {
+  enum { B = 2, L = 2, HQ = 4, HKV = 2, D = 64, R = 16, DP = 8, T = 100 };
+  int32_t n_spans[B], n_raw[B];
+  int32_t span_start[2 * T], span_len[2 * T], raw_pos[2 * T];
+  int ns_all = 0, nr_all = 0, ntok_all = 0, nres_all = 0;
+  for (int b = 0; b < B; ++b) {
+    int ns = 0, nr = 0;
+    for (int t = 0; t < T;) {
+      const int len = (next_u32() % 3 == 0 || t == 0) ? 0 : 1 + (int)(next_u32() % 12);
+      if (len == 0 || t + len > T) {
+        raw_pos[nr_all + nr++] = t++;
+      } else {
+        span_start[ns_all + ns] = t;
+        span_len[ns_all + ns++] = len;
+        ntok_all += len;
+        t += len;
+      }
+    }
+    n_spans[b] = ns;
+    n_raw[b] = nr;
+    ns_all += ns;
+    nr_all += nr;
+    nres_all += ns + nr;
+  }
+  const size_t n_kres = (size_t)L * HKV * nres_all * D, n_s = (size_t)L * HQ * DP * ns_all;
+  const size_t n_u = (size_t)L * HKV * ntok_all * R, n_vt = (size_t)L * HKV * ns_all * R * D;
+  const size_t n_sm = (size_t)L * HKV * ns_all * R, n_w = (size_t)L * HQ * DP * D;
+  uint16_t* kres = malloc(2 * n_kres); uint16_t* vres = malloc(2 * n_kres);
+  float* sk = malloc(4 * n_s);
+  uint16_t* uk = malloc(2 * n_u); uint16_t* uv = malloc(2 * n_u);
+  uint16_t* vkt = malloc(2 * n_vt); uint16_t* vvt = malloc(2 * n_vt);
+  float* smk = malloc(4 * n_sm); float* smv = malloc(4 * n_sm);
+  float* W = malloc(4 * n_w);
+  for (size_t i = 0; i < n_kres; ++i) { kres[i] = rand_bf16(); vres[i] = rand_bf16(); }
+  for (size_t i = 0; i < n_s; ++i) sk[i] = (float)(int32_t)next_u32() * 1e-9f;
+  for (size_t i = 0; i < n_u; ++i) { uk[i] = rand_bf16(); uv[i] = rand_bf16(); }
+  for (size_t i = 0; i < n_vt; ++i) { vkt[i] = rand_bf16(); vvt[i] = rand_bf16(); }
+  for (size_t i = 0; i < n_sm; ++i) { smk[i] = rand_sigma(); smv[i] = rand_sigma(); }
+  for (size_t i = 0; i < n_w; ++i) W[i] = (float)(int32_t)next_u32() * 1e-9f;
+
+  sekv_build_params p;
+  memset(&p, 0, sizeof p);
+  p.B = B; p.L = L; p.Hq = HQ; p.Hkv = HKV; p.d = D; p.T = T; p.R = R; p.dprime = DP;
+  p.alpha_sp = 2.0f; p.l_min = 1; p.oversample = 8; p.power_iters = 2; p.tier = tier;
+  sekv_host_index h = {n_spans, n_raw, span_start, span_len, raw_pos, kres, vres, sk,
+                       uk, uv, vkt, vvt, smk, smv, W};
+  sekv_index* x = NULL;
+  const sekv_status st = sekv_index_import(c, &p, &h, &x);
+  CHECK(st == SEKV_OK && x != NULL, "import of a ragged two-sequence index");
+  if (st == SEKV_OK) {
+    sekv_index_info info;
+    CHECK(sekv_index_get_info(x, &info) == SEKV_OK && info.total_spans == ns_all &&
+              info.total_raw == nr_all && info.total_span_tokens == ntok_all && info.tier == tier,
+          "index info after import");
+    int32_t cs[B], cr[B];
+    CHECK(sekv_index_counts(x, cs, cr) == SEKV_OK && cs[0] == n_spans[0] && cs[1] == n_spans[1] &&
+              cr[0] == n_raw[0] && cr[1] == n_raw[1], "span and raw counts after import");
+    int32_t* o_ss = calloc(ns_all, 4); int32_t* o_sl = calloc(ns_all, 4); int32_t* o_rp = calloc(nr_all, 4);
+    uint16_t* o_kres = calloc(n_kres, 2); uint16_t* o_vres = calloc(n_kres, 2);
+    float* o_s = calloc(n_s, 4);
+    uint16_t* o_uk = calloc(n_u, 2); uint16_t* o_uv = calloc(n_u, 2);
+    uint16_t* o_vkt = calloc(n_vt, 2); uint16_t* o_vvt = calloc(n_vt, 2);
+    float* o_smk = calloc(n_sm, 4); float* o_smv = calloc(n_sm, 4);
+    int32_t* o_rank = calloc(2 * n_sm / R, 4);
+    sekv_host_index_out o = {o_ss, o_sl, o_rp, o_kres, o_vres, o_s, o_uk, o_uv, o_vkt, o_vvt, o_smk, o_smv, o_rank};
+    CHECK(sekv_index_export(c, x, &o) == SEKV_OK, "export");
+    CHECK(!memcmp(o_ss, span_start, 4 * ns_all) && !memcmp(o_sl, span_len, 4 * ns_all) &&
+              !memcmp(o_rp, raw_pos, 4 * nr_all), "span tables round trip");
+    CHECK(!memcmp(o_kres, kres, 2 * n_kres) && !memcmp(o_vres, vres, 2 * n_kres), "resident rows round trip");
+    CHECK(!memcmp(o_s, sk, 4 * n_s), "summary keys round trip");
+    CHECK(!memcmp(o_uk, uk, 2 * n_u) && !memcmp(o_uv, uv, 2 * n_u), "left factors round trip");
+    CHECK(!memcmp(o_vkt, vkt, 2 * n_vt) && !memcmp(o_vvt, vvt, 2 * n_vt), "right factors round trip");
+    CHECK(!memcmp(o_smk, smk, 4 * n_sm) && !memcmp(o_smv, smv, 4 * n_sm), "sigma m round trip");
+    int ranks_ok = 1;
+    for (size_t i = 0; i < 2 * n_sm / R; ++i) ranks_ok &= o_rank[i] == R;
+    CHECK(ranks_ok, "every blob stores R components");
+    CHECK(sekv_index_export_part(c, x, 1, 1, 1, 1, &o) == SEKV_OK, "partial export");
+    CHECK(sekv_index_export_part(c, x, 1, 2, 0, 1, &o) == SEKV_EINVAL, "partial export past B");
+    CHECK(sekv_index_export_part(c, x, 0, 1, 1, 2, &o) == SEKV_EINVAL, "partial export past L");
+    free(o_ss); free(o_sl); free(o_rp); free(o_kres); free(o_vres); free(o_s); free(o_uk); free(o_uv);
+    free(o_vkt); free(o_vvt); free(o_smk); free(o_smv); free(o_rank);
+    sekv_index_free(x);
+    CHECK(sekv_index_get_info(x, &info) == SEKV_ESTATE, "info of a freed index");
+    CHECK(sekv_index_export(c, x, &o) == SEKV_ESTATE, "export of a freed index");
+    sekv_index_free(x);   /* a second free is a no-op */
+  }
+  /* a partition with a gap is refused before any device work */
+  span_len[0] += 1;
+  x = NULL;
+  CHECK(sekv_index_import(c, &p, &h, &x) == SEKV_EINVAL && x == NULL, "import of overlapping spans refused");
+  span_len[0] -= 1;
+  free(kres); free(vres); free(sk); free(uk); free(uv); free(vkt); free(vvt); free(smk); free(smv); free(W);
+}
+
 static void check_context(void) {
   sekv_ctx* c = NULL;
   const sekv_status st = sekv_create(0, NULL, &c);
   if (st == SEKV_OK) {
     CHECK(c != NULL, "a created context");
+    check_roundtrip(c, SEKV_TIER_HBM);
+    check_roundtrip(c, SEKV_TIER_PINNED_HOST);
     sekv_destroy(c);
+    CHECK(sekv_index_import(c, NULL, NULL, NULL) != SEKV_OK, "a destroyed context is refused");
   } else {
     CHECK(st == SEKV_EHIP && c == NULL, "no device: EHIP and no context");
     CHECK(sekv_last_error()[0] != '\0', "no device: a message");

@@ -4,8 +4,10 @@ Every source is compiled as for the product library (device code for gfx950
 unchanged) with the two sanitizers on the host side only, linked with
 tests/host_checks.c into an executable, and run.  The checks make no kernel
 launch (validation, null arguments, the span bound, context creation with or
-without a device, and a random sweep of parameters), so they run on the CPU.
-The build is cached under _build/asan by a hash of the sources."""
+without a device, and a random sweep of parameters), so they run on the CPU;
+where a device is present the driver also round-trips a small index through
+import and export in both tiers.  The build is cached under _build/asan by a
+hash of the sources."""
 import concurrent.futures as cf
 import hashlib
 import os
