@@ -170,6 +170,10 @@ struct RouteArgs {
   float* alpha;             // [B][Lc][Hq][Wd*64] sigmoid of the score, or NULL
   float* score;             // [B][Lc][Hq][Wd*64] score a = u . s (library
                             // scratch the budget kernels rank), or NULL
+  uint32_t* packed;         // [B][Lc][Hq][Wd][64] order keys of the routed
+                            // spans of each mask word, packed at the start of
+                            // the word's 64 slots in span order (scratch of
+                            // the pooled budget), or NULL
   int32_t layer_begin, layer_count;
   int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
   int32_t budget;           // pooled budget per sequence (route_pool_kernel)

@@ -190,6 +190,9 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   if (lane == 0) mrow[wi] = word;
   if (arow) arow[S] = alpha;
   if (srow) srow[S] = dot;
+  // the routed spans' keys, packed per word in span order (the pooled budget
+  // then touches only the routed spans)
+  if (a.packed && z) a.packed[(row * a.Wd + wi) * 64 + __popcll(word & ((1ull << lane) - 1))] = order_key(dot);
 }
 
 // Budget cap, one workgroup per (b, h, lc), after route_kernel: when more than
@@ -503,11 +506,13 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
 // lower (layer, head, span) position (the flat order of the mask words).  The budget rule of the
 // Technical-details section of the SeKV article, read over the whole call
 // instead of one (layer, head).
-//  * Collect: threads take 32-span halves of the mask words, two a round, each
-//    with its 32 scores as eight 16-byte loads, all issued before use; every
-//    routed triple (score key, flat position) goes to an LDS list at a slot
-//    from one LDS counter per wave (wave prefixes by bit-sliced ballots).  A
-//    sequence within its budget stops there.
+//  * Collect: the routing kernel has packed the score keys of each word's
+//    routed spans at the start of the word's 64 slots, so only routed spans
+//    are touched here.  Threads take two mask words a round, each with its
+//    first 32 packed keys as eight 16-byte loads, all issued before use;
+//    every routed triple (score key, flat position) goes to an LDS list at a
+//    slot from one LDS counter per wave (wave prefixes by bit-sliced
+//    ballots).  A sequence within its budget stops there.
 //  * Radix select of the budget-th largest key over the list, binned over the
 //    keys' own range (offsets key - min, at most 11 bits a pass from the top
 //    of max - min; the keys order like the scores).
@@ -545,12 +550,13 @@ __device__ int block_scan_pool(int v, int* s_tmp, int& total) {
   return v + add;
 }
 
-// Exclusive wave prefix and wave total of per-lane counts below 128.
+// Exclusive wave prefix and wave total of per-lane counts below 2^BITS.
+template <int BITS>
 __device__ __forceinline__ int wave_prefix_pool(int c, int lane, int& total) {
   const uint64_t lt = (1ull << lane) - 1;
   int s = 0, t = 0;
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < BITS; ++i) {
     const uint64_t bal = __ballot((c >> i) & 1);
     s += (int)__popcll(bal & lt) << i;
     t += (int)__popcll(bal) << i;
@@ -611,45 +617,70 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
   if (tid == 0) s_count = 0;
   for (int i = tid; i < kPoolHalves; i += kPoolThreads) s_new[i] = 0u;
   __syncthreads();
-  // ---- collect
+  // ---- collect: thread t takes words t and t + 1024 of a round, each word's
+  // first 32 packed keys by eight 16-byte loads (all issued before use), and
+  // appends (key, flat position) of its routed spans to the LDS list at a
+  // slot from one LDS counter per wave
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int64_t base = 0; base < nh; base += 2 * kPoolThreads) {
-    uint32_t bits0, bits1;
-    float4 av0[8], av1[8];
-    const int64_t t0 = base + tid, t1 = t0 + kPoolThreads;
-    load_half(mh, ab, t0, nh, bits0, av0);
-    load_half(mh, ab, t1, nh, bits1, av1);
+  const int64_t nwords = nh >> 1;
+  const uint64_t* mw = a.mask + (int64_t)b * rows * a.Wd;
+  const uint4* pk = (const uint4*)(a.packed + (int64_t)b * rows * a.Wd * 64);
+  auto append = [&](uint64_t bits, const uint4 (&kv)[8], int64_t w, int& pos) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (bits) {
+        const int j = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        const uint4 v = kv[k >> 2];
+        const uint32_t key = (k & 3) == 0 ? v.x : ((k & 3) == 1 ? v.y : ((k & 3) == 2 ? v.z : v.w));
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+        if (pos < kPoolList) {
+          s_key[pos] = key;
+          s_pos[pos] = (int32_t)(64 * w + j);
+        }
+        ++pos;
+      }
+    }
+    // a word with more than 32 routed spans: the rest, four keys a load
+    for (int k = 32; bits; k += 4) {
+      const uint4 v = pk[w * 16 + (k >> 2)];
+      const uint32_t vk[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bits) {
+          const int j = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          kmin = min(kmin, vk[e]);
+          kmax = max(kmax, vk[e]);
+          if (pos < kPoolList) {
+            s_key[pos] = vk[e];
+            s_pos[pos] = (int32_t)(64 * w + j);
+          }
+          ++pos;
+        }
+      }
+    }
+  };
+  for (int64_t base = 0; base < nwords; base += 2 * kPoolThreads) {
+    const int64_t w0 = base + tid, w1 = w0 + kPoolThreads;
+    const int64_t c0 = w0 < nwords ? w0 : nwords - 1, c1 = w1 < nwords ? w1 : nwords - 1;   // in range
+    uint64_t bits0 = mw[c0], bits1 = mw[c1];
+    uint4 kv0[8], kv1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      kv0[i] = pk[c0 * 16 + i];
+      kv1[i] = pk[c1 * 16 + i];
+    }
+    if (w0 >= nwords) bits0 = 0ull;
+    if (w1 >= nwords) bits1 = 0ull;
     int wt;
-    const int pre = wave_prefix_pool(__popc(bits0) + __popc(bits1), lane, wt);
+    const int pre = wave_prefix_pool<8>(__popcll(bits0) + __popcll(bits1), lane, wt);
     int wb = 0;
     if (lane == 0 && wt > 0) wb = atomicAdd(&s_count, wt);
     int pos = __shfl(wb, 0) + pre;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((bits0 >> j) & 1u) {
-        const uint32_t key = order_key(f4_at(av0[j >> 2], j & 3));
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-        if (pos < kPoolList) {
-          s_key[pos] = key;
-          s_pos[pos] = (int32_t)(32 * t0 + j);
-        }
-        ++pos;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((bits1 >> j) & 1u) {
-        const uint32_t key = order_key(f4_at(av1[j >> 2], j & 3));
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-        if (pos < kPoolList) {
-          s_key[pos] = key;
-          s_pos[pos] = (int32_t)(32 * t1 + j);
-        }
-        ++pos;
-      }
-    }
+    append(bits0, kv0, w0, pos);
+    append(bits1, kv1, w1, pos);
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {

@@ -219,7 +219,7 @@ struct sekv_index {
   std::vector<int32_t> bg_first;
   DBuf d_items, d_bg_first, d_part;
   // routing scratch: scores ranked by the budget kernels; alpha for calibration
-  DBuf d_score, d_alpha, d_tau_inf;
+  DBuf d_score, d_packed, d_alpha, d_tau_inf;
   // pinned tier: the copy stream the gathers of multi-layer calls run on, the
   // events that order them against the attention, and gather timing events
   hipStream_t copy = nullptr;
@@ -460,7 +460,7 @@ void free_index(sekv_index* x) {
   DBuf* bufs[] = {&x->d_meta, &x->d_span_start, &x->d_span_len, &x->d_logn, &x->d_bref, &x->d_layer_off,
                   &x->d_raw_pos, &x->d_kres, &x->d_vres, &x->d_s, &x->d_W, &x->d_pool,
                   &x->d_ring, &x->d_gstat, &x->d_items, &x->d_bg_first, &x->d_part,
-                  &x->d_score, &x->d_alpha, &x->d_tau_inf};
+                  &x->d_score, &x->d_packed, &x->d_alpha, &x->d_tau_inf};
   for (DBuf* b : bufs) b->release();
   if (x->h_pool) (void)hipHostFree(x->h_pool);
   if (x->copy) (void)hipStreamDestroy(x->copy);
@@ -1167,7 +1167,8 @@ extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int3
   if (budget < 0) return fail(SEKV_EINVAL, "budget < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
-  if (budget > 0 && (st = ensure_route_scratch(x, lc, x->d_score))) return st;
+  if (budget > 0 && ((st = ensure_route_scratch(x, lc, x->d_score)) || (st = ensure_route_scratch(x, lc, x->d_packed))))
+    return st;
   RouteArgs ra{};
   ra.q = (const bf16_t*)q;
   ra.tau = tau;
@@ -1177,6 +1178,7 @@ extern "C" sekv_status sekv_route_pooled(sekv_ctx* c, const sekv_index* xc, int3
   ra.mask = mask;
   ra.alpha = alpha;
   ra.score = budget > 0 ? (float*)x->d_score.p : nullptr;
+  ra.packed = budget > 0 ? (uint32_t*)x->d_packed.p : nullptr;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = 0;
