@@ -515,7 +515,9 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
 //    ballots).  A sequence within its budget stops there.
 //  * Radix select of the budget-th largest key over the list, binned over the
 //    keys' own range (offsets key - min, at most 11 bits a pass from the top
-//    of max - min; the keys order like the scores).
+//    of max - min; the keys order like the scores); once the boundary bin
+//    holds at most kPoolRank keys they are ranked against each other instead
+//    of binned again.
 //  * Keep every larger key.  If the boundary key's equals are not all kept,
 //    their positions are ranked against each other and the lowest kept.
 // When the routed triples or the halves do not fit in LDS (or the boundary
@@ -526,6 +528,7 @@ constexpr int kPoolThreads = 1024;
 constexpr int kPoolBins = 2048;
 constexpr int kPoolList = 12288;    // routed triples held in LDS
 constexpr int kPoolHalves = 4096;   // 32-span halves of the new mask held in LDS
+constexpr int kPoolRank = 512;      // boundary bins up to this size are ranked directly
 
 // Block-wide inclusive scan over kPoolThreads threads; total = block sum.
 __device__ int block_scan_pool(int v, int* s_tmp, int& total) {
@@ -626,20 +629,24 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
   const uint64_t* mw = a.mask + (int64_t)b * rows * a.Wd;
   const uint4* pk = (const uint4*)(a.packed + (int64_t)b * rows * a.Wd * 64);
   auto append = [&](uint64_t bits, const uint4 (&kv)[8], int64_t w, int& pos) {
+    // four keys a step; the wave stops once none of its lanes has any left
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      if (bits) {
-        const int j = __builtin_ctzll(bits);
-        bits &= bits - 1;
-        const uint4 v = kv[k >> 2];
-        const uint32_t key = (k & 3) == 0 ? v.x : ((k & 3) == 1 ? v.y : ((k & 3) == 2 ? v.z : v.w));
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-        if (pos < kPoolList) {
-          s_key[pos] = key;
-          s_pos[pos] = (int32_t)(64 * w + j);
+    for (int q = 0; q < 8; ++q) {
+      if (__ballot(bits != 0ull) == 0ull) break;
+      const uint32_t vk[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bits) {
+          const int j = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          kmin = min(kmin, vk[e]);
+          kmax = max(kmax, vk[e]);
+          if (pos < kPoolList) {
+            s_key[pos] = vk[e];
+            s_pos[pos] = (int32_t)(64 * w + j);
+          }
+          ++pos;
         }
-        ++pos;
       }
     }
     // a word with more than 32 routed spans: the rest, four keys a load
@@ -706,6 +713,7 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
     const int nb = r ? 32 - __clz((int)r) : 0;
     uint32_t prefix = 0, pmask = 0;
     int ceq = total;   // keys equal to the selected one
+    bool ranked = false;
     for (int top = nb; top > 0; top -= 11) {
       const int shift = max(top - 11, 0), nbins = 1 << (top - shift);
       for (int i = tid; i < kPoolBins; i += kPoolThreads) s_hist[i] = 0;
@@ -721,8 +729,40 @@ __global__ __launch_bounds__(kPoolThreads) void route_pool_kernel(const RouteArg
       k = s_sel[1];
       ceq = s_sel[2];
       __syncthreads();
+      if (shift > 0 && ceq <= kPoolRank) {   // uniform
+        // a small boundary bin: its keys ranked against each other give the
+        // boundary key, its rank among equals and their count at once
+        if (tid == 0) s_count = 0;
+        __syncthreads();
+        for (int i = tid; i < total; i += kPoolThreads) {
+          const uint32_t o = s_key[i] - kmin;
+          if ((o & pmask) == prefix) s_hist[atomicAdd(&s_count, 1)] = s_key[i];
+        }
+        __syncthreads();
+        for (int i = tid; i < ceq; i += kPoolThreads) {
+          const uint32_t ki = s_hist[i];
+          int gt = 0, ge = 0;
+          for (int j = 0; j < ceq; ++j) {
+            const uint32_t kj = s_hist[j];
+            gt += kj > ki;
+            ge += kj >= ki;
+          }
+          if (gt < k && k <= ge) {   // every thread holding this key writes the same
+            s_sel[0] = (int)ki;
+            s_sel[1] = k - gt;
+            s_sel[2] = ge - gt;
+          }
+        }
+        __syncthreads();
+        ranked = true;
+        vstar = (uint32_t)s_sel[0];
+        k = s_sel[1];
+        ceq = s_sel[2];
+        __syncthreads();
+        break;
+      }
     }
-    vstar = kmin + prefix;
+    if (!ranked) vstar = kmin + prefix;
     // ---- keep: every larger key, and the k lowest-position equal keys
     bool done = false;
     if (k == ceq) {
