@@ -44,16 +44,20 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Loads of the streamed operands (resident rows and factor blobs, each read
-// once a step) carry the non-temporal hint, so that they do not push the
-// small shared tables (mask words, span metadata, partials) and the next
-// kernels' inputs out of L2 and the Infinity Cache (measured 763 -> 775
-// query-tokens/s at 128K; the asynchronous loads to LDS use the same hint,
-// cache-policy bit 2 of their last operand).
-template <class T>
+// once a step) carry the non-temporal hint when the index is larger than
+// the cache can hold across steps (NT), so that they do not push the small
+// shared tables (mask words, span metadata, partials) and the next kernels'
+// inputs out of L2 and the Infinity Cache (measured 763 -> 775
+// query-tokens/s at 128K).  A small index keeps plain loads: its layer stays
+// cache-resident from step to step.  The asynchronous loads to LDS take the
+// same hint as cache-policy bit 2 of their last operand.
+template <int NT, class T>
 __device__ __forceinline__ T ld_stream(const void* p) {
-  return __builtin_nontemporal_load((const T*)p);
+  if constexpr (NT) return __builtin_nontemporal_load((const T*)p);
+  else return *(const T*)p;
 }
-constexpr int kLdsStream = 2;
+template <int NT>
+constexpr int kLdsStream = NT ? 2 : 0;
 
 __device__ __forceinline__ floatx4 mfma32(u32x4 a, u32x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -144,7 +148,7 @@ __device__ __forceinline__ float online(floatx4 (&sc)[NB], int nb, float& m, flo
 // The blob holds nrk (nrv) 16-component blocks of key (value) factors, at most
 // R / 16 each: the registers are sized for R and the blocks past the stored
 // ones are neither loaded nor multiplied (wave-uniform branches).
-template <int D, int R>
+template <int D, int R, int NT>
 struct SpanRegs {
   static constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
   static constexpr int VV_BYTES = 2 * D * R;
@@ -180,7 +184,7 @@ struct SpanRegs {
     for (int ib = 0; ib < NR16; ++ib)
       if (ib < nrk)
 #pragma unroll
-        for (int s = 0; s < NS32; ++s) vkt[ib][s] = ld_stream<u32x4>(pk + ib * 16 * D + s * 512 + lane * 8);
+        for (int s = 0; s < NS32; ++s) vkt[ib][s] = ld_stream<NT, u32x4>(pk + ib * 16 * D + s * 512 + lane * 8);
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib) {
       if (ib < nrk) smk[ib] = *(const floatx4*)(sk + 16 * ib + 4 * grp);
@@ -192,7 +196,7 @@ struct SpanRegs {
       const int tbc = min(tb, ntb - 1);
 #pragma unroll
       for (int kb = 0; kb < NR16; ++kb)
-        if (kb < nrk) uk[tb][kb] = ld_stream<u32x2>(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
+        if (kb < nrk) uk[tb][kb] = ld_stream<NT, u32x2>(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
     }
 #pragma unroll
     for (int ib = 0; ib < NR16; ++ib)
@@ -200,14 +204,14 @@ struct SpanRegs {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
           const int tbc = min(tb, ntb - 1);
-          uvt[ib][tb] = ld_stream<u32x2>(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
+          uvt[ib][tb] = ld_stream<NT, u32x2>(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
         }
     // V^V: D rv bf16 = D nrv / 32 KB
 #pragma unroll
     for (int c = 0; c < VV_BYTES / 1024; ++c)
       if (c < D * nrv / 32)
         __builtin_amdgcn_global_load_lds((const void*)(pv + c * 1024 + lane * 16),
-                                         (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, kLdsStream);
+                                         (__attribute__((address_space(3))) void*)(lds_vv + c * 1024), 16, 0, kLdsStream<NT>);
     if (CK && ntb > 4) {   // wave-uniform
       // 512-byte blocks: U^K (tb, kb) at tb' nrk + kb, then U^V^T (ib, tb) at
       // 4 nrk + 4 ib + tb', tb' = tb - 4; blocks past the span re-read its
@@ -231,7 +235,7 @@ struct SpanRegs {
             src += (int64_t)(uv8 - b);
           }
           __builtin_amdgcn_global_load_lds((const void*)(b + src + (lane & 31) * 16),
-                                           (__attribute__((address_space(3))) void*)(lds_ck + c * 1024), 16, 0, kLdsStream);
+                                           (__attribute__((address_space(3))) void*)(lds_ck + c * 1024), 16, 0, kLdsStream<NT>);
         }
       }
     }
@@ -285,8 +289,8 @@ __device__ __forceinline__ void span_chunk(const u32x2 (&uk)[4][R / 16], const u
 }
 
 // Attention over one routed span in factored form, folded into (m, l, o).
-template <int D, int G, int R>
-__device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 (&qB)[D / 32], float scale,
+template <int D, int G, int R, int NT>
+__device__ __forceinline__ void span_pass(const SpanRegs<D, R, NT>& sr, const u32x4 (&qB)[D / 32], float scale,
                                           int lane, int hl, int grp, float& m, float& l,
                                           floatx4 (&o)[D / 16], const uint8_t* lds_vv, const uint8_t* lds_ck) {
   constexpr int NS32 = D / 32, ND16 = D / 16, NR16 = R / 16;
@@ -315,7 +319,7 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
     for (int tb0 = 4; tb0 < ntb; tb0 += 4) {
       const int nb = min(4, ntb - tb0);
       u32x2 uk[4][NR16], uvt[NR16][4];
-      if (SpanRegs<D, R>::CK && tb0 == 4) {
+      if (SpanRegs<D, R, NT>::CK && tb0 == 4) {
         // from the wave's LDS copy (wait for the wave's outstanding loads,
         // the asynchronous copies included)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -334,10 +338,10 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
           const int tbc = tb0 + min(tb, nb - 1);
 #pragma unroll
           for (int kb = 0; kb < NR16; ++kb)
-            if (kb < nrk) uk[tb][kb] = ld_stream<u32x2>(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
+            if (kb < nrk) uk[tb][kb] = ld_stream<NT, u32x2>(pu + ((int64_t)tbc * nrk + kb) * 256 + lane * 4);
 #pragma unroll
           for (int ib = 0; ib < NR16; ++ib)
-            if (ib < nrv) uvt[ib][tb] = ld_stream<u32x2>(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
+            if (ib < nrv) uvt[ib][tb] = ld_stream<NT, u32x2>(pw + ((int64_t)ib * ntb + tbc) * 256 + lane * 4);
         }
       }
       span_chunk<D, G, R>(uk, uvt, tb0, nb, n, act, grp, nrk, nrv, chi, clo, m, l, o, wacc);
@@ -370,7 +374,7 @@ __device__ __forceinline__ void span_pass(const SpanRegs<D, R>& sr, const u32x4 
 // here to the first fold is issued without a branch: the wait before the
 // fold then counts only the loads issued after this step's, which stay in
 // flight.
-template <int D, int G>
+template <int D, int G, int NT>
 struct ResStep {
   static constexpr int NS32 = D / 32, ND16 = D / 16;
   u32x4 kt[2][NS32], vt[ND16];
@@ -385,9 +389,9 @@ struct ResStep {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < NS32; ++s)
-        kt[kb][s] = ld_stream<u32x4>(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
+        kt[kb][s] = ld_stream<NT, u32x4>(Kb + (int64_t)(2 * t + kb) * 16 * D + s * 512 + lane * 8);
 #pragma unroll
-    for (int db = 0; db < ND16; ++db) vt[db] = ld_stream<u32x4>(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
+    for (int db = 0; db < ND16; ++db) vt[db] = ld_stream<NT, u32x4>(Vb + (int64_t)t * 32 * D + db * 512 + lane * 8);
     // pseudo-row inputs, loaded for every step (no branch, so that later
     // waits can count these loads); raw rows read span 0 and are masked
 #pragma unroll
@@ -465,7 +469,7 @@ __device__ __forceinline__ int wave_prefix_small(int c, int lane, int& total) {
 // the G heads' words, [(G + 1)][W] uint64.
 inline size_t attend_dyn_lds(int G, int W) { return (size_t)(G + 1) * W * sizeof(uint64_t); }
 
-template <int D, int G, int R>
+template <int D, int G, int R, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 16 ? 3 : (R <= 32 ? 2 : 1))))
 void attend_kernel(const AttendArgs a) {
   constexpr int NS32 = D / 32, ND16 = D / 16;
@@ -479,8 +483,8 @@ void attend_kernel(const AttendArgs a) {
   __shared__ int64_t s_woff[4][kMaxSpanList];
   __shared__ int32_t s_wn[4][kMaxSpanList];
   __shared__ int32_t s_wr[4][kMaxSpanList];   // stored ranks rk | rv << 16
-  __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R>::VV_BYTES];   // per wave
-  __shared__ __attribute__((aligned(16))) uint8_t s_ck[4][SpanRegs<D, R>::CK_BYTES];   // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t s_vv[4][SpanRegs<D, R, NT>::VV_BYTES];   // per wave
+  __shared__ __attribute__((aligned(16))) uint8_t s_ck[4][SpanRegs<D, R, NT>::CK_BYTES];   // per wave
   extern __shared__ uint64_t s_dyn[];
 
   const WorkItem it = a.items[blockIdx.x];
@@ -529,7 +533,7 @@ void attend_kernel(const AttendArgs a) {
   const bf16_t* Vb = a.vres + bm.res_base + lg * bm.n_res_pad * D;
   const uint64_t* mh = mrow + (int64_t)(hl < G ? hl : 0) * Wd;
   int t = it.step_begin + wave;
-  ResStep<D, G> rs;
+  ResStep<D, G, NT> rs;
   rs.load(Kb, Vb, mh, a.logn, bm, (it.step_begin < it.step_end) ? min(t, it.step_end - 1) : 0, lane, grp);
 
   // union of the G heads' mask words (bits at or past N_S(b) ignored,
@@ -652,10 +656,10 @@ void attend_kernel(const AttendArgs a) {
     const int nw = (int)__popcll(mine);
     for (int i = 0; i < nw; ++i) {
       const int nh = s_wn[wave][i];
-      SpanRegs<D, R> cur;
+      SpanRegs<D, R, NT> cur;
       cur.load(a.pool + uni64(s_woff[wave][i]), uni(nh & 0xffffff), uni((int)((uint32_t)nh >> 24)),
                uni(s_wr[wave][i]), lane, grp, s_vv[wave], s_ck[wave]);
-      span_pass<D, G, R>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave], s_ck[wave]);
+      span_pass<D, G, R, NT>(cur, qB, scale, lane, hl, grp, m, lsum, o, s_vv[wave], s_ck[wave]);
     }
   }
 
@@ -817,19 +821,50 @@ bool attend_supported(int D, int G, int R) {
          (R == 16 || R == 32 || R == 64) && R <= D;
 }
 
-hipError_t attend_slots(int D, int G, int R, int W, int device, int* slots) {
-  *slots = 0;
-  return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
+// Every instance the dispatch below can select, instantiated explicitly so
+// that each one's device code and host handle are emitted.
+#define SEKV_INST_ATTEND(D, G, R)                                        \
+  template __global__ void attend_kernel<D, G, R, 0>(const AttendArgs); \
+  template __global__ void attend_kernel<D, G, R, 1>(const AttendArgs);
+#define SEKV_INST_ATTEND_G(D, G) SEKV_INST_ATTEND(D, G, 16) SEKV_INST_ATTEND(D, G, 32) SEKV_INST_ATTEND(D, G, 64)
+SEKV_INST_ATTEND_G(64, 1) SEKV_INST_ATTEND_G(64, 2) SEKV_INST_ATTEND_G(64, 4) SEKV_INST_ATTEND_G(64, 8)
+SEKV_INST_ATTEND_G(128, 1) SEKV_INST_ATTEND_G(128, 2) SEKV_INST_ATTEND_G(128, 4) SEKV_INST_ATTEND_G(128, 8)
+#undef SEKV_INST_ATTEND_G
+#undef SEKV_INST_ATTEND
+
+// Host handles of the two streaming flavours of the attention kernel for
+// (D, G, R): [0] plain loads, [1] non-temporal.  Every host use goes through
+// this one place that names each instance (a kernel instance named from a
+// second host function template failed to compile or to link with this
+// toolchain).
+struct AttendKernels {
+  const void* fn[2];
+};
+AttendKernels attend_kernels(int D, int G, int R) {
+  AttendKernels out{{nullptr, nullptr}};
+  (void)dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
-    int per_cu = 0, cus = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_kernel<D_, G_, R_>, 256,
-                                                                attend_dyn_lds(G_, W));
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-    if (e != hipSuccess) return e;
-    *slots = per_cu * cus;
+    auto cached = attend_kernel<D_, G_, R_, 0>;
+    auto streamed = attend_kernel<D_, G_, R_, 1>;
+    out.fn[0] = (const void*)cached;
+    out.fn[1] = (const void*)streamed;
     return hipSuccess;
   });
+  return out;
+}
+
+hipError_t attend_slots(int D, int G, int R, int W, int device, int* slots) {
+  *slots = 0;
+  const AttendKernels k = attend_kernels(D, G, R);
+  if (!k.fn[1]) return hipErrorInvalidValue;
+  // both flavours use the same registers and LDS
+  int per_cu = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k.fn[1], 256, attend_dyn_lds(G, W));
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  *slots = per_cu * cus;
+  return hipSuccess;
 }
 
 hipError_t launch_merge(const MergeArgs& a, int D, int G, hipStream_t st) {
@@ -845,24 +880,27 @@ hipError_t launch_attend(const AttendArgs& a, int D, int G, int R, hipStream_t s
                          hipEvent_t ev_stop) {
   if (a.W > 1024 || a.lc_first < 0 || a.lc_count < 1 || a.lc_first + a.lc_count > a.layer_count)
     return hipErrorInvalidValue;
-  return dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
+  size_t fixed = 0;
+  const hipError_t e0 = dispatch(D, G, R, [&](auto d_, auto g_, auto r_) -> hipError_t {
     constexpr int D_ = decltype(d_)::value, G_ = decltype(g_)::value, R_ = decltype(r_)::value;
-    auto kern = attend_kernel<D_, G_, R_>;
-    const size_t dyn = attend_dyn_lds(G_, a.W);
-    constexpr size_t fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * 20 * kMaxSpanList +
-                             4 * (SpanRegs<D_, R_>::VV_BYTES + SpanRegs<D_, R_>::CK_BYTES);
-    if (fixed + dyn > 160 * 1024) return hipErrorInvalidValue;
-    if (dyn > 32 * 1024) {
-      const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-      if (e != hipSuccess) return e;
-    }
-    if (ev_start)
-      hipExtLaunchKernelGGL(kern, dim3(a.n_items, a.lc_count), dim3(256), (uint32_t)dyn, st, ev_start, ev_stop, 0u,
-                            a);
-    else
-      hipLaunchKernelGGL(kern, dim3(a.n_items, a.lc_count), dim3(256), dyn, st, a);
-    return hipGetLastError();
+    fixed = sizeof(float) * (4 * 2 * G_ + 4 * G_ * D_) + 4 * 20 * kMaxSpanList +
+            4 * (SpanRegs<D_, R_, 1>::VV_BYTES + SpanRegs<D_, R_, 1>::CK_BYTES);
+    return hipSuccess;
   });
+  if (e0 != hipSuccess) return e0;
+  const size_t dyn = attend_dyn_lds(G, a.W);
+  if (fixed + dyn > 160 * 1024) return hipErrorInvalidValue;
+  const void* kern = attend_kernels(D, G, R).fn[a.stream ? 1 : 0];
+  if (!kern) return hipErrorInvalidValue;
+  if (dyn > 32 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+  }
+  AttendArgs arg = a;
+  void* args[] = {&arg};
+  if (ev_start)
+    return hipExtLaunchKernel(kern, dim3(a.n_items, a.lc_count), dim3(256), args, dyn, st, ev_start, ev_stop, 0);
+  return hipLaunchKernel(kern, dim3(a.n_items, a.lc_count), dim3(256), args, dyn, st);
 }
 
 }  // namespace sekv

@@ -150,6 +150,9 @@ struct AttendArgs {
   int32_t lc_first, lc_count;   // this launch: layers [lc_first, lc_first + lc_count) of the call
   int32_t B, L, Hq, Hkv, W, max_spans;
   float scale;              // 1/sqrt(d)
+  int32_t stream;           // 1: the streamed operands (resident rows, factor
+                            // blobs) are loaded with the non-temporal hint
+                            // (chooses the kernel instance on the host)
 };
 
 struct MergeArgs {
@@ -177,6 +180,8 @@ struct RouteArgs {
   int32_t layer_begin, layer_count;
   int32_t B, L, Hq, Hkv, D, dp, Wd, cap;
   int32_t budget;           // pooled budget per sequence (route_pool_kernel)
+  int32_t stream;           // 1: the summary keys are loaded with the
+                            // non-temporal hint (chooses the kernel instance)
 };
 
 struct CalibArgs {

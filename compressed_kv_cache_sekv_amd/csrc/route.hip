@@ -96,21 +96,26 @@ __device__ uint32_t radix_select(int n, int& k, Cand cand, uint32_t* s_hist, int
   return prefix;
 }
 
-// The summary keys are streamed once a step: their loads carry the
-// non-temporal hint so that they do not evict the cached tables of the
-// kernels that follow (with the attention kernel's streamed loads, 775 ->
-// 798 query-tokens/s at 128K).
+// The summary keys are streamed once a step: on an index larger than the
+// cache holds across steps (NT) their loads carry the non-temporal hint, so
+// that they do not evict the cached tables of the kernels that follow (with
+// the attention kernel's streamed loads, 775 -> 798 query-tokens/s at 128K).
+template <bool NT>
 __device__ __forceinline__ float4 load_stream4(const float* p) {
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
-  return make_float4(v.x, v.y, v.z, v.w);
+  if constexpr (NT) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+  } else {
+    return *(const float4*)p;
+  }
 }
 
 // Summary-key dimensions held in registers per lane (d' <= kMaxDp; entries
 // past d' are zero, and s_u is zero there, so they add nothing).
 constexpr int kMaxDp = 64;
 
-template <int D, int NW>
+template <int D, int NW, bool NT>
 __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   __shared__ float s_u[kMaxDp];
   __shared__ double s_thr;
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
     const float* sp = a.s + bm.s_base + ((int64_t)l * a.Hq + h) * d4 * bm.s_pad;
     const int Sc = live ? S : 0;
 #pragma unroll
-    for (int k = 0; k < kMaxDp / 4; ++k) v4[k] = load_stream4(sp + skey_index(Sc, 4 * min(k, (d4 >> 2) - 1), d4));
+    for (int k = 0; k < kMaxDp / 4; ++k) v4[k] = load_stream4<NT>(sp + skey_index(Sc, 4 * min(k, (d4 >> 2) - 1), d4));
   }
   // logit(tau) once per workgroup, by one lane, while the loads are in flight
   if (threadIdx.x == 0) s_thr = logit_threshold(tau_h);
@@ -895,8 +900,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
   const int nchunk = (a.Wd + NW - 1) / NW;
   const int nbh8 = (a.B * a.Hq + 7) / 8;
   const dim3 grid(nbh8 * 8 * nchunk, a.layer_count);
-  if (a.D == 128) hipLaunchKernelGGL((route_kernel<128, NW>), grid, dim3(64 * NW), 0, st, a);
-  else if (a.D == 64) hipLaunchKernelGGL((route_kernel<64, NW>), grid, dim3(64 * NW), 0, st, a);
+  if (a.D == 128 && a.stream) hipLaunchKernelGGL((route_kernel<128, NW, true>), grid, dim3(64 * NW), 0, st, a);
+  else if (a.D == 128) hipLaunchKernelGGL((route_kernel<128, NW, false>), grid, dim3(64 * NW), 0, st, a);
+  else if (a.D == 64 && a.stream) hipLaunchKernelGGL((route_kernel<64, NW, true>), grid, dim3(64 * NW), 0, st, a);
+  else if (a.D == 64) hipLaunchKernelGGL((route_kernel<64, NW, false>), grid, dim3(64 * NW), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
