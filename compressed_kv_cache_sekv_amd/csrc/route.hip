@@ -205,8 +205,8 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
   if (lane == 0) mrow[wi] = word;
   if (arow) arow[S] = alpha;
   if (srow) srow[S] = dot;
-  // the routed spans' keys, packed per word in span order (the pooled budget
-  // then touches only the routed spans)
+  // the routed spans' keys, packed per word in span order (the budget
+  // kernels then touch only the routed spans)
   if (a.packed && z) a.packed[(row * a.Wd + wi) * 64 + __popcll(word & ((1ull << lane) - 1))] = order_key(dot);
 }
 
@@ -216,9 +216,10 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(const RouteArgs a) {
 // score, complemented span index): the key order is score descending then
 // index ascending, and keys are distinct, so the kept set is exactly the keys
 // at or above the cap-th largest key K*.
-//  * Collect: thread t takes spans 32t .. 32t+31 (half a mask word and eight
-//    16-byte alpha loads, all issued together); a block scan of the per-thread
-//    counts places the candidates in LDS in span order.
+//  * Collect: thread t takes mask word t and its first 32 packed keys (eight
+//    16-byte loads, all issued together; the routing kernel packs the routed
+//    spans' keys of each word); a block scan of the per-thread counts places
+//    the candidates in LDS in span order.
 //  * Select: one histogram of the score keys over the candidates' own range
 //    (1024 bins by a shift of (key - min); the keys order like the scores, so
 //    the binning is monotone) finds the bin holding K* and how many of its
@@ -364,31 +365,56 @@ __global__ __launch_bounds__(256) void route_cap_kernel(const RouteArgs a) {
   const float* arow = a.score + row * (int64_t)a.Wd * 64;
   for (int w = tid; w < a.Wd; w += 256) s_new[w] = 0ull;
   if (tid == 0) s_nb = 0;
-  // collect (mask bits at or past N_S are 0, so their alpha is never used)
-  const int nh = 2 * a.Wd;
+  // collect (mask bits at or past N_S are 0, so their scores are never
+  // used): thread t takes mask word t with its first 32 packed keys (the
+  // routing kernel packed the routed spans' keys in span order), a block
+  // scan of the counts places the candidates in LDS in span order
+  const uint4* pk = (const uint4*)(a.packed + row * (int64_t)a.Wd * 64);
   int nc = 0;
   uint32_t lo = 0xffffffffu, hi = 0u;
   int par = 0;
-  for (int base = 0; base < nh; base += 256, par ^= 1) {
-    const int t = min(base + tid, nh - 1);
-    const uint64_t word = mrow[t >> 1];
-    const float4* ap = (const float4*)(arow + 32 * (int64_t)t);
-    float4 av[8];
+  for (int base = 0; base < a.Wd; base += 256, par ^= 1) {
+    const int w = min(base + tid, a.Wd - 1);
+    uint64_t bits = mrow[w];
+    uint4 kv[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) av[k] = ap[k];
-    const uint32_t bits = (base + tid < nh) ? (uint32_t)(word >> (32 * (t & 1))) : 0u;
-    const int c = __popc(bits);
+    for (int i = 0; i < 8; ++i) kv[i] = pk[w * 16 + i];
+    if (base + tid >= a.Wd) bits = 0ull;
+    const int c = __popcll(bits);
     int total;
-    const int incl = block_scan_small<6>(c, s_tmp + 4 * par, total);
+    const int incl = block_scan_small<7>(c, s_tmp + 4 * par, total);
     int pos = nc + incl - c;
+    auto put = [&](uint32_t key, int j) {
+      if (pos < kCapList) s_cand[pos] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(64 * w + j));
+      ++pos;
+      lo = min(lo, key);
+      hi = max(hi, key);
+    };
+    // four keys a step; the wave stops once none of its lanes has any left
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((bits >> j) & 1u) {
-        const uint32_t ab = order_key(f4_at(av[j >> 2], j & 3));
-        if (pos < kCapList) s_cand[pos] = ((uint64_t)ab << 32) | (uint64_t)(~(uint32_t)(32 * t + j));
-        ++pos;
-        lo = min(lo, ab);
-        hi = max(hi, ab);
+    for (int q = 0; q < 8; ++q) {
+      if (__ballot(bits != 0ull) == 0ull) break;
+      const uint32_t vk[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bits) {
+          const int j = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          put(vk[e], j);
+        }
+      }
+    }
+    // a word with more than 32 routed spans: the rest, four keys a load
+    for (int k = 32; bits; k += 4) {
+      const uint4 v = pk[w * 16 + (k >> 2)];
+      const uint32_t vk[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bits) {
+          const int j = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          put(vk[e], j);
+        }
       }
     }
     nc += total;

@@ -1147,7 +1147,8 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   if (cap < 0) return fail(SEKV_EINVAL, "cap < 0");
   if (alpha && ((uintptr_t)alpha & 15)) return fail(SEKV_EINVAL, "alpha must be 16-byte aligned");
   if ((st = set_device(c))) return st;
-  if (cap > 0 && (st = ensure_route_scratch(x, lc, x->d_score))) return st;
+  if (cap > 0 && ((st = ensure_route_scratch(x, lc, x->d_score)) || (st = ensure_route_scratch(x, lc, x->d_packed))))
+    return st;
   RouteArgs ra{};
   ra.q = (const bf16_t*)q;
   ra.tau = tau;
@@ -1157,6 +1158,7 @@ extern "C" sekv_status sekv_route(sekv_ctx* c, const sekv_index* xc, int32_t lb,
   ra.mask = mask;
   ra.alpha = alpha;
   ra.score = cap > 0 ? (float*)x->d_score.p : nullptr;
+  ra.packed = cap > 0 ? (uint32_t*)x->d_packed.p : nullptr;
   ra.layer_begin = lb; ra.layer_count = lc;
   ra.B = x->B; ra.L = x->L; ra.Hq = x->Hq; ra.Hkv = x->Hkv; ra.D = x->D; ra.dp = x->dp; ra.Wd = x->Wd;
   ra.cap = cap;
