@@ -50,7 +50,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // inputs out of L2 and the Infinity Cache (measured 763 -> 775
 // query-tokens/s at 128K).  A small index keeps plain loads: its layer stays
 // cache-resident from step to step.  The asynchronous loads to LDS take the
-// same hint as cache-policy bit 2 of their last operand.
+// same hint as the cache-policy operand value 2 (the non-temporal bit).
 template <int NT, class T>
 __device__ __forceinline__ T ld_stream(const void* p) {
   if constexpr (NT) return __builtin_nontemporal_load((const T*)p);
