@@ -469,6 +469,18 @@ __device__ __forceinline__ int wave_prefix_small(int c, int lane, int& total) {
 // the G heads' words, [(G + 1)][W] uint64.
 inline size_t attend_dyn_lds(int G, int W) { return (size_t)(G + 1) * W * sizeof(uint64_t); }
 
+// Work split of the merge: DSPLIT workgroups per (b, g), each taking DS of
+// the D dims of all G heads, NPL outputs per lane.  A partial (one work
+// item's G heads) is stored as o[DSPLIT][G][DS] followed by (m, l) of each
+// head, so that a merge workgroup reads its slice of every head as one
+// contiguous run and the (m, l) of all heads from one line.
+template <int D, int G>
+struct MergeShape {   // lane layout of the merge
+  static constexpr int DSPLIT = (G * D >= 64) ? G * D / 64 : 1;
+  static constexpr int DS = D / DSPLIT;            // dims per workgroup
+  static constexpr int NPL = G * DS / 64;          // outputs per lane (1 or 2)
+};
+
 template <int D, int G, int R, int NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R <= 16 ? 3 : (R <= 32 ? 2 : 1))))
 void attend_kernel(const AttendArgs a) {
@@ -677,8 +689,10 @@ void attend_kernel(const AttendArgs a) {
   __syncthreads();
   const int64_t pstride = (int64_t)G * (D + 2);
   float* part = a.part + ((int64_t)lc * a.n_items + it.slot) * pstride;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, dim = idx - h * D;
+  constexpr int DS = MergeShape<D, G>::DS;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {   // idx: position in o[DSPLIT][G][DS]
+    const int zs = idx / (G * DS), rem = idx - zs * (G * DS);
+    const int h = rem / DS, dim = zs * DS + (rem - h * DS);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][h]);
@@ -690,10 +704,10 @@ void attend_kernel(const AttendArgs a) {
       O += e * s_o[w][h][dim];
       L += e * s_ml[w][1][h];
     }
-    part[h * (D + 2) + dim] = O;
+    part[idx] = O;
     if (dim == 0) {
-      part[h * (D + 2) + D] = M;
-      part[h * (D + 2) + D + 1] = L;
+      part[G * D + 2 * h] = M;
+      part[G * D + 2 * h + 1] = L;
     }
   }
 
@@ -706,12 +720,6 @@ void attend_kernel(const AttendArgs a) {
 // partials into a running (max, denominator, sum) with every load of a
 // 24-partial chunk issued before any use, and the four wave states are
 // combined in LDS.  grid (B * Hkv * DSPLIT, Lc).
-template <int D, int G>
-struct MergeShape {   // lane layout of the merge
-  static constexpr int DSPLIT = (G * D >= 64) ? G * D / 64 : 1;
-  static constexpr int DS = D / DSPLIT;            // dims per workgroup
-  static constexpr int NPL = G * DS / 64;          // outputs per lane (1 or 2)
-};
 
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
@@ -729,7 +737,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int P = a.bg_first[2 * bg + 1];
   const int64_t pstride = (int64_t)G * (D + 2);
   const float* base = a.part + ((int64_t)lc * a.n_items + first) * pstride;
-  const int o0 = lane * NPL, h = o0 / DS, dim = z * DS + (o0 - h * DS);
+  const int o0 = lane * NPL, h = o0 / DS;   // this lane: head h, dim z * DS + o0 - h * DS
   // online merge over this wave's partials i = wave (mod 4), CH at a time
   float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int c0 = wave; c0 < P; c0 += 4 * CH) {
@@ -739,16 +747,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
       // branch-free: partials past P re-read partial P - 1 and are ignored
       const int i = c0 + 4 * c;
       const bool ok = i < P;
-      const float* p = base + min(i, P - 1) * pstride + h * (D + 2);
-      const float2 ml = *(const float2*)(p + D);
+      const float* p = base + min(i, P - 1) * pstride;
+      const float2 ml = *(const float2*)(p + G * D + 2 * h);
       mv[c] = ok ? ml.x : -INFINITY;
       lv[c] = ok ? ml.y : 0.f;
+      const float* po = p + z * (G * DS) + o0;   // this workgroup's slice, lane o0
       if (NPL == 2) {
-        const float2 v = *(const float2*)(p + dim);
+        const float2 v = *(const float2*)po;
         v0[c] = ok ? v.x : 0.f;
         v1[c] = ok ? v.y : 0.f;
       } else {
-        v0[c] = ok ? p[dim] : 0.f;
+        v0[c] = ok ? po[0] : 0.f;
         v1[c] = 0.f;
       }
     }
