@@ -226,6 +226,30 @@ def test_bench_path_32_layers_128k(ctx, sl):
     idx.free()
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_bench_path_128k_other_seeds(ctx, sl, seed):
+    """The same 32-layer 128K workload and per-layer call pattern under other
+    seeds (new cache, surprisal, projections, queries and SVD test
+    matrices); layers 0, 13 and 31 checked against the oracle routing and
+    decoding the library's exported index of each.  The index is larger
+    than half the Infinity Cache, so this runs the non-temporal flavour of
+    the kernels."""
+    w = synth.WORKLOADS["llama8b_l32_128k"].scaled(tier="hbm", seed=seed)
+    H, K, V = synth.kv_cache(w, device="cuda")
+    W = torch.stack([synth.routing_w(w, l, "cuda") for l in range(w.L)])
+    idx = ctx.build_index(sl.build_params(w, tier=sl.TIER_HBM), K, V, H, W, None)
+    del H, K, V
+    tau = torch.zeros(w.L, w.Hq, device="cuda")
+    idx.calibrate_tau(0, w.L, synth.calibration_query(w, "cuda"), w.frac, tau)
+    cap = int(math.floor(w.cap_frac * int(idx.n_spans.min())))
+    q = synth.query(w, 11)
+    words, out = _bench_loop(idx, w, q, tau.cpu().numpy(), cap)
+    worst = check_layers_against_export(idx, w, W, q, tau.cpu().numpy(), cap, words, out, [0, 13, 31],
+                                        f"bench path 128k seed {seed}")
+    print(f"[bench path 128k seed {seed}] worst rel-L2 {worst:.3e}", flush=True)
+    idx.free()
+
+
 def _tau_for(score, frac):
     """alpha threshold midway (in score) between the k-th and (k+1)-th largest
     score, k = round(frac * N), as an fp32 value."""
